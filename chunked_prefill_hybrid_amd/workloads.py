@@ -1,0 +1,251 @@
+"""Seeded synthetic workloads for the hybrid-batch decoder layer.
+
+A hybrid batch is one prefill chunk of C tokens plus B single-token decodes, each decode with its own
+KV cache ("decode-maximal batching", SARATHI: Efficient LLM Inference by Piggybacking Decodes with
+Chunked Prefills, section 3 "Decode-Maximal Batching").  This module holds the five layer shapes and
+batch compositions the library is measured and checked on, and a seeded generator of host arrays:
+weights, hidden states, KV caches and lengths.
+
+None of the layer's arithmetic lives here.  The HIP path and the CPU oracle both consume these arrays
+as they are; the only numeric step is rounding the drawn values to bfloat16 (round to nearest even)
+for the bf16 workloads, so that both sides see identical, exactly representable inputs.
+
+Draw order (fixed, so that every sweep point of one shape shares its weights): W_qkv, W_o, W_gate,
+W_up, W_down, then X, then the chunk request's prefix cache (K then V), then the decode lengths, then
+each decode cache in request order (K then V).
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "LayerShape", "BatchSpec", "Workload", "SHAPES", "bf16_round", "bf16_bits",
+    "make_weights", "make_batch", "workload", "sweep", "tiny_schedule", "WORKLOADS",
+]
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    """One decoder layer's shape.  arch 'llama': RMSNorm, RoPE, SwiGLU FFN.  arch 'gpt': LayerNorm,
+    no RoPE, GELU MLP.  w_std is the standard deviation of the weight draws; None means
+    1/sqrt(fan_in) per matrix (fan_in = the matrix's input width)."""
+    name: str
+    arch: str
+    hidden: int
+    n_heads: int
+    head_dim: int
+    ffn: int
+    dtype: str               # 'f32' or 'bf16': storage type of weights, activations and caches
+    norm_eps: float
+    rope_base: float
+    w_std: Optional[float]
+
+    @property
+    def attn_width(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def gated(self) -> bool:
+        return self.arch == "llama"
+
+    def n_params(self) -> int:
+        h, a, f = self.hidden, self.attn_width, self.ffn
+        return 3 * a * h + h * a + (2 if self.gated else 1) * f * h + h * f
+
+
+@dataclass(frozen=True)
+class BatchSpec:
+    """Composition of one hybrid batch.  Rows 0..C-1 are the chunk at positions offset..offset+C-1 of
+    a prompt of prompt_len tokens; row C+i is decode i at position decode_len[i] (its cache already
+    holds decode_len[i] entries).  decode_lens fixes the lengths; otherwise they are drawn uniformly
+    from the closed range decode_len_range."""
+    chunk_len: int
+    chunk_offset: int
+    prompt_len: int
+    n_decodes: int
+    decode_lens: Optional[Tuple[int, ...]] = None
+    decode_len_range: Optional[Tuple[int, int]] = None
+
+
+SHAPES = {
+    "tiny": LayerShape("tiny-llama", "llama", 256, 4, 64, 688, "f32", 1e-6, 10000.0, None),
+    "llama13b": LayerShape("llama-13b", "llama", 5120, 40, 128, 13824, "bf16", 1e-6, 10000.0, 0.02),
+    "llama33b": LayerShape("llama-33b", "llama", 6656, 52, 128, 17920, "bf16", 1e-6, 10000.0, 0.02),
+    "gpt3tp8": LayerShape("gpt3-175b-tp8-shard", "gpt", 12288, 12, 128, 6144, "bf16", 1e-5, 10000.0, 0.02),
+}
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    shape: LayerShape
+    batch: BatchSpec
+    seed: int = 0
+    note: str = ""
+
+
+WORKLOADS = {
+    # Tiny fp32 layer; the 128-token prompt runs as 4 chunks of 32 (see tiny_schedule); this entry is
+    # the first of those steps.
+    "tiny": Workload("tiny", SHAPES["tiny"], BatchSpec(32, 0, 128, 4, decode_lens=(17, 33, 64, 100))),
+    "llama13b": Workload("llama13b", SHAPES["llama13b"],
+                         BatchSpec(256, 768, 1024, 18, decode_lens=(1024,) * 18)),
+    "llama33b": Workload("llama33b", SHAPES["llama33b"],
+                         BatchSpec(512, 0, 512, 32, decode_len_range=(256, 2048))),
+    "gpt3tp8": Workload("gpt3tp8", SHAPES["gpt3tp8"],
+                        BatchSpec(256, 0, 256, 64, decode_lens=(2048,) * 64)),
+    "llama13b_long": Workload("llama13b_long", SHAPES["llama13b"],
+                              BatchSpec(512, 7680, 8192, 48, decode_len_range=(2048, 8192))),
+}
+
+
+def workload(key: str, **batch_changes) -> Workload:
+    """A named workload, optionally with fields of its BatchSpec replaced (sweep points)."""
+    w = WORKLOADS[key]
+    if batch_changes:
+        w = dataclasses.replace(w, batch=dataclasses.replace(w.batch, **batch_changes))
+    return w
+
+
+def sweep(key: str) -> List[Workload]:
+    """Sweep points of a workload: the hybrid batch, its chunk-only (B=0) and decode-only (C=0) parts,
+    and the C or B sweep the workload is measured on."""
+    w = WORKLOADS[key]
+    b = w.batch
+    pts: List[Workload] = [w, workload(key, n_decodes=0, decode_lens=() if b.decode_lens else None),
+                           workload(key, chunk_len=0)]
+    if key == "llama33b":
+        for c in (128, 256, 257):
+            pts.append(workload(key, chunk_len=c, prompt_len=max(c, 1)))
+    if key == "gpt3tp8":
+        for nd in (1, 2, 4, 8, 16, 32):
+            pts.append(workload(key, n_decodes=nd, decode_lens=(2048,) * nd))
+    return pts
+
+
+# ----------------------------------------------------------------------------------------------
+# bfloat16 rounding of the drawn values (input preparation only)
+# ----------------------------------------------------------------------------------------------
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Bit patterns (uint16) of x rounded to bfloat16 with round-to-nearest-even.  x must be finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """x rounded to the nearest bfloat16 (ties to even), returned as float32."""
+    b = bf16_bits(x).astype(np.uint32) << 16
+    return b.view(np.float32).reshape(np.shape(x))
+
+
+def _finish(a: np.ndarray, dtype: str) -> np.ndarray:
+    a = a.astype(np.float32, copy=False)
+    return bf16_round(a) if dtype == "bf16" else a
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return _finish(a, dtype)
+
+
+def make_weights(shape: LayerShape, rng: np.random.Generator) -> dict:
+    """Layer weights, each stored [out_features, in_features] (y = x @ W.T).  W_qkv's rows are
+    [Q | K | V], each block head-major.  Norm gains are 1 and biases 0 (none are drawn)."""
+    h, a, f = shape.hidden, shape.attn_width, shape.ffn
+
+    def std(fan_in):
+        return shape.w_std if shape.w_std is not None else 1.0 / np.sqrt(fan_in)
+
+    w = {}
+    w["w_qkv"] = _normal(rng, (3 * a, h), std(h), shape.dtype)
+    w["w_o"] = _normal(rng, (h, a), std(a), shape.dtype)
+    w["w_gate"] = _normal(rng, (f, h), std(h), shape.dtype) if shape.gated else None
+    w["w_up"] = _normal(rng, (f, h), std(h), shape.dtype)
+    w["w_down"] = _normal(rng, (h, f), std(f), shape.dtype)
+    w["norm1_w"] = np.ones(h, np.float32)
+    w["norm2_w"] = np.ones(h, np.float32)
+    w["norm1_b"] = np.zeros(h, np.float32) if shape.arch == "gpt" else None
+    w["norm2_b"] = np.zeros(h, np.float32) if shape.arch == "gpt" else None
+    return w
+
+
+def _cache(rng, shape: LayerShape, cap: int, filled: int, fill_rest: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One request's K and V caches, each [n_heads, cap, head_dim]; slots 0..filled-1 hold N(0,1)
+    draws (K first, then V), the remaining slots hold fill_rest."""
+    nh, d = shape.n_heads, shape.head_dim
+    out = []
+    for _ in range(2):
+        c = np.full((nh, cap, d), fill_rest, np.float32)
+        if filled:
+            c[:, :filled, :] = _normal(rng, (nh, filled, d), 1.0, shape.dtype)
+        out.append(c)
+    return out[0], out[1]
+
+
+def make_batch(shape: LayerShape, spec: BatchSpec, rng: np.random.Generator,
+               fill_rest: float = 0.0) -> dict:
+    """Hidden states and caches of one hybrid batch (drawn after the weights from the same rng).
+
+    The chunk request's cache has capacity prompt_len (at least offset+C) and holds N(0,1) entries in
+    its prefix slots 0..offset-1.  Decode i's cache has capacity decode_len[i]+1 and holds N(0,1)
+    entries in slots 0..decode_len[i]-1.  Unwritten slots hold fill_rest (tests use NaN there to
+    catch reads past a request's keys)."""
+    C, B = spec.chunk_len, spec.n_decodes
+    x = _normal(rng, (C + B, shape.hidden), 1.0, shape.dtype)
+    cap = max(spec.prompt_len, spec.chunk_offset + C, 1)
+    ck, cv = _cache(rng, shape, cap, spec.chunk_offset, fill_rest)
+    if spec.decode_lens is not None:
+        lens = list(spec.decode_lens)[:B]
+        assert len(lens) == B, "decode_lens must list one length per decode"
+    elif B:
+        lo, hi = spec.decode_len_range
+        lens = [int(v) for v in rng.integers(lo, hi, size=B, endpoint=True)]
+    else:
+        lens = []
+    dk, dv = [], []
+    for L in lens:
+        k, v = _cache(rng, shape, L + 1, L, fill_rest)
+        dk.append(k)
+        dv.append(v)
+    return {"x": x, "chunk_len": C, "chunk_offset": spec.chunk_offset, "chunk_k": ck, "chunk_v": cv,
+            "decode_len": lens, "decode_k": dk, "decode_v": dv}
+
+
+def generate(w: Workload, fill_rest: float = 0.0) -> Tuple[dict, dict]:
+    """(weights, batch) of a workload, drawn from default_rng(seed) in the fixed order."""
+    rng = np.random.default_rng(w.seed)
+    weights = make_weights(w.shape, rng)
+    batch = make_batch(w.shape, w.batch, rng, fill_rest)
+    return weights, batch
+
+
+def tiny_schedule(seed: int = 0, n_chunks: int = 4, chunk: int = 32,
+                  decode_lens: Sequence[int] = (17, 33, 64, 100), fill_rest: float = 0.0):
+    """The tiny fp32 workload as a sequence of hybrid steps over one 128-token prompt.
+
+    Step k holds prompt rows k*chunk..k*chunk+chunk-1 (chunk offset k*chunk) plus the same decodes at
+    lengths decode_lens[i]+k, each with a fresh N(0,1) hidden row per step.  The prompt cache starts
+    empty (the layer fills it chunk by chunk); decode caches start with decode_lens[i] N(0,1)
+    entries and capacity decode_lens[i]+n_chunks.
+
+    Returns (shape, weights, prompt_x [n_chunks*chunk, H], decode_x [n_chunks, B, H],
+    decode_k, decode_v, decode_lens)."""
+    shape = SHAPES["tiny"]
+    rng = np.random.default_rng(seed)
+    weights = make_weights(shape, rng)
+    prompt_x = _normal(rng, (n_chunks * chunk, shape.hidden), 1.0, shape.dtype)
+    dk, dv = [], []
+    for L in decode_lens:
+        k, v = _cache(rng, shape, L + n_chunks, L, fill_rest)
+        dk.append(k)
+        dv.append(v)
+    decode_x = _normal(rng, (n_chunks, len(decode_lens), shape.hidden), 1.0, shape.dtype)
+    return shape, weights, prompt_x, decode_x, dk, dv, list(decode_lens)
