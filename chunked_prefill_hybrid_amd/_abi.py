@@ -1,0 +1,171 @@
+"""ctypes binding of libsarathi.so (the C ABI of include/sarathi.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP kernels.  Functions keep
+the C names (sarathi_layer_create, sarathi_layer_forward, ...).  Loading fails loudly when the
+library has not been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_float, c_int32, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsarathi.so")
+
+SARATHI_OK = 0
+SARATHI_ERR_INVALID = -1
+SARATHI_ERR_UNSUPPORTED = -2
+SARATHI_ERR_CAPACITY = -3
+SARATHI_ERR_HIP = -4
+SARATHI_ERR_NOMEM = -5
+SARATHI_ERR_WORKSPACE = -6
+SARATHI_ERR_INTERNAL = -7
+
+SARATHI_F32 = 0
+SARATHI_BF16 = 1
+SARATHI_ARCH_LLAMA = 0
+SARATHI_ARCH_GPT = 1
+
+EXPORTED = [
+    "sarathi_layer_create", "sarathi_layer_destroy", "sarathi_batch_check", "sarathi_workspace_size",
+    "sarathi_layer_forward", "sarathi_layer_forward_debug", "sarathi_gemm", "sarathi_attention",
+    "sarathi_status_str", "sarathi_last_error",
+]
+
+
+class sarathi_layer_desc(ctypes.Structure):
+    _fields_ = [("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32), ("ffn", c_int32),
+                ("arch", c_int32), ("dtype", c_int32), ("norm_eps", c_float), ("rope_base", c_float),
+                ("max_tokens", c_int32), ("max_pos", c_int32)]
+
+
+class sarathi_weights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("w_qkv", "w_o", "w_gate", "w_up", "w_down",
+                                        "norm1_w", "norm1_b", "norm2_w", "norm2_b")]
+
+
+class sarathi_kv(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("capacity", c_int32), ("reserved", c_int32)]
+
+
+class sarathi_batch(ctypes.Structure):
+    _fields_ = [("chunk_len", c_int32), ("chunk_offset", c_int32), ("chunk_kv", sarathi_kv),
+                ("n_decodes", c_int32), ("reserved", c_int32),
+                ("decode_kv", POINTER(sarathi_kv)), ("decode_len", POINTER(c_int32)),
+                ("x", c_void_p), ("y", c_void_p)]
+
+
+class sarathi_debug_dump(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("n1", "qkv", "q_rot", "attn", "h1", "n2", "act")]
+
+
+class SarathiError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: status {status} ({sarathi_status_str(status)}): {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m chunked_prefill_hybrid_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sarathi_layer_create.argtypes = [POINTER(sarathi_layer_desc), POINTER(sarathi_weights),
+                                           POINTER(c_void_p)]
+        L.sarathi_layer_create.restype = c_int32
+        L.sarathi_layer_destroy.argtypes = [c_void_p]
+        L.sarathi_layer_destroy.restype = None
+        L.sarathi_batch_check.argtypes = [POINTER(sarathi_layer_desc), POINTER(sarathi_batch)]
+        L.sarathi_batch_check.restype = c_int32
+        L.sarathi_workspace_size.argtypes = [POINTER(sarathi_layer_desc), POINTER(sarathi_batch)]
+        L.sarathi_workspace_size.restype = c_size_t
+        L.sarathi_layer_forward.argtypes = [c_void_p, POINTER(sarathi_batch), c_void_p, c_size_t, c_void_p]
+        L.sarathi_layer_forward.restype = c_int32
+        L.sarathi_layer_forward_debug.argtypes = [c_void_p, POINTER(sarathi_batch), c_void_p, c_size_t,
+                                                  c_void_p, POINTER(sarathi_debug_dump)]
+        L.sarathi_layer_forward_debug.restype = c_int32
+        L.sarathi_gemm.argtypes = [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.sarathi_gemm.restype = c_int32
+        L.sarathi_attention.argtypes = [POINTER(sarathi_layer_desc), POINTER(sarathi_batch), c_void_p,
+                                        c_void_p, c_void_p, c_size_t, c_void_p]
+        L.sarathi_attention.restype = c_int32
+        L.sarathi_status_str.argtypes = [c_int32]
+        L.sarathi_status_str.restype = c_char_p
+        L.sarathi_last_error.argtypes = []
+        L.sarathi_last_error.restype = c_char_p
+        _lib = L
+    return _lib
+
+
+def sarathi_status_str(status: int) -> str:
+    return lib().sarathi_status_str(status).decode()
+
+
+def sarathi_last_error() -> str:
+    return lib().sarathi_last_error().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SARATHI_OK:
+        raise SarathiError(status, where, sarathi_last_error())
+
+
+def sarathi_layer_create(desc: sarathi_layer_desc, weights: sarathi_weights) -> int:
+    h = c_void_p()
+    _check(lib().sarathi_layer_create(byref(desc), byref(weights), byref(h)), "sarathi_layer_create")
+    return h.value
+
+
+def sarathi_layer_destroy(handle: int) -> None:
+    lib().sarathi_layer_destroy(handle)
+
+
+def sarathi_batch_check(desc: sarathi_layer_desc, batch: sarathi_batch) -> int:
+    return lib().sarathi_batch_check(byref(desc), byref(batch))
+
+
+def sarathi_workspace_size(desc: sarathi_layer_desc, batch: sarathi_batch) -> int:
+    return lib().sarathi_workspace_size(byref(desc), byref(batch))
+
+
+def sarathi_layer_forward(handle: int, batch: sarathi_batch, ws: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().sarathi_layer_forward(handle, byref(batch), ws, ws_bytes, stream), "sarathi_layer_forward")
+
+
+def sarathi_layer_forward_debug(handle: int, batch: sarathi_batch, ws: int, ws_bytes: int, stream: int,
+                                dump: sarathi_debug_dump) -> None:
+    _check(lib().sarathi_layer_forward_debug(handle, byref(batch), ws, ws_bytes, stream, byref(dump)),
+           "sarathi_layer_forward_debug")
+
+
+def sarathi_gemm(dtype: int, m: int, n: int, k: int, a: int, w: int, out: int, stream: int) -> None:
+    _check(lib().sarathi_gemm(dtype, m, n, k, a, w, out, stream), "sarathi_gemm")
+
+
+def sarathi_attention(desc: sarathi_layer_desc, batch: sarathi_batch, q: int, out: int, ws: int,
+                      ws_bytes: int, stream: int) -> None:
+    _check(lib().sarathi_attention(byref(desc), byref(batch), q, out, ws, ws_bytes, stream),
+           "sarathi_attention")
+
+
+def make_batch(chunk_len: int, chunk_offset: int, chunk_kv, decode_kv, decode_len, x: int, y: int):
+    """Build a sarathi_batch.  chunk_kv: (k_ptr, v_ptr, capacity) or None; decode_kv: list of
+    (k_ptr, v_ptr, capacity); decode_len: list of ints.  Returns (batch, keepalive) — keep the second
+    value alive while the batch is used (it owns the host arrays the batch points to)."""
+    B = len(decode_len)
+    kv_arr = (sarathi_kv * max(B, 1))()
+    len_arr = (c_int32 * max(B, 1))()
+    for i, ((k, v, cap), L) in enumerate(zip(decode_kv, decode_len)):
+        kv_arr[i] = sarathi_kv(k, v, int(cap), 0)
+        len_arr[i] = int(L)
+    ck = sarathi_kv(0, 0, 0, 0) if chunk_kv is None else sarathi_kv(chunk_kv[0], chunk_kv[1], int(chunk_kv[2]), 0)
+    b = sarathi_batch(int(chunk_len), int(chunk_offset), ck, B, 0,
+                      ctypes.cast(kv_arr, POINTER(sarathi_kv)), ctypes.cast(len_arr, POINTER(c_int32)),
+                      x or 0, y or 0)
+    return b, (kv_arr, len_arr)

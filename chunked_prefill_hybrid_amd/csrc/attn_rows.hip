@@ -1,0 +1,214 @@
+// Single-query attention per (row, head) with the key range split across workgroups, plus the merge
+// of the split partials.
+//
+// A decode query attends over its request's cached entries plus its own new entry, i.e. keys
+// 0..pos with pos = the decode's cached length (Sarathi-Serve Guide: Chunked-Prefills & LLM Serving,
+// "Deep Dive", "Attention Complexity Across Mixed Batches"); each decode reads only its own cache
+// because decode attention is not fused across requests (SARATHI: Efficient LLM Inference by
+// Piggybacking Decodes with Chunked Prefills, section 3, "Decode-Maximal Batching").  The same kernel
+// serves chunk rows (keys 0..offset+t, Figure 6 of that page) in float32 mode.
+//
+// Memory-bound design: the head-major cache makes each (request, head) key stream contiguous; a key
+// row of d elements is read by d*size/16 lanes with 16-byte loads, so one wave load instruction covers
+// 4 bf16 keys of d=128 (1 KiB).  Each wave streams its keys in steps of 8 loads of K and 8 of V per
+// lane (an online softmax across steps), the four waves of a workgroup merge through LDS, and each
+// workgroup writes one split partial (max m and sum l in the log2 domain, unnormalised output).
+#include <math.h>
+
+#include "kernels.h"
+
+namespace sarathi {
+namespace {
+
+constexpr int kUnroll = 8;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int nh, int row0,
+                                                       ChunkRef ch, DecodeGroup dg, int max_splits,
+                                                       float *part_o, float *part_ml, float qscale) {
+  constexpr int E = Packet<T>::E;      // elements per 16-byte packet
+  constexpr int LPK = D / E;           // lanes per key row
+  constexpr int KPI = kWave / LPK;     // keys per wave load step
+  constexpr int KPW = kAttnSplit / 4;  // keys per wave per split
+  constexpr int NIT = KPW / KPI;
+  static_assert(NIT % kUnroll == 0, "whole unrolled steps");
+  const int r = row0 + blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const RowRef rr = row_ref(r, ch, dg);
+  const int n_keys = rr.pos + 1;
+  const int nsp = attn_splits(n_keys);
+  const size_t pidx = ((size_t)r * nh + h) * max_splits + s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (s >= nsp) {  // no keys for this split: an empty partial
+    if (tid == 0) {
+      part_ml[2 * pidx] = -INFINITY;
+      part_ml[2 * pidx + 1] = 0.f;
+    }
+    return;
+  }
+  const int per = (n_keys + nsp - 1) / nsp;
+  const int k_begin = s * per, k_end = min(n_keys, k_begin + per);
+  const int sub = lane % LPK, grp = lane / LPK;
+
+  float qv[E];
+  unpack<T>(ld16(q + (size_t)r * ld_q + h * D + sub * E), qv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) qv[e] *= qscale;
+  const T *Kh = reinterpret_cast<const T *>(rr.k) + (size_t)h * rr.cap * D + sub * E;
+  const T *Vh = reinterpret_cast<const T *>(rr.v) + (size_t)h * rr.cap * D + sub * E;
+  const int wbeg = k_begin + wave * KPW;
+
+  float m_run = -INFINITY, l_run = 0.f, o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+
+  for (int c0 = 0; c0 < NIT; c0 += kUnroll) {
+    if (wbeg + c0 * KPI >= k_end) break;
+    uint4 kr[kUnroll], vr[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = wbeg + (c0 + u) * KPI + grp;
+      ok[u] = j < k_end;
+      kr[u] = ok[u] ? ld16(Kh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = wbeg + (c0 + u) * KPI + grp;
+      vr[u] = ok[u] ? ld16(Vh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
+    }
+    float sc[kUnroll];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float kv[E];
+      unpack<T>(kr[u], kv);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
+#pragma unroll
+      for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
+      sc[u] = ok[u] ? dot : -INFINITY;
+      cmax = fmaxf(cmax, sc[u]);
+    }
+    cmax = wave_max(cmax, LPK);
+    const float m_new = fmaxf(m_run, cmax);
+    const float corr = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    l_run *= corr;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float p = ok[u] ? exp2f(sc[u] - m_new) : 0.f;
+      l_run += p;
+      float vv[E];
+      unpack<T>(vr[u], vv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[e], o[e]);
+    }
+    m_run = m_new;
+  }
+  // Sum over the key groups of the wave (lanes with equal `sub`); scores were replicated per group.
+  l_run = wave_sum(l_run, LPK);
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = wave_sum(o[e], LPK);
+
+  __shared__ float sm[4], sl[4];
+  __shared__ float so[4][D];
+  if (grp == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) so[wave][sub * E + e] = o[e];
+  }
+  if (lane == 0) {
+    sm[wave] = m_run;
+    sl[wave] = l_run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    float w[4], L = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = (sm[i] == -INFINITY) ? 0.f : exp2f(sm[i] - M);
+      L += sl[i] * w[i];
+    }
+    for (int c = lane; c < D; c += kWave) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += (w[i] != 0.f) ? so[i][c] * w[i] : 0.f;
+      part_o[pidx * D + c] = acc;
+    }
+    if (lane == 0) {
+      part_ml[2 * pidx] = M;
+      part_ml[2 * pidx + 1] = L;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_combine(int nh, int row0, int max_splits,
+                                                   const float *part_o, const float *part_ml,
+                                                   T *out, int ld_out) {
+  const int r = row0 + blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const size_t base = ((size_t)r * nh + h) * max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < max_splits; ++s)
+    if (part_ml[2 * (base + s) + 1] > 0.f) M = fmaxf(M, part_ml[2 * (base + s)]);
+  constexpr int PER = D / kWave;
+  float acc[PER] = {};
+  float L = 0.f;
+  for (int s = 0; s < max_splits; ++s) {
+    const float l = part_ml[2 * (base + s) + 1];
+    if (!(l > 0.f)) continue;
+    const float w = exp2f(part_ml[2 * (base + s)] - M);
+    L += l * w;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += w * part_o[(base + s) * D + lane + i * kWave];
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    out[(size_t)r * ld_out + h * D + lane + i * kWave] = from_f32<T>(acc[i] * inv);
+}
+
+template <typename T, int D>
+hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, const ChunkRef &ch,
+                     const DecodeGroup &dg, int max_splits, float *po, float *pml, hipStream_t s) {
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL((attn_rows_split<T, D>), dim3(n_rows, max_splits, nh), dim3(256), 0, s,
+                     static_cast<const T *>(q), ld_q, nh, row0, ch, dg, max_splits, po, pml, qscale);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, const float *po,
+                       const float *pml, void *out, int ld_out, hipStream_t s) {
+  hipLaunchKernelGGL((attn_combine<T, D>), dim3(n_rows, nh), dim3(64), 0, s, nh, row0, max_splits,
+                     po, pml, static_cast<T *>(out), ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
+                            const ChunkRef &ch, const DecodeGroup &dg, int max_splits,
+                            float *part_o, float *part_ml, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (type == kF32 && d == 64) return run_split<float, 64>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
+  if (type == kF32 && d == 128) return run_split<float, 128>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
+  if (type == kBF16 && d == 64) return run_split<bf16_t, 64>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
+  if (type == kBF16 && d == 128) return run_split<bf16_t, 128>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int max_splits,
+                               const float *part_o, const float *part_ml, void *out, int ld_out,
+                               hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (type == kF32 && d == 64) return run_combine<float, 64>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
+  if (type == kF32 && d == 128) return run_combine<float, 128>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
+  if (type == kBF16 && d == 64) return run_combine<bf16_t, 64>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
+  if (type == kBF16 && d == 128) return run_combine<bf16_t, 128>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sarathi

@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels: bfloat16 storage, 16-byte packets, wave64 reductions,
+// MFMA operand types, and the per-launch request descriptors passed by value as kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sarathi {
+
+typedef uint16_t bf16_t;  // bfloat16 storage (upper half of an IEEE float32)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// float32 -> bfloat16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// A 16-byte packet of storage elements: 4 floats or 8 bfloat16.
+template <typename T> struct Packet { static constexpr int E = 16 / (int)sizeof(T); };
+
+template <typename T> __device__ __forceinline__ void unpack(const uint4 &v, float *out);
+template <> __device__ __forceinline__ void unpack<float>(const uint4 &v, float *out) {
+  out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+}
+template <> __device__ __forceinline__ void unpack<bf16_t>(const uint4 &v, float *out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename T> __device__ __forceinline__ uint4 pack(const float *in);
+template <> __device__ __forceinline__ uint4 pack<float>(const float *in) {
+  return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                    __float_as_uint(in[3]));
+}
+template <> __device__ __forceinline__ uint4 pack<bf16_t>(const float *in) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_bf16(in[2 * i]) | ((uint32_t)f32_to_bf16(in[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(void *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// Butterfly reductions over the lanes whose index differs only in the bits of [lo_mask, 32].
+__device__ __forceinline__ float wave_sum(float v, int from = 1) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1)
+    if (m >= from) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v, int from = 1) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1)
+    if (m >= from) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Request descriptors, passed by value as kernel arguments.  A launch covers rows
+// [row0, row0 + n_rows) of the batch: rows below chunk.len are the chunk; row chunk.len + i is
+// decode i, which must lie in [dec.base, dec.base + dec.n).
+constexpr int kMaxDecodesPerLaunch = 64;
+
+struct ChunkRef {
+  uint64_t k, v;      // device [nh, cap, d] each (0 when chunk.len == 0)
+  int32_t cap, len;   // capacity; number of chunk rows C
+  int32_t off, pad;   // chunk offset (entries already cached)
+};
+
+struct DecodeGroup {
+  uint64_t k[kMaxDecodesPerLaunch];
+  uint64_t v[kMaxDecodesPerLaunch];
+  int32_t len[kMaxDecodesPerLaunch];   // cached entries before this step = the new token's slot
+  int32_t cap[kMaxDecodesPerLaunch];
+  int32_t n, base;                      // decodes base .. base+n-1 of the batch
+};
+
+// Position, cache and key count of batch row r (keys 0..pos are attended; pos is the write slot).
+struct RowRef {
+  uint64_t k, v;
+  int32_t cap, pos;
+};
+
+__device__ __forceinline__ RowRef row_ref(int r, const ChunkRef &ch, const DecodeGroup &dg) {
+  RowRef rr;
+  if (r < ch.len) {
+    rr.k = ch.k; rr.v = ch.v; rr.cap = ch.cap; rr.pos = ch.off + r;
+  } else {
+    const int i = r - ch.len - dg.base;
+    rr.k = dg.k[i]; rr.v = dg.v[i]; rr.cap = dg.cap[i]; rr.pos = dg.len[i];
+  }
+  return rr;
+}
+
+}  // namespace sarathi

@@ -1,0 +1,441 @@
+// Host side of the C ABI declared in include/sarathi.h: validation, workspace planning, the RoPE
+// table, and the launch sequence of one hybrid-batch layer forward.
+//
+// Launch sequence (all on the caller's stream, no host synchronisation):
+//   norm1 -> QKV GEMM over the C+B rows -> RoPE + KV append -> attention (chunk rows and decode rows
+//   split per request) -> O GEMM + residual -> norm2 -> gate/up GEMM + SiLU*mul (or up + GELU) ->
+//   down GEMM + residual.
+// This is the hybrid iteration of SARATHI: Efficient LLM Inference by Piggybacking Decodes with
+// Chunked Prefills, section 3, "Decode-Maximal Batching": linear ops fused over the concatenated
+// chunk and decode tokens, attention computed separately per request.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/sarathi.h"
+#include "kernels.h"
+
+using namespace sarathi;
+
+struct sarathi_layer {
+  sarathi_layer_desc desc;
+  sarathi_weights w;
+  float2 *rope_tab;  // device [max_pos, head_dim/2] (LLAMA), else null
+  int device;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sarathi_status fail(sarathi_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+size_t elem_size(int dtype) { return dtype == SARATHI_BF16 ? 2 : 4; }
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+sarathi_status check_desc(const sarathi_layer_desc *d) {
+  if (!d) return fail(SARATHI_ERR_INVALID, "layer description is null");
+  if (d->hidden <= 0 || d->n_heads <= 0 || d->head_dim <= 0 || d->ffn <= 0)
+    return fail(SARATHI_ERR_INVALID, "hidden, n_heads, head_dim and ffn must be positive");
+  if (d->max_tokens <= 0 || d->max_pos <= 0)
+    return fail(SARATHI_ERR_INVALID, "max_tokens and max_pos must be positive");
+  if (d->arch != SARATHI_ARCH_LLAMA && d->arch != SARATHI_ARCH_GPT)
+    return fail(SARATHI_ERR_INVALID, "unknown arch %d", d->arch);
+  if (d->dtype != SARATHI_F32 && d->dtype != SARATHI_BF16)
+    return fail(SARATHI_ERR_INVALID, "unknown dtype %d", d->dtype);
+  if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps))
+    return fail(SARATHI_ERR_INVALID, "norm_eps must be finite and >= 0");
+  if (d->arch == SARATHI_ARCH_LLAMA && !(d->rope_base > 0.f))
+    return fail(SARATHI_ERR_INVALID, "rope_base must be > 0");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SARATHI_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->hidden % 64 || (d->n_heads * d->head_dim) % 64)
+    return fail(SARATHI_ERR_UNSUPPORTED, "hidden and n_heads*head_dim must be multiples of 64");
+  if (d->dtype == SARATHI_BF16 && d->ffn % 64)
+    return fail(SARATHI_ERR_UNSUPPORTED, "ffn must be a multiple of 64 in bf16 mode");
+  if ((long long)d->max_tokens * 3 * d->n_heads * d->head_dim > (1ll << 31))
+    return fail(SARATHI_ERR_UNSUPPORTED, "max_tokens too large");
+  return SARATHI_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  const char *what;
+  int idx;
+};
+
+// need_xy: forward requires x and y; the attention-only entry does not.
+sarathi_status check_batch(const sarathi_layer_desc *d, const sarathi_batch *b, bool need_xy) {
+  sarathi_status st = check_desc(d);
+  if (st != SARATHI_OK) return st;
+  if (!b) return fail(SARATHI_ERR_INVALID, "batch is null");
+  const int C = b->chunk_len, B = b->n_decodes;
+  if (C < 0 || B < 0) return fail(SARATHI_ERR_INVALID, "chunk_len and n_decodes must be >= 0");
+  if (C + B < 1) return fail(SARATHI_ERR_INVALID, "empty batch (chunk_len + n_decodes == 0)");
+  if (C + B > d->max_tokens)
+    return fail(SARATHI_ERR_INVALID, "C+B = %d exceeds max_tokens %d", C + B, d->max_tokens);
+  if (b->reserved != 0) return fail(SARATHI_ERR_INVALID, "batch.reserved must be 0");
+  if (need_xy && (!b->x || !b->y)) return fail(SARATHI_ERR_INVALID, "x and y must be non-null");
+  const size_t el = elem_size(d->dtype);
+  const size_t per_slot = (size_t)d->n_heads * d->head_dim * el;
+  std::vector<Range> ranges;
+  if (C > 0) {
+    const sarathi_kv &kv = b->chunk_kv;
+    if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "chunk cache pointers are null");
+    if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "chunk_kv.reserved must be 0");
+    if (b->chunk_offset < 0) return fail(SARATHI_ERR_INVALID, "chunk_offset must be >= 0");
+    if (kv.capacity <= 0 || (long long)b->chunk_offset + C > kv.capacity)
+      return fail(SARATHI_ERR_CAPACITY, "chunk offset %d + C %d exceeds cache capacity %d",
+                  b->chunk_offset, C, kv.capacity);
+    if ((long long)b->chunk_offset + C > d->max_pos)
+      return fail(SARATHI_ERR_CAPACITY, "chunk positions reach %d >= max_pos %d",
+                  b->chunk_offset + C - 1, d->max_pos);
+    ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "chunk K", -1});
+    ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "chunk V", -1});
+  }
+  if (B > 0) {
+    if (!b->decode_kv || !b->decode_len)
+      return fail(SARATHI_ERR_INVALID, "decode_kv and decode_len must be non-null when n_decodes > 0");
+    for (int i = 0; i < B; ++i) {
+      const sarathi_kv &kv = b->decode_kv[i];
+      const int L = b->decode_len[i];
+      if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "decode %d cache pointers are null", i);
+      if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "decode_kv[%d].reserved must be 0", i);
+      if (L < 0) return fail(SARATHI_ERR_INVALID, "decode_len[%d] = %d < 0", i, L);
+      if ((long long)L + 1 > kv.capacity)
+        return fail(SARATHI_ERR_CAPACITY, "decode %d: slot %d does not fit capacity %d", i, L,
+                    kv.capacity);
+      if (L >= d->max_pos)
+        return fail(SARATHI_ERR_CAPACITY, "decode %d: position %d >= max_pos %d", i, L, d->max_pos);
+      ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "decode K", i});
+      ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "decode V", i});
+    }
+  }
+  if (need_xy) {
+    const size_t rows = (size_t)(C + B) * d->hidden * el;
+    ranges.push_back({(uintptr_t)b->y, (uintptr_t)b->y + rows, "y", -1});
+    const uintptr_t xl = (uintptr_t)b->x, xh = xl + rows;
+    const uintptr_t yl = (uintptr_t)b->y, yh = yl + rows;
+    if (xl < yh && yl < xh) return fail(SARATHI_ERR_INVALID, "y overlaps x");
+  }
+  std::sort(ranges.begin(), ranges.end(),
+            [](const Range &a, const Range &c) { return a.lo < c.lo; });
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].lo < ranges[i - 1].hi)
+      return fail(SARATHI_ERR_INVALID, "%s (%d) overlaps %s (%d): requests must not share caches",
+                  ranges[i].what, ranges[i].idx, ranges[i - 1].what, ranges[i - 1].idx);
+  return SARATHI_OK;
+}
+
+// Workspace layout of one forward.
+struct Plan {
+  int T, T_alloc, max_splits;
+  size_t n1, qkv, q, attn, h1, n2, act, part_o, part_ml, total;
+};
+
+int max_key_splits(const sarathi_batch *b) {
+  int ms = 1;
+  if (b->chunk_len > 0) ms = std::max(ms, attn_splits(b->chunk_offset + b->chunk_len));
+  for (int i = 0; i < b->n_decodes; ++i) ms = std::max(ms, attn_splits(b->decode_len[i] + 1));
+  return ms;
+}
+
+Plan make_plan(const sarathi_layer_desc *d, const sarathi_batch *b) {
+  Plan p{};
+  p.T = b->chunk_len + b->n_decodes;
+  p.T_alloc = round_up(p.T, 64);
+  p.max_splits = max_key_splits(b);
+  const size_t el = elem_size(d->dtype), R = p.T_alloc;
+  const size_t H = d->hidden, A = (size_t)d->n_heads * d->head_dim, F = d->ffn;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  p.n1 = take(R * H * el);
+  p.qkv = take(R * 3 * A * el);
+  p.q = take(R * A * el);
+  p.attn = take(R * A * el);
+  p.h1 = take(R * H * 4);
+  p.n2 = take(R * H * el);
+  p.act = take(R * F * el);
+  p.part_o = take((size_t)p.T * d->n_heads * p.max_splits * d->head_dim * 4);
+  p.part_ml = take((size_t)p.T * d->n_heads * p.max_splits * 2 * 4);
+  p.total = off;
+  return p;
+}
+
+ChunkRef chunk_ref(const sarathi_batch *b) {
+  ChunkRef c{};
+  c.len = b->chunk_len;
+  if (b->chunk_len > 0) {
+    c.k = (uint64_t)b->chunk_kv.k;
+    c.v = (uint64_t)b->chunk_kv.v;
+    c.cap = b->chunk_kv.capacity;
+    c.off = b->chunk_offset;
+  }
+  return c;
+}
+
+DecodeGroup decode_group(const sarathi_batch *b, int base) {
+  DecodeGroup g{};
+  g.base = base;
+  g.n = std::min(kMaxDecodesPerLaunch, b->n_decodes - base);
+  if (g.n < 0) g.n = 0;
+  for (int i = 0; i < g.n; ++i) {
+    g.k[i] = (uint64_t)b->decode_kv[base + i].k;
+    g.v[i] = (uint64_t)b->decode_kv[base + i].v;
+    g.len[i] = b->decode_len[base + i];
+    g.cap[i] = b->decode_kv[base + i].capacity;
+  }
+  return g;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail(SARATHI_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));        \
+  } while (0)
+
+// Attention of all batch rows, split per request: writes out [T, A] (storage type).
+sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b, const Plan &p,
+                             const void *q, void *out, char *ws, hipStream_t s) {
+  const int A = d->n_heads * d->head_dim;
+  const ChunkRef ch = chunk_ref(b);
+  float *po = reinterpret_cast<float *>(ws + p.part_o);
+  float *pml = reinterpret_cast<float *>(ws + p.part_ml);
+  // Launch groups: the chunk rows with the first decodes, then further decodes 64 at a time.
+  int base = 0;
+  do {
+    const DecodeGroup g = decode_group(b, base);
+    const int row0 = base == 0 ? 0 : b->chunk_len + base;
+    const int n_rows = (base == 0 ? b->chunk_len : 0) + g.n;
+    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, row0, n_rows, ch, g,
+                             p.max_splits, po, pml, s));
+    HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, row0, n_rows, p.max_splits, po,
+                                pml, out, A, s));
+    base += kMaxDecodesPerLaunch;
+  } while (base < b->n_decodes);
+  return SARATHI_OK;
+}
+
+sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *workspace,
+                            size_t ws_bytes, void *stream, const sarathi_debug_dump *dump) {
+  if (!L) return fail(SARATHI_ERR_INVALID, "layer is null");
+  const sarathi_layer_desc *d = &L->desc;
+  sarathi_status st = check_batch(d, b, true);
+  if (st != SARATHI_OK) return st;
+  const Plan p = make_plan(d, b);
+  if (!workspace) return fail(SARATHI_ERR_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(SARATHI_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (ws_bytes < p.total)
+    return fail(SARATHI_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  const int ty = d->dtype, T = p.T, R = p.T_alloc;
+  const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
+  const bool llama = d->arch == SARATHI_ARCH_LLAMA;
+  void *n1 = ws + p.n1, *qkv = ws + p.qkv, *q = ws + p.q, *attn = ws + p.attn;
+  float *h1 = reinterpret_cast<float *>(ws + p.h1);
+  void *n2 = ws + p.n2, *act = ws + p.act;
+
+  // 1. norm 1 over the C+B rows (pad rows zeroed)
+  HIP_TRY(launch_norm(ty, ty, !llama, b->x, L->w.norm1_w, L->w.norm1_b, n1, H, T, R, d->norm_eps, s));
+  // 2. QKV projection: one GEMM over chunk and decode rows
+  GemmArgs g{};
+  g.a = n1; g.lda = H; g.w0 = L->w.w_qkv; g.ldw = H; g.out = qkv; g.ldo = 3 * A;
+  g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
+  HIP_TRY(launch_gemm(ty, kEpiStore, g, s));
+  // 3. RoPE + KV append (per launch group of decodes)
+  const ChunkRef ch = chunk_ref(b);
+  {
+    int base = 0;
+    do {
+      const DecodeGroup dg = decode_group(b, base);
+      const int row0 = base == 0 ? 0 : b->chunk_len + base;
+      const int n_rows = (base == 0 ? b->chunk_len : 0) + dg.n;
+      HIP_TRY(launch_rope_append(ty, qkv, 3 * A, q, A, L->rope_tab, llama ? 1 : 0, d->n_heads,
+                                 d->head_dim, row0, n_rows, ch, dg, s));
+      base += kMaxDecodesPerLaunch;
+    } while (base < b->n_decodes);
+  }
+  // 4. attention, split per request
+  st = run_attention(d, b, p, q, attn, ws, s);
+  if (st != SARATHI_OK) return st;
+  // 5. O projection + residual (h1 kept in float32)
+  g = GemmArgs{};
+  g.a = attn; g.lda = A; g.w0 = L->w.w_o; g.ldw = A; g.out = h1; g.ldo = H;
+  g.resid = b->x; g.ldr = H; g.m_alloc = R; g.m_store = T; g.n = H; g.k = A;
+  HIP_TRY(launch_gemm(ty, kEpiResidF32, g, s));
+  // 6. norm 2
+  HIP_TRY(launch_norm(kF32, ty, !llama, h1, L->w.norm2_w, L->w.norm2_b, n2, H, T, R, d->norm_eps, s));
+  // 7. FFN up (+gate) with the activation fused
+  g = GemmArgs{};
+  g.a = n2; g.lda = H; g.ldw = H; g.out = act; g.ldo = F; g.m_alloc = R; g.m_store = T; g.n = F;
+  g.k = H;
+  if (llama) {
+    g.w0 = L->w.w_gate; g.w1 = L->w.w_up;
+    HIP_TRY(launch_gemm(ty, kEpiSwiGLU, g, s));
+  } else {
+    g.w0 = L->w.w_up;
+    HIP_TRY(launch_gemm(ty, kEpiGelu, g, s));
+  }
+  // 8. down projection + residual -> y
+  g = GemmArgs{};
+  g.a = act; g.lda = F; g.w0 = L->w.w_down; g.ldw = F; g.out = b->y; g.ldo = H;
+  g.resid = h1; g.ldr = H; g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
+  HIP_TRY(launch_gemm(ty, kEpiResidOut, g, s));
+
+  if (dump) {
+    if (dump->n1) HIP_TRY(launch_to_f32(ty, n1, H, dump->n1, H, T, H, s));
+    if (dump->qkv) HIP_TRY(launch_to_f32(ty, qkv, 3 * A, dump->qkv, 3 * A, T, 3 * A, s));
+    if (dump->q_rot) HIP_TRY(launch_to_f32(ty, q, A, dump->q_rot, A, T, A, s));
+    if (dump->attn) HIP_TRY(launch_to_f32(ty, attn, A, dump->attn, A, T, A, s));
+    if (dump->h1) HIP_TRY(launch_to_f32(kF32, h1, H, dump->h1, H, T, H, s));
+    if (dump->n2) HIP_TRY(launch_to_f32(ty, n2, H, dump->n2, H, T, H, s));
+    if (dump->act) HIP_TRY(launch_to_f32(ty, act, F, dump->act, F, T, F, s));
+  }
+  return SARATHI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarathi_weights *weights,
+                                    sarathi_layer **out) {
+  if (!out) return fail(SARATHI_ERR_INVALID, "out is null");
+  *out = nullptr;
+  sarathi_status st = check_desc(desc);
+  if (st != SARATHI_OK) return st;
+  if (!weights) return fail(SARATHI_ERR_INVALID, "weights is null");
+  const bool llama = desc->arch == SARATHI_ARCH_LLAMA;
+  if (!weights->w_qkv || !weights->w_o || !weights->w_up || !weights->w_down || !weights->norm1_w ||
+      !weights->norm2_w)
+    return fail(SARATHI_ERR_INVALID, "a required weight pointer is null");
+  if (llama && !weights->w_gate) return fail(SARATHI_ERR_INVALID, "w_gate is required for LLAMA");
+  if (!llama && (!weights->norm1_b || !weights->norm2_b))
+    return fail(SARATHI_ERR_INVALID, "LayerNorm biases are required for GPT");
+  sarathi_layer *L = new (std::nothrow) sarathi_layer();
+  if (!L) return fail(SARATHI_ERR_NOMEM, "host allocation failed");
+  L->desc = *desc;
+  L->w = *weights;
+  if (!llama) L->w.w_gate = nullptr;
+  L->rope_tab = nullptr;
+  if (hipGetDevice(&L->device) != hipSuccess) {
+    delete L;
+    return fail(SARATHI_ERR_HIP, "hipGetDevice failed");
+  }
+  if (llama) {
+    const int half = desc->head_dim / 2;
+    std::vector<float2> tab((size_t)desc->max_pos * half);
+    for (int pos = 0; pos < desc->max_pos; ++pos)
+      for (int j = 0; j < half; ++j) {
+        const double inv = std::pow((double)desc->rope_base, -2.0 * j / desc->head_dim);
+        const double ang = (double)pos * inv;
+        tab[(size_t)pos * half + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+    const size_t bytes = tab.size() * sizeof(float2);
+    hipError_t e = hipMalloc(&L->rope_tab, bytes);
+    if (e != hipSuccess) {
+      delete L;
+      return fail(SARATHI_ERR_NOMEM, "hipMalloc of the RoPE table failed: %s", hipGetErrorString(e));
+    }
+    e = hipMemcpy(L->rope_tab, tab.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(L->rope_tab);
+      delete L;
+      return fail(SARATHI_ERR_HIP, "copying the RoPE table failed: %s", hipGetErrorString(e));
+    }
+  }
+  *out = L;
+  return SARATHI_OK;
+}
+
+void sarathi_layer_destroy(sarathi_layer *layer) {
+  if (!layer) return;
+  if (layer->rope_tab) (void)hipFree(layer->rope_tab);
+  delete layer;
+}
+
+sarathi_status sarathi_batch_check(const sarathi_layer_desc *desc, const sarathi_batch *batch) {
+  return check_batch(desc, batch, true);
+}
+
+size_t sarathi_workspace_size(const sarathi_layer_desc *desc, const sarathi_batch *batch) {
+  if (check_batch(desc, batch, false) != SARATHI_OK) return 0;
+  return make_plan(desc, batch).total;
+}
+
+sarathi_status sarathi_layer_forward(sarathi_layer *layer, const sarathi_batch *batch,
+                                     void *workspace, size_t ws_bytes, void *stream) {
+  return forward_impl(layer, batch, workspace, ws_bytes, stream, nullptr);
+}
+
+sarathi_status sarathi_layer_forward_debug(sarathi_layer *layer, const sarathi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           const sarathi_debug_dump *dump) {
+  return forward_impl(layer, batch, workspace, ws_bytes, stream, dump);
+}
+
+sarathi_status sarathi_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a,
+                            const void *w, void *out, void *stream) {
+  if (dtype != SARATHI_F32 && dtype != SARATHI_BF16)
+    return fail(SARATHI_ERR_INVALID, "unknown dtype %d", dtype);
+  if (m <= 0 || n <= 0 || k <= 0) return fail(SARATHI_ERR_INVALID, "m, n, k must be positive");
+  if (!a || !w || !out) return fail(SARATHI_ERR_INVALID, "null pointer");
+  if (dtype == SARATHI_BF16 && k % 64)
+    return fail(SARATHI_ERR_UNSUPPORTED, "bf16 GEMM needs k %% 64 == 0 (k = %d)", k);
+  GemmArgs g{};
+  g.a = a; g.lda = k; g.w0 = w; g.ldw = k; g.out = out; g.ldo = n;
+  g.m_alloc = m; g.m_store = m; g.n = n; g.k = k;
+  HIP_TRY(launch_gemm(dtype, kEpiStore, g, static_cast<hipStream_t>(stream)));
+  return SARATHI_OK;
+}
+
+sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_batch *batch,
+                                 const void *q, void *out, void *workspace, size_t ws_bytes,
+                                 void *stream) {
+  sarathi_status st = check_batch(desc, batch, false);
+  if (st != SARATHI_OK) return st;
+  if (!q || !out) return fail(SARATHI_ERR_INVALID, "q and out must be non-null");
+  const Plan p = make_plan(desc, batch);
+  if (!workspace) return fail(SARATHI_ERR_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(SARATHI_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (ws_bytes < p.total)
+    return fail(SARATHI_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+  return run_attention(desc, batch, p, q, out, static_cast<char *>(workspace),
+                       static_cast<hipStream_t>(stream));
+}
+
+const char *sarathi_status_str(sarathi_status status) {
+  switch (status) {
+    case SARATHI_OK: return "ok";
+    case SARATHI_ERR_INVALID: return "invalid argument";
+    case SARATHI_ERR_UNSUPPORTED: return "unsupported shape";
+    case SARATHI_ERR_CAPACITY: return "cache or position capacity exceeded";
+    case SARATHI_ERR_HIP: return "HIP runtime error";
+    case SARATHI_ERR_NOMEM: return "out of memory";
+    case SARATHI_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SARATHI_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+const char *sarathi_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

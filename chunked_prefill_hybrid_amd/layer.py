@@ -1,0 +1,142 @@
+"""Torch-facing wrapper of the C ABI: marshals device tensors into the library's structs.
+
+PyTorch supplies device memory and streams only; every step of the layer runs in libsarathi.so.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _abi
+
+_DT = {"f32": (_abi.SARATHI_F32, torch.float32), "bf16": (_abi.SARATHI_BF16, torch.bfloat16)}
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_desc(shape, max_tokens: int, max_pos: int) -> _abi.sarathi_layer_desc:
+    return _abi.sarathi_layer_desc(
+        shape.hidden, shape.n_heads, shape.head_dim, shape.ffn,
+        _abi.SARATHI_ARCH_LLAMA if shape.arch == "llama" else _abi.SARATHI_ARCH_GPT,
+        _DT[shape.dtype][0], float(shape.norm_eps), float(shape.rope_base), int(max_tokens), int(max_pos))
+
+
+KV = Tuple[torch.Tensor, torch.Tensor]   # (K, V), each [n_heads, capacity, head_dim]
+
+
+class HybridLayer:
+    """One decoder layer bound to caller-owned device weights.
+
+    weights: dict with w_qkv [3A,H], w_o [H,A], w_gate [F,H] (llama), w_up [F,H], w_down [H,F] in the
+    storage dtype, and float32 norm1_w, norm2_w (+ norm1_b, norm2_b for gpt).  The tensors must stay
+    alive and unchanged while the layer exists (the wrapper keeps references)."""
+
+    def __init__(self, shape, weights: dict, max_tokens: int, max_pos: int):
+        self.shape = shape
+        self.dtype = _DT[shape.dtype][1]
+        self.desc = make_desc(shape, max_tokens, max_pos)
+        self._weights = dict(weights)
+        dt = self.dtype
+        w = _abi.sarathi_weights(
+            _ptr(weights["w_qkv"], dt), _ptr(weights["w_o"], dt), _ptr(weights.get("w_gate"), dt),
+            _ptr(weights["w_up"], dt), _ptr(weights["w_down"], dt),
+            _ptr(weights["norm1_w"], torch.float32), _ptr(weights.get("norm1_b"), torch.float32),
+            _ptr(weights["norm2_w"], torch.float32), _ptr(weights.get("norm2_b"), torch.float32))
+        self.handle = _abi.sarathi_layer_create(self.desc, w)
+
+    def close(self) -> None:
+        if self.handle:
+            _abi.sarathi_layer_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def batch(self, x: Optional[torch.Tensor], y: Optional[torch.Tensor], chunk_len: int,
+              chunk_offset: int, chunk_kv: Optional[KV], decode_kv: Sequence[KV],
+              decode_len: Sequence[int]):
+        """(sarathi_batch, keepalive) for the given tensors."""
+        dt = self.dtype
+        ck = None
+        if chunk_kv is not None and chunk_len > 0:
+            ck = (_ptr(chunk_kv[0], dt), _ptr(chunk_kv[1], dt), chunk_kv[0].shape[1])
+        dkv = [(_ptr(k, dt), _ptr(v, dt), k.shape[1]) for k, v in decode_kv]
+        return _abi.make_batch(chunk_len, chunk_offset, ck, dkv, list(decode_len),
+                               _ptr(x, dt), _ptr(y, dt))
+
+    def workspace_size(self, batch) -> int:
+        return _abi.sarathi_workspace_size(self.desc, batch)
+
+    def forward(self, x, y, chunk_len, chunk_offset, chunk_kv, decode_kv, decode_len,
+                workspace: Optional[torch.Tensor] = None, stream=None, dump: Optional[dict] = None):
+        """Enqueue the layer over one hybrid batch (y and the caches are written in place).
+        dump: optional dict name -> float32 [C+B, width] tensor for the intermediates n1, qkv, q_rot,
+        attn, h1, n2, act."""
+        b, keep = self.batch(x, y, chunk_len, chunk_offset, chunk_kv, decode_kv, decode_len)
+        need = self.workspace_size(b)
+        if need == 0:
+            st = _abi.sarathi_batch_check(self.desc, b)
+            raise _abi.SarathiError(st, "batch", _abi.sarathi_last_error())
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr = _ptr(workspace)
+        nbytes = workspace.numel() * workspace.element_size()
+        if dump:
+            d = _abi.sarathi_debug_dump(*[_ptr(dump.get(n), torch.float32) for n in
+                                          ("n1", "qkv", "q_rot", "attn", "h1", "n2", "act")])
+            _abi.sarathi_layer_forward_debug(self.handle, b, ws_ptr, nbytes, _stream(stream), d)
+        else:
+            _abi.sarathi_layer_forward(self.handle, b, ws_ptr, nbytes, _stream(stream))
+        del keep
+        return y
+
+
+def gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """out[M,N] = a[M,K] w[N,K]^T with the library's GEMM kernel."""
+    m, k = a.shape
+    n = w.shape[0]
+    dt = _abi.SARATHI_BF16 if a.dtype == torch.bfloat16 else _abi.SARATHI_F32
+    if out is None:
+        out = torch.empty((m, n), dtype=a.dtype, device=a.device)
+    _abi.sarathi_gemm(dt, m, n, k, _ptr(a, a.dtype), _ptr(w, a.dtype), _ptr(out, a.dtype), _stream(stream))
+    return out
+
+
+def attention(shape, q: torch.Tensor, out: torch.Tensor, chunk_len: int, chunk_offset: int,
+              chunk_kv: Optional[KV], decode_kv: Sequence[KV], decode_len: Sequence[int],
+              max_pos: int, stream=None):
+    """The split attention alone over caches that already hold this step's K/V rows."""
+    desc = make_desc(shape, q.shape[0], max_pos)
+    dt = _DT[shape.dtype][1]
+    ck = None
+    if chunk_kv is not None and chunk_len > 0:
+        ck = (_ptr(chunk_kv[0], dt), _ptr(chunk_kv[1], dt), chunk_kv[0].shape[1])
+    dkv = [(_ptr(k, dt), _ptr(v, dt), k.shape[1]) for k, v in decode_kv]
+    b, keep = _abi.make_batch(chunk_len, chunk_offset, ck, dkv, list(decode_len), 0, 0)
+    need = _abi.sarathi_workspace_size(desc, b)
+    if need == 0:
+        raise _abi.SarathiError(_abi.sarathi_batch_check(desc, b), "batch", _abi.sarathi_last_error())
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _abi.sarathi_attention(desc, b, _ptr(q, dt), _ptr(out, dt), _ptr(ws), need, _stream(stream))
+    del keep
+    return out

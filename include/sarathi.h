@@ -1,0 +1,181 @@
+/*
+ * sarathi.h — C ABI of the hybrid-batch decoder-layer library for AMD Instinct MI355X (gfx950).
+ *
+ * The library runs the forward pass of one LLaMA-style (or GPT-style) decoder layer over a HYBRID
+ * BATCH: one prefill chunk of C tokens from one request plus B single-token decodes, each decode
+ * request with its own KV cache.  The linear ops (QKV, O, gate/up, down) run as single GEMMs over the
+ * C+B concatenated rows, so the decodes share the chunk's weight fetches; attention is split per
+ * request: causal attention of the chunk over its cached prefix plus itself, and single-query
+ * attention of each decode over its own cache plus its own new token.
+ *   - Hybrid batch, fused linear ops, separate attention, in-place KV writes into caches allocated at
+ *     maximum length: "SARATHI: Efficient LLM Inference by Piggybacking Decodes with Chunked
+ *     Prefills", section 3, "Decode-Maximal Batching" and "Implementation" (KV cache
+ *     pre-allocation).
+ *   - Chunk mask (query at absolute position p sees keys 0..p): same page, "Chunked-Prefills",
+ *     Figure 6.
+ *   - A decode with S cached entries attends over S+1 keys: "Sarathi-Serve Guide: Chunked-Prefills &
+ *     LLM Serving", "Deep Dive", "Attention Complexity Across Mixed Batches".
+ *   - The caller advances prompt progress and decode lengths after the step (same guide, the
+ *     co-scheduler's step update); the library never changes a length.
+ *
+ * Conventions for every entry point
+ *   - Device pointers point to memory of the current HIP device; host pointers to host memory.
+ *   - Matrices are row-major.  Weights are stored [out_features, in_features] (y = x W^T).
+ *   - Storage type (weights, x, y, caches): float32 (SARATHI_F32) or bfloat16 (SARATHI_BF16), per
+ *     the layer's dtype.  Norm gains/biases are always float32.  Arithmetic accumulates in float32.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only ENQUEUE work on it and return;
+ *     they never synchronise the device.  All validation runs on the host before anything is
+ *     enqueued; on any error nothing is launched and no buffer is written.
+ *   - No C++ exception crosses this boundary.  Every failing call records a message readable with
+ *     sarathi_last_error() (thread-local, valid until the thread's next failing call).
+ */
+#ifndef SARATHI_H
+#define SARATHI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SARATHI_OK = 0,
+    SARATHI_ERR_INVALID = -1,      /* bad argument: null pointer, negative size, aliasing, ... */
+    SARATHI_ERR_UNSUPPORTED = -2,  /* valid but not supported shape (e.g. head_dim not 64/128) */
+    SARATHI_ERR_CAPACITY = -3,     /* a position or write slot does not fit a cache / the RoPE table */
+    SARATHI_ERR_HIP = -4,          /* a HIP runtime call failed */
+    SARATHI_ERR_NOMEM = -5,        /* host or device allocation failed (create only) */
+    SARATHI_ERR_WORKSPACE = -6,    /* workspace null, too small or misaligned */
+    SARATHI_ERR_INTERNAL = -7
+} sarathi_status;
+
+typedef enum { SARATHI_F32 = 0, SARATHI_BF16 = 1 } sarathi_dtype;
+
+/* LLAMA: RMSNorm, RoPE on Q and K (adjacent pairs (2j, 2j+1), angle pos * base^(-2j/head_dim)),
+ *        SwiGLU FFN act = silu(x W_gate^T) * (x W_up^T).
+ * GPT:   LayerNorm (biased variance) with bias, no RoPE, GELU MLP act = gelu(x W_up^T) (erf form). */
+typedef enum { SARATHI_ARCH_LLAMA = 0, SARATHI_ARCH_GPT = 1 } sarathi_arch;
+
+typedef struct {
+    int32_t hidden;      /* H: model width; multiple of 64 */
+    int32_t n_heads;     /* nh */
+    int32_t head_dim;    /* d: 64 or 128.  Attention width A = nh*d; multiple of 64 */
+    int32_t ffn;         /* F: FFN width; multiple of 64 in bf16 mode, of 16 in f32 mode */
+    int32_t arch;        /* sarathi_arch */
+    int32_t dtype;       /* sarathi_dtype */
+    float norm_eps;      /* e.g. 1e-6 (RMSNorm) or 1e-5 (LayerNorm) */
+    float rope_base;     /* e.g. 10000; unused for GPT */
+    int32_t max_tokens;  /* largest C+B a forward call may pass */
+    int32_t max_pos;     /* every position must be < max_pos (size of the RoPE table) */
+} sarathi_layer_desc;
+
+/* Device pointers to caller-owned weights; they must stay valid and unchanged while the layer exists.
+ *   w_qkv [3A, H]: rows [Q | K | V], each block head-major (head h = rows h*d .. h*d+d-1 of it)
+ *   w_o [H, A];  w_gate [F, H] (LLAMA only; NULL for GPT);  w_up [F, H];  w_down [H, F]
+ *   norm1_w, norm2_w: float32 [H];  norm1_b, norm2_b: float32 [H] (GPT only; NULL for LLAMA) */
+typedef struct {
+    const void *w_qkv, *w_o, *w_gate, *w_up, *w_down;
+    const float *norm1_w, *norm1_b, *norm2_w, *norm2_b;
+} sarathi_weights;
+
+/* One request's KV cache: two device buffers, each [n_heads, capacity, head_dim] (head-major, one
+ * contiguous [capacity, head_dim] slab per head), storage type = the layer's dtype.  K is stored
+ * after RoPE.  Slot j holds the token at position j. */
+typedef struct {
+    void *k;
+    void *v;
+    int32_t capacity;
+    int32_t reserved;    /* must be 0 */
+} sarathi_kv;
+
+/* One hybrid batch.  Rows 0..chunk_len-1 of x are the chunk, at positions chunk_offset+t; row
+ * chunk_len+i is decode i, at position decode_len[i] (its cache already holds decode_len[i] entries).
+ * The call writes: y; chunk K/V into chunk_kv slots [chunk_offset, chunk_offset+chunk_len); decode
+ * i's K/V into its slot decode_len[i].  chunk_len == 0 is a decode-only batch (chunk_kv ignored);
+ * n_decodes == 0 is a chunk-only batch.  chunk_len + n_decodes >= 1. */
+typedef struct {
+    int32_t chunk_len;          /* C >= 0 */
+    int32_t chunk_offset;       /* entries already in the chunk request's cache, >= 0 */
+    sarathi_kv chunk_kv;        /* device buffers; capacity >= chunk_offset + chunk_len */
+    int32_t n_decodes;          /* B >= 0 */
+    int32_t reserved;           /* must be 0 */
+    const sarathi_kv *decode_kv;  /* HOST array [n_decodes]; capacity >= decode_len[i] + 1 */
+    const int32_t *decode_len;    /* HOST array [n_decodes]; >= 0 */
+    const void *x;              /* device [C+B, H] input hidden states, chunk rows first */
+    void *y;                    /* device [C+B, H] output; must not overlap x, caches or workspace */
+} sarathi_batch;
+
+/* Device buffers, each float32 [C+B, width], that sarathi_layer_forward_debug fills with the layer's
+ * intermediates (NULL entries are skipped):
+ *   n1 [.,H] norm-1 output;  qkv [.,3A] projection before RoPE;  q_rot [.,A] rotated queries;
+ *   attn [.,A] attention output (heads concatenated);  h1 [.,H] x + attn W_o^T;
+ *   n2 [.,H] norm-2 output;  act [.,F] FFN activation (silu(gate)*up or gelu(up)). */
+typedef struct {
+    float *n1, *qkv, *q_rot, *attn, *h1, *n2, *act;
+} sarathi_debug_dump;
+
+typedef struct sarathi_layer sarathi_layer;   /* opaque, immutable after create */
+
+/* Creates a layer handle for the current HIP device.  Copies *desc; keeps the weight pointers (does
+ * not copy weights).  Allocates only the device RoPE cos/sin table [max_pos, head_dim/2] (LLAMA),
+ * built on the host in float64.  Errors: INVALID (null pointers, non-positive sizes), UNSUPPORTED
+ * (head_dim not 64/128, widths not multiples of 64), NOMEM, HIP.  On error *out is set to NULL. */
+sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarathi_weights *weights,
+                                    sarathi_layer **out);
+
+/* Frees the handle and its RoPE table.  NULL is a no-op.  No call using the handle may be in flight
+ * (the caller synchronises its streams first). */
+void sarathi_layer_destroy(sarathi_layer *layer);
+
+/* Host-only validation of a batch against a layer description (no HIP call).  Checks: C, B >= 0 and
+ * C+B in [1, max_tokens]; non-null x, y, caches and host arrays; reserved fields 0; chunk_offset +
+ * chunk_len <= chunk capacity; decode_len[i] + 1 <= capacity_i; every position < max_pos; no two
+ * requests share a K or V buffer; y does not overlap x.  Returns OK, INVALID or CAPACITY. */
+sarathi_status sarathi_batch_check(const sarathi_layer_desc *desc, const sarathi_batch *batch);
+
+/* Bytes of device workspace sarathi_layer_forward needs for this batch (depends on C+B, the number
+ * of decodes and their lengths).  Returns 0 if the batch fails sarathi_batch_check. */
+size_t sarathi_workspace_size(const sarathi_layer_desc *desc, const sarathi_batch *batch);
+
+/* Enqueues the layer's forward pass over the hybrid batch on `stream`.
+ * workspace: caller-owned device buffer of ws_bytes >= sarathi_workspace_size(...), 256-byte aligned,
+ * not shared with another call in flight.  Its contents on entry do not matter.
+ * Errors (all before any launch): everything sarathi_batch_check reports, WORKSPACE, HIP. */
+sarathi_status sarathi_layer_forward(sarathi_layer *layer, const sarathi_batch *batch,
+                                     void *workspace, size_t ws_bytes, void *stream);
+
+/* As sarathi_layer_forward, then also copies the intermediates named in *dump (float32 device
+ * buffers of C+B rows) on the same stream.  dump may be NULL. */
+sarathi_status sarathi_layer_forward_debug(sarathi_layer *layer, const sarathi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           const sarathi_debug_dump *dump);
+
+/* The fused linear op alone: out[M, N] = a[M, K] w[N, K]^T, in `dtype` storage with float32
+ * accumulation (the GEMM each of the layer's projections runs over the C+B rows).  a, w, out are
+ * device pointers, densely packed row-major.  M >= 1; in bf16 mode K must be a multiple of 64.
+ * Errors: INVALID, UNSUPPORTED, HIP. */
+sarathi_status sarathi_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a,
+                            const void *w, void *out, void *stream);
+
+/* The split attention alone, over caches that ALREADY hold this step's K/V rows (chunk slots
+ * chunk_offset..chunk_offset+C-1 and decode slots decode_len[i]).  q: device [C+B, nh*d] queries
+ * (after RoPE), out: device [C+B, nh*d].  Chunk row t attends to chunk keys 0..chunk_offset+t;
+ * decode i attends to its keys 0..decode_len[i].  Scores are scaled by 1/sqrt(d).  batch->x and
+ * batch->y are ignored.  workspace: as for the forward (sarathi_workspace_size of the same batch is
+ * enough).  Errors: as sarathi_batch_check (x/y not required), WORKSPACE, HIP. */
+sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_batch *batch,
+                                 const void *q, void *out, void *workspace, size_t ws_bytes,
+                                 void *stream);
+
+/* Static description of a status code. */
+const char *sarathi_status_str(sarathi_status status);
+
+/* Message of this thread's last failing call ("" if none). */
+const char *sarathi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SARATHI_H */

@@ -86,12 +86,12 @@ def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray) -
     scores = q.k / sqrt(d); masked scores are -inf; softmax is max-subtracted; output = sum_j a_j v_j.
     Returns [R, nh, d]."""
     d = q.shape[-1]
-    s = np.einsum("rhd,hsd->hrs", q, k) / math.sqrt(d)
+    s = np.matmul(q.transpose(1, 0, 2), k.transpose(0, 2, 1)) / math.sqrt(d)   # [nh, R, S]
     s = np.where(mask[None, :, :], s, -np.inf)
     s = s - np.max(s, axis=-1, keepdims=True)
     p = np.exp(s)
     p = p / np.sum(p, axis=-1, keepdims=True)
-    return np.einsum("hrs,hsd->rhd", p, v)
+    return np.matmul(p, v).transpose(1, 0, 2)
 
 
 def silu(z: np.ndarray) -> np.ndarray:

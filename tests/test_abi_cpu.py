@@ -1,0 +1,125 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry point its header declares,
+and its host-side validation returns the documented status codes without touching any device
+memory (sarathi_batch_check and sarathi_workspace_size never dereference device pointers)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_prefill_hybrid_amd import _abi, build
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "sarathi.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        build.build()
+    return _abi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sarathi_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in sarathi.h but not exported"
+    assert set(names) == set(_abi.EXPORTED)
+
+
+def test_struct_layouts_match_header():
+    # sizes fixed by the header's field order and natural alignment
+    assert ctypes.sizeof(_abi.sarathi_layer_desc) == 40
+    assert ctypes.sizeof(_abi.sarathi_kv) == 24
+    assert ctypes.sizeof(_abi.sarathi_batch) == 72
+    assert _abi.sarathi_batch.x.offset == 56 and _abi.sarathi_batch.decode_kv.offset == 40
+    assert ctypes.sizeof(_abi.sarathi_weights) == 72
+    assert ctypes.sizeof(_abi.sarathi_debug_dump) == 56
+
+
+def desc(**kw):
+    d = dict(hidden=256, n_heads=4, head_dim=64, ffn=688, arch=0, dtype=0, norm_eps=1e-6,
+             rope_base=10000.0, max_tokens=64, max_pos=256)
+    d.update(kw)
+    return _abi.sarathi_layer_desc(*[d[f] for f, _ in _abi.sarathi_layer_desc._fields_])
+
+
+# Fake, non-overlapping "device" addresses: validation only compares them.
+BASE = 1 << 40
+SLAB = 1 << 30
+
+
+def addr(i):
+    return BASE + i * SLAB
+
+
+def batch(C=32, off=0, cap=128, lens=(17, 33), caps=None, x=addr(0), y=addr(1), share=None):
+    caps = caps or [L + 1 for L in lens]
+    dkv = [(addr(10 + 2 * i), addr(11 + 2 * i), c) for i, c in enumerate(caps)]
+    if share is not None:
+        dkv[share[0]] = dkv[share[1]]
+    return _abi.make_batch(C, off, (addr(2), addr(3), cap), dkv, list(lens), x, y)
+
+
+def test_valid_batch_ok(lib):
+    b, keep = batch()
+    assert _abi.sarathi_batch_check(desc(), b) == _abi.SARATHI_OK
+    n = _abi.sarathi_workspace_size(desc(), b)
+    assert n > 0 and n % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=0, lens=()), _abi.SARATHI_ERR_INVALID),                 # empty batch
+    (dict(C=-1), _abi.SARATHI_ERR_INVALID),
+    (dict(C=30, cap=128, off=100), _abi.SARATHI_ERR_CAPACITY),       # chunk past capacity
+    (dict(lens=(17, 40), caps=[18, 40]), _abi.SARATHI_ERR_CAPACITY),  # decode slot past capacity
+    (dict(lens=(17, -1), caps=[18, 5]), _abi.SARATHI_ERR_INVALID),   # negative length
+    (dict(share=(0, 1)), _abi.SARATHI_ERR_INVALID),                  # two decodes share a cache
+    (dict(y=addr(0) + 100), _abi.SARATHI_ERR_INVALID),               # y overlaps x
+    (dict(x=0), _abi.SARATHI_ERR_INVALID),                           # null x
+    (dict(lens=(300,), caps=[400]), _abi.SARATHI_ERR_CAPACITY),      # position >= max_pos
+    (dict(C=60, lens=(1, 2, 3, 4, 5)), _abi.SARATHI_ERR_INVALID),    # C+B > max_tokens
+])
+def test_invalid_batches(lib, kw, status):
+    b, keep = batch(**kw)
+    assert _abi.sarathi_batch_check(desc(), b) == status
+    assert _abi.sarathi_last_error() != ""
+    if "x" not in kw and "y" not in kw:   # the workspace query does not need x and y
+        assert _abi.sarathi_workspace_size(desc(), b) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), _abi.SARATHI_ERR_UNSUPPORTED),
+    (dict(hidden=200), _abi.SARATHI_ERR_UNSUPPORTED),
+    (dict(dtype=1, ffn=688), _abi.SARATHI_ERR_UNSUPPORTED),   # bf16 needs ffn % 64 == 0
+    (dict(arch=7), _abi.SARATHI_ERR_INVALID),
+    (dict(max_pos=0), _abi.SARATHI_ERR_INVALID),
+])
+def test_invalid_descriptions(lib, kw, status):
+    b, keep = batch()
+    assert _abi.sarathi_batch_check(desc(**kw), b) == status
+
+
+def test_chunk_cache_ignored_for_decode_only(lib):
+    b, keep = _abi.make_batch(0, 0, None, [(addr(10), addr(11), 18)], [17], addr(0), addr(1))
+    assert _abi.sarathi_batch_check(desc(), b) == _abi.SARATHI_OK
+
+
+def test_status_strings(lib):
+    assert _abi.sarathi_status_str(0) == "ok"
+    assert "capacity" in _abi.sarathi_status_str(_abi.SARATHI_ERR_CAPACITY)
+    assert _abi.sarathi_status_str(-99) == "unknown status"
+
+
+def test_create_rejects_bad_description_before_any_hip_call(lib):
+    w = _abi.sarathi_weights(*([addr(20)] * 9))
+    with pytest.raises(_abi.SarathiError) as e:
+        _abi.sarathi_layer_create(desc(head_dim=96), w)
+    assert e.value.status == _abi.SARATHI_ERR_UNSUPPORTED
