@@ -1,0 +1,240 @@
+"""Throughput of the hybrid-batch decoder-layer forward on one MI355X.
+
+One step = one forward of one decoder layer over one hybrid batch: a prefill chunk plus piggybacked
+decodes (SARATHI: Efficient LLM Inference by Piggybacking Decodes with Chunked Prefills, section 3,
+"Decode-Maximal Batching").  Default workload: LLaMA-13B layer shape in bf16, chunk C=256 at offset
+768 of a 1024-token prompt plus B=18 decodes with 1024 cached entries each.  Inputs are seeded and
+synthetic and already resident in HBM when timing starts.  Three replicas of the weights, caches and
+activations are rotated step by step so that the 256 MB last-level cache cannot hold a step's data.
+
+Prints ONE JSON line: tokens/s over the timed steps, the roofline of the dominant kernel (per-kernel
+durations come from HIP events the library records on the launch stream during the timed steps), the
+per-stage breakdown, and the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "hybrid-batch layer tokens/s (chunk+decodes); % bf16 MFMA and HBM roofline"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha1()
+    for p in sorted(glob.glob(os.path.join(ROOT, "chunked_prefill_hybrid_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:12]
+
+
+def stage_work(shape, C, off, lens):
+    """Algorithmic work of each stage: (flops, bytes).  GEMM flops use the unpadded row count."""
+    T = C + len(lens)
+    H, A, F = shape.hidden, shape.attn_width, shape.ffn
+    el = 2 if shape.dtype == "bf16" else 4
+    up_n = 2 * F if shape.gated else F
+    w = {
+        "qkv": (2.0 * T * H * 3 * A, el * (3 * A * H + T * H + T * 3 * A)),
+        "o": (2.0 * T * A * H, el * (H * A + T * A + T * H) + 4 * T * H),
+        "ffn_up": (2.0 * T * H * up_n, el * (up_n * H + T * H + T * F)),
+        "ffn_down": (2.0 * T * F * H, el * (H * F + T * F + T * H) + 4 * T * H),
+        # decode attention streams each decode's K and V over its L_i + 1 keys, plus its query
+        "attn_decode": (4.0 * A * sum(L + 1 for L in lens), el * sum(2 * A * (L + 1) + A for L in lens)),
+        "attn_chunk": (4.0 * A * (C * off + C * (C + 1) / 2), el * (2 * A * (off + C) + 2 * C * A)),
+        "norm1": (0.0, el * 2 * T * H),
+        "norm2": (0.0, (4 + el) * T * H),
+        "rope_append": (0.0, el * 2 * T * 3 * A),
+        "attn_merge": (0.0, 0.0),
+    }
+    return w
+
+
+BOUND = {"qkv": "mfma", "o": "mfma", "ffn_up": "mfma", "ffn_down": "mfma", "attn_chunk": "mfma",
+         "attn_decode": "hbm", "norm1": "hbm", "norm2": "hbm", "rope_append": "hbm", "attn_merge": "hbm"}
+
+
+def roofline_entry(stage, avg_ms, flops, nbytes, dtype):
+    bound = BOUND[stage]
+    if bound == "mfma":
+        achieved = flops / (avg_ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+        unit = "TFLOP/s"
+    else:
+        achieved = nbytes / (avg_ms * 1e-3) / 1e9
+        peak = PEAK_HBM_GBS
+        unit = "GB/s"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4)}
+
+
+def load_traffic(stage, workload_key):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel source, if recorded."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{workload_key}:{stage}")
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wk, weights, batch, budget_s=25.0):
+    """The CPU oracle (as it is, float64 NumPy) on the full batch, repeated while it stays within the
+    time budget; BLAS threads capped at 16 (one GPU's share of host cores)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    cores = min(16, os.cpu_count() or 1)
+    times = []
+    with threadpool_limits(limits=cores, user_api="blas"):
+        used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.layer_forward(wk.shape, weights, batch)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start + times[-1] > budget_s or len(times) >= 3:
+                break
+    T = batch["chunk_len"] + len(batch["decode_len"])
+    t = statistics.median(times)
+    return {"value": round(T / t, 2), "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"full batch ({T} rows, one layer, float64 NumPy), {len(times)} run(s), median {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama13b")
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build measures a single MI355X "
+              f"(got --gpus {args.gpus}); multi-GPU sharding is described in the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from chunked_prefill_hybrid_amd import _abi
+    from chunked_prefill_hybrid_amd import layer as hl
+    from chunked_prefill_hybrid_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    wk = wl.workload(args.workload)
+    shape = wk.shape
+    weights, batch = wl.generate(wk)
+    C, off, lens = batch["chunk_len"], batch["chunk_offset"], list(batch["decode_len"])
+    T = C + len(lens)
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+
+    def dev(a, t=dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+
+    wdev = {k: dev(v, torch.float32 if k.startswith("norm") else dt) for k, v in weights.items() if v is not None}
+    base = {"x": dev(batch["x"]), "ck": dev(batch["chunk_k"]), "cv": dev(batch["chunk_v"]),
+            "dk": [dev(k) for k in batch["decode_k"]], "dv": [dev(v) for v in batch["decode_v"]]}
+    max_pos = max([off + C] + [L + 1 for L in lens])
+    reps = []
+    for r in range(args.replicas):
+        cl = (lambda t: t) if r == 0 else (lambda t: t.clone())
+        wr = {k: cl(v) for k, v in wdev.items()}
+        layer = hl.HybridLayer(shape, wr, max_tokens=T, max_pos=max_pos)
+        x = cl(base["x"])
+        y = torch.empty_like(x)
+        ck, cv = cl(base["ck"]), cl(base["cv"])
+        dkv = [(cl(k), cl(v)) for k, v in zip(base["dk"], base["dv"])]
+        b, keep = layer.batch(x, y, C, off, (ck, cv), dkv, lens)
+        ws = torch.empty(layer.workspace_size(b), dtype=torch.uint8, device="cuda")
+        reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, bufs=(x, y, ck, cv, dkv, wr)))
+    stream = torch.cuda.current_stream().cuda_stream
+    timer = _abi.sarathi_timer_create(args.steps)
+
+    def step(i, timed):
+        r = reps[i % len(reps)]
+        nb = r["ws"].numel()
+        if timed:
+            _abi.sarathi_layer_forward_timed(r["layer"].handle, r["b"], r["ws"].data_ptr(), nb, stream, timer)
+        else:
+            _abi.sarathi_layer_forward(r["layer"].handle, r["b"], r["ws"].data_ptr(), nb, stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stages = _abi.sarathi_timer_read(timer)
+    _abi.sarathi_timer_destroy(timer)
+
+    work = stage_work(shape, C, off, lens)
+    breakdown = {}
+    for name, (tot, cnt) in stages.items():
+        if cnt == 0:
+            continue
+        avg = tot / cnt
+        fl, by = work[name]
+        e = roofline_entry(name, avg, fl, by, shape.dtype)
+        breakdown[name] = {"avg_us": round(avg * 1e3, 2), "frac": e["frac"], "bound": e["bound"],
+                           "achieved": e["achieved"], "unit": e["unit"]}
+    dominant = max(breakdown, key=lambda n: breakdown[n]["avg_us"])
+    dom_avg_ms = breakdown[dominant]["avg_us"] / 1e3
+    roof = roofline_entry(dominant, dom_avg_ms, *work[dominant], shape.dtype)
+    roof["traffic"] = load_traffic(dominant, wk.key)
+    roof["kernel"] = dominant
+    gemm_ms = sum(breakdown[n]["avg_us"] for n in ("qkv", "o", "ffn_up", "ffn_down")) / 1e3
+    gemm_flops = sum(work[n][0] for n in ("qkv", "o", "ffn_up", "ffn_down"))
+    summary = {
+        "gemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "decode_attn_hbm_frac": breakdown.get("attn_decode", {}).get("frac"),
+        "sum_of_stages_us": round(sum(v["avg_us"] for v in breakdown.values()), 2),
+    }
+
+    ms_per_step = elapsed / args.steps * 1e3
+    value = T * args.steps / elapsed
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name} layer, chunk C={C} at offset {off} + {len(lens)} decodes "
+                               f"(KV lengths {min(lens) if lens else 0}..{max(lens) if lens else 0})",
+                   "hidden": shape.hidden, "heads": shape.n_heads, "head_dim": shape.head_dim,
+                   "ffn": shape.ffn, "chunk": C, "chunk_offset": off, "decodes": len(lens),
+                   "rows": T, "replicas": args.replicas},
+        "roofline": roof,
+        "stages": breakdown,
+        "summary": summary,
+        "kernel_source": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wk, weights, batch)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    for r in reps:
+        r["layer"].close()
+
+
+if __name__ == "__main__":
+    main()

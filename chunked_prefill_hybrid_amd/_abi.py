@@ -29,8 +29,13 @@ SARATHI_ARCH_GPT = 1
 EXPORTED = [
     "sarathi_layer_create", "sarathi_layer_destroy", "sarathi_batch_check", "sarathi_workspace_size",
     "sarathi_layer_forward", "sarathi_layer_forward_debug", "sarathi_gemm", "sarathi_attention",
-    "sarathi_status_str", "sarathi_last_error",
+    "sarathi_status_str", "sarathi_last_error", "sarathi_timer_create", "sarathi_timer_destroy",
+    "sarathi_layer_forward_timed", "sarathi_timer_read",
 ]
+
+STAGES = ["norm1", "qkv", "rope_append", "attn_chunk", "attn_decode", "attn_merge", "o", "norm2",
+          "ffn_up", "ffn_down"]
+N_STAGES = len(STAGES)
 
 
 class sarathi_layer_desc(ctypes.Structure):
@@ -95,6 +100,15 @@ def lib():
         L.sarathi_attention.argtypes = [POINTER(sarathi_layer_desc), POINTER(sarathi_batch), c_void_p,
                                         c_void_p, c_void_p, c_size_t, c_void_p]
         L.sarathi_attention.restype = c_int32
+        L.sarathi_timer_create.argtypes = [c_int32, POINTER(c_void_p)]
+        L.sarathi_timer_create.restype = c_int32
+        L.sarathi_timer_destroy.argtypes = [c_void_p]
+        L.sarathi_timer_destroy.restype = None
+        L.sarathi_layer_forward_timed.argtypes = [c_void_p, POINTER(sarathi_batch), c_void_p, c_size_t,
+                                                  c_void_p, c_void_p]
+        L.sarathi_layer_forward_timed.restype = c_int32
+        L.sarathi_timer_read.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int32)]
+        L.sarathi_timer_read.restype = c_int32
         L.sarathi_status_str.argtypes = [c_int32]
         L.sarathi_status_str.restype = c_char_p
         L.sarathi_last_error.argtypes = []
@@ -152,6 +166,30 @@ def sarathi_attention(desc: sarathi_layer_desc, batch: sarathi_batch, q: int, ou
                       ws_bytes: int, stream: int) -> None:
     _check(lib().sarathi_attention(byref(desc), byref(batch), q, out, ws, ws_bytes, stream),
            "sarathi_attention")
+
+
+def sarathi_timer_create(capacity: int) -> int:
+    h = c_void_p()
+    _check(lib().sarathi_timer_create(capacity, byref(h)), "sarathi_timer_create")
+    return h.value
+
+
+def sarathi_timer_destroy(timer: int) -> None:
+    lib().sarathi_timer_destroy(timer)
+
+
+def sarathi_layer_forward_timed(handle: int, batch: sarathi_batch, ws: int, ws_bytes: int, stream: int,
+                                timer: int) -> None:
+    _check(lib().sarathi_layer_forward_timed(handle, byref(batch), ws, ws_bytes, stream, timer),
+           "sarathi_layer_forward_timed")
+
+
+def sarathi_timer_read(timer: int):
+    """{stage name: (total_ms, count)} over the forwards recorded since the last read."""
+    tot = (ctypes.c_double * N_STAGES)()
+    cnt = (c_int32 * N_STAGES)()
+    _check(lib().sarathi_timer_read(timer, tot, cnt), "sarathi_timer_read")
+    return {STAGES[i]: (tot[i], cnt[i]) for i in range(N_STAGES)}
 
 
 def make_batch(chunk_len: int, chunk_offset: int, chunk_kv, decode_kv, decode_len, x: int, y: int):

@@ -30,6 +30,13 @@ struct sarathi_layer {
   int device;
 };
 
+struct sarathi_timer {
+  int capacity;
+  int used;                       // forwards recorded since the last read
+  std::vector<hipEvent_t> ev;     // [capacity][SARATHI_N_STAGES + 1]
+  std::vector<uint32_t> ran;      // per recorded forward: bit s set if stage s launched work
+};
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -210,30 +217,58 @@ DecodeGroup decode_group(const sarathi_batch *b, int base) {
       return fail(SARATHI_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));        \
   } while (0)
 
-// Attention of all batch rows, split per request: writes out [T, A] (storage type).
+// Records one event before the first stage and one after every stage position (stages without work
+// still get their event so that indices stay fixed; their bit in `ran` stays clear).
+struct Marker {
+  sarathi_timer *t = nullptr;
+  hipStream_t s = nullptr;
+  int f = 0;
+  hipError_t begin() {
+    if (!t) return hipSuccess;
+    f = t->used;
+    t->ran[f] = 0;
+    return hipEventRecord(t->ev[(size_t)f * (SARATHI_N_STAGES + 1)], s);
+  }
+  hipError_t end(int stage, bool ran) {
+    if (!t) return hipSuccess;
+    if (ran) t->ran[f] |= 1u << stage;
+    return hipEventRecord(t->ev[(size_t)f * (SARATHI_N_STAGES + 1) + stage + 1], s);
+  }
+  void commit() {
+    if (t) t->used++;
+  }
+};
+
+// Attention of all batch rows, split per request: chunk rows, then decode rows (64 per launch
+// group), then one merge of the split partials; writes out [T, A] (storage type).
 sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b, const Plan &p,
-                             const void *q, void *out, char *ws, hipStream_t s) {
+                             const void *q, void *out, char *ws, hipStream_t s, Marker &mk) {
   const int A = d->n_heads * d->head_dim;
+  const int C = b->chunk_len, B = b->n_decodes;
   const ChunkRef ch = chunk_ref(b);
   float *po = reinterpret_cast<float *>(ws + p.part_o);
   float *pml = reinterpret_cast<float *>(ws + p.part_ml);
-  // Launch groups: the chunk rows with the first decodes, then further decodes 64 at a time.
-  int base = 0;
-  do {
+  if (C > 0) {
+    const DecodeGroup none = decode_group(b, B);   // empty group
+    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, ch, none, p.max_splits,
+                             po, pml, s));
+  }
+  HIP_TRY(mk.end(SARATHI_STAGE_ATTN_CHUNK, C > 0));
+  for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
     const DecodeGroup g = decode_group(b, base);
-    const int row0 = base == 0 ? 0 : b->chunk_len + base;
-    const int n_rows = (base == 0 ? b->chunk_len : 0) + g.n;
-    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, row0, n_rows, ch, g,
+    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, ch, g,
                              p.max_splits, po, pml, s));
-    HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, row0, n_rows, p.max_splits, po,
-                                pml, out, A, s));
-    base += kMaxDecodesPerLaunch;
-  } while (base < b->n_decodes);
+  }
+  HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
+  HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, 0, C + B, p.max_splits, po, pml,
+                              out, A, s));
+  HIP_TRY(mk.end(SARATHI_STAGE_ATTN_MERGE, true));
   return SARATHI_OK;
 }
 
 sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *workspace,
-                            size_t ws_bytes, void *stream, const sarathi_debug_dump *dump) {
+                            size_t ws_bytes, void *stream, const sarathi_debug_dump *dump,
+                            sarathi_timer *timer) {
   if (!L) return fail(SARATHI_ERR_INVALID, "layer is null");
   const sarathi_layer_desc *d = &L->desc;
   sarathi_status st = check_batch(d, b, true);
@@ -243,9 +278,15 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   if ((uintptr_t)workspace % 256) return fail(SARATHI_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (ws_bytes < p.total)
     return fail(SARATHI_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+  if (timer && timer->used >= timer->capacity)
+    return fail(SARATHI_ERR_INVALID, "timer is full (%d unread forwards)", timer->used);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
+  Marker mk;
+  mk.t = timer;
+  mk.s = s;
+  HIP_TRY(mk.begin());
   const int ty = d->dtype, T = p.T, R = p.T_alloc;
   const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
   const bool llama = d->arch == SARATHI_ARCH_LLAMA;
@@ -255,11 +296,13 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
 
   // 1. norm 1 over the C+B rows (pad rows zeroed)
   HIP_TRY(launch_norm(ty, ty, !llama, b->x, L->w.norm1_w, L->w.norm1_b, n1, H, T, R, d->norm_eps, s));
+  HIP_TRY(mk.end(SARATHI_STAGE_NORM1, true));
   // 2. QKV projection: one GEMM over chunk and decode rows
   GemmArgs g{};
   g.a = n1; g.lda = H; g.w0 = L->w.w_qkv; g.ldw = H; g.out = qkv; g.ldo = 3 * A;
   g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
   HIP_TRY(launch_gemm(ty, kEpiStore, g, s));
+  HIP_TRY(mk.end(SARATHI_STAGE_QKV, true));
   // 3. RoPE + KV append (per launch group of decodes)
   const ChunkRef ch = chunk_ref(b);
   {
@@ -273,16 +316,19 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
       base += kMaxDecodesPerLaunch;
     } while (base < b->n_decodes);
   }
+  HIP_TRY(mk.end(SARATHI_STAGE_ROPE_APPEND, true));
   // 4. attention, split per request
-  st = run_attention(d, b, p, q, attn, ws, s);
+  st = run_attention(d, b, p, q, attn, ws, s, mk);
   if (st != SARATHI_OK) return st;
   // 5. O projection + residual (h1 kept in float32)
   g = GemmArgs{};
   g.a = attn; g.lda = A; g.w0 = L->w.w_o; g.ldw = A; g.out = h1; g.ldo = H;
   g.resid = b->x; g.ldr = H; g.m_alloc = R; g.m_store = T; g.n = H; g.k = A;
   HIP_TRY(launch_gemm(ty, kEpiResidF32, g, s));
+  HIP_TRY(mk.end(SARATHI_STAGE_O, true));
   // 6. norm 2
   HIP_TRY(launch_norm(kF32, ty, !llama, h1, L->w.norm2_w, L->w.norm2_b, n2, H, T, R, d->norm_eps, s));
+  HIP_TRY(mk.end(SARATHI_STAGE_NORM2, true));
   // 7. FFN up (+gate) with the activation fused
   g = GemmArgs{};
   g.a = n2; g.lda = H; g.ldw = H; g.out = act; g.ldo = F; g.m_alloc = R; g.m_store = T; g.n = F;
@@ -294,11 +340,14 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
     g.w0 = L->w.w_up;
     HIP_TRY(launch_gemm(ty, kEpiGelu, g, s));
   }
+  HIP_TRY(mk.end(SARATHI_STAGE_FFN_UP, true));
   // 8. down projection + residual -> y
   g = GemmArgs{};
   g.a = act; g.lda = F; g.w0 = L->w.w_down; g.ldw = F; g.out = b->y; g.ldo = H;
   g.resid = h1; g.ldr = H; g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
   HIP_TRY(launch_gemm(ty, kEpiResidOut, g, s));
+  HIP_TRY(mk.end(SARATHI_STAGE_FFN_DOWN, true));
+  mk.commit();
 
   if (dump) {
     if (dump->n1) HIP_TRY(launch_to_f32(ty, n1, H, dump->n1, H, T, H, s));
@@ -383,13 +432,13 @@ size_t sarathi_workspace_size(const sarathi_layer_desc *desc, const sarathi_batc
 
 sarathi_status sarathi_layer_forward(sarathi_layer *layer, const sarathi_batch *batch,
                                      void *workspace, size_t ws_bytes, void *stream) {
-  return forward_impl(layer, batch, workspace, ws_bytes, stream, nullptr);
+  return forward_impl(layer, batch, workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
 sarathi_status sarathi_layer_forward_debug(sarathi_layer *layer, const sarathi_batch *batch,
                                            void *workspace, size_t ws_bytes, void *stream,
                                            const sarathi_debug_dump *dump) {
-  return forward_impl(layer, batch, workspace, ws_bytes, stream, dump);
+  return forward_impl(layer, batch, workspace, ws_bytes, stream, dump, nullptr);
 }
 
 sarathi_status sarathi_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a,
@@ -418,8 +467,67 @@ sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_b
   if ((uintptr_t)workspace % 256) return fail(SARATHI_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (ws_bytes < p.total)
     return fail(SARATHI_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+  Marker none;
   return run_attention(desc, batch, p, q, out, static_cast<char *>(workspace),
-                       static_cast<hipStream_t>(stream));
+                       static_cast<hipStream_t>(stream), none);
+}
+
+sarathi_status sarathi_timer_create(int32_t capacity, sarathi_timer **out) {
+  if (!out) return fail(SARATHI_ERR_INVALID, "out is null");
+  *out = nullptr;
+  if (capacity <= 0 || capacity > (1 << 20)) return fail(SARATHI_ERR_INVALID, "bad timer capacity");
+  sarathi_timer *t = new (std::nothrow) sarathi_timer();
+  if (!t) return fail(SARATHI_ERR_NOMEM, "host allocation failed");
+  t->capacity = capacity;
+  t->used = 0;
+  t->ran.assign(capacity, 0);
+  t->ev.reserve((size_t)capacity * (SARATHI_N_STAGES + 1));
+  for (size_t i = 0; i < (size_t)capacity * (SARATHI_N_STAGES + 1); ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      sarathi_timer_destroy(t);
+      return fail(SARATHI_ERR_HIP, "hipEventCreate failed");
+    }
+    t->ev.push_back(e);
+  }
+  *out = t;
+  return SARATHI_OK;
+}
+
+void sarathi_timer_destroy(sarathi_timer *timer) {
+  if (!timer) return;
+  for (hipEvent_t e : timer->ev) (void)hipEventDestroy(e);
+  delete timer;
+}
+
+sarathi_status sarathi_layer_forward_timed(sarathi_layer *layer, const sarathi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           sarathi_timer *timer) {
+  if (!timer) return fail(SARATHI_ERR_INVALID, "timer is null");
+  return forward_impl(layer, batch, workspace, ws_bytes, stream, nullptr, timer);
+}
+
+sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_t *count) {
+  if (!timer || !total_ms || !count) return fail(SARATHI_ERR_INVALID, "null argument");
+  for (int st = 0; st < SARATHI_N_STAGES; ++st) {
+    total_ms[st] = 0.0;
+    count[st] = 0;
+  }
+  const int n = timer->used;
+  timer->used = 0;
+  if (n == 0) return SARATHI_OK;
+  HIP_TRY(hipEventSynchronize(timer->ev[(size_t)(n - 1) * (SARATHI_N_STAGES + 1) + SARATHI_N_STAGES]));
+  for (int f = 0; f < n; ++f) {
+    const hipEvent_t *e = &timer->ev[(size_t)f * (SARATHI_N_STAGES + 1)];
+    for (int st = 0; st < SARATHI_N_STAGES; ++st) {
+      if (!(timer->ran[f] >> st & 1u)) continue;
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, e[st], e[st + 1]));
+      total_ms[st] += ms;
+      count[st] += 1;
+    }
+  }
+  return SARATHI_OK;
 }
 
 const char *sarathi_status_str(sarathi_status status) {

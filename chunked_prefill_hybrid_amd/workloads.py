@@ -10,13 +10,18 @@ None of the layer's arithmetic lives here.  The HIP path and the CPU oracle both
 as they are; the only numeric step is rounding the drawn values to bfloat16 (round to nearest even)
 for the bf16 workloads, so that both sides see identical, exactly representable inputs.
 
-Draw order (fixed, so that every sweep point of one shape shares its weights): W_qkv, W_o, W_gate,
-W_up, W_down, then X, then the chunk request's prefix cache (K then V), then the decode lengths, then
-each decode cache in request order (K then V).
+Seeding.  A workload's root numpy SeedSequence(seed) spawns one child stream per drawn tensor, in a
+fixed order (so every sweep point of one shape shares its weights): W_qkv, W_o, W_gate (gated shapes
+only), W_up, W_down, then X, then the chunk request's prefix cache (K then V), then the decode
+lengths, then each decode cache in request order (K then V).  A tensor's values are drawn in fixed
+blocks of 2^22 elements, block i from PCG64 seeded by the i-th child of the tensor's stream, so the
+result does not depend on how many threads fill the blocks.
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
 import dataclasses
+import os
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence, Tuple
 
@@ -144,21 +149,59 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return b.view(np.float32).reshape(np.shape(x))
 
 
-def _finish(a: np.ndarray, dtype: str) -> np.ndarray:
-    a = a.astype(np.float32, copy=False)
-    return bf16_round(a) if dtype == "bf16" else a
+_BLOCK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
-def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
-    a = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        a *= np.float32(std)
-    return _finish(a, dtype)
+class Draws:
+    """The ordered child streams of one workload seed."""
+
+    def __init__(self, seed: int):
+        self._root = np.random.SeedSequence(seed)
+
+    def next(self) -> np.random.SeedSequence:
+        return self._root.spawn(1)[0]
+
+    def generator(self) -> np.random.Generator:
+        return np.random.Generator(np.random.PCG64(self.next()))
 
 
-def make_weights(shape: LayerShape, rng: np.random.Generator) -> dict:
+def as_draws(rng) -> Draws:
+    """A Draws from a Draws, an int seed, or a numpy Generator (which supplies the seed)."""
+    if isinstance(rng, Draws):
+        return rng
+    if isinstance(rng, np.random.Generator):
+        return Draws(int(rng.integers(0, 2 ** 63 - 1)))
+    return Draws(int(rng))
+
+
+def _normal(draws: Draws, shape, std: float, dtype: str) -> np.ndarray:
+    """float32 N(0, std^2) values of the given shape from the next stream, bf16-rounded if asked."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    seeds = draws.next().spawn(max(1, -(-n // _BLOCK)))
+
+    def fill(i):
+        seg = out[i * _BLOCK:(i + 1) * _BLOCK]
+        np.random.Generator(np.random.PCG64(seeds[i])).standard_normal(out=seg, dtype=np.float32)
+        if std != 1.0:
+            seg *= np.float32(std)
+        if dtype == "bf16":
+            seg[:] = bf16_round(seg)
+
+    if len(seeds) == 1:
+        fill(0)
+    else:
+        with _cf.ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(len(seeds))))
+    return out.reshape(shape)
+
+
+def make_weights(shape: LayerShape, rng) -> dict:
     """Layer weights, each stored [out_features, in_features] (y = x @ W.T).  W_qkv's rows are
-    [Q | K | V], each block head-major.  Norm gains are 1 and biases 0 (none are drawn)."""
+    [Q | K | V], each block head-major.  Norm gains are 1 and biases 0 (none are drawn).
+    rng: a Draws (or a seed)."""
+    rng = as_draws(rng)
     h, a, f = shape.hidden, shape.attn_width, shape.ffn
 
     def std(fan_in):
@@ -177,27 +220,32 @@ def make_weights(shape: LayerShape, rng: np.random.Generator) -> dict:
     return w
 
 
-def _cache(rng, shape: LayerShape, cap: int, filled: int, fill_rest: float) -> Tuple[np.ndarray, np.ndarray]:
+def _cache(draws: Draws, shape: LayerShape, cap: int, filled: int, fill_rest: float):
     """One request's K and V caches, each [n_heads, cap, head_dim]; slots 0..filled-1 hold N(0,1)
-    draws (K first, then V), the remaining slots hold fill_rest."""
+    draws (K from one stream, then V from the next), the remaining slots hold fill_rest."""
     nh, d = shape.n_heads, shape.head_dim
     out = []
     for _ in range(2):
-        c = np.full((nh, cap, d), fill_rest, np.float32)
-        if filled:
-            c[:, :filled, :] = _normal(rng, (nh, filled, d), 1.0, shape.dtype)
+        vals = _normal(draws, (nh, filled, d), 1.0, shape.dtype) if filled else None
+        if filled == cap:
+            c = vals
+        else:
+            c = np.empty((nh, cap, d), np.float32)
+            c[:, filled:, :] = fill_rest
+            if filled:
+                c[:, :filled, :] = vals
         out.append(c)
     return out[0], out[1]
 
 
-def make_batch(shape: LayerShape, spec: BatchSpec, rng: np.random.Generator,
-               fill_rest: float = 0.0) -> dict:
+def make_batch(shape: LayerShape, spec: BatchSpec, rng, fill_rest: float = 0.0) -> dict:
     """Hidden states and caches of one hybrid batch (drawn after the weights from the same rng).
 
     The chunk request's cache has capacity prompt_len (at least offset+C) and holds N(0,1) entries in
     its prefix slots 0..offset-1.  Decode i's cache has capacity decode_len[i]+1 and holds N(0,1)
     entries in slots 0..decode_len[i]-1.  Unwritten slots hold fill_rest (tests use NaN there to
-    catch reads past a request's keys)."""
+    catch reads past a request's keys).  rng: the Draws the weights came from (or a seed)."""
+    rng = as_draws(rng)
     C, B = spec.chunk_len, spec.n_decodes
     x = _normal(rng, (C + B, shape.hidden), 1.0, shape.dtype)
     cap = max(spec.prompt_len, spec.chunk_offset + C, 1)
@@ -207,7 +255,7 @@ def make_batch(shape: LayerShape, spec: BatchSpec, rng: np.random.Generator,
         assert len(lens) == B, "decode_lens must list one length per decode"
     elif B:
         lo, hi = spec.decode_len_range
-        lens = [int(v) for v in rng.integers(lo, hi, size=B, endpoint=True)]
+        lens = [int(v) for v in rng.generator().integers(lo, hi, size=B, endpoint=True)]
     else:
         lens = []
     dk, dv = [], []
@@ -220,8 +268,8 @@ def make_batch(shape: LayerShape, spec: BatchSpec, rng: np.random.Generator,
 
 
 def generate(w: Workload, fill_rest: float = 0.0) -> Tuple[dict, dict]:
-    """(weights, batch) of a workload, drawn from default_rng(seed) in the fixed order."""
-    rng = np.random.default_rng(w.seed)
+    """(weights, batch) of a workload, drawn from its seed in the fixed order."""
+    rng = Draws(w.seed)
     weights = make_weights(w.shape, rng)
     batch = make_batch(w.shape, w.batch, rng, fill_rest)
     return weights, batch
@@ -239,7 +287,7 @@ def tiny_schedule(seed: int = 0, n_chunks: int = 4, chunk: int = 32,
     Returns (shape, weights, prompt_x [n_chunks*chunk, H], decode_x [n_chunks, B, H],
     decode_k, decode_v, decode_lens)."""
     shape = SHAPES["tiny"]
-    rng = np.random.default_rng(seed)
+    rng = Draws(seed)
     weights = make_weights(shape, rng)
     prompt_x = _normal(rng, (n_chunks * chunk, shape.hidden), 1.0, shape.dtype)
     dk, dv = [], []

@@ -168,6 +168,47 @@ sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_b
                                  const void *q, void *out, void *workspace, size_t ws_bytes,
                                  void *stream);
 
+/* ---- Per-stage timing (measurement only) ------------------------------------------------------
+ * The layer's forward runs as the stages below, in this order (per-operation profile of a hybrid
+ * iteration: preproj, attention, postproj, FFN; SARATHI: Efficient LLM Inference by Piggybacking
+ * Decodes with Chunked Prefills, section 3, "Implementation" (per-operation profiling) and section 5,
+ * per-operation runtime breakdown).  A stage with no work in a batch (e.g. chunk attention when
+ * C == 0) is not counted. */
+typedef enum {
+    SARATHI_STAGE_NORM1 = 0,       /* norm 1 over the C+B rows */
+    SARATHI_STAGE_QKV = 1,         /* QKV GEMM */
+    SARATHI_STAGE_ROPE_APPEND = 2, /* RoPE + KV-cache append */
+    SARATHI_STAGE_ATTN_CHUNK = 3,  /* chunk attention (prefix + causal chunk) */
+    SARATHI_STAGE_ATTN_DECODE = 4, /* decode attention (split-KV partials) */
+    SARATHI_STAGE_ATTN_MERGE = 5,  /* merge of split partials */
+    SARATHI_STAGE_O = 6,           /* O GEMM + residual */
+    SARATHI_STAGE_NORM2 = 7,
+    SARATHI_STAGE_FFN_UP = 8,      /* gate/up GEMM + SiLU*mul, or up GEMM + GELU */
+    SARATHI_STAGE_FFN_DOWN = 9,    /* down GEMM + residual */
+    SARATHI_N_STAGES = 10
+} sarathi_stage;
+
+typedef struct sarathi_timer sarathi_timer;   /* opaque */
+
+/* Creates a timer able to hold the events of `capacity` forwards between two reads (it creates
+ * capacity * (SARATHI_N_STAGES + 1) HIP events on the current device).  Errors: INVALID, HIP. */
+sarathi_status sarathi_timer_create(int32_t capacity, sarathi_timer **out);
+
+/* Destroys the timer's events.  No forward recording into it may be in flight.  NULL is a no-op. */
+void sarathi_timer_destroy(sarathi_timer *timer);
+
+/* As sarathi_layer_forward, and records one HIP event on `stream` before the first stage and after
+ * each stage into the timer (no synchronisation).  Errors: as the forward; INVALID if the timer
+ * already holds `capacity` unread forwards (nothing is enqueued then). */
+sarathi_status sarathi_layer_forward_timed(sarathi_layer *layer, const sarathi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           sarathi_timer *timer);
+
+/* Waits for the recorded events, adds each stage's elapsed milliseconds over all recorded forwards
+ * into total_ms[s] and the number of forwards in which stage s ran into count[s] (host arrays of
+ * SARATHI_N_STAGES entries, overwritten), then empties the timer.  Errors: INVALID, HIP. */
+sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_t *count);
+
 /* Static description of a status code. */
 const char *sarathi_status_str(sarathi_status status);
 

@@ -1,0 +1,48 @@
+"""GPU parity at the workloads' full sizes (needs an MI355X): every configured layer shape and batch,
+run through the C ABI in the launch configuration the benchmark times, compared with the CPU oracle
+evaluated on the whole batch (float64)."""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_prefill_hybrid_amd import layer as hl
+from chunked_prefill_hybrid_amd import workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+def run_full(wk):
+    t0 = time.time()
+    gu.say(f"case full-size {wk.key} C={wk.batch.chunk_len} off={wk.batch.chunk_offset} "
+           f"B={wk.batch.n_decodes}")
+    w, b = wl.generate(wk)
+    gu.say(f"  generated in {time.time() - t0:.1f}s; lengths {b['decode_len'][:8]}...")
+    shape = wk.shape
+    T = b["chunk_len"] + len(b["decode_len"])
+    max_pos = max([b["chunk_offset"] + b["chunk_len"]] + [L + 1 for L in b["decode_len"]])
+    layer = hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=T, max_pos=max_pos)
+    db = gu.upload_batch(shape, b)
+    dd = gu.run(layer, db)
+    gu.say(f"  gpu done at {time.time() - t0:.1f}s")
+    ref = oracle.layer_forward(shape, w, b)
+    gu.say(f"  oracle done at {time.time() - t0:.1f}s")
+    gu.compare(shape, b, ref, db, dd, label=f"{wk.key} full")
+    layer.close()
+
+
+@pytest.mark.parametrize("key", ["llama13b", "gpt3tp8", "llama33b", "llama13b_long"])
+def test_full_size_workload(key):
+    run_full(wl.workload(key))
+
+
+@pytest.mark.parametrize("key,changes", [
+    ("llama13b", dict(chunk_len=0)),                         # decode-only part
+    ("llama13b", dict(n_decodes=0, decode_lens=())),         # chunk-only part
+    ("llama33b", dict(chunk_len=257, prompt_len=257)),       # tile-quantization point
+    ("gpt3tp8", dict(n_decodes=1, decode_lens=(2048,))),     # P:D sweep end point
+])
+def test_full_size_sweep_points(key, changes):
+    run_full(wl.workload(key, **changes))
