@@ -4,12 +4,16 @@
 // decode rows together, so each weight tile crosses HBM once for the whole batch and the decodes
 // share the chunk's weight fetches (SARATHI: Efficient LLM Inference by Piggybacking Decodes with
 // Chunked Prefills, section 3, "Decode-Maximal Batching", "How fusion works").  The token dimension
-// is padded only to the tile height; rows past C+B are never stored (the tile-quantization point of
-// the same page, "Identifying the Ideal Chunk Size", Figure 7).
+// is padded only to 32 rows; rows past C+B are never stored (the tile-quantization point of the same
+// page, "Identifying the Ideal Chunk Size", Figure 7, restated for 16-row MFMA blocks).
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16, 4 waves per workgroup, A and W tiles staged through LDS with
-// double buffering, BK = 64.  Workgroup b runs on XCD b % 8; the tiles of one weight stripe (all its
-// row tiles) are given to workgroups of the same XCD so that the stripe's re-reads hit that XCD's L2.
+// bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 320; larger batches
+// take a few row tiles) and a 128-column stripe of the weights, so a weight tile is read once for
+// the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 160 rows x 32 columns.  A and W
+// k-tiles (64 wide) are staged through LDS with double buffering.  When the weight stripes alone do
+// not fill the 256 compute units, the k range is split: each split writes a float32 partial and the
+// kernel that consumes the product sums the partials in a fixed order (deterministic, no atomics).
+// Workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight stripe.
 // fp32 path: a plain FMA tile kernel (exact float32 products, used by the float32 layer mode).
 #include <math.h>
 
@@ -20,121 +24,166 @@ namespace {
 
 constexpr int kBK = 64;         // k extent of one LDS stage (bf16 elements)
 constexpr int kLdsK = kBK + 8;  // padded LDS row: 144 bytes keeps the 16-byte fragment reads spread
+constexpr int kWM = 2, kWN = 4, kThreads = 64 * kWM * kWN;
+constexpr int kMBW = 10;        // max 16-row blocks per wave row: 320 rows per tile
+constexpr int kNB = 2;          // 16-column blocks per wave: 128 columns per tile
+constexpr int kBN = 16 * kNB * kWN;
+constexpr int kBMX = 16 * kMBW * kWM;
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_mfma(GemmArgs g, int m_tiles, int n_tiles,
-                                                       int n_per_xcd) {
-  static_assert(WM * WN == 4, "four waves per workgroup");
-  constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
-  constexpr int MB = WTM / 16, NB = WTN / 16;       // 16x16 MFMA blocks per wave
+template <int MB, int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
+  static_assert(MB >= 1 && MB <= kMBW, "16-row blocks per wave row");
   constexpr bool kGlu = EPI == kEpiSwiGLU;
-  static_assert(!kGlu || NB % 2 == 0, "SwiGLU pairs gate and up blocks inside a wave");
-  constexpr int A_LD = BM * (kBK / 8) / 256, B_LD = BN * (kBK / 8) / 256;
-  static_assert(A_LD * 256 == BM * (kBK / 8) && B_LD * 256 == BN * (kBK / 8), "whole 16-B loads");
-  constexpr int kStage = (BM + BN) * kLdsK;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kStage];
+  constexpr int A_CH = (kBMX * (kBK / 8) + kThreads - 1) / kThreads;   // 16-B A chunks per thread
+  constexpr int B_CH = kBN * (kBK / 8) / kThreads;
+  constexpr int kStage = (kBMX + kBN) * kLdsK;
+  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
 
-  // XCD-aware tile order: consecutive slots of one XCD walk the row tiles of one weight stripe.
+  // Tile of this workgroup (XCD-aware order: slot s of XCD x takes tile x * per_xcd + s).
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int n_tile = xcd * n_per_xcd + slot / m_tiles;
-  const int m_tile = slot % m_tiles;
-  if (n_tile >= n_tiles) return;
-  const int m0 = m_tile * BM;
-  const int n0 = n_tile * (kGlu ? BN / 2 : BN);      // first output column of the tile
+  const int t = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (t >= p.m_tiles * p.n_tiles * p.splits) return;
+  const int m_tile = t % p.m_tiles;
+  const int rest = t / p.m_tiles;
+  const int split = rest % p.splits;
+  const int n_tile = rest / p.splits;
+  constexpr int mbw = MB;                   // 16-row blocks per wave row
+  constexpr int rows = 32 * MB;             // rows of the tile
+  const int m0 = m_tile * rows;
+  const int n0 = n_tile * (kGlu ? kBN / 2 : kBN);
+  const int nk = g.k / kBK;
+  const int kb = (int)((long long)split * nk / p.splits);
+  const int ke = (int)((long long)(split + 1) * nk / p.splits);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / kWN, wn = wave % kWN;
   const bf16_t *A = static_cast<const bf16_t *>(g.a);
   const bf16_t *W0 = static_cast<const bf16_t *>(g.w0);
   const bf16_t *W1 = static_cast<const bf16_t *>(g.w1);
 
-  const bf16_t *a_src[A_LD];
-  int a_dst[A_LD];
+  // Every thread always loads its chunks (rows clamped into the matrix): rows past the tile land in
+  // LDS rows no wave reads, and branch-free loads keep the load counters exact across the k loop.
+  static_assert(A_CH * kThreads == kBMX * (kBK / 8), "A chunks cover the LDS rows exactly");
+  const bf16_t *a_src[A_CH];
+  int a_dst[A_CH];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int c = tid + i * 256, row = c >> 3, kc = c & 7;
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + i * kThreads, row = c >> 3, kc = c & 7;
     const int gr = min(m0 + row, g.m_alloc - 1);
-    a_src[i] = A + (size_t)gr * g.lda + kc * 8;
+    a_src[i] = A + (size_t)gr * g.lda + kc * 8 + (size_t)kb * kBK;
     a_dst[i] = row * kLdsK + kc * 8;
   }
-  const bf16_t *b_src[B_LD];
-  int b_dst[B_LD];
+  const bf16_t *b_src[B_CH];
+  int b_dst[B_CH];
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int c = tid + i * 256, row = c >> 3, kc = c & 7;
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = tid + i * kThreads, row = c >> 3, kc = c & 7;
     int src_row;
     const bf16_t *Wp = W0;
     if (kGlu) {
-      // LDS rows of wave wv: NB/2 gate blocks then the NB/2 up blocks of the same columns.
-      const int wv = row / WTN, bb = (row % WTN) >> 4, rl = row & 15;
-      const int cb = wv * (NB / 2) + bb % (NB / 2);
+      // LDS rows of wave column wv: its gate block(s), then the up block(s) of the same columns.
+      const int wv = row / (16 * kNB), bb = (row >> 4) % kNB, rl = row & 15;
+      const int cb = wv * (kNB / 2) + bb % (kNB / 2);
       src_row = n0 + cb * 16 + rl;
-      Wp = (bb >= NB / 2) ? W1 : W0;
+      Wp = (bb >= kNB / 2) ? W1 : W0;
     } else {
-      src_row = n0 + row;
+      src_row = min(n0 + row, g.n - 1);
+      if (g.w1 && src_row >= g.n_w0) {   // the second weight continues the product's rows
+        Wp = W1;
+        src_row -= g.n_w0;
+      }
     }
-    src_row = min(src_row, g.n - 1);
-    b_src[i] = Wp + (size_t)src_row * g.ldw + kc * 8;
-    b_dst[i] = (BM + row) * kLdsK + kc * 8;
+    src_row = kGlu ? min(src_row, g.n - 1) : src_row;
+    b_src[i] = Wp + (size_t)src_row * g.ldw + kc * 8 + (size_t)kb * kBK;
+    b_dst[i] = (kBMX + row) * kLdsK + kc * 8;
   }
 
-  f32x4_t acc[MB][NB];
+  f32x4_t acc[MB][kNB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[A_LD], rb[B_LD];
-  const int nk = g.k / kBK;
+  // Register rings: weight k-tiles are fetched kDW tiles ahead of their use (they come from HBM),
+  // activation k-tiles kDA ahead (they are shared by every workgroup and mostly hit L2).  Two LDS
+  // stages: tile j is computed from stage j&1 while tile j+1 is written into the other stage.
+  // Tile indices past the end are clamped (a few redundant loads) so that the steady-state loop body
+  // has no branches around its loads.
+  constexpr int kDW = 4, kDA = 1, kUnrollK = 4;   // kUnrollK: multiple of both ring depths
+  uint4 ra[kDA][A_CH], rb[kDW][B_CH];
+  const int ntiles = ke - kb;
+  auto tile = [&](int j) { return min(j, ntiles - 1) * kBK; };
+  auto load_a = [&](int slot, int j) {
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) ra[i] = ld16(a_src[i]);
+    for (int i = 0; i < A_CH; ++i) ra[slot][i] = ld16(a_src[i] + tile(j));
+  };
+  auto load_b = [&](int slot, int j) {
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) rb[i] = ld16(b_src[i]);
+    for (int i = 0; i < B_CH; ++i) rb[slot][i] = ld16(b_src[i] + tile(j));
+  };
+  auto store_tile = [&](int aslot, int bslot, int stage) {
+    bf16_t *Ls = lds + stage * kStage;
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) st16(&lds[a_dst[i]], ra[i]);
+    for (int i = 0; i < A_CH; ++i) st16(&Ls[a_dst[i]], ra[aslot][i]);
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) st16(&lds[b_dst[i]], rb[i]);
-  __syncthreads();
-
+    for (int i = 0; i < B_CH; ++i) st16(&Ls[b_dst[i]], rb[bslot][i]);
+  };
   const int frag_row = lane & 15, frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const bf16_t *L = lds + (kt & 1) * kStage;
-    if (kt + 1 < nk) {
-      const int ko = (kt + 1) * kBK;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) ra[i] = ld16(a_src[i] + ko);
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) rb[i] = ld16(b_src[i] + ko);
-    }
+  const int a_row0 = wm * 16 * mbw;
+  auto compute = [&](int stage) {
+    const bf16_t *L = lds + stage * kStage;
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
-      bf16x8_t af[MB], bw[NB];
+      bf16x8_t bw[kNB];
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        bw[nb] = *reinterpret_cast<const bf16x8_t *>(
+            &L[(kBMX + wn * 16 * kNB + nb * 16 + frag_row) * kLdsK + ks * 32 + frag_k]);
+      bf16x8_t af[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         af[mb] = *reinterpret_cast<const bf16x8_t *>(
-            &L[(wm * WTM + mb * 16 + frag_row) * kLdsK + ks * 32 + frag_k]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        bw[nb] = *reinterpret_cast<const bf16x8_t *>(
-            &L[(BM + wn * WTN + nb * 16 + frag_row) * kLdsK + ks * 32 + frag_k]);
+            &L[(a_row0 + mb * 16 + frag_row) * kLdsK + ks * 32 + frag_k]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bw[nb], acc[mb][nb], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      bf16_t *Ln = lds + ((kt + 1) & 1) * kStage;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) st16(&Ln[a_dst[i]], ra[i]);
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) st16(&Ln[b_dst[i]], rb[i]);
-    }
+  };
+  // One step: compute tile j (ring position u = j mod kUnrollK), stage tile j+1 into the other LDS
+  // buffer, refill the freed ring slots, barrier.
+  auto step = [&](int u, int j) {
+    compute(u & 1);
+    const int as = (u + 1) % kDA, bs = (u + 1) % kDW;   // ring slots of tile j+1
+    store_tile(as, bs, (u + 1) & 1);
+    load_a(as, j + 1 + kDA);
+    load_b(bs, j + 1 + kDW);
     __syncthreads();
+  };
+
+#pragma unroll
+  for (int j = 0; j < kDW; ++j) load_b(j, j);
+#pragma unroll
+  for (int j = 0; j < kDA; ++j) load_a(j, j);
+  store_tile(0, 0, 0);
+  load_a(0, kDA);
+  load_b(0, kDW);
+  __syncthreads();
+
+  const int nsteps = ntiles - 1;   // tiles followed by another tile
+  int j0 = 0;
+  for (; j0 + kUnrollK <= nsteps; j0 += kUnrollK) {
+#pragma unroll
+    for (int u = 0; u < kUnrollK; ++u) step(u, j0 + u);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnrollK; ++u) {
+    if (j0 + u < nsteps) step(u, j0 + u);
+    else if (j0 + u == nsteps) compute(u & 1);   // the last tile
   }
 
   // Epilogue.  Lane l of a 16x16 block holds rows 4*(l/16)+i, column l%16.
@@ -142,27 +191,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(GemmArgs g, int m_tiles, i
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * WTM + mb * 16 + (lane >> 4) * 4 + i;
+      const int m = m0 + a_row0 + mb * 16 + (lane >> 4) * 4 + i;
       if (m >= g.m_store) continue;
 #pragma unroll
-      for (int nb = 0; nb < (kGlu ? NB / 2 : NB); ++nb) {
+      for (int nb = 0; nb < (kGlu ? kNB / 2 : kNB); ++nb) {
         if (kGlu) {
-          const int n = n0 + (wn * (NB / 2) + nb) * 16 + (lane & 15);
+          const int n = n0 + (wn * (kNB / 2) + nb) * 16 + (lane & 15);
           if (n >= g.n) continue;
-          const float gt = acc[mb][nb][i], up = acc[mb][nb + NB / 2][i];
+          const float gt = acc[mb][nb][i], up = acc[mb][nb + kNB / 2][i];
           static_cast<bf16_t *>(g.out)[(size_t)m * g.ldo + n] = f32_to_bf16(silu_f(gt) * up);
         } else {
-          const int n = n0 + wn * WTN + nb * 16 + (lane & 15);
+          const int n = n0 + wn * 16 * kNB + nb * 16 + (lane & 15);
           if (n >= g.n) continue;
           const float v = acc[mb][nb][i];
-          if (EPI == kEpiStore) {
+          if (EPI == kEpiPartial) {
+            g.part[((size_t)split * g.m_store + m) * g.n + n] = v;
+          } else if (EPI == kEpiStore) {
             static_cast<bf16_t *>(g.out)[(size_t)m * g.ldo + n] = f32_to_bf16(v);
-          } else if (EPI == kEpiResidF32) {
-            const float r = to_f32(static_cast<const bf16_t *>(g.resid)[(size_t)m * g.ldr + n]);
-            static_cast<float *>(g.out)[(size_t)m * g.ldo + n] = v + r;
-          } else if (EPI == kEpiResidOut) {
-            const float r = static_cast<const float *>(g.resid)[(size_t)m * g.ldr + n];
-            static_cast<bf16_t *>(g.out)[(size_t)m * g.ldo + n] = f32_to_bf16(v + r);
           } else {  // kEpiGelu
             static_cast<bf16_t *>(g.out)[(size_t)m * g.ldo + n] = f32_to_bf16(gelu_f(v));
           }
@@ -225,32 +270,47 @@ __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs g) {
       const int n = n0 + tx + 16 * j;
       if (n >= g.n) continue;
       const float v = acc[i][j];
-      float *o = static_cast<float *>(g.out) + (size_t)m * g.ldo + n;
-      if (EPI == kEpiStore) *o = v;
-      else if (EPI == kEpiResidF32 || EPI == kEpiResidOut)
-        *o = v + static_cast<const float *>(g.resid)[(size_t)m * g.ldr + n];
-      else if (EPI == kEpiSwiGLU) *o = silu_f(v) * acc2[i][j];
-      else *o = gelu_f(v);
+      if (EPI == kEpiPartial) g.part[(size_t)m * g.n + n] = v;   // one split in float32 mode
+      else {
+        float *o = static_cast<float *>(g.out) + (size_t)m * g.ldo + n;
+        if (EPI == kEpiStore) *o = v;
+        else if (EPI == kEpiSwiGLU) *o = silu_f(v) * acc2[i][j];
+        else *o = gelu_f(v);
+      }
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
-  const int m_tiles = (g.m_store + BM - 1) / BM;
-  const int cols_per_tile = EPI == kEpiSwiGLU ? BN / 2 : BN;
-  const int n_tiles = (g.n + cols_per_tile - 1) / cols_per_tile;
-  const int n_per_xcd = (n_tiles + 7) / 8;
-  const int grid = 8 * n_per_xcd * m_tiles;
-  hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, WM, WN, EPI>), dim3(grid), dim3(256), 0, s, g, m_tiles,
-                     n_tiles, n_per_xcd);
+constexpr size_t kLdsBytes = 2 * (size_t)(kBMX + kBN) * kLdsK * sizeof(bf16_t);
+
+template <int MB, int EPI>
+hipError_t run_bf16_mb(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  static bool attr_set = false;   // one LDS opt-in per instantiation (host-side, idempotent)
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_rows<MB, EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_bf16_rows<MB, EPI>), dim3(p.grid), dim3(kThreads), kLdsBytes, s, g, p);
   return hipGetLastError();
 }
 
 template <int EPI>
-hipError_t dispatch_bf16(const GemmArgs &g, hipStream_t s) {
-  if (g.m_store <= 32) return run_bf16<32, 128, 1, 4, EPI>(g, s);
-  return run_bf16<64, 128, 2, 2, EPI>(g, s);
+hipError_t run_bf16(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  switch (p.mbw) {
+    case 1: return run_bf16_mb<1, EPI>(g, p, s);
+    case 2: return run_bf16_mb<2, EPI>(g, p, s);
+    case 3: return run_bf16_mb<3, EPI>(g, p, s);
+    case 4: return run_bf16_mb<4, EPI>(g, p, s);
+    case 5: return run_bf16_mb<5, EPI>(g, p, s);
+    case 6: return run_bf16_mb<6, EPI>(g, p, s);
+    case 7: return run_bf16_mb<7, EPI>(g, p, s);
+    case 8: return run_bf16_mb<8, EPI>(g, p, s);
+    case 9: return run_bf16_mb<9, EPI>(g, p, s);
+    case 10: return run_bf16_mb<10, EPI>(g, p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int EPI>
@@ -262,39 +322,83 @@ hipError_t run_f32(const GemmArgs &g, hipStream_t s) {
 
 }  // namespace
 
-GemmPlan plan_gemm(int type, int epi, int m, int n, int /*k*/) {
+GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
   GemmPlan p{};
+  p.epi = epi;
   if (type == kF32) {
-    p.bm = 64; p.bn = 64;
-    p.m_tiles = (m + 63) / 64; p.n_tiles = (n + 63) / 64;
+    p.m_tiles = (m + 63) / 64;
+    p.n_tiles = (n_out + 63) / 64;
+    p.splits = 1;
     p.grid = p.m_tiles * p.n_tiles;
     return p;
   }
-  p.bm = m <= 32 ? 32 : 64;
-  p.bn = 128;
-  const int cols = epi == kEpiSwiGLU ? p.bn / 2 : p.bn;
-  p.m_tiles = (m + p.bm - 1) / p.bm;
-  p.n_tiles = (n + cols - 1) / cols;
-  p.grid = 8 * ((p.n_tiles + 7) / 8) * p.m_tiles;
+  p.m_tiles = (m + kBMX - 1) / kBMX;
+  const int rows = (m + p.m_tiles - 1) / p.m_tiles;
+  p.mbw = (rows + 31) / 32;
+  const int nk = k / kBK;
+  // The split count and the epilogue form depend on the weight shape only, never on the number of
+  // batch rows: a row's k-sum is then cut at the same points whatever else is in the batch, so a
+  // decode run alone and the same decode inside a hybrid batch give bitwise-equal results.
+  // Time model for one 256-row tile: whole rounds of `cus` workgroups, each k-tile at ~half of a
+  // CU's MFMA rate, plus the float32 partials written and read back at ~5 TB/s.
+  const double m_ref = 256.0;
+  const double t_k = 2.0 * m_ref * kBN * kBK / 5.0e12;
+  auto est = [&](int tiles, int sp, double part_cols) {
+    const int rounds = (tiles * sp + cus - 1) / cus;
+    return rounds * (double)((nk + sp - 1) / sp) * t_k + (double)sp * m_ref * part_cols * 8.0 / 5.0e12;
+  };
+  auto best_split = [&](int tiles, double part_cols, double *t) {
+    int bs = 1;
+    double bt = 1e30;
+    for (int sp = 1; sp <= 8 && sp <= nk; ++sp) {
+      const double v = est(tiles, sp, part_cols);
+      if (v < bt * 0.98) { bt = v; bs = sp; }
+    }
+    *t = bt;
+    return bs;
+  };
+  if (epi == kEpiPartial || epi == kEpiStore) {
+    p.n_tiles = (n_out + kBN - 1) / kBN;
+    double t;
+    p.splits = epi == kEpiPartial ? best_split(p.n_tiles, n_out, &t) : 1;
+  } else {
+    // Fused activation (one pass, no partials) vs split product + activation pass.
+    const int n_prod = epi == kEpiSwiGLU ? 2 * n_out : n_out;
+    const int fcols = epi == kEpiSwiGLU ? kBN / 2 : kBN;
+    const int fused_tiles = (n_out + fcols - 1) / fcols;
+    const double t_fused = est(fused_tiles, 1, 0.0);
+    double t_split;
+    const int tiles_p = (n_prod + kBN - 1) / kBN;
+    const int sp = best_split(tiles_p, n_prod, &t_split);
+    if (t_split < 0.9 * t_fused) {
+      p.epi = kEpiPartial;
+      p.n_tiles = tiles_p;
+      p.splits = sp;
+    } else {
+      p.n_tiles = fused_tiles;
+      p.splits = 1;
+    }
+  }
+  const int total = p.m_tiles * p.n_tiles * p.splits;
+  p.per_xcd = (total + 7) / 8;
+  p.grid = 8 * p.per_xcd;
   return p;
 }
 
-hipError_t launch_gemm(int type, int epi, const GemmArgs &g, hipStream_t s) {
+hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   if (type == kF32) {
     switch (epi) {
       case kEpiStore: return run_f32<kEpiStore>(g, s);
-      case kEpiResidF32: return run_f32<kEpiResidF32>(g, s);
-      case kEpiResidOut: return run_f32<kEpiResidOut>(g, s);
+      case kEpiPartial: return run_f32<kEpiPartial>(g, s);
       case kEpiSwiGLU: return run_f32<kEpiSwiGLU>(g, s);
       case kEpiGelu: return run_f32<kEpiGelu>(g, s);
     }
   } else {
     switch (epi) {
-      case kEpiStore: return dispatch_bf16<kEpiStore>(g, s);
-      case kEpiResidF32: return dispatch_bf16<kEpiResidF32>(g, s);
-      case kEpiResidOut: return dispatch_bf16<kEpiResidOut>(g, s);
-      case kEpiSwiGLU: return dispatch_bf16<kEpiSwiGLU>(g, s);
-      case kEpiGelu: return dispatch_bf16<kEpiGelu>(g, s);
+      case kEpiStore: return run_bf16<kEpiStore>(g, p, s);
+      case kEpiPartial: return run_bf16<kEpiPartial>(g, p, s);
+      case kEpiSwiGLU: return run_bf16<kEpiSwiGLU>(g, p, s);
+      case kEpiGelu: return run_bf16<kEpiGelu>(g, p, s);
     }
   }
   return hipErrorInvalidValue;

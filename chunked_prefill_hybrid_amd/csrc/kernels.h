@@ -12,49 +12,68 @@ namespace sarathi {
 enum StorageType { kF32 = 0, kBF16 = 1 };
 
 // ---------------------------------------------------------------------------------------------
-// Row norms: out[r] = RMSNorm(x[r]) * g  or  LayerNorm(x[r]) * g + b, for r < rows; rows
-// rows..rows_alloc-1 of out are zero-filled.  x is `in_type` storage [rows, H]; out is `out_type`.
-hipError_t launch_norm(int in_type, int out_type, bool layernorm, const void *x, const float *g,
-                       const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                       hipStream_t s);
+// Row norms.  v[r] = resid[r] + sum_{s < splits} part[s][r]  (resid in `res_type` storage, the
+// split partials of a GEMM in float32 with slice stride rows*H; splits may be 0).  If sum_out is
+// non-null it receives v (float32).  out[r] = RMSNorm(v) * g  or  LayerNorm(v) * g + b for r < rows;
+// rows rows..rows_alloc-1 of out are zero-filled.
+hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
+                            const float *part, int splits, float *sum_out, const float *g,
+                            const float *b, void *out, int H, int rows, int rows_alloc, float eps,
+                            hipStream_t s);
+
+// FFN activation from split partials ([splits][rows][n_part] float32): gated (n_part = 2F):
+// out[r, j] = silu(sum_s part[s][r][j]) * sum_s part[s][r][F + j];  else (n_part = F):
+// out[r, j] = gelu(sum_s part[s][r][j]).  out is storage type [rows, F].
+hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int splits, void *out,
+                          int rows, int F, hipStream_t s);
+
+// out[r, c] = resid[r, c] + sum_{s < splits} part[s][r][c]  (resid float32, out storage type).
+hipError_t launch_resid_sum(int out_type, const float *resid, const float *part, int splits,
+                            void *out, int rows, int cols, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
-// GEMM  out[m, n] = epilogue( sum_k a[m, k] * w[n, k] )  over the concatenated batch rows.
+// GEMM  epilogue( sum_k a[m, k] * w[n, k] )  over the concatenated batch rows.
 enum Epilogue {
   kEpiStore = 0,     // out (storage) = acc
-  kEpiResidF32 = 1,  // out (float32) = acc + resid (storage)          [x + attn W_o^T]
-  kEpiResidOut = 2,  // out (storage) = acc + resid (float32)          [h1 + act W_down^T]
-  kEpiSwiGLU = 3,    // out (storage) = silu(a w0^T) * (a w1^T)         [gate, up]
-  kEpiGelu = 4,      // out (storage) = gelu(acc)                      [GPT MLP up]
+  kEpiPartial = 1,   // part[split][m][n] (float32) = acc over the split's k range
+  kEpiSwiGLU = 2,    // out (storage) = silu(a w0^T) * (a w1^T)         [gate, up]
+  kEpiGelu = 3,      // out (storage) = gelu(acc)                      [GPT MLP up]
 };
 
 struct GemmArgs {
   const void *a;      // [m_alloc, k], row stride lda (elements)
-  const void *w0;     // [n, k] row stride ldw
-  const void *w1;     // second weight of SwiGLU (up), else null
-  void *out;          // row stride ldo
-  const void *resid;  // residual input for kEpiResid*, row stride ldr
-  int lda, ldw, ldo, ldr;
+  const void *w0;     // [n, k] row stride ldw (rows 0..n_w0-1 when w1 continues it)
+  const void *w1;     // SwiGLU: the up weight.  kEpiPartial: rows n_w0..n-1 of the product's
+                      // weight (the up half of a gate|up product), else null
+  void *out;          // row stride ldo (kEpiStore / kEpiSwiGLU / kEpiGelu)
+  float *part;        // [splits][m_store][n] (kEpiPartial)
+  int lda, ldw, ldo;
   int m_alloc;        // rows of a that may be read
-  int m_store;        // rows of out that are written (m_store <= m_alloc)
+  int m_store;        // rows of the product that are written (m_store <= m_alloc)
   int n;              // output columns
-  int k;
+  int k;              // multiple of 64 in bf16 mode
+  int n_w0;           // kEpiPartial with w1: rows of the product taken from w0
 };
 
-hipError_t launch_gemm(int type, int epi, const GemmArgs &g, hipStream_t s);
-
-// Planned bf16 tile shape for a GEMM (exposed for tests and reports).
-struct GemmPlan { int bm, bn, m_tiles, n_tiles, grid; };
-GemmPlan plan_gemm(int type, int epi, int m, int n, int k);
+// Launch shape of one GEMM: m_tiles x n_tiles output tiles, each k range cut into `splits`;
+// mbw = 16-row blocks per wave row; the grid is 8 * per_xcd workgroups.
+struct GemmPlan { int epi, m_tiles, n_tiles, splits, mbw, per_xcd, grid; };
+// Plans a GEMM with epilogue `epi` (kEpiSwiGLU / kEpiGelu may come back as kEpiPartial when a split
+// product plus a separate activation pass is estimated faster; n is then the product width:
+// 2F for SwiGLU).  n_out is the output width of the epilogue (F for the FFN up products).
+GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus);
+hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
-// RoPE + KV append: for rows [row0, row0+n_rows) of the batch, reads q, k, v from qkv
-// [rows, 3A] (row stride ld_qkv), rotates q and k at the row's position (if use_rope) with the
-// float32 cos/sin table tab[pos * d/2 + j], writes q to q_out (row stride ld_q) and k, v into the
-// row's caches at slot pos.
-hipError_t launch_rope_append(int type, const void *qkv, int ld_qkv, void *q_out, int ld_q,
-                              const float2 *tab, int use_rope, int nh, int d, int row0, int n_rows,
-                              const ChunkRef &ch, const DecodeGroup &dg, hipStream_t s);
+// RoPE + KV append: for rows [row0, row0+n_rows) of the batch, sums the QKV GEMM's split partials
+// (float32 [splits][rows_total][3A]), rotates q and k at the row's position (if use_rope) with the
+// float32 cos/sin table tab[pos * d/2 + j], writes q to q_out (storage, row stride ld_q) and k, v
+// into the row's caches at slot pos.  If qkv_dump is non-null it receives the summed, unrotated
+// q|k|v row (float32 [rows, 3A]).
+hipError_t launch_rope_append(int type, const float *part, int splits, int rows_total, void *q_out,
+                              int ld_q, float *qkv_dump, const float2 *tab, int use_rope, int nh,
+                              int d, int row0, int n_rows, const ChunkRef &ch, const DecodeGroup &dg,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Split-KV single-query attention for rows [row0, row0+n_rows): each (row, head) attends over keys

@@ -1,14 +1,41 @@
-// Token-wise norms of the hybrid batch (run on the flattened C+B rows, like every non-attention op of
-// a hybrid iteration: junupark.xyz notes on Sarathi-Serve, "The effect of mixed batching", step 1).
-// RMSNorm: x / sqrt(mean(x^2) + eps) * g.  LayerNorm: (x - mean) / sqrt(var + eps) * g + b with the
-// biased variance.  One workgroup per row, 16-byte packets, float32 sums; rows past the batch are
-// written as zeros so the GEMM that consumes them computes on zeros.
+// Token-wise row ops of the hybrid batch (they run on the flattened C+B rows, like every
+// non-attention op of a hybrid iteration: junupark.xyz notes on Sarathi-Serve, "The effect of mixed
+// batching", step 1).
+//
+//   norm_rows:  v = resid + sum of a GEMM's split partials (in a fixed order), optionally stored
+//               (the residual stream h1), then RMSNorm v / sqrt(mean(v^2) + eps) * g or LayerNorm
+//               (v - mean) / sqrt(var + eps) * g + b (biased variance).  Rows past the batch are
+//               written as zeros so the next GEMM computes on zeros there.
+//   ffn_act:    the FFN activation silu(gate) * up or gelu(up) from split partials of the up GEMM.
+//   resid_sum:  out = resid + sum of a GEMM's split partials (the layer output y = h1 + FFN).
+// One workgroup per row, 4-element vectors, float32 sums.
 #include "kernels.h"
 
 namespace sarathi {
 namespace {
 
 constexpr int kThreads = 256;
+
+template <typename T> __device__ __forceinline__ void load4(const T *p, float *v);
+template <> __device__ __forceinline__ void load4<float>(const float *p, float *v) {
+  const float4 f = *reinterpret_cast<const float4 *>(p);
+  v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+}
+template <> __device__ __forceinline__ void load4<bf16_t>(const bf16_t *p, float *v) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+template <typename T> __device__ __forceinline__ void store4(T *p, const float *v);
+template <> __device__ __forceinline__ void store4<float>(float *p, const float *v) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, const float *v) {
+  uint2 u;
+  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2 *>(p) = u;
+}
 
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
@@ -22,79 +49,166 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
   return t;
 }
 
-template <typename Tin, typename Tout, bool LN>
-__global__ __launch_bounds__(kThreads) void norm_rows(const Tin *x, const float *g, const float *b,
-                                                      Tout *out, int H, int rows, float eps) {
-  __shared__ float red[kThreads / 64];
-  const int r = blockIdx.x;
-  constexpr int Ei = Packet<Tin>::E, Eo = Packet<Tout>::E;
-  Tout *o = out + (size_t)r * H;
-  if (r >= rows) {
-    for (int c = threadIdx.x * Eo; c < H; c += kThreads * Eo) st16(o + c, make_uint4(0, 0, 0, 0));
-    return;
-  }
-  const Tin *xr = x + (size_t)r * H;
-  float s = 0.f;
-  for (int c = threadIdx.x * Ei; c < H; c += kThreads * Ei) {
-    float v[Ei];
-    unpack<Tin>(ld16(xr + c), v);
+// v[0..3] = resid[r, c..c+3] + sum_s part[s][r][c..c+3]
+template <typename Tres>
+__device__ __forceinline__ void row_value(const Tres *resid, const float *part, int splits,
+                                          size_t slice, size_t off, float *v) {
+  load4<Tres>(resid + off, v);
+  for (int s = 0; s < splits; ++s) {
+    float p[4];
+    load4<float>(part + s * slice + off, p);
 #pragma unroll
-    for (int e = 0; e < Ei; ++e) s += LN ? v[e] : v[e] * v[e];
-  }
-  s = block_sum(s, red);
-  float mean = 0.f, ms;
-  if (LN) {
-    mean = s / (float)H;
-    float q = 0.f;
-    for (int c = threadIdx.x * Ei; c < H; c += kThreads * Ei) {
-      float v[Ei];
-      unpack<Tin>(ld16(xr + c), v);
-#pragma unroll
-      for (int e = 0; e < Ei; ++e) q += (v[e] - mean) * (v[e] - mean);
-    }
-    ms = block_sum(q, red) / (float)H;
-  } else {
-    ms = s / (float)H;
-  }
-  const float rstd = 1.0f / sqrtf(ms + eps);
-  for (int c = threadIdx.x * Eo; c < H; c += kThreads * Eo) {
-    float v[Eo];
-#pragma unroll
-    for (int e0 = 0; e0 < Eo; e0 += Ei) unpack<Tin>(ld16(xr + c + e0), v + e0);
-#pragma unroll
-    for (int e = 0; e < Eo; ++e) {
-      v[e] = (v[e] - mean) * rstd * g[c + e];
-      if (LN) v[e] += b[c + e];
-    }
-    st16(o + c, pack<Tout>(v));
+    for (int e = 0; e < 4; ++e) v[e] += p[e];
   }
 }
 
-template <typename Tin, typename Tout>
-hipError_t run(bool ln, const void *x, const float *g, const float *b, void *out, int H, int rows,
-               int rows_alloc, float eps, hipStream_t s) {
+template <typename Tres, typename Tout, bool LN>
+__global__ __launch_bounds__(kThreads) void norm_rows(const Tres *resid, const float *part,
+                                                      int splits, float *sum_out, const float *g,
+                                                      const float *b, Tout *out, int H, int rows,
+                                                      float eps) {
+  __shared__ float red[kThreads / 64];
+  const int r = blockIdx.x;
+  Tout *o = out + (size_t)r * H;
+  if (r >= rows) {
+    const float z[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) store4<Tout>(o + c, z);
+    return;
+  }
+  const size_t slice = (size_t)rows * H, row_off = (size_t)r * H;
+  float s1 = 0.f;
+  for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) {
+    float v[4];
+    row_value<Tres>(resid, part, splits, slice, row_off + c, v);
+    if (sum_out) store4<float>(sum_out + row_off + c, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s1 += LN ? v[e] : v[e] * v[e];
+  }
+  s1 = block_sum(s1, red);
+  float mean = 0.f, ms;
+  // The second and third passes re-read v: from sum_out (this thread's own writes) when kept,
+  // otherwise recomputed from the inputs.
+  auto value = [&](int c, float *v) {
+    if (sum_out) load4<float>(sum_out + row_off + c, v);
+    else row_value<Tres>(resid, part, splits, slice, row_off + c, v);
+  };
+  if (LN) {
+    mean = s1 / (float)H;
+    float q = 0.f;
+    for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) {
+      float v[4];
+      value(c, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q += (v[e] - mean) * (v[e] - mean);
+    }
+    ms = block_sum(q, red) / (float)H;
+  } else {
+    ms = s1 / (float)H;
+  }
+  const float rstd = 1.0f / sqrtf(ms + eps);
+  for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) {
+    float v[4];
+    value(c, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = (v[e] - mean) * rstd * g[c + e];
+      if (LN) v[e] += b[c + e];
+    }
+    store4<Tout>(o + c, v);
+  }
+}
+
+template <typename Tout>
+__global__ __launch_bounds__(kThreads) void resid_sum(const float *resid, const float *part,
+                                                      int splits, Tout *out, int rows, int cols) {
+  const size_t slice = (size_t)rows * cols, row_off = (size_t)blockIdx.x * cols;
+  for (int c = threadIdx.x * 4; c < cols; c += kThreads * 4) {
+    float v[4];
+    row_value<float>(resid, part, splits, slice, row_off + c, v);
+    store4<Tout>(out + row_off + c, v);
+  }
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+template <typename Tout, bool GATED>
+__global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int splits, Tout *out,
+                                                    int rows, int F) {
+  const int n_part = GATED ? 2 * F : F;
+  const size_t slice = (size_t)rows * n_part, row_off = (size_t)blockIdx.x * n_part;
+  for (int c = threadIdx.x * 4; c < F; c += kThreads * 4) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; ++s) {
+      float p[4];
+      load4<float>(part + s * slice + row_off + c, p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += p[e];
+      if (GATED) {
+        load4<float>(part + s * slice + row_off + F + c, p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] += p[e];
+      }
+    }
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = GATED ? silu_f(a[e]) * u[e] : gelu_f(a[e]);
+    store4<Tout>(out + (size_t)blockIdx.x * F + c, v);
+  }
+}
+
+template <typename Tres, typename Tout>
+hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, float *sum_out,
+                    const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
+                    float eps, hipStream_t s) {
   if (ln)
-    hipLaunchKernelGGL((norm_rows<Tin, Tout, true>), dim3(rows_alloc), dim3(kThreads), 0, s,
-                       static_cast<const Tin *>(x), g, b, static_cast<Tout *>(out), H, rows, eps);
+    hipLaunchKernelGGL((norm_rows<Tres, Tout, true>), dim3(rows_alloc), dim3(kThreads), 0, s,
+                       static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
+                       static_cast<Tout *>(out), H, rows, eps);
   else
-    hipLaunchKernelGGL((norm_rows<Tin, Tout, false>), dim3(rows_alloc), dim3(kThreads), 0, s,
-                       static_cast<const Tin *>(x), g, b, static_cast<Tout *>(out), H, rows, eps);
+    hipLaunchKernelGGL((norm_rows<Tres, Tout, false>), dim3(rows_alloc), dim3(kThreads), 0, s,
+                       static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
+                       static_cast<Tout *>(out), H, rows, eps);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_norm(int in_type, int out_type, bool layernorm, const void *x, const float *g,
-                       const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                       hipStream_t s) {
+hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
+                            const float *part, int splits, float *sum_out, const float *g,
+                            const float *b, void *out, int H, int rows, int rows_alloc, float eps,
+                            hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
-  if (in_type == kF32 && out_type == kF32)
-    return run<float, float>(layernorm, x, g, b, out, H, rows, rows_alloc, eps, s);
-  if (in_type == kBF16 && out_type == kBF16)
-    return run<bf16_t, bf16_t>(layernorm, x, g, b, out, H, rows, rows_alloc, eps, s);
-  if (in_type == kF32 && out_type == kBF16)
-    return run<float, bf16_t>(layernorm, x, g, b, out, H, rows, rows_alloc, eps, s);
+  if (res_type == kF32 && out_type == kF32)
+    return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, s);
+  if (res_type == kBF16 && out_type == kBF16)
+    return run_norm<bf16_t, bf16_t>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int splits, void *out,
+                          int rows, int F, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (out_type == kF32) {
+    if (gated) hipLaunchKernelGGL((ffn_act<float, true>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
+    else hipLaunchKernelGGL((ffn_act<float, false>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
+  } else {
+    if (gated) hipLaunchKernelGGL((ffn_act<bf16_t, true>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
+    else hipLaunchKernelGGL((ffn_act<bf16_t, false>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_sum(int out_type, const float *resid, const float *part, int splits,
+                            void *out, int rows, int cols, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (out_type == kF32)
+    hipLaunchKernelGGL(resid_sum<float>, dim3(rows), dim3(kThreads), 0, s, resid, part, splits,
+                       static_cast<float *>(out), rows, cols);
+  else
+    hipLaunchKernelGGL(resid_sum<bf16_t>, dim3(rows), dim3(kThreads), 0, s, resid, part, splits,
+                       static_cast<bf16_t *>(out), rows, cols);
+  return hipGetLastError();
 }
 
 }  // namespace sarathi

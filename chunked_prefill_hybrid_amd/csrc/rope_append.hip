@@ -6,33 +6,62 @@
 // Efficient LLM Inference by Piggybacking Decodes with Chunked Prefills, section 3,
 // "Implementation", KV cache pre-allocation).  The rotation pairs adjacent elements (2j, 2j+1) with
 // angle pos * base^(-2j/d); cos/sin come from a float32 table built on the host in float64.
-// One workgroup per row; every thread moves one 16-byte packet of q, k and v.
+// The q|k|v row is the sum of the QKV GEMM's float32 split partials, taken in split order; it is
+// rounded to the storage type only once, after the rotation.
+// One workgroup per row; every thread moves 4 consecutive elements of q, k and v.
 #include "kernels.h"
 
 namespace sarathi {
 namespace {
 
+template <typename T> __device__ __forceinline__ void put4(T *p, const float *v);
+template <> __device__ __forceinline__ void put4<float>(float *p, const float *v) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void put4<bf16_t>(bf16_t *p, const float *v) {
+  uint2 u;
+  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2 *>(p) = u;
+}
+
+__device__ __forceinline__ void sum4(const float *part, int splits, size_t slice, size_t off,
+                                     float *v) {
+  float4 a = *reinterpret_cast<const float4 *>(part + off);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  for (int s = 1; s < splits; ++s) {
+    a = *reinterpret_cast<const float4 *>(part + s * slice + off);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void rope_append(const T *qkv, int ld_qkv, T *q_out, int ld_q,
+__global__ __launch_bounds__(256) void rope_append(const float *part, int splits, int rows_total,
+                                                   T *q_out, int ld_q, float *qkv_dump,
                                                    const float2 *tab, int use_rope, int nh, int d,
                                                    int row0, ChunkRef ch, DecodeGroup dg) {
-  constexpr int E = Packet<T>::E;
   const int r = row0 + blockIdx.x;
   const int A = nh * d;
   const RowRef rr = row_ref(r, ch, dg);
   T *kc = reinterpret_cast<T *>(rr.k);
   T *vc = reinterpret_cast<T *>(rr.v);
-  const T *src = qkv + (size_t)r * ld_qkv;
-  for (int c = threadIdx.x * E; c < A; c += blockDim.x * E) {
+  const size_t slice = (size_t)rows_total * 3 * A, src = (size_t)r * 3 * A;
+  for (int c = threadIdx.x * 4; c < A; c += blockDim.x * 4) {
     const int h = c / d, e0 = c - h * d;
-    float q[E], k[E], v[E];
-    unpack<T>(ld16(src + c), q);
-    unpack<T>(ld16(src + A + c), k);
-    unpack<T>(ld16(src + 2 * A + c), v);
+    float q[4], k[4], v[4];
+    sum4(part, splits, slice, src + c, q);
+    sum4(part, splits, slice, src + A + c, k);
+    sum4(part, splits, slice, src + 2 * A + c, v);
+    if (qkv_dump) {
+      float *dr = qkv_dump + src;
+      *reinterpret_cast<float4 *>(dr + c) = make_float4(q[0], q[1], q[2], q[3]);
+      *reinterpret_cast<float4 *>(dr + A + c) = make_float4(k[0], k[1], k[2], k[3]);
+      *reinterpret_cast<float4 *>(dr + 2 * A + c) = make_float4(v[0], v[1], v[2], v[3]);
+    }
     if (use_rope) {
       const float2 *t = tab + (size_t)rr.pos * (d / 2) + e0 / 2;
 #pragma unroll
-      for (int u = 0; u < E / 2; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const float2 cs = t[u];
         const float q0 = q[2 * u], q1 = q[2 * u + 1], k0 = k[2 * u], k1 = k[2 * u + 1];
         q[2 * u] = q0 * cs.x - q1 * cs.y;
@@ -41,27 +70,26 @@ __global__ __launch_bounds__(256) void rope_append(const T *qkv, int ld_qkv, T *
         k[2 * u + 1] = k0 * cs.y + k1 * cs.x;
       }
     }
-    st16(q_out + (size_t)r * ld_q + c, pack<T>(q));
+    put4<T>(q_out + (size_t)r * ld_q + c, q);
     const size_t slot = ((size_t)h * rr.cap + rr.pos) * d + e0;
-    st16(kc + slot, pack<T>(k));
-    st16(vc + slot, pack<T>(v));
+    put4<T>(kc + slot, k);
+    put4<T>(vc + slot, v);
   }
 }
 
 }  // namespace
 
-hipError_t launch_rope_append(int type, const void *qkv, int ld_qkv, void *q_out, int ld_q,
-                              const float2 *tab, int use_rope, int nh, int d, int row0, int n_rows,
-                              const ChunkRef &ch, const DecodeGroup &dg, hipStream_t s) {
+hipError_t launch_rope_append(int type, const float *part, int splits, int rows_total, void *q_out,
+                              int ld_q, float *qkv_dump, const float2 *tab, int use_rope, int nh,
+                              int d, int row0, int n_rows, const ChunkRef &ch, const DecodeGroup &dg,
+                              hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
   if (type == kF32)
-    hipLaunchKernelGGL(rope_append<float>, dim3(n_rows), dim3(256), 0, s,
-                       static_cast<const float *>(qkv), ld_qkv, static_cast<float *>(q_out), ld_q,
-                       tab, use_rope, nh, d, row0, ch, dg);
+    hipLaunchKernelGGL(rope_append<float>, dim3(n_rows), dim3(256), 0, s, part, splits, rows_total,
+                       static_cast<float *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, ch, dg);
   else
-    hipLaunchKernelGGL(rope_append<bf16_t>, dim3(n_rows), dim3(256), 0, s,
-                       static_cast<const bf16_t *>(qkv), ld_qkv, static_cast<bf16_t *>(q_out), ld_q,
-                       tab, use_rope, nh, d, row0, ch, dg);
+    hipLaunchKernelGGL(rope_append<bf16_t>, dim3(n_rows), dim3(256), 0, s, part, splits, rows_total,
+                       static_cast<bf16_t *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, ch, dg);
   return hipGetLastError();
 }
 

@@ -149,10 +149,14 @@ sarathi_status check_batch(const sarathi_layer_desc *d, const sarathi_batch *b, 
   return SARATHI_OK;
 }
 
-// Workspace layout of one forward.
+// Workspace layout of one forward.  The GEMM plans are fixed by the shapes alone (planned for the
+// 256 compute units of an MI355X), so the workspace size depends only on the description and batch.
+constexpr int kPlanCUs = 256;
+
 struct Plan {
   int T, T_alloc, max_splits;
-  size_t n1, qkv, q, attn, h1, n2, act, part_o, part_ml, total;
+  GemmPlan qkv, o, up, down;
+  size_t n1, q, attn, h1, n2, act, part, part_o, part_ml, total;
 };
 
 int max_key_splits(const sarathi_batch *b) {
@@ -167,17 +171,27 @@ Plan make_plan(const sarathi_layer_desc *d, const sarathi_batch *b) {
   p.T = b->chunk_len + b->n_decodes;
   p.T_alloc = round_up(p.T, 64);
   p.max_splits = max_key_splits(b);
-  const size_t el = elem_size(d->dtype), R = p.T_alloc;
-  const size_t H = d->hidden, A = (size_t)d->n_heads * d->head_dim, F = d->ffn;
+  const int ty = d->dtype;
+  const size_t el = elem_size(ty), R = p.T_alloc;
+  const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
+  const bool llama = d->arch == SARATHI_ARCH_LLAMA;
+  p.qkv = plan_gemm(ty, kEpiPartial, p.T, 3 * A, H, kPlanCUs);
+  p.o = plan_gemm(ty, kEpiPartial, p.T, H, A, kPlanCUs);
+  p.up = plan_gemm(ty, llama ? kEpiSwiGLU : kEpiGelu, p.T, F, H, kPlanCUs);
+  p.down = plan_gemm(ty, kEpiPartial, p.T, H, F, kPlanCUs);
+  const size_t up_cols = p.up.epi == kEpiPartial ? (llama ? 2 * (size_t)F : F) : 0;
+  const size_t part_elems = std::max({(size_t)p.qkv.splits * p.T * 3 * A, (size_t)p.o.splits * p.T * H,
+                                      (size_t)p.down.splits * p.T * H,
+                                      (size_t)p.up.splits * p.T * up_cols});
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   p.n1 = take(R * H * el);
-  p.qkv = take(R * 3 * A * el);
   p.q = take(R * A * el);
   p.attn = take(R * A * el);
   p.h1 = take(R * H * 4);
   p.n2 = take(R * H * el);
   p.act = take(R * F * el);
+  p.part = take(part_elems * 4);
   p.part_o = take((size_t)p.T * d->n_heads * p.max_splits * d->head_dim * 4);
   p.part_ml = take((size_t)p.T * d->n_heads * p.max_splits * 2 * 4);
   p.total = off;
@@ -290,20 +304,22 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   const int ty = d->dtype, T = p.T, R = p.T_alloc;
   const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
   const bool llama = d->arch == SARATHI_ARCH_LLAMA;
-  void *n1 = ws + p.n1, *qkv = ws + p.qkv, *q = ws + p.q, *attn = ws + p.attn;
+  void *n1 = ws + p.n1, *q = ws + p.q, *attn = ws + p.attn;
   float *h1 = reinterpret_cast<float *>(ws + p.h1);
+  float *part = reinterpret_cast<float *>(ws + p.part);
   void *n2 = ws + p.n2, *act = ws + p.act;
 
   // 1. norm 1 over the C+B rows (pad rows zeroed)
-  HIP_TRY(launch_norm(ty, ty, !llama, b->x, L->w.norm1_w, L->w.norm1_b, n1, H, T, R, d->norm_eps, s));
+  HIP_TRY(launch_norm_rows(ty, ty, !llama, b->x, nullptr, 0, nullptr, L->w.norm1_w, L->w.norm1_b, n1,
+                           H, T, R, d->norm_eps, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM1, true));
-  // 2. QKV projection: one GEMM over chunk and decode rows
+  // 2. QKV projection: one GEMM over chunk and decode rows (float32 split partials)
   GemmArgs g{};
-  g.a = n1; g.lda = H; g.w0 = L->w.w_qkv; g.ldw = H; g.out = qkv; g.ldo = 3 * A;
+  g.a = n1; g.lda = H; g.w0 = L->w.w_qkv; g.ldw = H; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
-  HIP_TRY(launch_gemm(ty, kEpiStore, g, s));
+  HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.qkv, s));
   HIP_TRY(mk.end(SARATHI_STAGE_QKV, true));
-  // 3. RoPE + KV append (per launch group of decodes)
+  // 3. sum of the partials + RoPE + KV append (per launch group of decodes)
   const ChunkRef ch = chunk_ref(b);
   {
     int base = 0;
@@ -311,8 +327,9 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
       const DecodeGroup dg = decode_group(b, base);
       const int row0 = base == 0 ? 0 : b->chunk_len + base;
       const int n_rows = (base == 0 ? b->chunk_len : 0) + dg.n;
-      HIP_TRY(launch_rope_append(ty, qkv, 3 * A, q, A, L->rope_tab, llama ? 1 : 0, d->n_heads,
-                                 d->head_dim, row0, n_rows, ch, dg, s));
+      HIP_TRY(launch_rope_append(ty, part, p.qkv.splits, T, q, A, dump ? dump->qkv : nullptr,
+                                 L->rope_tab, llama ? 1 : 0, d->n_heads, d->head_dim, row0, n_rows,
+                                 ch, dg, s));
       base += kMaxDecodesPerLaunch;
     } while (base < b->n_decodes);
   }
@@ -320,38 +337,41 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   // 4. attention, split per request
   st = run_attention(d, b, p, q, attn, ws, s, mk);
   if (st != SARATHI_OK) return st;
-  // 5. O projection + residual (h1 kept in float32)
+  // 5. O projection (float32 split partials)
   g = GemmArgs{};
-  g.a = attn; g.lda = A; g.w0 = L->w.w_o; g.ldw = A; g.out = h1; g.ldo = H;
-  g.resid = b->x; g.ldr = H; g.m_alloc = R; g.m_store = T; g.n = H; g.k = A;
-  HIP_TRY(launch_gemm(ty, kEpiResidF32, g, s));
+  g.a = attn; g.lda = A; g.w0 = L->w.w_o; g.ldw = A; g.part = part;
+  g.m_alloc = R; g.m_store = T; g.n = H; g.k = A;
+  HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.o, s));
   HIP_TRY(mk.end(SARATHI_STAGE_O, true));
-  // 6. norm 2
-  HIP_TRY(launch_norm(kF32, ty, !llama, h1, L->w.norm2_w, L->w.norm2_b, n2, H, T, R, d->norm_eps, s));
+  // 6. h1 = x + sum of the O partials (kept in float32), then norm 2
+  HIP_TRY(launch_norm_rows(ty, ty, !llama, b->x, part, p.o.splits, h1, L->w.norm2_w, L->w.norm2_b, n2,
+                           H, T, R, d->norm_eps, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM2, true));
-  // 7. FFN up (+gate) with the activation fused
+  // 7. FFN up (+gate): activation fused into the GEMM, or split product + activation pass
   g = GemmArgs{};
-  g.a = n2; g.lda = H; g.ldw = H; g.out = act; g.ldo = F; g.m_alloc = R; g.m_store = T; g.n = F;
-  g.k = H;
-  if (llama) {
-    g.w0 = L->w.w_gate; g.w1 = L->w.w_up;
-    HIP_TRY(launch_gemm(ty, kEpiSwiGLU, g, s));
+  g.a = n2; g.lda = H; g.ldw = H; g.m_alloc = R; g.m_store = T; g.k = H;
+  g.w0 = llama ? L->w.w_gate : L->w.w_up;
+  g.w1 = llama ? L->w.w_up : nullptr;
+  if (p.up.epi == kEpiPartial) {
+    g.part = part; g.n = llama ? 2 * F : F; g.n_w0 = F;
+    HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.up, s));
+    HIP_TRY(launch_ffn_act(ty, llama, part, p.up.splits, act, T, F, s));
   } else {
-    g.w0 = L->w.w_up;
-    HIP_TRY(launch_gemm(ty, kEpiGelu, g, s));
+    g.out = act; g.ldo = F; g.n = F;
+    HIP_TRY(launch_gemm(ty, p.up.epi, g, p.up, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_FFN_UP, true));
-  // 8. down projection + residual -> y
+  // 8. down projection (split partials), y = h1 + sum of the partials
   g = GemmArgs{};
-  g.a = act; g.lda = F; g.w0 = L->w.w_down; g.ldw = F; g.out = b->y; g.ldo = H;
-  g.resid = h1; g.ldr = H; g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
-  HIP_TRY(launch_gemm(ty, kEpiResidOut, g, s));
+  g.a = act; g.lda = F; g.w0 = L->w.w_down; g.ldw = F; g.part = part;
+  g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
+  HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.down, s));
+  HIP_TRY(launch_resid_sum(ty, h1, part, p.down.splits, b->y, T, H, s));
   HIP_TRY(mk.end(SARATHI_STAGE_FFN_DOWN, true));
   mk.commit();
 
   if (dump) {
     if (dump->n1) HIP_TRY(launch_to_f32(ty, n1, H, dump->n1, H, T, H, s));
-    if (dump->qkv) HIP_TRY(launch_to_f32(ty, qkv, 3 * A, dump->qkv, 3 * A, T, 3 * A, s));
     if (dump->q_rot) HIP_TRY(launch_to_f32(ty, q, A, dump->q_rot, A, T, A, s));
     if (dump->attn) HIP_TRY(launch_to_f32(ty, attn, A, dump->attn, A, T, A, s));
     if (dump->h1) HIP_TRY(launch_to_f32(kF32, h1, H, dump->h1, H, T, H, s));
@@ -452,7 +472,8 @@ sarathi_status sarathi_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, cons
   GemmArgs g{};
   g.a = a; g.lda = k; g.w0 = w; g.ldw = k; g.out = out; g.ldo = n;
   g.m_alloc = m; g.m_store = m; g.n = n; g.k = k;
-  HIP_TRY(launch_gemm(dtype, kEpiStore, g, static_cast<hipStream_t>(stream)));
+  const GemmPlan plan = plan_gemm(dtype, kEpiStore, m, n, k, kPlanCUs);
+  HIP_TRY(launch_gemm(dtype, kEpiStore, g, plan, static_cast<hipStream_t>(stream)));
   return SARATHI_OK;
 }
 
