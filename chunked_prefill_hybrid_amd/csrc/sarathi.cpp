@@ -159,9 +159,14 @@ struct Plan {
   size_t n1, q, attn, h1, n2, act, part, part_o, part_ml, total;
 };
 
-int max_key_splits(const sarathi_batch *b) {
+// bf16 chunk rows run the flash-style MFMA kernel; the split-KV kernel (and its partials) serves the
+// decode rows, and the chunk rows too in float32 mode.
+bool chunk_uses_split(const sarathi_layer_desc *d) { return d->dtype != SARATHI_BF16; }
+
+int max_key_splits(const sarathi_layer_desc *d, const sarathi_batch *b) {
   int ms = 1;
-  if (b->chunk_len > 0) ms = std::max(ms, attn_splits(b->chunk_offset + b->chunk_len));
+  if (b->chunk_len > 0 && chunk_uses_split(d))
+    ms = std::max(ms, attn_splits(b->chunk_offset + b->chunk_len));
   for (int i = 0; i < b->n_decodes; ++i) ms = std::max(ms, attn_splits(b->decode_len[i] + 1));
   return ms;
 }
@@ -170,7 +175,7 @@ Plan make_plan(const sarathi_layer_desc *d, const sarathi_batch *b) {
   Plan p{};
   p.T = b->chunk_len + b->n_decodes;
   p.T_alloc = round_up(p.T, 64);
-  p.max_splits = max_key_splits(b);
+  p.max_splits = max_key_splits(d, b);
   const int ty = d->dtype;
   const size_t el = elem_size(ty), R = p.T_alloc;
   const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
@@ -262,10 +267,15 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
   const ChunkRef ch = chunk_ref(b);
   float *po = reinterpret_cast<float *>(ws + p.part_o);
   float *pml = reinterpret_cast<float *>(ws + p.part_ml);
+  const bool split_chunk = chunk_uses_split(d);
   if (C > 0) {
-    const DecodeGroup none = decode_group(b, B);   // empty group
-    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, ch, none, p.max_splits,
-                             po, pml, s));
+    if (split_chunk) {
+      const DecodeGroup none = decode_group(b, B);   // empty group
+      HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, ch, none,
+                               p.max_splits, po, pml, s));
+    } else {
+      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, ch, out, A, s));
+    }
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_CHUNK, C > 0));
   for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
@@ -274,9 +284,11 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
                              p.max_splits, po, pml, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
-  HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, 0, C + B, p.max_splits, po, pml,
-                              out, A, s));
-  HIP_TRY(mk.end(SARATHI_STAGE_ATTN_MERGE, true));
+  const int merge_row0 = split_chunk ? 0 : C;
+  if (C + B > merge_row0)
+    HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, merge_row0, C + B - merge_row0,
+                                p.max_splits, po, pml, out, A, s));
+  HIP_TRY(mk.end(SARATHI_STAGE_ATTN_MERGE, C + B > merge_row0));
   return SARATHI_OK;
 }
 
