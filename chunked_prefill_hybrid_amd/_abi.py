@@ -100,7 +100,7 @@ def lib():
         L.sarathi_attention.argtypes = [POINTER(sarathi_layer_desc), POINTER(sarathi_batch), c_void_p,
                                         c_void_p, c_void_p, c_size_t, c_void_p]
         L.sarathi_attention.restype = c_int32
-        L.sarathi_timer_create.argtypes = [c_int32, POINTER(c_void_p)]
+        L.sarathi_timer_create.argtypes = [c_int32, ctypes.c_uint32, POINTER(c_void_p)]
         L.sarathi_timer_create.restype = c_int32
         L.sarathi_timer_destroy.argtypes = [c_void_p]
         L.sarathi_timer_destroy.restype = None
@@ -168,9 +168,16 @@ def sarathi_attention(desc: sarathi_layer_desc, batch: sarathi_batch, q: int, ou
            "sarathi_attention")
 
 
-def sarathi_timer_create(capacity: int) -> int:
+ALL_STAGES = (1 << N_STAGES) - 1
+
+
+def stage_mask(*names) -> int:
+    return sum(1 << STAGES.index(n) for n in names)
+
+
+def sarathi_timer_create(capacity: int, mask: int = ALL_STAGES) -> int:
     h = c_void_p()
-    _check(lib().sarathi_timer_create(capacity, byref(h)), "sarathi_timer_create")
+    _check(lib().sarathi_timer_create(capacity, mask, byref(h)), "sarathi_timer_create")
     return h.value
 
 

@@ -10,7 +10,7 @@
 // bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 320; larger batches
 // take a few row tiles) and a 128-column stripe of the weights, so a weight tile is read once for
 // the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 160 rows x 32 columns.  A and W
-// k-tiles (64 wide) are staged through LDS with double buffering.  When the weight stripes alone do
+// k-tiles (64 wide) are staged through LDS (swizzled rows, no bank conflicts) with double buffering.  When the weight stripes alone do
 // not fill the 256 compute units, the k range is split: each split writes a float32 partial and the
 // kernel that consumes the product sums the partials in a fixed order (deterministic, no atomics).
 // Workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight stripe.
@@ -23,19 +23,41 @@ namespace sarathi {
 namespace {
 
 constexpr int kBK = 64;         // k extent of one LDS stage (bf16 elements)
-constexpr int kLdsK = kBK + 8;  // padded LDS row: 144 bytes keeps the 16-byte fragment reads spread
-constexpr int kWM = 2, kWN = 4, kThreads = 64 * kWM * kWN;
+constexpr int kLdsK = kBK;      // LDS row: 128 bytes = 8 chunks of 16 bytes, stored swizzled
+// Chunk c of LDS row r is stored in slot c ^ ((r >> 1) & 7).  A 16-byte store of two consecutive
+// rows then covers the two halves of the 64 banks once each, and the 16 rows a fragment read touches
+// at one chunk fall in 16 distinct 4-bank groups: both directions are free of bank conflicts.
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ ((row >> 1) & 7)) * 8; }
+#ifndef SARATHI_GEMM_W_RING
+#define SARATHI_GEMM_W_RING 2     // weight k-tiles in flight in registers
+#endif
+#ifndef SARATHI_GEMM_A_RING
+#define SARATHI_GEMM_A_RING 1     // activation k-tiles in flight in registers
+#endif
+#ifndef SARATHI_GEMM_WAVE_COLS
+#define SARATHI_GEMM_WAVE_COLS 4   // 4: 8 waves per workgroup, 2: 4 waves
+#endif
+constexpr int kPlanWaveCols = SARATHI_GEMM_WAVE_COLS;
+constexpr int kWM = 2;          // wave rows of a workgroup
 constexpr int kMBW = 10;        // max 16-row blocks per wave row: 320 rows per tile
-constexpr int kNB = 2;          // 16-column blocks per wave: 128 columns per tile
-constexpr int kBN = 16 * kNB * kWN;
+#ifndef SARATHI_GEMM_BN
+#define SARATHI_GEMM_BN 128
+#endif
+constexpr int kBN = SARATHI_GEMM_BN;   // columns per tile (weight rows per stripe)
 constexpr int kBMX = 16 * kMBW * kWM;
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
-template <int MB, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
+// WN wave columns: WN = 4 gives 8 waves with 144x32 wave tiles (two waves per SIMD); WN = 2 gives
+// 4 waves with 144x64 wave tiles (one wave per SIMD, whose 512 registers hold the larger
+// accumulator tile), which halves the LDS bytes read per MFMA.
+template <int WN, int MB, int EPI>
+__global__ __launch_bounds__(64 * kWM * WN) __attribute__((amdgpu_waves_per_eu(WN == 2 ? 1 : 2, WN == 2 ? 1 : 2)))
+void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   static_assert(MB >= 1 && MB <= kMBW, "16-row blocks per wave row");
+  constexpr int kThreads = 64 * kWM * WN;
+  constexpr int kNB = kBN / (16 * WN);  // 16-column blocks per wave
   constexpr bool kGlu = EPI == kEpiSwiGLU;
   constexpr int A_CH = (kBMX * (kBK / 8) + kThreads - 1) / kThreads;   // 16-B A chunks per thread
   constexpr int B_CH = kBN * (kBK / 8) / kThreads;
@@ -59,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_rows(GemmArgs g, GemmPlan 
   const int ke = (int)((long long)(split + 1) * nk / p.splits);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / kWN, wn = wave % kWN;
+  const int wm = wave / WN, wn = wave % WN;
   const bf16_t *A = static_cast<const bf16_t *>(g.a);
   const bf16_t *W0 = static_cast<const bf16_t *>(g.w0);
   const bf16_t *W1 = static_cast<const bf16_t *>(g.w1);
@@ -74,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_rows(GemmArgs g, GemmPlan 
     const int c = tid + i * kThreads, row = c >> 3, kc = c & 7;
     const int gr = min(m0 + row, g.m_alloc - 1);
     a_src[i] = A + (size_t)gr * g.lda + kc * 8 + (size_t)kb * kBK;
-    a_dst[i] = row * kLdsK + kc * 8;
+    a_dst[i] = row * kLdsK + swz(row, kc);
   }
   const bf16_t *b_src[B_CH];
   int b_dst[B_CH];
@@ -98,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_rows(GemmArgs g, GemmPlan 
     }
     src_row = kGlu ? min(src_row, g.n - 1) : src_row;
     b_src[i] = Wp + (size_t)src_row * g.ldw + kc * 8 + (size_t)kb * kBK;
-    b_dst[i] = (kBMX + row) * kLdsK + kc * 8;
+    b_dst[i] = (kBMX + row) * kLdsK + swz(row, kc);   // kBMX is a multiple of 16: same swizzle
   }
 
   f32x4_t acc[MB][kNB];
@@ -112,7 +134,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_rows(GemmArgs g, GemmPlan 
   // stages: tile j is computed from stage j&1 while tile j+1 is written into the other stage.
   // Tile indices past the end are clamped (a few redundant loads) so that the steady-state loop body
   // has no branches around its loads.
-  constexpr int kDW = 4, kDA = 1, kUnrollK = 4;   // kUnrollK: multiple of both ring depths
+  constexpr int kDW = SARATHI_GEMM_W_RING, kDA = SARATHI_GEMM_A_RING;
+  constexpr int kUnrollK = kDW * kDA;             // a multiple of both ring depths
   uint4 ra[kDA][A_CH], rb[kDW][B_CH];
   const int ntiles = ke - kb;
   auto tile = [&](int j) { return min(j, ntiles - 1) * kBK; };
@@ -131,29 +154,54 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_rows(GemmArgs g, GemmPlan 
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) st16(&Ls[b_dst[i]], rb[bslot][i]);
   };
-  const int frag_row = lane & 15, frag_k = (lane >> 4) * 8;
+  // Fragment rows start at multiples of 16, so a lane's swizzle term is ((lane & 15) >> 1).
+  const int frag_row = lane & 15;
+  const int frag_k0 = (((lane >> 4) + 0) ^ (frag_row >> 1)) * 8;   // k-step 0: chunks 0..3
+  const int frag_k1 = (((lane >> 4) + 4) ^ (frag_row >> 1)) * 8;   // k-step 1: chunks 4..7
   const int a_row0 = wm * 16 * mbw;
+  // Fragment reads are grouped ahead of the MFMAs that use them, so each MFMA waits only for its
+  // own operands (descending LDS counters) rather than a read round trip every two MFMAs.  With
+  // narrow wave tiles both k-steps' fragments fit in registers at once (the MFMAs of k-step 0 then
+  // run while k-step 1's reads are in flight); wide wave tiles read one k-step at a time.
+  constexpr bool kAllK = kNB <= 2;
   auto compute = [&](int stage) {
     const bf16_t *L = lds + stage * kStage;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
-      bf16x8_t bw[kNB];
+    bf16x8_t bw[kAllK ? 2 : 1][kNB], af[kAllK ? 2 : 1][MB];
+    auto read = [&](int ks, int slot) {
+      const int fk = ks == 0 ? frag_k0 : frag_k1;
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
-        bw[nb] = *reinterpret_cast<const bf16x8_t *>(
-            &L[(kBMX + wn * 16 * kNB + nb * 16 + frag_row) * kLdsK + ks * 32 + frag_k]);
-      bf16x8_t af[MB];
+        bw[slot][nb] = *reinterpret_cast<const bf16x8_t *>(
+            &L[(kBMX + wn * 16 * kNB + nb * 16 + frag_row) * kLdsK + fk]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8_t *>(
-            &L[(a_row0 + mb * 16 + frag_row) * kLdsK + ks * 32 + frag_k]);
+        af[slot][mb] = *reinterpret_cast<const bf16x8_t *>(
+            &L[(a_row0 + mb * 16 + frag_row) * kLdsK + fk]);
+    };
+    auto mfma = [&](int slot) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bw[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[slot][mb], bw[slot][nb], acc[mb][nb], 0, 0, 0);
+    };
+    if (kAllK) {
+      read(0, 0);
+      read(1, kAllK ? 1 : 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(0);
+      mfma(kAllK ? 1 : 0);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kBK / 32; ++ks) {
+        read(ks, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(0);
+      }
     }
   };
+
   // One step: compute tile j (ring position u = j mod kUnrollK), stage tile j+1 into the other LDS
   // buffer, refill the freed ring slots, barrier.
   auto step = [&](int u, int j) {
@@ -283,34 +331,41 @@ __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs g) {
 
 constexpr size_t kLdsBytes = 2 * (size_t)(kBMX + kBN) * kLdsK * sizeof(bf16_t);
 
-template <int MB, int EPI>
+template <int WN, int MB, int EPI>
 hipError_t run_bf16_mb(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   static bool attr_set = false;   // one LDS opt-in per instantiation (host-side, idempotent)
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_rows<MB, EPI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_rows<WN, MB, EPI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_bf16_rows<MB, EPI>), dim3(p.grid), dim3(kThreads), kLdsBytes, s, g, p);
+  hipLaunchKernelGGL((gemm_bf16_rows<WN, MB, EPI>), dim3(p.grid), dim3(64 * kWM * WN), kLdsBytes, s,
+                     g, p);
   return hipGetLastError();
+}
+
+template <int WN, int EPI>
+hipError_t run_bf16_wn(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  switch (p.mbw) {
+    case 1: return run_bf16_mb<WN, 1, EPI>(g, p, s);
+    case 2: return run_bf16_mb<WN, 2, EPI>(g, p, s);
+    case 3: return run_bf16_mb<WN, 3, EPI>(g, p, s);
+    case 4: return run_bf16_mb<WN, 4, EPI>(g, p, s);
+    case 5: return run_bf16_mb<WN, 5, EPI>(g, p, s);
+    case 6: return run_bf16_mb<WN, 6, EPI>(g, p, s);
+    case 7: return run_bf16_mb<WN, 7, EPI>(g, p, s);
+    case 8: return run_bf16_mb<WN, 8, EPI>(g, p, s);
+    case 9: return run_bf16_mb<WN, 9, EPI>(g, p, s);
+    case 10: return run_bf16_mb<WN, 10, EPI>(g, p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int EPI>
 hipError_t run_bf16(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  switch (p.mbw) {
-    case 1: return run_bf16_mb<1, EPI>(g, p, s);
-    case 2: return run_bf16_mb<2, EPI>(g, p, s);
-    case 3: return run_bf16_mb<3, EPI>(g, p, s);
-    case 4: return run_bf16_mb<4, EPI>(g, p, s);
-    case 5: return run_bf16_mb<5, EPI>(g, p, s);
-    case 6: return run_bf16_mb<6, EPI>(g, p, s);
-    case 7: return run_bf16_mb<7, EPI>(g, p, s);
-    case 8: return run_bf16_mb<8, EPI>(g, p, s);
-    case 9: return run_bf16_mb<9, EPI>(g, p, s);
-    case 10: return run_bf16_mb<10, EPI>(g, p, s);
-  }
-  return hipErrorInvalidValue;
+  if (p.wn != kPlanWaveCols) return hipErrorInvalidValue;
+  return run_bf16_wn<kPlanWaveCols, EPI>(g, p, s);
 }
 
 template <int EPI>
@@ -335,6 +390,7 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
   p.m_tiles = (m + kBMX - 1) / kBMX;
   const int rows = (m + p.m_tiles - 1) / p.m_tiles;
   p.mbw = (rows + 31) / 32;
+  p.wn = kPlanWaveCols;
   const int nk = k / kBK;
   // The split count and the epilogue form depend on the weight shape only, never on the number of
   // batch rows: a row's k-sum is then cut at the same points whatever else is in the batch, so a

@@ -49,19 +49,27 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
   return t;
 }
 
-// v[0..3] = resid[r, c..c+3] + sum_s part[s][r][c..c+3]
-template <typename Tres>
-__device__ __forceinline__ void row_value(const Tres *resid, const float *part, int splits,
-                                          size_t slice, size_t off, float *v) {
-  load4<Tres>(resid + off, v);
-  for (int s = 0; s < splits; ++s) {
-    float p[4];
-    load4<float>(part + s * slice + off, p);
+constexpr int kMaxSplits = 8;   // split partials a consumer sums (the planner never makes more)
+constexpr int kMaxChunks = 16;  // 4-element chunks per thread: rows up to 16384 wide
+
+// v[0..3] += sum_s part[s][off..off+3] in split order; every split's load is issued before its add
+// so a thread keeps several loads in flight.
+__device__ __forceinline__ void add_splits(const float *part, int splits, size_t slice, size_t off,
+                                           float *v) {
+  float p[kMaxSplits][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] += p[e];
-  }
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < splits) load4<float>(part + s * slice + off, p[s]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < splits) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += p[s][e];
+    }
 }
 
+// One row per workgroup: the row stays in registers (up to kMaxChunks 4-element chunks per thread),
+// so the norm needs one read of its inputs.
 template <typename Tres, typename Tout, bool LN>
 __global__ __launch_bounds__(kThreads) void norm_rows(const Tres *resid, const float *part,
                                                       int splits, float *sum_out, const float *g,
@@ -76,57 +84,66 @@ __global__ __launch_bounds__(kThreads) void norm_rows(const Tres *resid, const f
     return;
   }
   const size_t slice = (size_t)rows * H, row_off = (size_t)r * H;
-  float s1 = 0.f;
-  for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) {
-    float v[4];
-    row_value<Tres>(resid, part, splits, slice, row_off + c, v);
-    if (sum_out) store4<float>(sum_out + row_off + c, v);
+  const int nch = (H / 4 - threadIdx.x + kThreads - 1) / kThreads;   // chunks of this thread
+  float v[kMaxChunks][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s1 += LN ? v[e] : v[e] * v[e];
+  for (int i = 0; i < kMaxChunks; ++i)
+    if (i < nch) load4<Tres>(resid + row_off + (threadIdx.x + i * kThreads) * 4, v[i]);
+  if (splits > 0) {
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i)
+      if (i < nch) add_splits(part, splits, slice, row_off + (threadIdx.x + i * kThreads) * 4, v[i]);
   }
+  float s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i)
+    if (i < nch) {
+      if (sum_out) store4<float>(sum_out + row_off + (threadIdx.x + i * kThreads) * 4, v[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s1 += LN ? v[i][e] : v[i][e] * v[i][e];
+    }
   s1 = block_sum(s1, red);
   float mean = 0.f, ms;
-  // The second and third passes re-read v: from sum_out (this thread's own writes) when kept,
-  // otherwise recomputed from the inputs.
-  auto value = [&](int c, float *v) {
-    if (sum_out) load4<float>(sum_out + row_off + c, v);
-    else row_value<Tres>(resid, part, splits, slice, row_off + c, v);
-  };
   if (LN) {
     mean = s1 / (float)H;
     float q = 0.f;
-    for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) {
-      float v[4];
-      value(c, v);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q += (v[e] - mean) * (v[e] - mean);
-    }
+    for (int i = 0; i < kMaxChunks; ++i)
+      if (i < nch) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
+      }
     ms = block_sum(q, red) / (float)H;
   } else {
     ms = s1 / (float)H;
   }
   const float rstd = 1.0f / sqrtf(ms + eps);
-  for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) {
-    float v[4];
-    value(c, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = (v[e] - mean) * rstd * g[c + e];
-      if (LN) v[e] += b[c + e];
+  for (int i = 0; i < kMaxChunks; ++i)
+    if (i < nch) {
+      const int c = (threadIdx.x + i * kThreads) * 4;
+      float w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[e] = (v[i][e] - mean) * rstd * g[c + e];
+        if (LN) w[e] += b[c + e];
+      }
+      store4<Tout>(o + c, w);
     }
-    store4<Tout>(o + c, v);
-  }
 }
 
+// Elementwise over [rows, cols]: one 4-element chunk per thread.
 template <typename Tout>
 __global__ __launch_bounds__(kThreads) void resid_sum(const float *resid, const float *part,
                                                       int splits, Tout *out, int rows, int cols) {
-  const size_t slice = (size_t)rows * cols, row_off = (size_t)blockIdx.x * cols;
-  for (int c = threadIdx.x * 4; c < cols; c += kThreads * 4) {
-    float v[4];
-    row_value<float>(resid, part, splits, slice, row_off + c, v);
-    store4<Tout>(out + row_off + c, v);
-  }
+  const size_t n4 = (size_t)rows * cols / 4;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= n4) return;
+  const size_t off = idx * 4;
+  float v[4];
+  load4<float>(resid + off, v);
+  add_splits(part, splits, (size_t)rows * cols, off, v);
+  store4<Tout>(out + off, v);
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
@@ -135,26 +152,19 @@ __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erf
 template <typename Tout, bool GATED>
 __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int splits, Tout *out,
                                                     int rows, int F) {
+  const size_t n4 = (size_t)rows * F / 4;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= n4) return;
+  const int r = (int)(idx / (F / 4)), c = (int)(idx % (F / 4)) * 4;
   const int n_part = GATED ? 2 * F : F;
-  const size_t slice = (size_t)rows * n_part, row_off = (size_t)blockIdx.x * n_part;
-  for (int c = threadIdx.x * 4; c < F; c += kThreads * 4) {
-    float a[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-      float p[4];
-      load4<float>(part + s * slice + row_off + c, p);
+  const size_t slice = (size_t)rows * n_part, off = (size_t)r * n_part + c;
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+  add_splits(part, splits, slice, off, a);
+  if (GATED) add_splits(part, splits, slice, off + F, u);
+  float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] += p[e];
-      if (GATED) {
-        load4<float>(part + s * slice + row_off + F + c, p);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] += p[e];
-      }
-    }
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = GATED ? silu_f(a[e]) * u[e] : gelu_f(a[e]);
-    store4<Tout>(out + (size_t)blockIdx.x * F + c, v);
-  }
+  for (int e = 0; e < 4; ++e) v[e] = GATED ? silu_f(a[e]) * u[e] : gelu_f(a[e]);
+  store4<Tout>(out + (size_t)r * F + c, v);
 }
 
 template <typename Tres, typename Tout>
@@ -179,6 +189,7 @@ hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const vo
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
                             hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
+  if (splits > kMaxSplits || H > 4 * kThreads * kMaxChunks || H % 4) return hipErrorInvalidValue;
   if (res_type == kF32 && out_type == kF32)
     return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, s);
   if (res_type == kBF16 && out_type == kBF16)
@@ -189,12 +200,14 @@ hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const vo
 hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int splits, void *out,
                           int rows, int F, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (splits > kMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((size_t)rows * F / 4 + kThreads - 1) / kThreads));
   if (out_type == kF32) {
-    if (gated) hipLaunchKernelGGL((ffn_act<float, true>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
-    else hipLaunchKernelGGL((ffn_act<float, false>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
+    if (gated) hipLaunchKernelGGL((ffn_act<float, true>), grid, dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
+    else hipLaunchKernelGGL((ffn_act<float, false>), grid, dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
   } else {
-    if (gated) hipLaunchKernelGGL((ffn_act<bf16_t, true>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
-    else hipLaunchKernelGGL((ffn_act<bf16_t, false>), dim3(rows), dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
+    if (gated) hipLaunchKernelGGL((ffn_act<bf16_t, true>), grid, dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
+    else hipLaunchKernelGGL((ffn_act<bf16_t, false>), grid, dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
   }
   return hipGetLastError();
 }
@@ -202,11 +215,13 @@ hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int split
 hipError_t launch_resid_sum(int out_type, const float *resid, const float *part, int splits,
                             void *out, int rows, int cols, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (splits > kMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((size_t)rows * cols / 4 + kThreads - 1) / kThreads));
   if (out_type == kF32)
-    hipLaunchKernelGGL(resid_sum<float>, dim3(rows), dim3(kThreads), 0, s, resid, part, splits,
+    hipLaunchKernelGGL(resid_sum<float>, grid, dim3(kThreads), 0, s, resid, part, splits,
                        static_cast<float *>(out), rows, cols);
   else
-    hipLaunchKernelGGL(resid_sum<bf16_t>, dim3(rows), dim3(kThreads), 0, s, resid, part, splits,
+    hipLaunchKernelGGL(resid_sum<bf16_t>, grid, dim3(kThreads), 0, s, resid, part, splits,
                        static_cast<bf16_t *>(out), rows, cols);
   return hipGetLastError();
 }

@@ -8,7 +8,7 @@
 // angle pos * base^(-2j/d); cos/sin come from a float32 table built on the host in float64.
 // The q|k|v row is the sum of the QKV GEMM's float32 split partials, taken in split order; it is
 // rounded to the storage type only once, after the rotation.
-// One workgroup per row; every thread moves 4 consecutive elements of q, k and v.
+// Every thread moves 4 consecutive elements of one row's q, k and v.
 #include "kernels.h"
 
 namespace sarathi {
@@ -25,16 +25,24 @@ template <> __device__ __forceinline__ void put4<bf16_t>(bf16_t *p, const float 
   *reinterpret_cast<uint2 *>(p) = u;
 }
 
+constexpr int kMaxSplits = 8;
+
+// v = sum_s part[s][off..off+3] in split order (all loads issued before the adds).
 __device__ __forceinline__ void sum4(const float *part, int splits, size_t slice, size_t off,
                                      float *v) {
-  float4 a = *reinterpret_cast<const float4 *>(part + off);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  for (int s = 1; s < splits; ++s) {
-    a = *reinterpret_cast<const float4 *>(part + s * slice + off);
-    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-  }
+  float4 a[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < splits) a[s] = *reinterpret_cast<const float4 *>(part + s * slice + off);
+  v[0] = a[0].x; v[1] = a[0].y; v[2] = a[0].z; v[3] = a[0].w;
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s)
+    if (s < splits) {
+      v[0] += a[s].x; v[1] += a[s].y; v[2] += a[s].z; v[3] += a[s].w;
+    }
 }
 
+// grid: (rows, column blocks of 1024); one 4-element chunk of q, k and v per thread.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append(const float *part, int splits, int rows_total,
                                                    T *q_out, int ld_q, float *qkv_dump,
@@ -42,39 +50,39 @@ __global__ __launch_bounds__(256) void rope_append(const float *part, int splits
                                                    int row0, ChunkRef ch, DecodeGroup dg) {
   const int r = row0 + blockIdx.x;
   const int A = nh * d;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= A) return;
   const RowRef rr = row_ref(r, ch, dg);
   T *kc = reinterpret_cast<T *>(rr.k);
   T *vc = reinterpret_cast<T *>(rr.v);
   const size_t slice = (size_t)rows_total * 3 * A, src = (size_t)r * 3 * A;
-  for (int c = threadIdx.x * 4; c < A; c += blockDim.x * 4) {
-    const int h = c / d, e0 = c - h * d;
-    float q[4], k[4], v[4];
-    sum4(part, splits, slice, src + c, q);
-    sum4(part, splits, slice, src + A + c, k);
-    sum4(part, splits, slice, src + 2 * A + c, v);
-    if (qkv_dump) {
-      float *dr = qkv_dump + src;
-      *reinterpret_cast<float4 *>(dr + c) = make_float4(q[0], q[1], q[2], q[3]);
-      *reinterpret_cast<float4 *>(dr + A + c) = make_float4(k[0], k[1], k[2], k[3]);
-      *reinterpret_cast<float4 *>(dr + 2 * A + c) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    if (use_rope) {
-      const float2 *t = tab + (size_t)rr.pos * (d / 2) + e0 / 2;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float2 cs = t[u];
-        const float q0 = q[2 * u], q1 = q[2 * u + 1], k0 = k[2 * u], k1 = k[2 * u + 1];
-        q[2 * u] = q0 * cs.x - q1 * cs.y;
-        q[2 * u + 1] = q0 * cs.y + q1 * cs.x;
-        k[2 * u] = k0 * cs.x - k1 * cs.y;
-        k[2 * u + 1] = k0 * cs.y + k1 * cs.x;
-      }
-    }
-    put4<T>(q_out + (size_t)r * ld_q + c, q);
-    const size_t slot = ((size_t)h * rr.cap + rr.pos) * d + e0;
-    put4<T>(kc + slot, k);
-    put4<T>(vc + slot, v);
+  const int h = c / d, e0 = c - h * d;
+  float q[4], k[4], v[4];
+  sum4(part, splits, slice, src + c, q);
+  sum4(part, splits, slice, src + A + c, k);
+  sum4(part, splits, slice, src + 2 * A + c, v);
+  if (qkv_dump) {
+    float *dr = qkv_dump + src;
+    *reinterpret_cast<float4 *>(dr + c) = make_float4(q[0], q[1], q[2], q[3]);
+    *reinterpret_cast<float4 *>(dr + A + c) = make_float4(k[0], k[1], k[2], k[3]);
+    *reinterpret_cast<float4 *>(dr + 2 * A + c) = make_float4(v[0], v[1], v[2], v[3]);
   }
+  if (use_rope) {
+    const float2 *t = tab + (size_t)rr.pos * (d / 2) + e0 / 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float2 cs = t[u];
+      const float q0 = q[2 * u], q1 = q[2 * u + 1], k0 = k[2 * u], k1 = k[2 * u + 1];
+      q[2 * u] = q0 * cs.x - q1 * cs.y;
+      q[2 * u + 1] = q0 * cs.y + q1 * cs.x;
+      k[2 * u] = k0 * cs.x - k1 * cs.y;
+      k[2 * u + 1] = k0 * cs.y + k1 * cs.x;
+    }
+  }
+  put4<T>(q_out + (size_t)r * ld_q + c, q);
+  const size_t slot = ((size_t)h * rr.cap + rr.pos) * d + e0;
+  put4<T>(kc + slot, k);
+  put4<T>(vc + slot, v);
 }
 
 }  // namespace
@@ -84,11 +92,13 @@ hipError_t launch_rope_append(int type, const float *part, int splits, int rows_
                               int d, int row0, int n_rows, const ChunkRef &ch, const DecodeGroup &dg,
                               hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid(n_rows, (nh * d / 4 + 255) / 256);
   if (type == kF32)
-    hipLaunchKernelGGL(rope_append<float>, dim3(n_rows), dim3(256), 0, s, part, splits, rows_total,
+    hipLaunchKernelGGL(rope_append<float>, grid, dim3(256), 0, s, part, splits, rows_total,
                        static_cast<float *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, ch, dg);
   else
-    hipLaunchKernelGGL(rope_append<bf16_t>, dim3(n_rows), dim3(256), 0, s, part, splits, rows_total,
+    hipLaunchKernelGGL(rope_append<bf16_t>, grid, dim3(256), 0, s, part, splits, rows_total,
                        static_cast<bf16_t *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, ch, dg);
   return hipGetLastError();
 }

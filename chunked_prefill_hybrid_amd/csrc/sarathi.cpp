@@ -33,7 +33,10 @@ struct sarathi_layer {
 struct sarathi_timer {
   int capacity;
   int used;                       // forwards recorded since the last read
-  std::vector<hipEvent_t> ev;     // [capacity][SARATHI_N_STAGES + 1]
+  uint32_t mask;                  // timed stages
+  int slot[SARATHI_N_STAGES];     // index of a timed stage among the timed ones, else -1
+  int n_timed;
+  std::vector<hipEvent_t> ev;     // [capacity][n_timed][2]: before, after
   std::vector<uint32_t> ran;      // per recorded forward: bit s set if stage s launched work
 };
 
@@ -236,22 +239,28 @@ DecodeGroup decode_group(const sarathi_batch *b, int base) {
       return fail(SARATHI_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));        \
   } while (0)
 
-// Records one event before the first stage and one after every stage position (stages without work
-// still get their event so that indices stay fixed; their bit in `ran` stays clear).
+// Records the timer's events around the timed stages (nothing when there is no timer).
 struct Marker {
   sarathi_timer *t = nullptr;
   hipStream_t s = nullptr;
   int f = 0;
-  hipError_t begin() {
-    if (!t) return hipSuccess;
-    f = t->used;
-    t->ran[f] = 0;
-    return hipEventRecord(t->ev[(size_t)f * (SARATHI_N_STAGES + 1)], s);
+  hipEvent_t ev(int stage, int which) const {
+    return t->ev[((size_t)f * t->n_timed + t->slot[stage]) * 2 + which];
+  }
+  void begin() {
+    if (t) {
+      f = t->used;
+      t->ran[f] = 0;
+    }
+  }
+  hipError_t start(int stage) {
+    if (!t || !(t->mask >> stage & 1u)) return hipSuccess;
+    return hipEventRecord(ev(stage, 0), s);
   }
   hipError_t end(int stage, bool ran) {
-    if (!t) return hipSuccess;
+    if (!t || !(t->mask >> stage & 1u)) return hipSuccess;
     if (ran) t->ran[f] |= 1u << stage;
-    return hipEventRecord(t->ev[(size_t)f * (SARATHI_N_STAGES + 1) + stage + 1], s);
+    return hipEventRecord(ev(stage, 1), s);
   }
   void commit() {
     if (t) t->used++;
@@ -268,6 +277,7 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
   float *po = reinterpret_cast<float *>(ws + p.part_o);
   float *pml = reinterpret_cast<float *>(ws + p.part_ml);
   const bool split_chunk = chunk_uses_split(d);
+  HIP_TRY(mk.start(SARATHI_STAGE_ATTN_CHUNK));
   if (C > 0) {
     if (split_chunk) {
       const DecodeGroup none = decode_group(b, B);   // empty group
@@ -278,12 +288,14 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
     }
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_CHUNK, C > 0));
+  HIP_TRY(mk.start(SARATHI_STAGE_ATTN_DECODE));
   for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
     const DecodeGroup g = decode_group(b, base);
     HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, ch, g,
                              p.max_splits, po, pml, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
+  HIP_TRY(mk.start(SARATHI_STAGE_ATTN_MERGE));
   const int merge_row0 = split_chunk ? 0 : C;
   if (C + B > merge_row0)
     HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, merge_row0, C + B - merge_row0,
@@ -312,7 +324,7 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   Marker mk;
   mk.t = timer;
   mk.s = s;
-  HIP_TRY(mk.begin());
+  mk.begin();
   const int ty = d->dtype, T = p.T, R = p.T_alloc;
   const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
   const bool llama = d->arch == SARATHI_ARCH_LLAMA;
@@ -322,10 +334,12 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   void *n2 = ws + p.n2, *act = ws + p.act;
 
   // 1. norm 1 over the C+B rows (pad rows zeroed)
+  HIP_TRY(mk.start(SARATHI_STAGE_NORM1));
   HIP_TRY(launch_norm_rows(ty, ty, !llama, b->x, nullptr, 0, nullptr, L->w.norm1_w, L->w.norm1_b, n1,
                            H, T, R, d->norm_eps, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM1, true));
   // 2. QKV projection: one GEMM over chunk and decode rows (float32 split partials)
+  HIP_TRY(mk.start(SARATHI_STAGE_QKV));
   GemmArgs g{};
   g.a = n1; g.lda = H; g.w0 = L->w.w_qkv; g.ldw = H; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
@@ -333,6 +347,7 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   HIP_TRY(mk.end(SARATHI_STAGE_QKV, true));
   // 3. sum of the partials + RoPE + KV append (per launch group of decodes)
   const ChunkRef ch = chunk_ref(b);
+  HIP_TRY(mk.start(SARATHI_STAGE_ROPE_APPEND));
   {
     int base = 0;
     do {
@@ -350,16 +365,19 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   st = run_attention(d, b, p, q, attn, ws, s, mk);
   if (st != SARATHI_OK) return st;
   // 5. O projection (float32 split partials)
+  HIP_TRY(mk.start(SARATHI_STAGE_O));
   g = GemmArgs{};
   g.a = attn; g.lda = A; g.w0 = L->w.w_o; g.ldw = A; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = A;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.o, s));
   HIP_TRY(mk.end(SARATHI_STAGE_O, true));
   // 6. h1 = x + sum of the O partials (kept in float32), then norm 2
+  HIP_TRY(mk.start(SARATHI_STAGE_NORM2));
   HIP_TRY(launch_norm_rows(ty, ty, !llama, b->x, part, p.o.splits, h1, L->w.norm2_w, L->w.norm2_b, n2,
                            H, T, R, d->norm_eps, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM2, true));
   // 7. FFN up (+gate): activation fused into the GEMM, or split product + activation pass
+  HIP_TRY(mk.start(SARATHI_STAGE_FFN_UP));
   g = GemmArgs{};
   g.a = n2; g.lda = H; g.ldw = H; g.m_alloc = R; g.m_store = T; g.k = H;
   g.w0 = llama ? L->w.w_gate : L->w.w_up;
@@ -374,6 +392,7 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   }
   HIP_TRY(mk.end(SARATHI_STAGE_FFN_UP, true));
   // 8. down projection (split partials), y = h1 + sum of the partials
+  HIP_TRY(mk.start(SARATHI_STAGE_FFN_DOWN));
   g = GemmArgs{};
   g.a = act; g.lda = F; g.w0 = L->w.w_down; g.ldw = F; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
@@ -505,17 +524,23 @@ sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_b
                        static_cast<hipStream_t>(stream), none);
 }
 
-sarathi_status sarathi_timer_create(int32_t capacity, sarathi_timer **out) {
+sarathi_status sarathi_timer_create(int32_t capacity, uint32_t stage_mask, sarathi_timer **out) {
   if (!out) return fail(SARATHI_ERR_INVALID, "out is null");
   *out = nullptr;
   if (capacity <= 0 || capacity > (1 << 20)) return fail(SARATHI_ERR_INVALID, "bad timer capacity");
+  stage_mask &= (1u << SARATHI_N_STAGES) - 1u;
+  if (!stage_mask) return fail(SARATHI_ERR_INVALID, "timer stage mask selects no stage");
   sarathi_timer *t = new (std::nothrow) sarathi_timer();
   if (!t) return fail(SARATHI_ERR_NOMEM, "host allocation failed");
   t->capacity = capacity;
   t->used = 0;
+  t->mask = stage_mask;
+  t->n_timed = 0;
+  for (int st = 0; st < SARATHI_N_STAGES; ++st) t->slot[st] = (stage_mask >> st & 1u) ? t->n_timed++ : -1;
   t->ran.assign(capacity, 0);
-  t->ev.reserve((size_t)capacity * (SARATHI_N_STAGES + 1));
-  for (size_t i = 0; i < (size_t)capacity * (SARATHI_N_STAGES + 1); ++i) {
+  const size_t n_ev = (size_t)capacity * t->n_timed * 2;
+  t->ev.reserve(n_ev);
+  for (size_t i = 0; i < n_ev; ++i) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) {
       sarathi_timer_destroy(t);
@@ -548,14 +573,13 @@ sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_
   }
   const int n = timer->used;
   timer->used = 0;
-  if (n == 0) return SARATHI_OK;
-  HIP_TRY(hipEventSynchronize(timer->ev[(size_t)(n - 1) * (SARATHI_N_STAGES + 1) + SARATHI_N_STAGES]));
   for (int f = 0; f < n; ++f) {
-    const hipEvent_t *e = &timer->ev[(size_t)f * (SARATHI_N_STAGES + 1)];
     for (int st = 0; st < SARATHI_N_STAGES; ++st) {
-      if (!(timer->ran[f] >> st & 1u)) continue;
+      if (timer->slot[st] < 0 || !(timer->ran[f] >> st & 1u)) continue;
+      const size_t base = ((size_t)f * timer->n_timed + timer->slot[st]) * 2;
+      HIP_TRY(hipEventSynchronize(timer->ev[base + 1]));
       float ms = 0.f;
-      HIP_TRY(hipEventElapsedTime(&ms, e[st], e[st + 1]));
+      HIP_TRY(hipEventElapsedTime(&ms, timer->ev[base], timer->ev[base + 1]));
       total_ms[st] += ms;
       count[st] += 1;
     }

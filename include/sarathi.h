@@ -190,23 +190,28 @@ typedef enum {
 
 typedef struct sarathi_timer sarathi_timer;   /* opaque */
 
-/* Creates a timer able to hold the events of `capacity` forwards between two reads (it creates
- * capacity * (SARATHI_N_STAGES + 1) HIP events on the current device).  Errors: INVALID, HIP. */
-sarathi_status sarathi_timer_create(int32_t capacity, sarathi_timer **out);
+/* Creates a timer able to hold the events of `capacity` forwards between two reads.  Only the stages
+ * whose bit (1 << sarathi_stage) is set in stage_mask are timed: the forward records one HIP event
+ * right before and one right after each of them (every recorded event adds a little to a forward,
+ * so a measurement that must not be perturbed times one stage only).  It creates
+ * 2 * capacity * (number of stages in the mask) HIP events on the current device.
+ * Errors: INVALID (capacity <= 0, empty mask), HIP. */
+sarathi_status sarathi_timer_create(int32_t capacity, uint32_t stage_mask, sarathi_timer **out);
 
 /* Destroys the timer's events.  No forward recording into it may be in flight.  NULL is a no-op. */
 void sarathi_timer_destroy(sarathi_timer *timer);
 
-/* As sarathi_layer_forward, and records one HIP event on `stream` before the first stage and after
- * each stage into the timer (no synchronisation).  Errors: as the forward; INVALID if the timer
- * already holds `capacity` unread forwards (nothing is enqueued then). */
+/* As sarathi_layer_forward, and records the timer's events on `stream` (no synchronisation).
+ * Errors: as the forward; INVALID if the timer already holds `capacity` unread forwards (nothing is
+ * enqueued then). */
 sarathi_status sarathi_layer_forward_timed(sarathi_layer *layer, const sarathi_batch *batch,
                                            void *workspace, size_t ws_bytes, void *stream,
                                            sarathi_timer *timer);
 
-/* Waits for the recorded events, adds each stage's elapsed milliseconds over all recorded forwards
- * into total_ms[s] and the number of forwards in which stage s ran into count[s] (host arrays of
- * SARATHI_N_STAGES entries, overwritten), then empties the timer.  Errors: INVALID, HIP. */
+/* Waits for the recorded events, writes each timed stage's elapsed milliseconds summed over the
+ * recorded forwards into total_ms[s] and the number of forwards in which stage s ran into count[s]
+ * (host arrays of SARATHI_N_STAGES entries, overwritten; untimed stages read 0), then empties the
+ * timer.  Errors: INVALID, HIP. */
 sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_t *count);
 
 /* Static description of a status code. */
