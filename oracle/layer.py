@@ -15,7 +15,7 @@ rows: chunk rows first, then decodes in index order.
 
 The layer itself (norms, RoPE, SwiGLU or GELU MLP) is not spelled out on the pages beyond the operation
 list preproj / attention / postproj / FFN; the textbook LLaMA and GPT layer definitions are used, with
-the readings listed in the repository's design notes (adjacent-pair RoPE, angles in float64, softmax
+these readings (adjacent-pair RoPE, angles in float64, softmax
 scale 1/sqrt(d), no biases, weights stored [out, in]).
 
 Precision: float64 by default (dtype argument), inputs upcast once.  Loops are over requests and
