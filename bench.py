@@ -11,14 +11,14 @@ Passes: W warmup steps; a breakdown pass in which the library records HIP events
 (this perturbs the step time, so it is not the timed region); then exactly K timed steps in which
 events are recorded on the launch stream only around the dominant kernel's stage, giving that
 kernel's live average duration for the roofline.  Prints ONE JSON line: tokens/s over the K timed
-steps, the roofline of the dominant kernel, the per-stage breakdown, and the CPU oracle's throughput
-on a bounded sample of the same workload.
+steps, the roofline of the dominant kernel, the per-stage breakdown, the layer's roofline fraction,
+the piggybacking comparison (the same rows run as a chunk-only and a decode-only batch, giving the
+marginal cost of a decode that rides with the chunk), and the CPU oracle's throughput on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
-import glob
 import json
 import os
 import statistics
@@ -34,11 +34,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "hybrid-batch layer tokens/s (chunk+decodes); % bf16 MFMA and HBM roofline"
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha1()
-    for p in sorted(glob.glob(os.path.join(ROOT, "chunked_prefill_hybrid_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
-    return h.hexdigest()[:12]
+from chunked_prefill_hybrid_amd.profiling import kernel_source_hash  # noqa: E402
 
 
 def stage_work(shape, C, off, lens):
@@ -127,6 +123,8 @@ def main():
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the chunk-only / decode-only runs behind the decode-cost comparison")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures a single MI355X "
@@ -167,7 +165,14 @@ def main():
         dkv = [(cl(k), cl(v)) for k, v in zip(base["dk"], base["dv"])]
         b, keep = layer.batch(x, y, C, off, (ck, cv), dkv, lens)
         ws = torch.empty(layer.workspace_size(b), dtype=torch.uint8, device="cuda")
-        reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, bufs=(x, y, ck, cv, dkv, wr)))
+        sub = {}
+        if C > 0 and lens:
+            # the same rows split into a chunk-only and a decode-only batch (same caches, same slots)
+            sub["chunk_only"] = layer.batch(x[:C], y[:C], C, off, (ck, cv), [], [])
+            sub["decode_only"] = layer.batch(x[C:], y[C:], 0, 0, None, dkv, lens)
+            for name, (sb, _) in sub.items():
+                assert layer.workspace_size(sb) <= ws.numel(), name
+        reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, ck, cv, dkv, wr)))
     stream = torch.cuda.current_stream().cuda_stream
 
     def step(i, timer=None):
@@ -229,6 +234,43 @@ def main():
     }
 
     ms_per_step = elapsed / args.steps * 1e3
+    # Layer roofline fraction: sum over stages of the time each would take at its own bound, over the
+    # measured step time.
+    peak_c = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+    floor_us = sum(max(fl / (peak_c * 1e12), by / (PEAK_HBM_GBS * 1e9)) for fl, by in work.values()) * 1e6
+    summary["layer_floor_us"] = round(floor_us, 2)
+    summary["layer_roofline_frac"] = round(floor_us / (ms_per_step * 1e3), 4)
+
+    # Piggybacking comparison (SARATHI page, "Experiments", decode speedup): the marginal cost of a
+    # decode riding with the chunk, (t(C,B) - t(C,0)) / B, against a decode in a decode-only batch,
+    # t(0,B) / B.
+    sweep = None
+    if not args.no_sweep and reps[0]["sub"]:
+        n_sw = max(20, min(args.steps, 100))
+
+        def time_batch(name):
+            for i in range(5):
+                r = reps[i % len(reps)]
+                _abi.sarathi_layer_forward(r["layer"].handle, r["sub"][name][0], r["ws"].data_ptr(),
+                                           r["ws"].numel(), stream)
+            torch.cuda.synchronize()
+            t_0 = time.perf_counter()
+            for i in range(n_sw):
+                r = reps[i % len(reps)]
+                _abi.sarathi_layer_forward(r["layer"].handle, r["sub"][name][0], r["ws"].data_ptr(),
+                                           r["ws"].numel(), stream)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t_0) / n_sw * 1e6
+
+        t_c, t_d = time_batch("chunk_only"), time_batch("decode_only")
+        t_h = ms_per_step * 1e3
+        B = len(lens)
+        marginal = (t_h - t_c) / B
+        alone = t_d / B
+        sweep = {"steps": n_sw, "t_hybrid_us": round(t_h, 2), "t_chunk_only_us": round(t_c, 2),
+                 "t_decode_only_us": round(t_d, 2), "marginal_decode_us": round(marginal, 3),
+                 "decode_only_per_decode_us": round(alone, 3),
+                 "decode_speedup": round(alone / marginal, 2) if marginal > 0 else None}
     value = T * args.steps / elapsed
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -243,6 +285,7 @@ def main():
         "roofline": roof,
         "stages": breakdown,
         "summary": summary,
+        "piggyback": sweep,
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -10,7 +10,11 @@
 // bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 320; larger batches
 // take a few row tiles) and a 128-column stripe of the weights, so a weight tile is read once for
 // the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 160 rows x 32 columns.  A and W
-// k-tiles (64 wide) are staged through LDS (swizzled rows, no bank conflicts) with double buffering.  When the weight stripes alone do
+// k-tiles (64 deep) travel from global memory straight into LDS (global_load_lds_dwordx4: no
+// staging registers, no LDS store instructions) through a ring of up to 3 stages, so the loads of
+// tile j + 2 are in flight while tile j is multiplied.  The loads are what bounds this kernel at
+// small batches: a compute unit keeps only ~10 KB of reads in flight, so its fetch rate is set by
+// memory latency, and the A tile is fetched by every workgroup.  When the weight stripes alone do
 // not fill the 256 compute units, the k range is split: each split writes a float32 partial and the
 // kernel that consumes the product sums the partials in a fixed order (deterministic, no atomics).
 // Workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight stripe.
@@ -22,47 +26,91 @@
 namespace sarathi {
 namespace {
 
-constexpr int kBK = 64;         // k extent of one LDS stage (bf16 elements)
+constexpr int kBK = 64;         // k extent of one LDS stage (bf16 elements): two MFMA k-steps
 constexpr int kLdsK = kBK;      // LDS row: 128 bytes = 8 chunks of 16 bytes, stored swizzled
-// Chunk c of LDS row r is stored in slot c ^ ((r >> 1) & 7).  A 16-byte store of two consecutive
-// rows then covers the two halves of the 64 banks once each, and the 16 rows a fragment read touches
-// at one chunk fall in 16 distinct 4-bank groups: both directions are free of bank conflicts.
-__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ ((row >> 1) & 7)) * 8; }
-#ifndef SARATHI_GEMM_W_RING
-#define SARATHI_GEMM_W_RING 2     // weight k-tiles in flight in registers
-#endif
-#ifndef SARATHI_GEMM_A_RING
-#define SARATHI_GEMM_A_RING 1     // activation k-tiles in flight in registers
-#endif
-#ifndef SARATHI_GEMM_WAVE_COLS
-#define SARATHI_GEMM_WAVE_COLS 4   // 4: 8 waves per workgroup, 2: 4 waves
-#endif
-constexpr int kPlanWaveCols = SARATHI_GEMM_WAVE_COLS;
-constexpr int kWM = 2;          // wave rows of a workgroup
-constexpr int kMBW = 10;        // max 16-row blocks per wave row: 320 rows per tile
+constexpr int kChunks = kBK / 8;
+// Chunk c of LDS row r is stored in slot c ^ ((r >> 1) & 7).  A fragment read takes one chunk of 16
+// consecutive rows; those land in 16 distinct 4-bank groups, so fragment reads have no bank conflicts.
+__device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+constexpr int kMaxStages = 3;
+constexpr int kPlanWaveCols = 4;   // wave columns of a workgroup (8 waves: 2 rows x 4 columns)
+constexpr int kWM = 2;             // wave rows of a workgroup
+constexpr int kWaves = kWM * kPlanWaveCols;
+constexpr int kMBW = 10;           // max 16-row blocks per wave row: 320 rows per tile
 #ifndef SARATHI_GEMM_BN
 #define SARATHI_GEMM_BN 128
 #endif
 constexpr int kBN = SARATHI_GEMM_BN;   // columns per tile (weight rows per stripe)
 constexpr int kBMX = 16 * kMBW * kWM;
+constexpr int kLdsBudget = 160 * 1024;
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
-// WN wave columns: WN = 4 gives 8 waves with 144x32 wave tiles (two waves per SIMD); WN = 2 gives
-// 4 waves with 144x64 wave tiles (one wave per SIMD, whose 512 registers hold the larger
-// accumulator tile), which halves the LDS bytes read per MFMA.
-template <int WN, int MB, int EPI>
-__global__ __launch_bounds__(64 * kWM * WN) __attribute__((amdgpu_waves_per_eu(WN == 2 ? 1 : 2, WN == 2 ? 1 : 2)))
+// Stage geometry for MB 16-row blocks per wave row.  One global_load_lds_dwordx4 moves 64 lanes x
+// 16 bytes = 1 KiB, i.e. kRPL LDS rows; the A rows of a stage take kRowsA / kRPL such loads, the
+// weight rows kBN / kRPL, dealt round-robin to the 8 waves.  As many stages as fit in LDS (up to
+// kMaxStages) are kept in flight: the loads of a tile are issued that many steps before its use,
+// which is what hides the memory latency.
+constexpr int kRPL = 1024 / (kBK * 2);   // LDS rows per load
+template <int MB> struct StageGeom {
+  static constexpr int kRowsA = 32 * MB;
+  static constexpr int kElems = (kRowsA + kBN) * kLdsK;
+  static constexpr int kFit = kLdsBudget / (kElems * 2);
+  static constexpr int kStages = kFit < kMaxStages ? kFit : kMaxStages;
+  static_assert(kStages >= 2, "two stages fit in LDS");
+  static constexpr int kLoadsA = kRowsA / kRPL;
+  static constexpr int kAI = (kLoadsA + kWaves - 1) / kWaves;   // A loads per wave (some repeated)
+  static constexpr int kBI = kBN / kRPL / kWaves;               // weight loads per wave
+  static_assert(kRowsA % kRPL == 0, "whole loads of A rows");
+  static_assert(kBN % (kRPL * kWaves) == 0, "weight rows split evenly over the waves");
+  static_assert((kStages - 2) * (kAI + kBI) < 64, "loads in flight fit the wait counter");
+};
+
+// global -> LDS, 16 bytes per lane: lane l writes bytes [16 l, 16 l + 16) after the wave-uniform LDS
+// address `lds`.
+__device__ __forceinline__ void dma16(const bf16_t *src, bf16_t *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's global loads are outstanding and all its LDS operations are
+// done (s_waitcnt with vmcnt = N, lgkmcnt = 0, expcnt left open).
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without a memory fence (a fence would also wait for the loads still in flight
+// into the other stages); the empty asm statements keep the compiler from moving memory accesses
+// across it.  Visibility of the LDS stage that the next step reads comes from the explicit wait that
+// precedes each barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int MB, int EPI>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   static_assert(MB >= 1 && MB <= kMBW, "16-row blocks per wave row");
-  constexpr int kThreads = 64 * kWM * WN;
+  using G = StageGeom<MB>;
+  constexpr int WN = kPlanWaveCols;
   constexpr int kNB = kBN / (16 * WN);  // 16-column blocks per wave
   constexpr bool kGlu = EPI == kEpiSwiGLU;
-  constexpr int A_CH = (kBMX * (kBK / 8) + kThreads - 1) / kThreads;   // 16-B A chunks per thread
-  constexpr int B_CH = kBN * (kBK / 8) / kThreads;
-  constexpr int kStage = (kBMX + kBN) * kLdsK;
-  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+  constexpr int kNSt = G::kStages;
+  // One array per stage: the compiler then knows that reading one stage does not depend on the
+  // loads still landing in the others.
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[G::kElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[G::kElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[kNSt > 2 ? G::kElems : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[kNSt > 3 ? G::kElems : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st4[kNSt > 4 ? G::kElems : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st5[kNSt > 5 ? G::kElems : 8];
+  static_assert(kNSt <= 6, "stage arrays");
+  auto stage = [&](int u) -> bf16_t * {
+    return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : u == 3 ? st3 : u == 4 ? st4 : st5;
+  };
 
   // Tile of this workgroup (XCD-aware order: slot s of XCD x takes tile x * per_xcd + s).
   const int bid = blockIdx.x;
@@ -72,44 +120,48 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   const int rest = t / p.m_tiles;
   const int split = rest % p.splits;
   const int n_tile = rest / p.splits;
-  constexpr int mbw = MB;                   // 16-row blocks per wave row
-  constexpr int rows = 32 * MB;             // rows of the tile
-  const int m0 = m_tile * rows;
+  const int m0 = m_tile * G::kRowsA;
   const int n0 = n_tile * (kGlu ? kBN / 2 : kBN);
   const int nk = g.k / kBK;
   const int kb = (int)((long long)split * nk / p.splits);
   const int ke = (int)((long long)(split + 1) * nk / p.splits);
+  const int ntiles = ke - kb;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const bf16_t *A = static_cast<const bf16_t *>(g.a);
   const bf16_t *W0 = static_cast<const bf16_t *>(g.w0);
   const bf16_t *W1 = static_cast<const bf16_t *>(g.w1);
 
-  // Every thread always loads its chunks (rows clamped into the matrix): rows past the tile land in
-  // LDS rows no wave reads, and branch-free loads keep the load counters exact across the k loop.
-  static_assert(A_CH * kThreads == kBMX * (kBK / 8), "A chunks cover the LDS rows exactly");
-  const bf16_t *a_src[A_CH];
-  int a_dst[A_CH];
+  // Per-lane sources of this wave's loads.  Load q fills LDS rows kRPL q .. kRPL q + kRPL - 1; lane
+  // l lands in row kRPL q + l / kChunks, slot l % kChunks, so it fetches the chunk that the swizzle
+  // stores in that slot.  Every wave issues the same number of loads per stage (the wait counts are
+  // then the same immediate for all waves): a wave whose round-robin share of A loads is one short
+  // repeats the last A load, writing the same bytes to the same rows.  Rows are clamped into the
+  // matrices: rows past the batch fill LDS rows whose products are never stored.
+  const int lrow = lane / kChunks, lslot = lane % kChunks;
+  const bf16_t *a_src[G::kAI];
+  int a_lds[G::kAI];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * kThreads, row = c >> 3, kc = c & 7;
+  for (int i = 0; i < G::kAI; ++i) {
+    const int q = min(wave + kWaves * i, G::kLoadsA - 1);
+    const int row = kRPL * q + lrow;
     const int gr = min(m0 + row, g.m_alloc - 1);
-    a_src[i] = A + (size_t)gr * g.lda + kc * 8 + (size_t)kb * kBK;
-    a_dst[i] = row * kLdsK + swz(row, kc);
+    a_src[i] = A + (size_t)gr * g.lda + (size_t)kb * kBK + swz_slot(row, lslot) * 8;
+    a_lds[i] = kRPL * q * kLdsK;
   }
-  const bf16_t *b_src[B_CH];
-  int b_dst[B_CH];
+  const bf16_t *b_src[G::kBI];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * kThreads, row = c >> 3, kc = c & 7;
+  for (int i = 0; i < G::kBI; ++i) {
+    const int row = kRPL * (wave + kWaves * i) + lrow;   // weight row within the stripe's LDS block
     int src_row;
     const bf16_t *Wp = W0;
     if (kGlu) {
       // LDS rows of wave column wv: its gate block(s), then the up block(s) of the same columns.
       const int wv = row / (16 * kNB), bb = (row >> 4) % kNB, rl = row & 15;
       const int cb = wv * (kNB / 2) + bb % (kNB / 2);
-      src_row = n0 + cb * 16 + rl;
+      src_row = min(n0 + cb * 16 + rl, g.n - 1);
       Wp = (bb >= kNB / 2) ? W1 : W0;
     } else {
       src_row = min(n0 + row, g.n - 1);
@@ -118,10 +170,22 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
         src_row -= g.n_w0;
       }
     }
-    src_row = kGlu ? min(src_row, g.n - 1) : src_row;
-    b_src[i] = Wp + (size_t)src_row * g.ldw + kc * 8 + (size_t)kb * kBK;
-    b_dst[i] = (kBMX + row) * kLdsK + swz(row, kc);   // kBMX is a multiple of 16: same swizzle
+    // kRowsA is a multiple of 16, so the weight block's rows swizzle like rows 0..kBN-1
+    b_src[i] = Wp + (size_t)src_row * g.ldw + (size_t)kb * kBK + swz_slot(row, lslot) * 8;
   }
+
+  // Loads of k-tile j (clamped to the last tile, so every wave issues the same loads every step)
+  // into LDS stage `st`.
+  auto issue = [&](bf16_t *st, int j) {
+    const int kofs = min(j, ntiles - 1) * kBK;
+#pragma unroll
+    for (int i = 0; i < G::kAI; ++i) dma16(a_src[i] + kofs, st + a_lds[i]);
+#pragma unroll
+    for (int i = 0; i < G::kBI; ++i) {
+      const int q = wave + kWaves * i;
+      dma16(b_src[i] + kofs, st + (G::kRowsA + kRPL * q) * kLdsK);
+    }
+  };
 
   f32x4_t acc[MB][kNB];
 #pragma unroll
@@ -129,110 +193,61 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Register rings: weight k-tiles are fetched kDW tiles ahead of their use (they come from HBM),
-  // activation k-tiles kDA ahead (they are shared by every workgroup and mostly hit L2).  Two LDS
-  // stages: tile j is computed from stage j&1 while tile j+1 is written into the other stage.
-  // Tile indices past the end are clamped (a few redundant loads) so that the steady-state loop body
-  // has no branches around its loads.
-  constexpr int kDW = SARATHI_GEMM_W_RING, kDA = SARATHI_GEMM_A_RING;
-  constexpr int kUnrollK = kDW * kDA;             // a multiple of both ring depths
-  uint4 ra[kDA][A_CH], rb[kDW][B_CH];
-  const int ntiles = ke - kb;
-  auto tile = [&](int j) { return min(j, ntiles - 1) * kBK; };
-  auto load_a = [&](int slot, int j) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[slot][i] = ld16(a_src[i] + tile(j));
-  };
-  auto load_b = [&](int slot, int j) {
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[slot][i] = ld16(b_src[i] + tile(j));
-  };
-  auto store_tile = [&](int aslot, int bslot, int stage) {
-    bf16_t *Ls = lds + stage * kStage;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) st16(&Ls[a_dst[i]], ra[aslot][i]);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) st16(&Ls[b_dst[i]], rb[bslot][i]);
-  };
-  // Fragment rows start at multiples of 16, so a lane's swizzle term is ((lane & 15) >> 1).
+  // Fragment rows start at multiples of 16, so a lane's swizzle term depends on lane & 15 only.
+  // Both k-steps' fragments of a tile are read before its MFMAs, so the MFMAs of k-step 0 run while
+  // the reads of k-step 1 are in flight.
   const int frag_row = lane & 15;
-  const int frag_k0 = (((lane >> 4) + 0) ^ (frag_row >> 1)) * 8;   // k-step 0: chunks 0..3
-  const int frag_k1 = (((lane >> 4) + 4) ^ (frag_row >> 1)) * 8;   // k-step 1: chunks 4..7
-  const int a_row0 = wm * 16 * mbw;
-  // Fragment reads are grouped ahead of the MFMAs that use them, so each MFMA waits only for its
-  // own operands (descending LDS counters) rather than a read round trip every two MFMAs.  With
-  // narrow wave tiles both k-steps' fragments fit in registers at once (the MFMAs of k-step 0 then
-  // run while k-step 1's reads are in flight); wide wave tiles read one k-step at a time.
-  constexpr bool kAllK = kNB <= 2;
-  auto compute = [&](int stage) {
-    const bf16_t *L = lds + stage * kStage;
-    bf16x8_t bw[kAllK ? 2 : 1][kNB], af[kAllK ? 2 : 1][MB];
-    auto read = [&](int ks, int slot) {
+  const int frag_k0 = swz_slot(frag_row, (lane >> 4) + 0) * 8;   // k-step 0: chunks 0..3
+  const int frag_k1 = swz_slot(frag_row, (lane >> 4) + 4) * 8;   // k-step 1: chunks 4..7
+  const int a_row0 = wm * 16 * MB;
+  auto compute = [&](const bf16_t *L) {
+    bf16x8_t fa[2][MB], fb[2][kNB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
       const int fk = ks == 0 ? frag_k0 : frag_k1;
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
-        bw[slot][nb] = *reinterpret_cast<const bf16x8_t *>(
-            &L[(kBMX + wn * 16 * kNB + nb * 16 + frag_row) * kLdsK + fk]);
+        fb[ks][nb] = *reinterpret_cast<const bf16x8_t *>(
+            &L[(G::kRowsA + wn * 16 * kNB + nb * 16 + frag_row) * kLdsK + fk]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        af[slot][mb] = *reinterpret_cast<const bf16x8_t *>(
-            &L[(a_row0 + mb * 16 + frag_row) * kLdsK + fk]);
-    };
-    auto mfma = [&](int slot) {
+        fa[ks][mb] = *reinterpret_cast<const bf16x8_t *>(&L[(a_row0 + mb * 16 + frag_row) * kLdsK + fk]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          acc[mb][nb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[slot][mb], bw[slot][nb], acc[mb][nb], 0, 0, 0);
-    };
-    if (kAllK) {
-      read(0, 0);
-      read(1, kAllK ? 1 : 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma(0);
-      mfma(kAllK ? 1 : 0);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < kBK / 32; ++ks) {
-        read(ks, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma(0);
-      }
-    }
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][mb], fb[ks][nb], acc[mb][nb], 0, 0, 0);
   };
 
-  // One step: compute tile j (ring position u = j mod kUnrollK), stage tile j+1 into the other LDS
-  // buffer, refill the freed ring slots, barrier.
+  // Step j (stage u = j mod kNSt): start the loads of tile j + kNSt - 1 into the stage that step j - 1
+  // finished reading, multiply tile j, then wait until this wave's loads of tile j + 1 have landed
+  // (at most kNSt - 2 tiles' loads outstanding) and meet the other waves: tile j + 1 is then complete
+  // in LDS and nobody reads stage u any more.
+  constexpr int kLoads = G::kAI + G::kBI;
   auto step = [&](int u, int j) {
-    compute(u & 1);
-    const int as = (u + 1) % kDA, bs = (u + 1) % kDW;   // ring slots of tile j+1
-    store_tile(as, bs, (u + 1) & 1);
-    load_a(as, j + 1 + kDA);
-    load_b(bs, j + 1 + kDW);
-    __syncthreads();
+    issue(stage((u + kNSt - 1) % kNSt), j + kNSt - 1);
+    compute(stage(u));
+    wait_vm_lgkm0<(kNSt - 2) * kLoads>();
+    stage_barrier();
   };
 
 #pragma unroll
-  for (int j = 0; j < kDW; ++j) load_b(j, j);
-#pragma unroll
-  for (int j = 0; j < kDA; ++j) load_a(j, j);
-  store_tile(0, 0, 0);
-  load_a(0, kDA);
-  load_b(0, kDW);
-  __syncthreads();
-
-  const int nsteps = ntiles - 1;   // tiles followed by another tile
+  for (int u = 0; u < kNSt - 1; ++u) issue(stage(u), u);
+  wait_vm_lgkm0<(kNSt - 2) * kLoads>();   // tile 0 landed
+  stage_barrier();
   int j0 = 0;
-  for (; j0 + kUnrollK <= nsteps; j0 += kUnrollK) {
+  for (; j0 + kNSt <= ntiles; j0 += kNSt) {
 #pragma unroll
-    for (int u = 0; u < kUnrollK; ++u) step(u, j0 + u);
+    for (int u = 0; u < kNSt; ++u) step(u, j0 + u);
   }
 #pragma unroll
-  for (int u = 0; u < kUnrollK; ++u) {
-    if (j0 + u < nsteps) step(u, j0 + u);
-    else if (j0 + u == nsteps) compute(u & 1);   // the last tile
-  }
+  for (int u = 0; u < kNSt; ++u)
+    if (j0 + u < ntiles) step(u, j0 + u);
+  wait_vm_lgkm0<0>();   // the clamped loads past the last tile land before the workgroup ends
 
   // Epilogue.  Lane l of a 16x16 block holds rows 4*(l/16)+i, column l%16.
 #pragma unroll
@@ -329,43 +344,28 @@ __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs g) {
   }
 }
 
-constexpr size_t kLdsBytes = 2 * (size_t)(kBMX + kBN) * kLdsK * sizeof(bf16_t);
-
-template <int WN, int MB, int EPI>
+template <int MB, int EPI>
 hipError_t run_bf16_mb(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  static bool attr_set = false;   // one LDS opt-in per instantiation (host-side, idempotent)
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_rows<WN, MB, EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((gemm_bf16_rows<WN, MB, EPI>), dim3(p.grid), dim3(64 * kWM * WN), kLdsBytes, s,
-                     g, p);
+  hipLaunchKernelGGL((gemm_bf16_rows<MB, EPI>), dim3(p.grid), dim3(64 * kWaves), 0, s, g, p);
   return hipGetLastError();
-}
-
-template <int WN, int EPI>
-hipError_t run_bf16_wn(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  switch (p.mbw) {
-    case 1: return run_bf16_mb<WN, 1, EPI>(g, p, s);
-    case 2: return run_bf16_mb<WN, 2, EPI>(g, p, s);
-    case 3: return run_bf16_mb<WN, 3, EPI>(g, p, s);
-    case 4: return run_bf16_mb<WN, 4, EPI>(g, p, s);
-    case 5: return run_bf16_mb<WN, 5, EPI>(g, p, s);
-    case 6: return run_bf16_mb<WN, 6, EPI>(g, p, s);
-    case 7: return run_bf16_mb<WN, 7, EPI>(g, p, s);
-    case 8: return run_bf16_mb<WN, 8, EPI>(g, p, s);
-    case 9: return run_bf16_mb<WN, 9, EPI>(g, p, s);
-    case 10: return run_bf16_mb<WN, 10, EPI>(g, p, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 template <int EPI>
 hipError_t run_bf16(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   if (p.wn != kPlanWaveCols) return hipErrorInvalidValue;
-  return run_bf16_wn<kPlanWaveCols, EPI>(g, p, s);
+  switch (p.mbw) {
+    case 1: return run_bf16_mb<1, EPI>(g, p, s);
+    case 2: return run_bf16_mb<2, EPI>(g, p, s);
+    case 3: return run_bf16_mb<3, EPI>(g, p, s);
+    case 4: return run_bf16_mb<4, EPI>(g, p, s);
+    case 5: return run_bf16_mb<5, EPI>(g, p, s);
+    case 6: return run_bf16_mb<6, EPI>(g, p, s);
+    case 7: return run_bf16_mb<7, EPI>(g, p, s);
+    case 8: return run_bf16_mb<8, EPI>(g, p, s);
+    case 9: return run_bf16_mb<9, EPI>(g, p, s);
+    case 10: return run_bf16_mb<10, EPI>(g, p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int EPI>
