@@ -144,25 +144,70 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
   }
 }
 
+// One wave per (row, head), four per workgroup.  Lane l holds the (m, l) of splits l, l + 64, ...;
+// the wave max M and the weights w_s = 2^(m_s - M) (0 for empty splits) come from lane shuffles,
+// then each lane accumulates its D / 64 output elements over the splits, all loads of a group of
+// splits issued before their adds.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineSlots = kMaxKeySplits / kWave;   // splits per lane
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_combine(int nh, int row0, int max_splits,
-                                                   const float *part_o, const float *part_ml,
-                                                   T *out, int ld_out) {
-  const int r = row0 + blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int row0, int n_rows,
+                                                                   int max_splits, int chunk_rows,
+                                                                   int chunk_splits,
+                                                                   const float *part_o,
+                                                                   const float *part_ml, T *out,
+                                                                   int ld_out) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);   // (row, head) index
+  if (pair >= n_rows * nh) return;
+  const int r = row0 + pair / nh, h = pair % nh;
   const size_t base = ((size_t)r * nh + h) * max_splits;
+  const int n_used = r < chunk_rows ? chunk_splits : max_splits;
+  float m[kCombineSlots], l[kCombineSlots], w[kCombineSlots];
   float M = -INFINITY;
-  for (int s = 0; s < max_splits; ++s)
-    if (part_ml[2 * (base + s) + 1] > 0.f) M = fmaxf(M, part_ml[2 * (base + s)]);
+#pragma unroll
+  for (int k = 0; k < kCombineSlots; ++k) {
+    const int sp = lane + k * kWave;
+    m[k] = -INFINITY;
+    l[k] = 0.f;
+    if (sp < n_used) {
+      const float2 ml = *reinterpret_cast<const float2 *>(&part_ml[2 * (base + sp)]);
+      if (ml.y > 0.f) {
+        m[k] = ml.x;
+        l[k] = ml.y;
+      }
+    }
+    M = fmaxf(M, m[k]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineSlots; ++k) {
+    w[k] = l[k] > 0.f ? exp2f(m[k] - M) : 0.f;
+    L += l[k] * w[k];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, kWave);
   constexpr int PER = D / kWave;
   float acc[PER] = {};
-  float L = 0.f;
-  for (int s = 0; s < max_splits; ++s) {
-    const float l = part_ml[2 * (base + s) + 1];
-    if (!(l > 0.f)) continue;
-    const float w = exp2f(part_ml[2 * (base + s)] - M);
-    L += l * w;
+  constexpr int kGroup = 4;
+  for (int s0 = 0; s0 < n_used; s0 += kGroup) {
+    float v[kGroup][PER], ws[kGroup];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += w * part_o[(base + s) * D + lane + i * kWave];
+    for (int u = 0; u < kGroup; ++u) {
+      const int sp = min(s0 + u, n_used - 1);
+      float wk = w[0];
+#pragma unroll
+      for (int k = 1; k < kCombineSlots; ++k) wk = sp / kWave == k ? w[k] : wk;   // wave-uniform
+      ws[u] = s0 + u < n_used ? __shfl(wk, sp % kWave, kWave) : 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[u][i] = part_o[(base + sp) * D + lane + i * kWave];
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += ws[u] * v[u][i];
   }
   const float inv = 1.0f / L;
 #pragma unroll
@@ -180,10 +225,12 @@ hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, cons
 }
 
 template <typename T, int D>
-hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, const float *po,
-                       const float *pml, void *out, int ld_out, hipStream_t s) {
-  hipLaunchKernelGGL((attn_combine<T, D>), dim3(n_rows, nh), dim3(64), 0, s, nh, row0, max_splits,
-                     po, pml, static_cast<T *>(out), ld_out);
+hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, int chunk_rows, int chunk_splits,
+                       const float *po, const float *pml, void *out, int ld_out, hipStream_t s) {
+  const int pairs = n_rows * nh;
+  hipLaunchKernelGGL((attn_combine<T, D>), dim3((pairs + kCombineWaves - 1) / kCombineWaves),
+                     dim3(64 * kCombineWaves), 0, s, nh, row0, n_rows, max_splits, chunk_rows,
+                     chunk_splits, po, pml, static_cast<T *>(out), ld_out);
   return hipGetLastError();
 }
 
@@ -201,13 +248,18 @@ hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, in
 }
 
 hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int max_splits,
-                               const float *part_o, const float *part_ml, void *out, int ld_out,
-                               hipStream_t s) {
+                               int chunk_rows, int chunk_splits, const float *part_o,
+                               const float *part_ml, void *out, int ld_out, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (type == kF32 && d == 64) return run_combine<float, 64>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
-  if (type == kF32 && d == 128) return run_combine<float, 128>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
-  if (type == kBF16 && d == 64) return run_combine<bf16_t, 64>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
-  if (type == kBF16 && d == 128) return run_combine<bf16_t, 128>(nh, row0, n_rows, max_splits, part_o, part_ml, out, ld_out, s);
+  if (chunk_splits < 1 || chunk_splits > max_splits || max_splits > kMaxKeySplits)
+    return hipErrorInvalidValue;
+#define SARATHI_COMBINE(T, D) \
+  return run_combine<T, D>(nh, row0, n_rows, max_splits, chunk_rows, chunk_splits, part_o, part_ml, out, ld_out, s)
+  if (type == kF32 && d == 64) SARATHI_COMBINE(float, 64);
+  if (type == kF32 && d == 128) SARATHI_COMBINE(float, 128);
+  if (type == kBF16 && d == 64) SARATHI_COMBINE(bf16_t, 64);
+  if (type == kBF16 && d == 128) SARATHI_COMBINE(bf16_t, 128);
+#undef SARATHI_COMBINE
   return hipErrorInvalidValue;
 }
 

@@ -81,6 +81,7 @@ hipError_t launch_rope_append(int type, const float *part, int splits, int rows_
 // 0..pos of its cache in balanced splits of at most kAttnSplit keys; each split writes its partial
 // (running max m and sum l in the log2 domain, unnormalised output o) to part_ml / part_o.
 constexpr int kAttnSplit = 256;
+constexpr int kMaxKeySplits = 256;   // split partials per (row, head): keys up to 65536
 __host__ __device__ inline int attn_splits(int n_keys) {
   return (n_keys + kAttnSplit - 1) / kAttnSplit;
 }
@@ -89,15 +90,22 @@ hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, in
                             float *part_o, float *part_ml, hipStream_t s);
 
 // Merges the split partials of rows [row0, row0+n_rows) into out[row, h*d + e] (storage type,
-// row stride ld_out).
+// row stride ld_out).  Partials sit at ((row * nh + h) * max_splits + s); rows below chunk_rows
+// have chunk_splits of them, the others max_splits.
 hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int max_splits,
-                               const float *part_o, const float *part_ml, void *out, int ld_out,
-                               hipStream_t s);
+                               int chunk_rows, int chunk_splits, const float *part_o,
+                               const float *part_ml, void *out, int ld_out, hipStream_t s);
 
 // Flash-style causal chunk attention (bf16, MFMA): chunk rows [0, ch.len) attend to chunk keys
-// 0..ch.off+t.  q rows are the chunk rows of q (row stride ld_q); out likewise.
+// 0..ch.off+t.  q rows are the chunk rows of q (row stride ld_q); out likewise.  With n_split > 1
+// each 64-query block's key tiles are split n_split ways and the splits write partials (stride
+// `stride` splits per row and head) for launch_attn_combine instead of out.
+constexpr int kChunkTargetWorkgroups = 512;   // ~2 workgroups per compute unit
+constexpr int kMaxChunkSplits = 16;
+int chunk_attn_splits(int chunk_len, int chunk_offset, int nh);
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkRef &ch, void *out,
-                             int ld_out, hipStream_t s);
+                             int ld_out, int n_split, int stride, float *part_o, float *part_ml,
+                             hipStream_t s);
 
 // Zero-fill rows [row0, row1) of a [*, cols] storage matrix (row stride ld).
 hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int row1, hipStream_t s);

@@ -64,6 +64,9 @@ sarathi_status check_desc(const sarathi_layer_desc *d) {
     return fail(SARATHI_ERR_INVALID, "hidden, n_heads, head_dim and ffn must be positive");
   if (d->max_tokens <= 0 || d->max_pos <= 0)
     return fail(SARATHI_ERR_INVALID, "max_tokens and max_pos must be positive");
+  if (d->max_pos > kMaxKeySplits * kAttnSplit)
+    return fail(SARATHI_ERR_UNSUPPORTED, "max_pos %d > %d (attention key-range limit)", d->max_pos,
+                kMaxKeySplits * kAttnSplit);
   if (d->arch != SARATHI_ARCH_LLAMA && d->arch != SARATHI_ARCH_GPT)
     return fail(SARATHI_ERR_INVALID, "unknown arch %d", d->arch);
   if (d->dtype != SARATHI_F32 && d->dtype != SARATHI_BF16)
@@ -158,6 +161,7 @@ constexpr int kPlanCUs = 256;
 
 struct Plan {
   int T, T_alloc, max_splits;
+  int chunk_splits;   // key-range splits of the MFMA chunk kernel (1: it writes the output itself)
   GemmPlan qkv, o, up, down;
   size_t n1, q, attn, h1, n2, act, part, part_o, part_ml, total;
 };
@@ -166,8 +170,8 @@ struct Plan {
 // decode rows, and the chunk rows too in float32 mode.
 bool chunk_uses_split(const sarathi_layer_desc *d) { return d->dtype != SARATHI_BF16; }
 
-int max_key_splits(const sarathi_layer_desc *d, const sarathi_batch *b) {
-  int ms = 1;
+int max_key_splits(const sarathi_layer_desc *d, const sarathi_batch *b, int chunk_splits) {
+  int ms = chunk_splits;
   if (b->chunk_len > 0 && chunk_uses_split(d))
     ms = std::max(ms, attn_splits(b->chunk_offset + b->chunk_len));
   for (int i = 0; i < b->n_decodes; ++i) ms = std::max(ms, attn_splits(b->decode_len[i] + 1));
@@ -178,7 +182,8 @@ Plan make_plan(const sarathi_layer_desc *d, const sarathi_batch *b) {
   Plan p{};
   p.T = b->chunk_len + b->n_decodes;
   p.T_alloc = round_up(p.T, 64);
-  p.max_splits = max_key_splits(d, b);
+  p.chunk_splits = chunk_uses_split(d) ? 1 : chunk_attn_splits(b->chunk_len, b->chunk_offset, d->n_heads);
+  p.max_splits = max_key_splits(d, b, p.chunk_splits);
   const int ty = d->dtype;
   const size_t el = elem_size(ty), R = p.T_alloc;
   const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
@@ -284,7 +289,8 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
       HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, ch, none,
                                p.max_splits, po, pml, s));
     } else {
-      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, ch, out, A, s));
+      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, ch, out, A, p.chunk_splits,
+                                p.max_splits, po, pml, s));
     }
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_CHUNK, C > 0));
@@ -296,10 +302,13 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_MERGE));
-  const int merge_row0 = split_chunk ? 0 : C;
+  // Chunk rows need merging when the split-KV kernel served them or the MFMA kernel was split.
+  const bool merge_chunk = split_chunk || p.chunk_splits > 1;
+  const int merge_row0 = merge_chunk ? 0 : C;
+  const int chunk_splits = split_chunk ? p.max_splits : p.chunk_splits;
   if (C + B > merge_row0)
     HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, merge_row0, C + B - merge_row0,
-                                p.max_splits, po, pml, out, A, s));
+                                p.max_splits, C, chunk_splits, po, pml, out, A, s));
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_MERGE, C + B > merge_row0));
   return SARATHI_OK;
 }

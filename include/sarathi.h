@@ -67,7 +67,7 @@ typedef struct {
     float norm_eps;      /* e.g. 1e-6 (RMSNorm) or 1e-5 (LayerNorm) */
     float rope_base;     /* e.g. 10000; unused for GPT */
     int32_t max_tokens;  /* largest C+B a forward call may pass */
-    int32_t max_pos;     /* every position must be < max_pos (size of the RoPE table) */
+    int32_t max_pos;     /* every position must be < max_pos (size of the RoPE table); at most 65536 */
 } sarathi_layer_desc;
 
 /* Device pointers to caller-owned weights; they must stay valid and unchanged while the layer exists.
