@@ -23,9 +23,11 @@ ARCH = "gfx950"
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
-    # packed float32 VALU ops are left to the compiler's own selection only where it cannot form
-    # them: the feature is switched off for device code
+    # no packed float32 VALU instructions (v_pk_add/mul/fma_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the softmax and epilogues then read them without copies out of
+    # the accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -7,16 +7,24 @@
 // every chunk of the request, the overhead the same page discusses under "Overhead 2".
 //
 // Flash-style design for gfx950.  A workgroup takes one head and 64 queries (16 per wave) and streams
-// the request's keys in tiles of 64 through LDS with double buffering.  Per wave and tile:
+// a range of the request's keys in tiles of 64 through a 2- or 3-stage LDS ring filled by LDS DMA
+// (global_load_lds_dwordx4: no staging registers, no LDS store instructions).  Per wave and tile:
 //   S^T = K Q^T   (16 x v_mfma_f32_16x16x32_bf16 for d = 128): lane l then holds the scores of query
 //                 l % 16 for 16 of the tile's keys, so a query's row max / sum need only in-lane work
 //                 and two butterfly steps;
 //   online softmax in float32 (log2 domain, scale folded into the exponent);
-//   O^T += V^T P^T (16 more MFMAs): P^T is taken straight from the S^T registers (the MFMA's k order
-//                 is the same free permutation of the 32 keys on both operands), V^T comes from a
-//                 transposed copy of the V tile in LDS.
-// Only tiles that cross the diagonal are masked.  Keys at or past the chunk's end are zero-filled in
-// LDS (never loaded), so a masked probability of 0 never meets an unwritten cache slot.
+//   O^T += V^T P^T (16 more MFMAs): P^T is taken straight from the S^T registers, and V^T's operand
+//                 comes from the row-major V tile through transposing LDS reads (ds_read_b64_tr_b16:
+//                 in each group of 16 lanes, lane j addresses row j/4, columns 4(j%4)..4(j%4)+3, and
+//                 lane i receives column i of those 4 rows), so the keys of a lane's k-slots match
+//                 the keys of its P^T values without any register shuffling.
+// K rows are stored with their 16-byte chunks permuted (slot = chunk ^ f(row)) so the 16 rows of a
+// fragment read hit distinct banks; V rows likewise for the transposing reads.  Only tiles that cross
+// the diagonal are masked.  Rows past the last key any query of the block needs are loaded as copies
+// of that key (finite values whose probability is 0 after the mask), never from unwritten slots.
+//
+// The key range of each 64-query block can be split over several workgroups so that short chunks
+// still fill the GPU; a split writes (m, l, unnormalised O) partials for attn_combine.
 #include <math.h>
 
 #include "kernels.h"
@@ -26,34 +34,61 @@ namespace {
 
 constexpr int kBQ = 64;         // queries per workgroup (16 per wave)
 constexpr int kBKV = 64;        // keys per tile
-constexpr int kKPad = 8;        // K tile row padding (elements)
-constexpr int kVtPad = 4;       // transposed V tile row padding (elements)
+#ifndef SARATHI_CHUNK_STAGES
+#define SARATHI_CHUNK_STAGES 2
+#endif
+constexpr int kChunkStages = SARATHI_CHUNK_STAGES;   // LDS ring depth (2 or 3)
+static_assert(kChunkStages == 2 || kChunkStages == 3, "ring depth");
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const bf16_t gbf16_t;   // global memory
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 // 2^x for x <= 0 with the hardware exponential alone: results below the normal range flush to 0,
 // which is what a probability that small contributes anyway.
 __device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Split s of S covers key tiles [s nt / S, (s + 1) nt / S) of the workgroup's nt tiles.  With S = 1 the
-// workgroup writes the normalised output; otherwise it writes its split partial (running max m and
-// sum l in the log2 domain, unnormalised output) at ((row * nh + h) * stride + s), for the combine
-// kernel to merge.
+template <int D> struct TileGeom {
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
+  static constexpr int kRPL = 1024 / (2 * D);      // rows per DMA load (64 lanes x 16 bytes)
+  static constexpr int kLoadsPerWave = kBKV / kRPL / 4;
+  static constexpr int kElems = kBKV * D;
+};
+// Chunk slot of K row r (row within the tile): 16 rows at one logical chunk land in 16 distinct
+// 4-bank groups (256-byte rows: slot = c ^ (r & 15); 128-byte rows: slot = c ^ ((r >> 1) & 7)).
+template <int D> __device__ __forceinline__ int k_slot(int r, int c) {
+  return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+}
+// Chunk slot of V row r: a transposing read by 32 lanes covers 8 consecutive rows x 2 adjacent
+// chunks; for 256-byte rows slot = c ^ 2 (r & 7) spreads those 16 (row, chunk) pairs over all 64
+// banks; 128-byte rows already fall in distinct banks.
+template <int D> __device__ __forceinline__ int v_slot(int r, int c) {
+  return D == 128 ? c ^ ((r & 7) << 1) : c;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q, int nh,
                                                        ChunkRef ch, bf16_t *out, int ld_out,
                                                        float qscale_log2, int n_split, int stride,
-                                                       float *part_o, float *part_ml) {
+                                                       float *part_o, float *part_ml, int per_xcd) {
+  using G = TileGeom<D>;
   constexpr int KS = D / 32;             // k-steps of the score MFMA
   constexpr int DB = D / 16;             // 16-row blocks of O^T
-  constexpr int kKRow = D + kKPad;       // K tile LDS row (keys x d)
-  constexpr int kVtRow = kBKV + kVtPad;  // V^T tile LDS row (d x keys)
-  constexpr int kStage = kBKV * kKRow + D * kVtRow;
-  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];   // 2 * kStage elements
+  __shared__ __attribute__((aligned(1024))) bf16_t k0s[G::kElems], v0s[G::kElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t k1s[G::kElems], v1s[G::kElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t k2s[kChunkStages > 2 ? G::kElems : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t v2s[kChunkStages > 2 ? G::kElems : 8];
+  auto kst = [&](int u) -> bf16_t * { return u == 0 ? k0s : u == 1 ? k1s : k2s; };
+  auto vst = [&](int u) -> bf16_t * { return u == 0 ? v0s : u == 1 ? v1s : v2s; };
 
-  const int qb = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Work item (head, split, query block), XCD-aware: workgroup b runs on XCD b % 8 and the items of
+  // XCD x are the consecutive range [x per_xcd, (x + 1) per_xcd), so the query blocks and splits of a
+  // head share one XCD's L2 and its K/V crosses HBM about once.
+  const int q_blocks = (ch.len + kBQ - 1) / kBQ;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= q_blocks * n_split * nh) return;
+  const int qb = item % q_blocks, split = (item / q_blocks) % n_split, h = item / (q_blocks * n_split);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int C = ch.len, off = ch.off;
   const int q_first = qb * kBQ;
@@ -62,13 +97,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
   const int nt = (n_keys + kBKV - 1) / kBKV;
   const int t_begin = (int)((long long)split * nt / n_split);
   const int t_end = (int)((long long)(split + 1) * nt / n_split);
-  gbf16_t *Kh = reinterpret_cast<gbf16_t *>(ch.k) + (size_t)h * ch.cap * D;
-  gbf16_t *Vh = reinterpret_cast<gbf16_t *>(ch.v) + (size_t)h * ch.cap * D;
-  auto gld16 = [](gbf16_t *p) {
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4 *>(p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-  };
+  const bf16_t *Kh = reinterpret_cast<const bf16_t *>(ch.k) + (size_t)h * ch.cap * D;
+  const bf16_t *Vh = reinterpret_cast<const bf16_t *>(ch.v) + (size_t)h * ch.cap * D;
 
   // This lane's query (row of the wave's 16) and its fragments of q (B operand of S^T = K Q^T).
   const int my_q = q_first + wave * 16 + c16;
@@ -81,53 +111,25 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
       qf[ks] = *reinterpret_cast<const bf16x8_t *>(qr + ks * 32 + g * 8);
   }
 
-  // Tile loads: K as [key][d] rows of 16-byte chunks; V as key pairs x 16 d, written transposed.
-  constexpr int K_CH = kBKV * D / 8 / 256;                // 16-byte K chunks per thread
-  uint4 rk[K_CH], rv[4];
-  auto load_tile = [&](int t) {
-    const int k0 = t * kBKV;
+  // DMA sources: load i of this wave fills tile rows kRPL (wave + 4 i) .. + kRPL - 1; lane l lands
+  // in row kRPL (wave + 4 i) + l / kChunks, slot l % kChunks, so it fetches the chunk stored there.
+  int lr[G::kLoadsPerWave], kc[G::kLoadsPerWave], vc[G::kLoadsPerWave];
 #pragma unroll
-    for (int i = 0; i < K_CH; ++i) {
-      const int c = tid + i * 256, key = c / (D / 8), dc = c % (D / 8);
-      const int kg = k0 + key;
-      rk[i] = kg < n_keys ? gld16(Kh + (size_t)kg * D + dc * 8) : make_uint4(0, 0, 0, 0);
-    }
-    // V: thread -> key pair kp (32 pairs) x d chunk of 16 (D/16 chunks); 256 threads cover it when
-    // D == 128; for D == 64 each thread takes half as many d.
-    const int kp = tid & 31, dch = tid >> 5;
+  for (int i = 0; i < G::kLoadsPerWave; ++i) {
+    const int r = G::kRPL * (wave + 4 * i) + lane / G::kChunks, sl = lane % G::kChunks;
+    lr[i] = r;
+    kc[i] = k_slot<D>(r, sl);   // the slot permutation is an involution
+    vc[i] = v_slot<D>(r, sl);
+  }
+  // Tile t (clamped to the split's last tile, so every step issues the same loads) into stage u.
+  auto issue = [&](int u, int t) {
+    const int k0 = min(t, t_end - 1) * kBKV;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kg = k0 + 2 * kp + j;
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const int d0 = (D == 128 ? dch * 16 : (dch >> 1) * 16) + hlf * 8;
-        const bool use = (D == 128 || (dch & 1) == hlf) && kg < n_keys;
-        rv[j * 2 + hlf] = use ? gld16(Vh + (size_t)kg * D + d0) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    bf16_t *Ks = lds + stage * kStage;
-    bf16_t *Vt = Ks + kBKV * kKRow;
-#pragma unroll
-    for (int i = 0; i < K_CH; ++i) {
-      const int c = tid + i * 256, key = c / (D / 8), dc = c % (D / 8);
-      st16(&Ks[key * kKRow + dc * 8], rk[i]);
-    }
-    const int kp = tid & 31, dch = tid >> 5;
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      if (D == 64 && (dch & 1) != hlf) continue;
-      const int d0 = (D == 128 ? dch * 16 : (dch >> 1) * 16) + hlf * 8;
-      const uint4 a = rv[hlf], b = rv[2 + hlf];          // keys 2kp and 2kp+1, d0..d0+7
-      const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (wa[e] & 0xffffu) | (wb[e] << 16);          // d0+2e   : keys 2kp, 2kp+1
-        const uint32_t hi = (wa[e] >> 16) | (wb[e] & 0xffff0000u);      // d0+2e+1
-        *reinterpret_cast<uint32_t *>(&Vt[(d0 + 2 * e) * kVtRow + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t *>(&Vt[(d0 + 2 * e + 1) * kVtRow + 2 * kp]) = hi;
-      }
+    for (int i = 0; i < G::kLoadsPerWave; ++i) {
+      const size_t key = (size_t)min(k0 + lr[i], n_keys - 1);
+      const int dst = G::kRPL * (wave + 4 * i) * D;
+      dma16(Kh + key * D + kc[i] * 8, kst(u) + dst);
+      dma16(Vh + key * D + vc[i] * 8, vst(u) + dst);
     }
   };
 
@@ -136,39 +138,30 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
   for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (t_begin < t_end) {   // workgroup-uniform
-    load_tile(t_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bf16_t *Ks = lds + buf * kStage;
-    const bf16_t *Vt = Ks + kBKV * kKRow;
-    if (t + 1 < t_end) load_tile(t + 1);
-
+  auto compute = [&](int u, int t) {
+    const bf16_t *Ks = kst(u), *Vs = vst(u);
     // S^T for the tile: 4 key blocks of 16.
     f32x4_t sacc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int r = kb * 16 + c16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(
-            &Ks[(kb * 16 + c16) * kKRow + ks * 32 + g * 8]);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Ks[r * D + k_slot<D>(r, ks * 4 + g) * 8]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // Scores in the log2 domain, masked past each query's position (and past the chunk's keys);
-    // only tiles that reach past the wave's first query need the mask (a wave-uniform test).
+    // Raw scores, masked past each query's position; only tiles that reach past the wave's first
+    // query need the mask (a wave-uniform test).  The log2-domain scale (positive) is applied to the
+    // maximum and inside each exponent's multiply-add.
     const int k0 = t * kBKV;
     const bool diag = k0 + kBKV - 1 > off + q_first + wave * 16;
     float sc[4][4];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[kb][i] = sacc[kb][i] * qscale_log2;
+      for (int i = 0; i < 4; ++i) sc[kb][i] = sacc[kb][i];
     if (diag) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -176,6 +169,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
         for (int i = 0; i < 4; ++i)
           if (k0 + kb * 16 + g * 4 + i > my_pos) sc[kb][i] = -INFINITY;
     }
+    float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -184,10 +178,9 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     // A split that starts past a query's position leaves its row fully masked (m_new = -inf): then
     // the exponent base is 0, every p is 0 and the row's partial stays empty (l = 0).
-    const float m_new = fmaxf(m_run, tmax);
+    const float m_new = fmaxf(m_run, tmax * qscale_log2);
     const float m_base = m_new == -INFINITY ? 0.f : m_new;
-    // Rescale the running sums only when some query of the wave found a larger maximum (after the
-    // first tiles this is rare); otherwise the factor is exactly 1 for every lane.
+    // Rescale the running sums only when some query of the wave found a larger maximum.
     if (__any(m_new > m_run)) {
       const float corr = exp2_nonpos(m_run - m_base);
       l_run *= corr;
@@ -195,33 +188,62 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
       for (int db = 0; db < DB; ++db) o[db] *= corr;
     }
     m_run = m_new;
-    // P^T operands: k-step s covers key blocks 2s and 2s+1.
+    // P^T operands: k-step s holds keys s*32 + 4g + i (slots 0..3) and s*32 + 16 + 4g + i (4..7).
     bf16x8_t pf[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2_nonpos(sc[2 * s + hb][i] - m_base);
+          const float p = exp2_nonpos(fmaf(sc[2 * s + hb][i], qscale_log2, -m_base));
           l_run += p;
           pf[s][hb * 4 + i] = (__bf16)p;
         }
-    }
-    // O^T += V^T P^T.
+    // O^T += V^T P^T; V^T fragments by transposing reads of rows s*32 + 4g + (0..3) and + 16.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
+      const int col = db * 16 + 4 * (c16 & 3);          // this lane's 4 addressed columns
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16_t *vr = &Vt[(db * 16 + c16) * kVtRow + s * 32 + g * 4];
-        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(vr);
-        const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(vr + 16);
-        const bf16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[s], o[db], 0, 0, 0);
+        s16x4_t half[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r = s * 32 + hh * 16 + 4 * g + (c16 >> 2);
+          const bf16_t *a = &Vs[r * D + v_slot<D>(r, col >> 3) * 8 + (col & 7)];
+          half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t *)(a));
+        }
+        const s16x8_t vv = {half[0][0], half[0][1], half[0][2], half[0][3],
+                            half[1][0], half[1][1], half[1][2], half[1][3]};
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[s], o[db],
+                                                         0, 0, 0);
       }
     }
-    if (t + 1 < t_end) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+
+  if (t_begin < t_end) {   // workgroup-uniform: an empty split only writes its empty partial
+    constexpr int kL = 2 * G::kLoadsPerWave;   // loads per wave per tile
+    constexpr int kNSt = kChunkStages;
+    auto step = [&](int u, int t) {
+      issue((u + kNSt - 1) % kNSt, t + kNSt - 1);
+      compute(u, t);
+      wait_vm_lgkm0<(kNSt - 2) * kL>();   // this wave's loads of tile t + 1 have landed
+      stage_barrier();                    // ... and everyone's; stage u is free again
+    };
+#pragma unroll
+    for (int u = 0; u < kNSt - 1; ++u) issue(u, t_begin + u);
+    wait_vm_lgkm0<(kNSt - 2) * kL>();
+    stage_barrier();
+    int t0 = t_begin;
+    for (; t0 + kNSt <= t_end; t0 += kNSt) {
+#pragma unroll
+      for (int u = 0; u < kNSt; ++u) step(u, t0 + u);
+    }
+#pragma unroll
+    for (int u = 0; u < kNSt; ++u)
+      if (t0 + u < t_end) step(u, t0 + u);
+    wait_vm_lgkm0<0>();   // the clamped loads past the last tile land before the workgroup ends
   }
 
   // Row sums over the four lane groups of the query, then O[q][d] = O^T[d][q] / l.
@@ -255,19 +277,12 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
 template <int D>
 hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkRef &ch, void *out, int ld_out,
                      int n_split, int stride, float *part_o, float *part_ml, hipStream_t s) {
-  constexpr size_t bytes = 2 * sizeof(bf16_t) * ((size_t)kBKV * (D + kKPad) + (size_t)D * (kBKV + kVtPad));
-  static bool attr_set = false;   // one LDS opt-in per instantiation (host-side, idempotent)
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_chunk_mfma<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const dim3 grid((ch.len + kBQ - 1) / kBQ, nh, n_split);
+  const int items = (ch.len + kBQ - 1) / kBQ * n_split * nh;
+  const int per_xcd = (items + 7) / 8;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(attn_chunk_mfma<D>, grid, dim3(256), bytes, s, static_cast<const bf16_t *>(q),
-                     ld_q, nh, ch, static_cast<bf16_t *>(out), ld_out, qscale, n_split, stride,
-                     part_o, part_ml);
+  hipLaunchKernelGGL(attn_chunk_mfma<D>, dim3(8 * per_xcd), dim3(256), 0, s,
+                     static_cast<const bf16_t *>(q), ld_q, nh, ch, static_cast<bf16_t *>(out), ld_out,
+                     qscale, n_split, stride, part_o, part_ml, per_xcd);
   return hipGetLastError();
 }
 

@@ -61,6 +61,35 @@ template <> __device__ __forceinline__ uint4 pack<bf16_t>(const float *in) {
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(void *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
 
+// ---------------------------------------------------------------------------------------------
+// Global -> LDS streaming (gfx950 LDS DMA), shared by the GEMM and the chunk attention kernels.
+// A kernel keeps several LDS stages, one __shared__ array each (the compiler then knows a read of one
+// stage does not depend on loads still landing in another), issues the loads of a later tile,
+// computes the current one, waits for its own loads of the next tile and meets the other waves.
+
+// global -> LDS, 16 bytes per lane: lane l writes bytes [16 l, 16 l + 16) after the wave-uniform LDS
+// address `lds`.
+__device__ __forceinline__ void dma16(const bf16_t *src, bf16_t *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's global loads are outstanding and all its LDS operations are
+// done (s_waitcnt with vmcnt = N, lgkmcnt = 0, expcnt left open).
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without a memory fence (a fence would also wait for the loads still in flight
+// into the other stages); the empty asm statements keep the compiler from moving memory accesses
+// across it.  Visibility of the LDS stage that the next step reads comes from the explicit wait that
+// precedes each barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Butterfly reductions over the lanes whose index differs only in the bits of [lo_mask, 32].
 __device__ __forceinline__ float wave_sum(float v, int from = 1) {
 #pragma unroll

@@ -67,29 +67,6 @@ template <int MB> struct StageGeom {
   static_assert((kStages - 2) * (kAI + kBI) < 64, "loads in flight fit the wait counter");
 };
 
-// global -> LDS, 16 bytes per lane: lane l writes bytes [16 l, 16 l + 16) after the wave-uniform LDS
-// address `lds`.
-__device__ __forceinline__ void dma16(const bf16_t *src, bf16_t *lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
-// Wait until at most N of this wave's global loads are outstanding and all its LDS operations are
-// done (s_waitcnt with vmcnt = N, lgkmcnt = 0, expcnt left open).
-template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-// Workgroup barrier without a memory fence (a fence would also wait for the loads still in flight
-// into the other stages); the empty asm statements keep the compiler from moving memory accesses
-// across it.  Visibility of the LDS stage that the next step reads comes from the explicit wait that
-// precedes each barrier.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int MB, int EPI>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
