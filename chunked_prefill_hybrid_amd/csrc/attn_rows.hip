@@ -69,12 +69,12 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
     for (int u = 0; u < kUnroll; ++u) {
       const int j = wbeg + (c0 + u) * KPI + grp;
       ok[u] = j < k_end;
-      kr[u] = ok[u] ? ld16(Kh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
+      kr[u] = ok[u] ? ld16_stream(Kh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int j = wbeg + (c0 + u) * KPI + grp;
-      vr[u] = ok[u] ? ld16(Vh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
+      vr[u] = ok[u] ? ld16_stream(Vh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
     }
     float sc[kUnroll];
     float cmax = -INFINITY;

@@ -72,6 +72,14 @@ __device__ __forceinline__ void st16(void *p, const uint4 &v) { *reinterpret_cas
 __device__ __forceinline__ void dma16(const bf16_t *src, bf16_t *lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
+// 16-byte load of data read once per forward (KV caches in decode attention): non-temporal, which
+// streams from HBM measurably faster (6.3 vs 5.6 TB/s in a plain read) than loads that allocate in
+// the caches.
+__device__ __forceinline__ uint4 ld16_stream(const void *p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Wait until at most N of this wave's global loads are outstanding and all its LDS operations are
 // done (s_waitcnt with vmcnt = N, lgkmcnt = 0, expcnt left open).
