@@ -8,7 +8,7 @@
 //               written as zeros so the next GEMM computes on zeros there.
 //   ffn_act:    the FFN activation silu(gate) * up or gelu(up) from split partials of the up GEMM.
 //   resid_sum:  out = resid + sum of a GEMM's split partials (the layer output y = h1 + FFN).
-// One workgroup per row, 4-element vectors, float32 sums.
+// One workgroup per row (norms), 4-element vectors, float32 sums.
 #include "kernels.h"
 
 namespace sarathi {
@@ -37,7 +37,7 @@ template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, const floa
   *reinterpret_cast<uint2 *>(p) = u;
 }
 
-__device__ __forceinline__ float block_sum(float v, float *red) {
+template <int NT> __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
@@ -45,12 +45,15 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
   __syncthreads();
   float t = 0.f;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+  for (int w = 0; w < NT / 64; ++w) t += red[w];
   return t;
 }
 
 constexpr int kMaxSplits = 8;   // split partials a consumer sums (the planner never makes more)
-constexpr int kMaxChunks = 16;  // 4-element chunks per thread: rows up to 16384 wide
+// A norm row is handled by one workgroup of kNormThreads threads (16 waves, so that the ~300 rows of
+// a batch still keep several waves of memory requests per SIMD in flight).
+constexpr int kNormThreads = 1024;
+constexpr int kMaxChunks = 4;   // 4-element chunks per thread: rows up to 16384 wide
 
 // v[0..3] += sum_s part[s][off..off+3] in split order; every split's load is issued before its add
 // so a thread keeps several loads in flight.
@@ -71,38 +74,38 @@ __device__ __forceinline__ void add_splits(const float *part, int splits, size_t
 // One row per workgroup: the row stays in registers (up to kMaxChunks 4-element chunks per thread),
 // so the norm needs one read of its inputs.
 template <typename Tres, typename Tout, bool LN>
-__global__ __launch_bounds__(kThreads) void norm_rows(const Tres *resid, const float *part,
+__global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, const float *part,
                                                       int splits, float *sum_out, const float *g,
                                                       const float *b, Tout *out, int H, int rows,
                                                       float eps) {
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kNormThreads / 64];
   const int r = blockIdx.x;
   Tout *o = out + (size_t)r * H;
   if (r >= rows) {
     const float z[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) store4<Tout>(o + c, z);
+    for (int c = threadIdx.x * 4; c < H; c += kNormThreads * 4) store4<Tout>(o + c, z);
     return;
   }
   const size_t slice = (size_t)rows * H, row_off = (size_t)r * H;
-  const int nch = (H / 4 - threadIdx.x + kThreads - 1) / kThreads;   // chunks of this thread
+  const int nch = (H / 4 - threadIdx.x + kNormThreads - 1) / kNormThreads;   // chunks of this thread
   float v[kMaxChunks][4];
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i)
-    if (i < nch) load4<Tres>(resid + row_off + (threadIdx.x + i * kThreads) * 4, v[i]);
+    if (i < nch) load4<Tres>(resid + row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
   if (splits > 0) {
 #pragma unroll
     for (int i = 0; i < kMaxChunks; ++i)
-      if (i < nch) add_splits(part, splits, slice, row_off + (threadIdx.x + i * kThreads) * 4, v[i]);
+      if (i < nch) add_splits(part, splits, slice, row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
   }
   float s1 = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i)
     if (i < nch) {
-      if (sum_out) store4<float>(sum_out + row_off + (threadIdx.x + i * kThreads) * 4, v[i]);
+      if (sum_out) store4<float>(sum_out + row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s1 += LN ? v[i][e] : v[i][e] * v[i][e];
     }
-  s1 = block_sum(s1, red);
+  s1 = block_sum<kNormThreads>(s1, red);
   float mean = 0.f, ms;
   if (LN) {
     mean = s1 / (float)H;
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void norm_rows(const Tres *resid, const f
 #pragma unroll
         for (int e = 0; e < 4; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
       }
-    ms = block_sum(q, red) / (float)H;
+    ms = block_sum<kNormThreads>(q, red) / (float)H;
   } else {
     ms = s1 / (float)H;
   }
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void norm_rows(const Tres *resid, const f
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i)
     if (i < nch) {
-      const int c = (threadIdx.x + i * kThreads) * 4;
+      const int c = (threadIdx.x + i * kNormThreads) * 4;
       float w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -172,11 +175,11 @@ hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, f
                     const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
                     float eps, hipStream_t s) {
   if (ln)
-    hipLaunchKernelGGL((norm_rows<Tres, Tout, true>), dim3(rows_alloc), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((norm_rows<Tres, Tout, true>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
                        static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
                        static_cast<Tout *>(out), H, rows, eps);
   else
-    hipLaunchKernelGGL((norm_rows<Tres, Tout, false>), dim3(rows_alloc), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((norm_rows<Tres, Tout, false>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
                        static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
                        static_cast<Tout *>(out), H, rows, eps);
   return hipGetLastError();
@@ -189,7 +192,7 @@ hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const vo
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
                             hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
-  if (splits > kMaxSplits || H > 4 * kThreads * kMaxChunks || H % 4) return hipErrorInvalidValue;
+  if (splits > kMaxSplits || H > 4 * kNormThreads * kMaxChunks || H % 4) return hipErrorInvalidValue;
   if (res_type == kF32 && out_type == kF32)
     return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, s);
   if (res_type == kBF16 && out_type == kBF16)
