@@ -288,12 +288,17 @@ hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkRef &ch, void *
 
 }  // namespace
 
+// Splits of each query block's key range: enough to reach kChunkTargetWorkgroups workgroups, but only
+// while every split keeps at least kMinSplitTiles tiles (a split costs a partial write and a merge, which
+// only pays off when a block's key range is long), never more than the first block has tiles.
 int chunk_attn_splits(int chunk_len, int chunk_offset, int nh) {
   if (chunk_len <= 0) return 1;
   const int q_blocks = (chunk_len + kBQ - 1) / kBQ;
-  const int min_tiles = (chunk_offset + min(chunk_len, kBQ) + kBKV - 1) / kBKV;   // first block's
+  const int first_tiles = (chunk_offset + min(chunk_len, kBQ) + kBKV - 1) / kBKV;
+  const int avg_tiles = (chunk_offset + (chunk_len + 1) / 2 + kBKV - 1) / kBKV;
   const int want = (kChunkTargetWorkgroups + q_blocks * nh - 1) / (q_blocks * nh);
-  return max(1, min(min(want, kMaxChunkSplits), max(min_tiles, 1)));
+  const int by_length = max(1, avg_tiles / kMinSplitTiles);
+  return max(1, min(min(want, kMaxChunkSplits), min(by_length, first_tiles)));
 }
 
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkRef &ch, void *out,

@@ -100,7 +100,8 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
 // 0..ch.off+t.  q rows are the chunk rows of q (row stride ld_q); out likewise.  With n_split > 1
 // each 64-query block's key tiles are split n_split ways and the splits write partials (stride
 // `stride` splits per row and head) for launch_attn_combine instead of out.
-constexpr int kChunkTargetWorkgroups = 160;   // split a block's keys only for very small grids
+constexpr int kChunkTargetWorkgroups = 512;   // two workgroups per compute unit
+constexpr int kMinSplitTiles = 16;            // a split keeps at least 16 key tiles
 constexpr int kMaxChunkSplits = 16;
 int chunk_attn_splits(int chunk_len, int chunk_offset, int nh);
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkRef &ch, void *out,

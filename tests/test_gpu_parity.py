@@ -175,7 +175,8 @@ def test_mid_bf16_head_dim_64():
     (0, 0, [0]),                    # a decode with an empty history attends only to itself
     (257, 0, [3, 9]),               # ragged chunk just past a tile multiple
     (3, 5, list(range(1, 141, 2))), # 70 decodes: more than one launch group of 64
-    (200, 901, [5, 700]),           # chunk keys split 16 ways, offset off the 64-key tile grid
+    (200, 901, [5, 700]),           # chunk offset off the 64-key tile grid
+    (64, 2051, [5]),                # one query block, long prefix: its keys split in two
 ])
 def test_edge_batches(C, off, lens):
     run_case(MID, C, off, lens, seed=C + len(lens))
