@@ -7,9 +7,9 @@
 // is padded only to 32 rows; rows past C+B are never stored (the tile-quantization point of the same
 // page, "Identifying the Ideal Chunk Size", Figure 7, restated for 16-row MFMA blocks).
 //
-// bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 320; larger batches
+// bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 288; larger batches
 // take a few row tiles) and a 128-column stripe of the weights, so a weight tile is read once for
-// the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 160 rows x 32 columns.  A and W
+// the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 144 rows x 32 columns.  A and W
 // k-tiles (64 deep) travel from global memory straight into LDS (global_load_lds_dwordx4: no
 // staging registers, no LDS store instructions) through a ring of up to 3 stages, so the loads of
 // tile j + 2 are in flight while tile j is multiplied.  The loads are what bounds this kernel at
@@ -36,7 +36,10 @@ constexpr int kMaxStages = 3;
 constexpr int kPlanWaveCols = 4;   // wave columns of a workgroup (8 waves: 2 rows x 4 columns)
 constexpr int kWM = 2;             // wave rows of a workgroup
 constexpr int kWaves = kWM * kPlanWaveCols;
-constexpr int kMBW = 10;           // max 16-row blocks per wave row: 320 rows per tile
+// Max 16-row blocks per wave row: 288 rows per tile.  A 320-row tile would leave room for only two
+// LDS stages, which measured as slow as two 160-row tiles (and slower than three 200-row tiles at
+// 577..640 rows), so batches past 288 rows take several row tiles.
+constexpr int kMBW = 9;
 #ifndef SARATHI_GEMM_BN
 #define SARATHI_GEMM_BN 128
 #endif
@@ -340,7 +343,6 @@ hipError_t run_bf16(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
     case 7: return run_bf16_mb<7, EPI>(g, p, s);
     case 8: return run_bf16_mb<8, EPI>(g, p, s);
     case 9: return run_bf16_mb<9, EPI>(g, p, s);
-    case 10: return run_bf16_mb<10, EPI>(g, p, s);
   }
   return hipErrorInvalidValue;
 }
