@@ -30,7 +30,8 @@ EXPORTED = [
     "sarathi_layer_create", "sarathi_layer_destroy", "sarathi_batch_check", "sarathi_workspace_size",
     "sarathi_layer_forward", "sarathi_layer_forward_debug", "sarathi_gemm", "sarathi_attention",
     "sarathi_status_str", "sarathi_last_error", "sarathi_timer_create", "sarathi_timer_destroy",
-    "sarathi_layer_forward_timed", "sarathi_timer_read",
+    "sarathi_layer_forward_timed", "sarathi_timer_read", "sarathi_stack_workspace_size",
+    "sarathi_stack_forward",
 ]
 
 STAGES = ["norm1", "qkv", "rope_append", "attn_chunk", "attn_decode", "attn_merge", "o", "norm2",
@@ -58,6 +59,12 @@ class sarathi_batch(ctypes.Structure):
                 ("n_decodes", c_int32), ("reserved", c_int32),
                 ("decode_kv", POINTER(sarathi_kv)), ("decode_len", POINTER(c_int32)),
                 ("x", c_void_p), ("y", c_void_p)]
+
+
+class sarathi_stack_batch(ctypes.Structure):
+    _fields_ = [("chunk_len", c_int32), ("chunk_offset", c_int32), ("chunk_kv", POINTER(sarathi_kv)),
+                ("n_decodes", c_int32), ("reserved", c_int32), ("decode_kv", POINTER(sarathi_kv)),
+                ("decode_len", POINTER(c_int32)), ("x", c_void_p), ("y", c_void_p)]
 
 
 class sarathi_debug_dump(ctypes.Structure):
@@ -109,6 +116,11 @@ def lib():
         L.sarathi_layer_forward_timed.restype = c_int32
         L.sarathi_timer_read.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int32)]
         L.sarathi_timer_read.restype = c_int32
+        L.sarathi_stack_workspace_size.argtypes = [POINTER(c_void_p), c_int32, POINTER(sarathi_stack_batch)]
+        L.sarathi_stack_workspace_size.restype = c_size_t
+        L.sarathi_stack_forward.argtypes = [POINTER(c_void_p), c_int32, POINTER(sarathi_stack_batch),
+                                            c_void_p, c_size_t, c_void_p]
+        L.sarathi_stack_forward.restype = c_int32
         L.sarathi_status_str.argtypes = [c_int32]
         L.sarathi_status_str.restype = c_char_p
         L.sarathi_last_error.argtypes = []
@@ -197,6 +209,44 @@ def sarathi_timer_read(timer: int):
     cnt = (c_int32 * N_STAGES)()
     _check(lib().sarathi_timer_read(timer, tot, cnt), "sarathi_timer_read")
     return {STAGES[i]: (tot[i], cnt[i]) for i in range(N_STAGES)}
+
+
+def _handles(handles):
+    arr = (c_void_p * max(len(handles), 1))(*[h or 0 for h in handles])
+    return arr, len(handles)
+
+
+def sarathi_stack_workspace_size(handles, batch: sarathi_stack_batch) -> int:
+    arr, n = _handles(handles)
+    return lib().sarathi_stack_workspace_size(ctypes.cast(arr, POINTER(c_void_p)), n, byref(batch))
+
+
+def sarathi_stack_forward(handles, batch: sarathi_stack_batch, ws: int, ws_bytes: int, stream: int) -> None:
+    arr, n = _handles(handles)
+    _check(lib().sarathi_stack_forward(ctypes.cast(arr, POINTER(c_void_p)), n, byref(batch), ws,
+                                       ws_bytes, stream), "sarathi_stack_forward")
+
+
+def make_stack_batch(chunk_len: int, chunk_offset: int, chunk_kv, decode_kv, decode_len, x: int, y: int):
+    """Build a sarathi_stack_batch.  chunk_kv: list over layers of (k_ptr, v_ptr, capacity), or None;
+    decode_kv: list over layers of lists over decodes of (k_ptr, v_ptr, capacity); decode_len: list
+    of ints.  Returns (batch, keepalive) as make_batch."""
+    B = len(decode_len)
+    n_layers = len(decode_kv) if decode_kv else (len(chunk_kv) if chunk_kv else 0)
+    ck_arr = (sarathi_kv * max(n_layers, 1))()
+    if chunk_kv:
+        for l, (k, v, cap) in enumerate(chunk_kv):
+            ck_arr[l] = sarathi_kv(k, v, int(cap), 0)
+    dk_arr = (sarathi_kv * max(n_layers * B, 1))()
+    for l in range(n_layers if B else 0):
+        for i, (k, v, cap) in enumerate(decode_kv[l]):
+            dk_arr[l * B + i] = sarathi_kv(k, v, int(cap), 0)
+    len_arr = (c_int32 * max(B, 1))(*[int(L) for L in decode_len])
+    b = sarathi_stack_batch(int(chunk_len), int(chunk_offset),
+                            ctypes.cast(ck_arr, POINTER(sarathi_kv)) if chunk_kv else None, B, 0,
+                            ctypes.cast(dk_arr, POINTER(sarathi_kv)) if B else None,
+                            ctypes.cast(len_arr, POINTER(c_int32)), x or 0, y or 0)
+    return b, (ck_arr, dk_arr, len_arr)
 
 
 def make_batch(chunk_len: int, chunk_offset: int, chunk_kv, decode_kv, decode_len, x: int, y: int):

@@ -517,6 +517,90 @@ sarathi_status sarathi_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, cons
   return SARATHI_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Stack of layers: layer l's batch is the stack batch with its own caches and with x / y chained
+// through two activation buffers placed after the (largest) per-layer workspace.
+
+namespace {
+
+sarathi_batch stack_layer_batch(const sarathi_stack_batch *b, int l, const void *x, void *y) {
+  sarathi_batch bl{};
+  bl.chunk_len = b->chunk_len;
+  bl.chunk_offset = b->chunk_offset;
+  if (b->chunk_len > 0 && b->chunk_kv) bl.chunk_kv = b->chunk_kv[l];
+  bl.n_decodes = b->n_decodes;
+  bl.reserved = b->reserved;
+  bl.decode_kv = b->n_decodes > 0 && b->decode_kv ? b->decode_kv + (size_t)l * b->n_decodes : nullptr;
+  bl.decode_len = b->decode_len;
+  bl.x = x;
+  bl.y = y;
+  return bl;
+}
+
+struct StackPlan {
+  size_t layer_ws, act_bytes, total;
+};
+
+// Validates every layer's batch (before anything is launched) and sizes the workspace.
+sarathi_status stack_plan(sarathi_layer *const *layers, int n, const sarathi_stack_batch *b,
+                          bool report, StackPlan *out) {
+  auto bad = [&](sarathi_status st, const char *msg) { return report ? fail(st, "%s", msg) : st; };
+  if (!layers || n < 1) return bad(SARATHI_ERR_INVALID, "no layers");
+  if (!b) return bad(SARATHI_ERR_INVALID, "batch is null");
+  if (b->chunk_len > 0 && !b->chunk_kv) return bad(SARATHI_ERR_INVALID, "chunk_kv is null");
+  if (b->n_decodes > 0 && !b->decode_kv) return bad(SARATHI_ERR_INVALID, "decode_kv is null");
+  for (int l = 0; l < n; ++l)
+    if (!layers[l]) return bad(SARATHI_ERR_INVALID, "a layer handle is null");
+  const sarathi_layer_desc &d0 = layers[0]->desc;
+  StackPlan p{};
+  for (int l = 0; l < n; ++l) {
+    const sarathi_layer_desc &d = layers[l]->desc;
+    if (d.hidden != d0.hidden || d.dtype != d0.dtype)
+      return report ? fail(SARATHI_ERR_INVALID, "layer %d: hidden size or storage type differs from layer 0", l)
+                    : SARATHI_ERR_INVALID;
+    const sarathi_batch bl = stack_layer_batch(b, l, b->x, b->y);
+    const sarathi_status st = check_batch(&d, &bl, report);
+    if (st != SARATHI_OK) return st;
+    p.layer_ws = std::max(p.layer_ws, make_plan(&d, &bl).total);
+  }
+  const size_t T = (size_t)b->chunk_len + b->n_decodes;
+  p.act_bytes = n > 1 ? align256(T * d0.hidden * elem_size(d0.dtype)) : 0;
+  p.total = align256(p.layer_ws) + 2 * p.act_bytes;
+  *out = p;
+  return SARATHI_OK;
+}
+
+}  // namespace
+
+size_t sarathi_stack_workspace_size(sarathi_layer *const *layers, int32_t n_layers,
+                                    const sarathi_stack_batch *batch) {
+  StackPlan p;
+  if (stack_plan(layers, n_layers, batch, false, &p) != SARATHI_OK) return 0;
+  return p.total;
+}
+
+sarathi_status sarathi_stack_forward(sarathi_layer *const *layers, int32_t n_layers,
+                                     const sarathi_stack_batch *batch, void *workspace,
+                                     size_t ws_bytes, void *stream) {
+  StackPlan p;
+  sarathi_status st = stack_plan(layers, n_layers, batch, true, &p);
+  if (st != SARATHI_OK) return st;
+  if (!workspace) return fail(SARATHI_ERR_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(SARATHI_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (ws_bytes < p.total)
+    return fail(SARATHI_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+  char *ws = static_cast<char *>(workspace);
+  void *act[2] = {ws + align256(p.layer_ws), ws + align256(p.layer_ws) + p.act_bytes};
+  for (int l = 0; l < n_layers; ++l) {
+    const void *x = l == 0 ? batch->x : act[(l - 1) & 1];
+    void *y = l == n_layers - 1 ? batch->y : act[l & 1];
+    const sarathi_batch bl = stack_layer_batch(batch, l, x, y);
+    st = forward_impl(layers[l], &bl, ws, p.layer_ws, stream, nullptr, nullptr);
+    if (st != SARATHI_OK) return st;
+  }
+  return SARATHI_OK;
+}
+
 sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_batch *batch,
                                  const void *q, void *out, void *workspace, size_t ws_bytes,
                                  void *stream) {

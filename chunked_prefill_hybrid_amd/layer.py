@@ -140,3 +140,65 @@ def attention(shape, q: torch.Tensor, out: torch.Tensor, chunk_len: int, chunk_o
     _abi.sarathi_attention(desc, b, _ptr(q, dt), _ptr(out, dt), _ptr(ws), need, _stream(stream))
     del keep
     return out
+
+
+class HybridStack:
+    """A stack of decoder layers run over one hybrid batch per call: every layer sees the same chunk
+    and decodes, with its own KV caches; layer l's output rows are layer l+1's input rows (chained in
+    the workspace, so only x and y are caller tensors).
+
+    layers: HybridLayer objects of one hidden size and storage type (the stack keeps references)."""
+
+    def __init__(self, layers: Sequence[HybridLayer]):
+        if not layers:
+            raise ValueError("a stack needs at least one layer")
+        self.layers = list(layers)
+        self.dtype = self.layers[0].dtype
+        self._ws: Optional[torch.Tensor] = None
+
+    def batch(self, x, y, chunk_len: int, chunk_offset: int, chunk_kv: Optional[Sequence[KV]],
+              decode_kv: Sequence[Sequence[KV]], decode_len: Sequence[int]):
+        """(sarathi_stack_batch, keepalive).  chunk_kv: per layer (K, V) or None; decode_kv: per
+        layer, a list over decodes of (K, V)."""
+        dt = self.dtype
+        n = len(self.layers)
+        ck = None
+        if chunk_kv is not None and chunk_len > 0:
+            if len(chunk_kv) != n:
+                raise ValueError(f"chunk_kv has {len(chunk_kv)} layers, stack has {n}")
+            ck = [(_ptr(k, dt), _ptr(v, dt), k.shape[1]) for k, v in chunk_kv]
+        B = len(decode_len)
+        dkv = []
+        if B:
+            if len(decode_kv) != n or any(len(row) != B for row in decode_kv):
+                raise ValueError("decode_kv must hold one (K, V) per decode for every layer")
+            dkv = [[(_ptr(k, dt), _ptr(v, dt), k.shape[1]) for k, v in row] for row in decode_kv]
+        return _abi.make_stack_batch(chunk_len, chunk_offset, ck, dkv if B else None, list(decode_len),
+                                     _ptr(x, dt), _ptr(y, dt))
+
+    def workspace_size(self, batch) -> int:
+        return _abi.sarathi_stack_workspace_size([l.handle for l in self.layers], batch)
+
+    def forward(self, x, y, chunk_len, chunk_offset, chunk_kv, decode_kv, decode_len,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+        """Enqueue all layers over one hybrid batch; y and every layer's caches are written in place.
+        Without `workspace` the stack keeps one that grows to the largest batch seen."""
+        b, keep = self.batch(x, y, chunk_len, chunk_offset, chunk_kv, decode_kv, decode_len)
+        handles = [l.handle for l in self.layers]
+        need = _abi.sarathi_stack_workspace_size(handles, b)
+        if need == 0:
+            # Re-run with reporting so the error names the offending layer and field.
+            _abi.sarathi_stack_forward(handles, b, 0, 0, _stream(stream))
+            raise RuntimeError("stack batch rejected")
+        if workspace is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = self._ws
+        _abi.sarathi_stack_forward(handles, b, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream))
+        del keep
+        return y
+
+    def close(self) -> None:
+        for l in self.layers:
+            l.close()

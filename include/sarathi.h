@@ -168,6 +168,40 @@ sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_b
                                  const void *q, void *out, void *workspace, size_t ws_bytes,
                                  void *stream);
 
+/* ---- A stack of layers ------------------------------------------------------------------------
+ * One hybrid batch through n_layers layers in sequence: layer l's output rows are layer l+1's input
+ * rows, and every layer keeps its own KV caches.  This is how a prompt is prefilled chunk by chunk
+ * with decodes riding along: each chunk passes through all layers, appending its K/V to each layer's
+ * cache, before the next chunk (SARATHI: Efficient LLM Inference by Piggybacking Decodes with Chunked
+ * Prefills, section 3, "Chunked-Prefills" and "Decode-Maximal Batching").  Layers must share hidden
+ * size and storage type. */
+typedef struct {
+    int32_t chunk_len;          /* C >= 0 */
+    int32_t chunk_offset;       /* entries already in the chunk request's caches (same in every layer) */
+    const sarathi_kv *chunk_kv; /* HOST array [n_layers]: the chunk request's cache in layer l;
+                                   may be NULL when chunk_len == 0 */
+    int32_t n_decodes;          /* B >= 0 */
+    int32_t reserved;           /* must be 0 */
+    const sarathi_kv *decode_kv;  /* HOST array [n_layers * n_decodes], layer-major: decode i's
+                                     cache in layer l is decode_kv[l * n_decodes + i] */
+    const int32_t *decode_len;    /* HOST array [n_decodes], the same in every layer */
+    const void *x;              /* device [C+B, H] input of layer 0, chunk rows first */
+    void *y;                    /* device [C+B, H] output of the last layer; must not overlap x */
+} sarathi_stack_batch;
+
+/* Bytes of device workspace sarathi_stack_forward needs: the largest per-layer workspace plus two
+ * [C+B, H] activation buffers for the hand-off between layers.  Returns 0 if any layer's batch fails
+ * sarathi_batch_check or the layers do not share hidden size and storage type. */
+size_t sarathi_stack_workspace_size(sarathi_layer *const *layers, int32_t n_layers,
+                                    const sarathi_stack_batch *batch);
+
+/* Enqueues all layers on `stream`.  Every layer's batch is validated before the first launch: on an
+ * error nothing is written.  workspace as for sarathi_layer_forward, sized by
+ * sarathi_stack_workspace_size.  Errors: INVALID, CAPACITY, UNSUPPORTED, WORKSPACE, HIP. */
+sarathi_status sarathi_stack_forward(sarathi_layer *const *layers, int32_t n_layers,
+                                     const sarathi_stack_batch *batch, void *workspace,
+                                     size_t ws_bytes, void *stream);
+
 /* ---- Per-stage timing (measurement only) ------------------------------------------------------
  * The layer's forward runs as the stages below, in this order (per-operation profile of a hybrid
  * iteration: preproj, attention, postproj, FFN; SARATHI: Efficient LLM Inference by Piggybacking

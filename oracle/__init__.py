@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's cpu_bas
 or call this package.  The product path (the HIP library and its Python binding) never does, and this
 package imports nothing from it.
 """
-from .layer import (apply_new_rows, attend_rows, chunk_mask, gelu, layer_forward, layer_norm,
-                    positions, rms_norm, rope_inv_freq, rope_rotate, silu)
+from .layer import (apply_new_rows, apply_stack_rows, attend_rows, chunk_mask, gelu, layer_forward,
+                    layer_norm, positions, rms_norm, rope_inv_freq, rope_rotate, silu, stack_forward)
 
-__all__ = ["apply_new_rows", "attend_rows", "chunk_mask", "gelu", "layer_forward", "layer_norm",
-           "positions", "rms_norm", "rope_inv_freq", "rope_rotate", "silu"]
+__all__ = ["apply_new_rows", "apply_stack_rows", "attend_rows", "chunk_mask", "gelu", "layer_forward",
+           "layer_norm", "positions", "rms_norm", "rope_inv_freq", "rope_rotate", "silu", "stack_forward"]

@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "rms_norm", "layer_norm", "rope_inv_freq", "rope_rotate", "chunk_mask", "attend_rows",
-    "silu", "gelu", "layer_forward", "positions",
+    "silu", "gelu", "layer_forward", "positions", "apply_new_rows", "stack_forward", "apply_stack_rows",
 ]
 
 
@@ -192,3 +192,37 @@ def apply_new_rows(batch: Dict, out: Dict) -> None:
     for i, L in enumerate(batch["decode_len"]):
         batch["decode_k"][i][:, L, :] = out["new_k"][C + i]
         batch["decode_v"][i][:, L, :] = out["new_v"][C + i]
+
+
+def stack_forward(shape, layer_weights: Sequence[Dict[str, Optional[np.ndarray]]], batch: Dict,
+                  dtype=np.float64) -> Dict:
+    """A stack of layers over one hybrid batch: layer l's input rows are layer l-1's output rows, and
+    every layer attends over its own caches (SARATHI page, section 3: each chunk of a prompt passes
+    through all layers, appending to each layer's KV cache).
+
+    batch: x [C+B,H], chunk_len, chunk_offset, decode_len [B], and per layer l: chunk_k[l] /
+    chunk_v[l] [nh,cap,d], decode_k[l] / decode_v[l] lists of [nh,cap_i,d].  Nothing is modified.
+    Returns y (the last layer's output) and `layers`, each layer's layer_forward result."""
+    x = batch["x"]
+    outs = []
+    for l, w in enumerate(layer_weights):
+        bl = {"x": x, "chunk_len": batch["chunk_len"], "chunk_offset": batch["chunk_offset"],
+              "decode_len": batch["decode_len"],
+              "chunk_k": batch["chunk_k"][l] if batch["chunk_len"] else None,
+              "chunk_v": batch["chunk_v"][l] if batch["chunk_len"] else None,
+              "decode_k": batch["decode_k"][l], "decode_v": batch["decode_v"][l]}
+        out = layer_forward(shape, w, bl, dtype)
+        outs.append(out)
+        x = out["y"]
+    return {"y": x, "layers": outs}
+
+
+def apply_stack_rows(batch: Dict, res: Dict) -> None:
+    """apply_new_rows for every layer of a stack step (caches of layer l get layer l's new rows)."""
+    for l, out in enumerate(res["layers"]):
+        bl = {"chunk_len": batch["chunk_len"], "chunk_offset": batch["chunk_offset"],
+              "decode_len": batch["decode_len"],
+              "chunk_k": batch["chunk_k"][l] if batch["chunk_len"] else None,
+              "chunk_v": batch["chunk_v"][l] if batch["chunk_len"] else None,
+              "decode_k": batch["decode_k"][l], "decode_v": batch["decode_v"][l]}
+        apply_new_rows(bl, out)

@@ -42,6 +42,8 @@ def test_struct_layouts_match_header():
     assert _abi.sarathi_batch.x.offset == 56 and _abi.sarathi_batch.decode_kv.offset == 40
     assert ctypes.sizeof(_abi.sarathi_weights) == 72
     assert ctypes.sizeof(_abi.sarathi_debug_dump) == 56
+    assert ctypes.sizeof(_abi.sarathi_stack_batch) == 56
+    assert _abi.sarathi_stack_batch.decode_kv.offset == 24 and _abi.sarathi_stack_batch.x.offset == 40
 
 
 def desc(**kw):
@@ -123,3 +125,12 @@ def test_create_rejects_bad_description_before_any_hip_call(lib):
     with pytest.raises(_abi.SarathiError) as e:
         _abi.sarathi_layer_create(desc(head_dim=96), w)
     assert e.value.status == _abi.SARATHI_ERR_UNSUPPORTED
+
+
+def test_stack_rejects_empty_or_null_before_any_hip_call(lib):
+    b, keep = _abi.make_stack_batch(4, 0, [(addr(2), addr(3), 64)], [[]], [], addr(0), addr(1))
+    assert _abi.sarathi_stack_workspace_size([], b) == 0
+    assert _abi.sarathi_stack_workspace_size([None], b) == 0
+    with pytest.raises(_abi.SarathiError) as e:
+        _abi.sarathi_stack_forward([], b, addr(5), 1 << 20, 0)
+    assert e.value.status == _abi.SARATHI_ERR_INVALID
