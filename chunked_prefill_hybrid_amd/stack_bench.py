@@ -16,7 +16,8 @@ Piggybacking Decodes with Chunked Prefills):
   is the difference of the two passes divided by the decode tokens produced (chunks x (B - 1)); the
   baseline is a decode-only batch of B decodes at length L (time / B).  Speedup = baseline /
   marginal.  B is capped where the decodes' caches would exceed --kv-gib, as the page's batch size
-  is capped by memory.
+  is capped by memory.  Two more passes per point run the prompt with chunk sizes that make chunk
+  plus decodes a multiple of the GEMMs' 32-row time step (section 4.4's tile rule for these kernels).
 
 Weights and caches are drawn on the GPU from a seeded generator (values do not change timing: every
 kernel's work is fixed by the shapes).  Every time is a median over --reps repetitions of the whole
@@ -183,18 +184,34 @@ def table2(model, reps: int):
     return rows
 
 
+ROW_STEP = 32      # the layer GEMMs' time rises every 32 batch rows (measured by tile_sweep)
+ROW_TILE = 288     # ... and steps up further past a 288-row tile
+
+
+def aligned_chunks(chunk: int, nd: int):
+    """Chunk sizes that make chunk + nd decodes fill whole 32-row steps: `down` trims the chunk to the
+    step below (the page's rule: C + B a multiple of the tile), `up` gives the chunk the rows the last
+    step pads anyway (kept within one row tile when chunk + nd fits in one)."""
+    rows = chunk + nd
+    down = (rows // ROW_STEP) * ROW_STEP - nd
+    up_rows = -(-rows // ROW_STEP) * ROW_STEP
+    if rows <= ROW_TILE:
+        up_rows = min(up_rows, ROW_TILE)
+    return max(1, down), up_rows - nd
+
+
 def fig8(model, Ls, Bs, chunk: int, kv_gib: float, reps: int):
     """Decode speedup vs batch size for each length (page's Figure 8 setup), plus the same prompt run
-    with the tile-aligned chunk size chunk - (B - 1) (page's section 4.4 rule that chunk plus decodes
-    should fill whole tiles)."""
+    with chunk sizes that make chunk + decodes fill whole 32-row GEMM steps (page's section 4.4 rule
+    restated for these kernels)."""
     sh = model.shape
     el = 2 if sh.dtype == "bf16" else 4
     out = []
     for L in Ls:
         n_chunks = (L + chunk - 1) // chunk
         b_all = [B for B in Bs if B - 1 < chunk]
-        max_steps = max((L + chunk - (B - 1) - 1) // (chunk - (B - 1)) for B in b_all)
-        cap = L + max_steps + 1
+        max_steps = max((L + c - 1) // c for B in b_all for c in aligned_chunks(chunk, B - 1))
+        cap = L + max(max_steps, n_chunks) + 1
         per_req = model.n_layers * 2 * sh.n_heads * cap * sh.head_dim * el
         b_fit = [B for B in b_all if B * per_req <= kv_gib * 2**30]
         if not b_fit:
@@ -224,23 +241,31 @@ def fig8(model, Ls, Bs, chunk: int, kv_gib: float, reps: int):
             base = t_dec / B
             rec = {"L": L, "B": B, "decode_only_ms": t_dec, "baseline_ms_per_token": base,
                    "prompt_alone_ms": t_alone, "prompt_with_decodes_ms": None, "marginal_ms_per_token": None,
-                   "speedup": None, "aligned_chunk": None, "aligned_ms": None,
-                   "aligned_marginal_ms_per_token": None, "aligned_speedup": None}
+                   "speedup": None}
             if nd:
                 t_hyb = timed(model, prompt_pass(nd, chunk)[0], reps)
                 marg = (t_hyb - t_alone) / (n_chunks * nd)
-                run_a, n_a = prompt_pass(nd, chunk - nd)
-                t_al = timed(model, run_a, reps)
-                marg_a = (t_al - t_alone) / (n_a * nd)
                 rec.update(prompt_with_decodes_ms=t_hyb, marginal_ms_per_token=marg,
-                           speedup=base / marg if marg > 0 else None, aligned_chunk=chunk - nd,
-                           aligned_ms=t_al, aligned_marginal_ms_per_token=marg_a,
-                           aligned_speedup=base / marg_a if marg_a > 0 else None)
+                           speedup=base / marg if marg > 0 else None)
+                for tag, c_a in zip(("down", "up"), aligned_chunks(chunk, nd)):
+                    run_a, n_a = prompt_pass(nd, c_a)
+                    t_a = timed(model, run_a, reps)
+                    t_a0 = timed(model, prompt_pass(0, c_a)[0], reps)
+                    m_a = (t_a - t_a0) / (n_a * nd)
+                    rec[f"{tag}_chunk"] = c_a
+                    rec[f"{tag}_alone_ms"] = t_a0
+                    rec[f"{tag}_ms"] = t_a
+                    rec[f"{tag}_marginal_ms_per_token"] = m_a
+                    rec[f"{tag}_speedup"] = base / m_a if m_a > 0 else None
             out.append(rec)
-            say(f"    B={B:3d}: decode-only {base * 1e3:8.2f} us/token, piggybacked "
-                f"{(rec['marginal_ms_per_token'] or 0) * 1e3:8.2f} us/token (x{rec['speedup'] or 0:.2f}), "
-                f"aligned chunk {rec['aligned_chunk']}: {(rec['aligned_marginal_ms_per_token'] or 0) * 1e3:8.2f} "
-                f"us/token (x{rec['aligned_speedup'] or 0:.2f})")
+            msg = (f"    B={B:3d}: decode-only {base * 1e3:8.2f} us/token, piggybacked "
+                   f"{(rec['marginal_ms_per_token'] or 0) * 1e3:8.2f} us/token (x{rec['speedup'] or 0:.2f})")
+            for tag in ("down", "up"):
+                if f"{tag}_chunk" in rec:
+                    msg += (f", {tag} C={rec[tag + '_chunk']}: {rec[tag + '_marginal_ms_per_token'] * 1e3:8.2f}"
+                            f" us/token (x{rec[tag + '_speedup'] or 0:.2f}; prompt alone "
+                            f"{rec[tag + '_alone_ms']:.2f} ms)")
+            say(msg)
         del pf_cache, dec_cache, chunk_kv
         torch.cuda.empty_cache()
     return out
@@ -265,16 +290,26 @@ def markdown(res, command: str) -> str:
             f"(decode-only: {t2['decode_only']['ms_per_token']:.4f} ms/token; "
             f"{'n/a' if sp is None else f'{sp:.1f}x'}).", "",
             f"## Decode speedup vs batch size (chunk {res['chunk']})", "",
-            "B = 1 prompt + (B - 1) decodes; baseline = B decodes alone.  `aligned` runs the prompt in "
-            "chunks of C - (B - 1) so that chunk plus decodes fill the same rows as the chunk alone.", "",
-            "| L | B | decode-only ms/token | piggybacked ms/token | speedup | aligned ms/token | aligned speedup |",
-            "|---|---|---|---|---|---|---|"]
+            "B = 1 prompt + (B - 1) decodes; baseline = B decodes alone.  The marginal time is the "
+            "extra time of the whole prompt pass with the decodes riding along over the prompt pass "
+            f"alone in chunks of {res['chunk']}, per decode token.  `down` / `up` run the prompt in "
+            "chunks that make chunk + decodes a multiple of 32 rows (the layer GEMMs' time step): "
+            "`down` trims the chunk, `up` gives it the rows the last step pads anyway.  Their marginal "
+            "time is taken against the prompt alone in chunks of the same size, whose time is listed "
+            "(the prompt's own cost of the chunk choice).", "",
+            "| L | B | decode-only ms/token | piggybacked ms/token | speedup | down C | prompt alone ms | "
+            "down ms/token | down speedup | up C | prompt alone ms | up ms/token | up speedup |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+
     def f(v, spec):
         return "-" if v is None else format(v, spec)
     for r in f8:
         out.append(f"| {r['L']} | {r['B']} | {f(r['baseline_ms_per_token'], '.4f')} | "
                    f"{f(r['marginal_ms_per_token'], '.4f')} | {f(r['speedup'], '.2f')} | "
-                   f"{f(r.get('aligned_marginal_ms_per_token'), '.4f')} | {f(r.get('aligned_speedup'), '.2f')} |")
+                   f"{f(r.get('down_chunk'), 'd')} | {f(r.get('down_alone_ms'), '.2f')} | "
+                   f"{f(r.get('down_marginal_ms_per_token'), '.4f')} | "
+                   f"{f(r.get('down_speedup'), '.2f')} | {f(r.get('up_chunk'), 'd')} | {f(r.get('up_alone_ms'), '.2f')} | "
+                   f"{f(r.get('up_marginal_ms_per_token'), '.4f')} | {f(r.get('up_speedup'), '.2f')} |")
     return "\n".join(out) + "\n"
 
 
