@@ -31,8 +31,11 @@ EXPORTED = [
     "sarathi_layer_forward", "sarathi_layer_forward_debug", "sarathi_gemm", "sarathi_attention",
     "sarathi_status_str", "sarathi_last_error", "sarathi_timer_create", "sarathi_timer_destroy",
     "sarathi_layer_forward_timed", "sarathi_timer_read", "sarathi_stack_workspace_size",
-    "sarathi_stack_forward",
+    "sarathi_stack_forward", "sarathi_multi_batch_check", "sarathi_multi_workspace_size",
+    "sarathi_multi_forward", "sarathi_multi_forward_debug", "sarathi_multi_forward_timed",
 ]
+
+SARATHI_MAX_CHUNKS = 16
 
 STAGES = ["norm1", "qkv", "rope_append", "attn_chunk", "attn_decode", "attn_merge", "o", "norm2",
           "ffn_up", "ffn_down"]
@@ -64,6 +67,16 @@ class sarathi_batch(ctypes.Structure):
 class sarathi_stack_batch(ctypes.Structure):
     _fields_ = [("chunk_len", c_int32), ("chunk_offset", c_int32), ("chunk_kv", POINTER(sarathi_kv)),
                 ("n_decodes", c_int32), ("reserved", c_int32), ("decode_kv", POINTER(sarathi_kv)),
+                ("decode_len", POINTER(c_int32)), ("x", c_void_p), ("y", c_void_p)]
+
+
+class sarathi_chunk(ctypes.Structure):
+    _fields_ = [("len", c_int32), ("offset", c_int32), ("kv", sarathi_kv)]
+
+
+class sarathi_multi_batch(ctypes.Structure):
+    _fields_ = [("n_chunks", c_int32), ("reserved", c_int32), ("chunks", POINTER(sarathi_chunk)),
+                ("n_decodes", c_int32), ("reserved2", c_int32), ("decode_kv", POINTER(sarathi_kv)),
                 ("decode_len", POINTER(c_int32)), ("x", c_void_p), ("y", c_void_p)]
 
 
@@ -121,6 +134,18 @@ def lib():
         L.sarathi_stack_forward.argtypes = [POINTER(c_void_p), c_int32, POINTER(sarathi_stack_batch),
                                             c_void_p, c_size_t, c_void_p]
         L.sarathi_stack_forward.restype = c_int32
+        MB = POINTER(sarathi_multi_batch)
+        L.sarathi_multi_batch_check.argtypes = [POINTER(sarathi_layer_desc), MB]
+        L.sarathi_multi_batch_check.restype = c_int32
+        L.sarathi_multi_workspace_size.argtypes = [POINTER(sarathi_layer_desc), MB]
+        L.sarathi_multi_workspace_size.restype = c_size_t
+        L.sarathi_multi_forward.argtypes = [c_void_p, MB, c_void_p, c_size_t, c_void_p]
+        L.sarathi_multi_forward.restype = c_int32
+        L.sarathi_multi_forward_debug.argtypes = [c_void_p, MB, c_void_p, c_size_t, c_void_p,
+                                                  POINTER(sarathi_debug_dump)]
+        L.sarathi_multi_forward_debug.restype = c_int32
+        L.sarathi_multi_forward_timed.argtypes = [c_void_p, MB, c_void_p, c_size_t, c_void_p, c_void_p]
+        L.sarathi_multi_forward_timed.restype = c_int32
         L.sarathi_status_str.argtypes = [c_int32]
         L.sarathi_status_str.restype = c_char_p
         L.sarathi_last_error.argtypes = []
@@ -264,3 +289,47 @@ def make_batch(chunk_len: int, chunk_offset: int, chunk_kv, decode_kv, decode_le
                       ctypes.cast(kv_arr, POINTER(sarathi_kv)), ctypes.cast(len_arr, POINTER(c_int32)),
                       x or 0, y or 0)
     return b, (kv_arr, len_arr)
+
+
+def sarathi_multi_batch_check(desc: sarathi_layer_desc, batch: sarathi_multi_batch) -> int:
+    return lib().sarathi_multi_batch_check(byref(desc), byref(batch))
+
+
+def sarathi_multi_workspace_size(desc: sarathi_layer_desc, batch: sarathi_multi_batch) -> int:
+    return lib().sarathi_multi_workspace_size(byref(desc), byref(batch))
+
+
+def sarathi_multi_forward(handle: int, batch: sarathi_multi_batch, ws: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().sarathi_multi_forward(handle, byref(batch), ws, ws_bytes, stream), "sarathi_multi_forward")
+
+
+def sarathi_multi_forward_debug(handle: int, batch: sarathi_multi_batch, ws: int, ws_bytes: int, stream: int,
+                                dump: sarathi_debug_dump) -> None:
+    _check(lib().sarathi_multi_forward_debug(handle, byref(batch), ws, ws_bytes, stream, byref(dump)),
+           "sarathi_multi_forward_debug")
+
+
+def sarathi_multi_forward_timed(handle: int, batch: sarathi_multi_batch, ws: int, ws_bytes: int, stream: int,
+                                timer: int) -> None:
+    _check(lib().sarathi_multi_forward_timed(handle, byref(batch), ws, ws_bytes, stream, timer),
+           "sarathi_multi_forward_timed")
+
+
+def make_multi_batch(chunks, decode_kv, decode_len, x: int, y: int):
+    """Build a sarathi_multi_batch.  chunks: list of (len, offset, k_ptr, v_ptr, capacity);
+    decode_kv: list of (k_ptr, v_ptr, capacity); decode_len: list of ints.  Returns (batch, keepalive)
+    as make_batch."""
+    n = len(chunks)
+    ch_arr = (sarathi_chunk * max(n, 1))()
+    for j, (ln, off, k, v, cap) in enumerate(chunks):
+        ch_arr[j] = sarathi_chunk(int(ln), int(off), sarathi_kv(k, v, int(cap), 0))
+    B = len(decode_len)
+    kv_arr = (sarathi_kv * max(B, 1))()
+    len_arr = (c_int32 * max(B, 1))()
+    for i, ((k, v, cap), L) in enumerate(zip(decode_kv, decode_len)):
+        kv_arr[i] = sarathi_kv(k, v, int(cap), 0)
+        len_arr[i] = int(L)
+    b = sarathi_multi_batch(n, 0, ctypes.cast(ch_arr, POINTER(sarathi_chunk)) if n else None, B, 0,
+                            ctypes.cast(kv_arr, POINTER(sarathi_kv)) if B else None,
+                            ctypes.cast(len_arr, POINTER(c_int32)), x or 0, y or 0)
+    return b, (ch_arr, kv_arr, len_arr)

@@ -25,6 +25,11 @@
 //
 // The key range of each 64-query block can be split over several workgroups so that short chunks
 // still fill the GPU; a split writes (m, l, unnormalised O) partials for attn_combine.
+//
+// One launch serves every prefill chunk of the batch.  A batch may carry several partial prefills of
+// different requests next to its decodes, as in token-budget ("stall-free") batching (junupark.xyz
+// notes on Sarathi-Serve, "Stall Free Batching"); each chunk attends only to its own request's cache,
+// so a work item names its chunk, and the items of all chunks share one grid.
 #include <math.h>
 
 #include "kernels.h"
@@ -67,7 +72,7 @@ template <int D> __device__ __forceinline__ int v_slot(int r, int c) {
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q, int nh,
-                                                       ChunkRef ch, bf16_t *out, int ld_out,
+                                                       ChunkSet cs, bf16_t *out, int ld_out,
                                                        float qscale_log2, int n_split, int stride,
                                                        float *part_o, float *part_ml, int per_xcd) {
   using G = TileGeom<D>;
@@ -80,32 +85,40 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
   auto kst = [&](int u) -> bf16_t * { return u == 0 ? k0s : u == 1 ? k1s : k2s; };
   auto vst = [&](int u) -> bf16_t * { return u == 0 ? v0s : u == 1 ? v1s : v2s; };
 
-  // Work item (head, split, query block), XCD-aware: workgroup b runs on XCD b % 8 and the items of
-  // XCD x are the consecutive range [x per_xcd, (x + 1) per_xcd), so the query blocks and splits of a
-  // head share one XCD's L2 and its K/V crosses HBM about once.
-  const int q_blocks = (ch.len + kBQ - 1) / kBQ;
+  // Work item (chunk, head, split, query block), XCD-aware: workgroup b runs on XCD b % 8 and the
+  // items of XCD x are the consecutive range [x per_xcd, (x + 1) per_xcd), so the query blocks and
+  // splits of a head share one XCD's L2 and its K/V crosses HBM about once.  Items are numbered
+  // chunk by chunk; the scan over the chunks is uniform across the workgroup.
   const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (item >= q_blocks * n_split * nh) return;
-  const int qb = item % q_blocks, split = (item / q_blocks) % n_split, h = item / (q_blocks * n_split);
+  int cj = 0, first_item = 0;
+  for (; cj < cs.n; ++cj) {
+    const int n_items = (cs.len[cj] + kBQ - 1) / kBQ * n_split * nh;
+    if (item < first_item + n_items) break;
+    first_item += n_items;
+  }
+  if (cj >= cs.n) return;
+  const int C = cs.len[cj], off = cs.off[cj], row0 = cs.row0[cj], cap = cs.cap[cj];
+  const int q_blocks = (C + kBQ - 1) / kBQ;
+  const int local = item - first_item;
+  const int qb = local % q_blocks, split = (local / q_blocks) % n_split, h = local / (q_blocks * n_split);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  const int C = ch.len, off = ch.off;
   const int q_first = qb * kBQ;
   const int q_last = min(C, q_first + kBQ) - 1;          // last query of the workgroup
   const int n_keys = off + q_last + 1;                    // keys any of its queries sees
   const int nt = (n_keys + kBKV - 1) / kBKV;
   const int t_begin = (int)((long long)split * nt / n_split);
   const int t_end = (int)((long long)(split + 1) * nt / n_split);
-  const bf16_t *Kh = reinterpret_cast<const bf16_t *>(ch.k) + (size_t)h * ch.cap * D;
-  const bf16_t *Vh = reinterpret_cast<const bf16_t *>(ch.v) + (size_t)h * ch.cap * D;
+  const bf16_t *Kh = reinterpret_cast<const bf16_t *>(cs.k[cj]) + (size_t)h * cap * D;
+  const bf16_t *Vh = reinterpret_cast<const bf16_t *>(cs.v[cj]) + (size_t)h * cap * D;
 
   // This lane's query (row of the wave's 16) and its fragments of q (B operand of S^T = K Q^T).
   const int my_q = q_first + wave * 16 + c16;
   const int my_pos = off + min(my_q, C - 1);
   bf16x8_t qf[KS];
   {
-    const bf16_t *qr = q + (size_t)min(my_q, C - 1) * ld_q + h * D;
+    const bf16_t *qr = q + (size_t)(row0 + min(my_q, C - 1)) * ld_q + h * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8_t *>(qr + ks * 32 + g * 8);
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
   l_run += __shfl_xor(l_run, 32, kWave);
   if (n_split > 1) {
     if (my_q < C) {
-      const size_t pidx = ((size_t)my_q * nh + h) * stride + split;
+      const size_t pidx = ((size_t)(row0 + my_q) * nh + h) * stride + split;
       if (g == 0) {
         part_ml[2 * pidx] = m_run;
         part_ml[2 * pidx + 1] = l_run;
@@ -263,7 +276,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
     }
   } else if (my_q < C) {
     const float inv = 1.0f / l_run;
-    bf16_t *orow = out + (size_t)my_q * ld_out + h * D;
+    bf16_t *orow = out + (size_t)(row0 + my_q) * ld_out + h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       uint2 u;
@@ -275,40 +288,47 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
 }
 
 template <int D>
-hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkRef &ch, void *out, int ld_out,
+hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkSet &cs, void *out, int ld_out,
                      int n_split, int stride, float *part_o, float *part_ml, hipStream_t s) {
-  const int items = (ch.len + kBQ - 1) / kBQ * n_split * nh;
+  int items = 0;
+  for (int j = 0; j < cs.n; ++j) items += (cs.len[j] + kBQ - 1) / kBQ * n_split * nh;
   const int per_xcd = (items + 7) / 8;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL(attn_chunk_mfma<D>, dim3(8 * per_xcd), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(q), ld_q, nh, ch, static_cast<bf16_t *>(out), ld_out,
+                     static_cast<const bf16_t *>(q), ld_q, nh, cs, static_cast<bf16_t *>(out), ld_out,
                      qscale, n_split, stride, part_o, part_ml, per_xcd);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Splits of each query block's key range: enough to reach kChunkTargetWorkgroups workgroups, but only
-// while every split keeps at least kMinSplitTiles tiles (a split costs a partial write and a merge, which
-// only pays off when a block's key range is long), never more than the first block has tiles.
-int chunk_attn_splits(int chunk_len, int chunk_offset, int nh) {
-  if (chunk_len <= 0) return 1;
-  const int q_blocks = (chunk_len + kBQ - 1) / kBQ;
-  const int first_tiles = (chunk_offset + min(chunk_len, kBQ) + kBKV - 1) / kBKV;
-  const int avg_tiles = (chunk_offset + (chunk_len + 1) / 2 + kBKV - 1) / kBKV;
+// Splits of each query block's key range, one count for every chunk of the set: enough to reach
+// kChunkTargetWorkgroups workgroups, but only while every split keeps at least kMinSplitTiles tiles (a
+// split costs a partial write and a merge, which only pays off when the key ranges are long), and never
+// more than any chunk's first block has tiles (so no split is empty).
+int chunk_attn_splits(const ChunkSet &cs, int nh) {
+  if (cs.n <= 0) return 1;
+  int q_blocks = 0, first_tiles = 1 << 30, by_length = 1 << 30;
+  for (int j = 0; j < cs.n; ++j) {
+    const int C = cs.len[j], off = cs.off[j];
+    q_blocks += (C + kBQ - 1) / kBQ;
+    first_tiles = min(first_tiles, (off + min(C, kBQ) + kBKV - 1) / kBKV);
+    const int avg_tiles = (off + (C + 1) / 2 + kBKV - 1) / kBKV;
+    by_length = min(by_length, max(1, avg_tiles / kMinSplitTiles));
+  }
   const int want = (kChunkTargetWorkgroups + q_blocks * nh - 1) / (q_blocks * nh);
-  const int by_length = max(1, avg_tiles / kMinSplitTiles);
   return max(1, min(min(want, kMaxChunkSplits), min(by_length, first_tiles)));
 }
 
-hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkRef &ch, void *out,
+hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs, void *out,
                              int ld_out, int n_split, int stride, float *part_o, float *part_ml,
                              hipStream_t s) {
-  if (ch.len <= 0) return hipSuccess;
+  if (cs.n <= 0 || cs.rows <= 0) return hipSuccess;
+  if (cs.n > kMaxChunks) return hipErrorInvalidValue;
   if (n_split < 1 || n_split > stride || (n_split > 1 && (!part_o || !part_ml)))
     return hipErrorInvalidValue;
-  if (d == 128) return run_chunk<128>(q, ld_q, nh, ch, out, ld_out, n_split, stride, part_o, part_ml, s);
-  if (d == 64) return run_chunk<64>(q, ld_q, nh, ch, out, ld_out, n_split, stride, part_o, part_ml, s);
+  if (d == 128) return run_chunk<128>(q, ld_q, nh, cs, out, ld_out, n_split, stride, part_o, part_ml, s);
+  if (d == 64) return run_chunk<64>(q, ld_q, nh, cs, out, ld_out, n_split, stride, part_o, part_ml, s);
   return hipErrorInvalidValue;
 }
 

@@ -24,7 +24,7 @@ constexpr int kUnroll = 8;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int nh, int row0,
-                                                       ChunkRef ch, DecodeGroup dg, int max_splits,
+                                                       ChunkSet cs, DecodeGroup dg, int max_splits,
                                                        float *part_o, float *part_ml, float qscale) {
   constexpr int E = Packet<T>::E;      // elements per 16-byte packet
   constexpr int LPK = D / E;           // lanes per key row
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
   constexpr int NIT = KPW / KPI;
   static_assert(NIT % kUnroll == 0, "whole unrolled steps");
   const int r = row0 + blockIdx.x, s = blockIdx.y, h = blockIdx.z;
-  const RowRef rr = row_ref(r, ch, dg);
+  const RowRef rr = row_ref(r, cs, dg);
   const int n_keys = rr.pos + 1;
   const int nsp = attn_splits(n_keys);
   const size_t pidx = ((size_t)r * nh + h) * max_splits + s;
@@ -204,10 +204,14 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
 #pragma unroll
       for (int i = 0; i < PER; ++i) v[u][i] = part_o[(base + sp) * D + lane + i * kWave];
     }
+    // A split with weight 0 (no keys, or a padding slot of the group) adds nothing; its o slot may
+    // never have been written, so it is skipped rather than multiplied by 0.
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
+      if (ws[u] != 0.f) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += ws[u] * v[u][i];
+        for (int i = 0; i < PER; ++i) acc[i] += ws[u] * v[u][i];
+      }
   }
   const float inv = 1.0f / L;
 #pragma unroll
@@ -216,11 +220,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
 }
 
 template <typename T, int D>
-hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, const ChunkRef &ch,
+hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, const ChunkSet &cs,
                      const DecodeGroup &dg, int max_splits, float *po, float *pml, hipStream_t s) {
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((attn_rows_split<T, D>), dim3(n_rows, max_splits, nh), dim3(256), 0, s,
-                     static_cast<const T *>(q), ld_q, nh, row0, ch, dg, max_splits, po, pml, qscale);
+                     static_cast<const T *>(q), ld_q, nh, row0, cs, dg, max_splits, po, pml, qscale);
   return hipGetLastError();
 }
 
@@ -237,13 +241,13 @@ hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, int chunk_r
 }  // namespace
 
 hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
-                            const ChunkRef &ch, const DecodeGroup &dg, int max_splits,
+                            const ChunkSet &cs, const DecodeGroup &dg, int max_splits,
                             float *part_o, float *part_ml, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (type == kF32 && d == 64) return run_split<float, 64>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
-  if (type == kF32 && d == 128) return run_split<float, 128>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
-  if (type == kBF16 && d == 64) return run_split<bf16_t, 64>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
-  if (type == kBF16 && d == 128) return run_split<bf16_t, 128>(q, ld_q, nh, row0, n_rows, ch, dg, max_splits, part_o, part_ml, s);
+  if (type == kF32 && d == 64) return run_split<float, 64>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
+  if (type == kF32 && d == 128) return run_split<float, 128>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
+  if (type == kBF16 && d == 64) return run_split<bf16_t, 64>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
+  if (type == kBF16 && d == 128) return run_split<bf16_t, 128>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
   return hipErrorInvalidValue;
 }
 

@@ -113,14 +113,20 @@ __device__ __forceinline__ float wave_max(float v, int from = 1) {
 }
 
 // Request descriptors, passed by value as kernel arguments.  A launch covers rows
-// [row0, row0 + n_rows) of the batch: rows below chunk.len are the chunk; row chunk.len + i is
-// decode i, which must lie in [dec.base, dec.base + dec.n).
+// [row0, row0 + n_rows) of the batch.  The batch's prefill chunks come first, in chunk order: chunk j
+// owns rows [row0[j], row0[j] + len[j]) at positions off[j] .. off[j] + len[j] - 1 of its request;
+// `rows` is the number of chunk rows.  Batch row rows + i is decode i, which must lie in
+// [dec.base, dec.base + dec.n).
 constexpr int kMaxDecodesPerLaunch = 64;
+constexpr int kMaxChunks = 16;
 
-struct ChunkRef {
-  uint64_t k, v;      // device [nh, cap, d] each (0 when chunk.len == 0)
-  int32_t cap, len;   // capacity; number of chunk rows C
-  int32_t off, pad;   // chunk offset (entries already cached)
+struct ChunkSet {
+  uint64_t k[kMaxChunks], v[kMaxChunks];   // device [nh, cap, d] each
+  int32_t cap[kMaxChunks];
+  int32_t len[kMaxChunks];                 // chunk rows (>= 1)
+  int32_t off[kMaxChunks];                 // entries already cached = position of the first row
+  int32_t row0[kMaxChunks];                // first batch row
+  int32_t n, rows;                         // chunks; total chunk rows
 };
 
 struct DecodeGroup {
@@ -137,12 +143,21 @@ struct RowRef {
   int32_t cap, pos;
 };
 
-__device__ __forceinline__ RowRef row_ref(int r, const ChunkRef &ch, const DecodeGroup &dg) {
+// Position, cache and key count of batch row r.  The chunk table is read at constant indices only
+// (a select per entry), which keeps the argument block out of per-lane scratch memory.
+__device__ __forceinline__ RowRef row_ref(int r, const ChunkSet &cs, const DecodeGroup &dg) {
   RowRef rr;
-  if (r < ch.len) {
-    rr.k = ch.k; rr.v = ch.v; rr.cap = ch.cap; rr.pos = ch.off + r;
+  if (r < cs.rows) {
+    uint64_t k = cs.k[0], v = cs.v[0];
+    int cap = cs.cap[0], pos = cs.off[0] + r;
+#pragma unroll
+    for (int i = 1; i < kMaxChunks; ++i)
+      if (i < cs.n && r >= cs.row0[i]) {
+        k = cs.k[i]; v = cs.v[i]; cap = cs.cap[i]; pos = cs.off[i] + (r - cs.row0[i]);
+      }
+    rr.k = k; rr.v = v; rr.cap = cap; rr.pos = pos;
   } else {
-    const int i = r - ch.len - dg.base;
+    const int i = r - cs.rows - dg.base;
     rr.k = dg.k[i]; rr.v = dg.v[i]; rr.cap = dg.cap[i]; rr.pos = dg.len[i];
   }
   return rr;

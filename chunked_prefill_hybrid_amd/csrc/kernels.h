@@ -73,7 +73,7 @@ hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, 
 // q|k|v row (float32 [rows, 3A]).
 hipError_t launch_rope_append(int type, const float *part, int splits, int rows_total, void *q_out,
                               int ld_q, float *qkv_dump, const float2 *tab, int use_rope, int nh,
-                              int d, int row0, int n_rows, const ChunkRef &ch, const DecodeGroup &dg,
+                              int d, int row0, int n_rows, const ChunkSet &cs, const DecodeGroup &dg,
                               hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
@@ -86,7 +86,7 @@ __host__ __device__ inline int attn_splits(int n_keys) {
   return (n_keys + kAttnSplit - 1) / kAttnSplit;
 }
 hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
-                            const ChunkRef &ch, const DecodeGroup &dg, int max_splits,
+                            const ChunkSet &cs, const DecodeGroup &dg, int max_splits,
                             float *part_o, float *part_ml, hipStream_t s);
 
 // Merges the split partials of rows [row0, row0+n_rows) into out[row, h*d + e] (storage type,
@@ -96,15 +96,16 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
                                int chunk_rows, int chunk_splits, const float *part_o,
                                const float *part_ml, void *out, int ld_out, hipStream_t s);
 
-// Flash-style causal chunk attention (bf16, MFMA): chunk rows [0, ch.len) attend to chunk keys
-// 0..ch.off+t.  q rows are the chunk rows of q (row stride ld_q); out likewise.  With n_split > 1
-// each 64-query block's key tiles are split n_split ways and the splits write partials (stride
-// `stride` splits per row and head) for launch_attn_combine instead of out.
+// Flash-style causal chunk attention (bf16, MFMA) over every chunk of the set: row row0[j] + t of
+// chunk j attends to keys 0..off[j]+t of chunk j's cache.  q and out are batch-row indexed (row
+// strides ld_q, ld_out).  With n_split > 1 each 64-query block's key tiles are split n_split ways
+// and the splits write partials (stride `stride` splits per row and head) for launch_attn_combine
+// instead of out.
 constexpr int kChunkTargetWorkgroups = 512;   // two workgroups per compute unit
 constexpr int kMinSplitTiles = 16;            // a split keeps at least 16 key tiles
 constexpr int kMaxChunkSplits = 16;
-int chunk_attn_splits(int chunk_len, int chunk_offset, int nh);
-hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkRef &ch, void *out,
+int chunk_attn_splits(const ChunkSet &cs, int nh);
+hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs, void *out,
                              int ld_out, int n_split, int stride, float *part_o, float *part_ml,
                              hipStream_t s);
 

@@ -53,7 +53,7 @@ constexpr int kMaxSplits = 8;   // split partials a consumer sums (the planner n
 // A norm row is handled by one workgroup of kNormThreads threads (16 waves, so that the ~300 rows of
 // a batch still keep several waves of memory requests per SIMD in flight).
 constexpr int kNormThreads = 1024;
-constexpr int kMaxChunks = 4;   // 4-element chunks per thread: rows up to 16384 wide
+constexpr int kRowPieces = 4;   // 4-element pieces per thread: rows up to 16384 wide
 
 // v[0..3] += sum_s part[s][off..off+3] in split order; every split's load is issued before its add
 // so a thread keeps several loads in flight.
@@ -71,7 +71,7 @@ __device__ __forceinline__ void add_splits(const float *part, int splits, size_t
     }
 }
 
-// One row per workgroup: the row stays in registers (up to kMaxChunks 4-element chunks per thread),
+// One row per workgroup: the row stays in registers (up to kRowPieces 4-element pieces per thread),
 // so the norm needs one read of its inputs.
 template <typename Tres, typename Tout, bool LN>
 __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, const float *part,
@@ -88,18 +88,18 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, con
   }
   const size_t slice = (size_t)rows * H, row_off = (size_t)r * H;
   const int nch = (H / 4 - threadIdx.x + kNormThreads - 1) / kNormThreads;   // chunks of this thread
-  float v[kMaxChunks][4];
+  float v[kRowPieces][4];
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i)
+  for (int i = 0; i < kRowPieces; ++i)
     if (i < nch) load4<Tres>(resid + row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
   if (splits > 0) {
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i)
+    for (int i = 0; i < kRowPieces; ++i)
       if (i < nch) add_splits(part, splits, slice, row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
   }
   float s1 = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i)
+  for (int i = 0; i < kRowPieces; ++i)
     if (i < nch) {
       if (sum_out) store4<float>(sum_out + row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
 #pragma unroll
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, con
     mean = s1 / (float)H;
     float q = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i)
+    for (int i = 0; i < kRowPieces; ++i)
       if (i < nch) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, con
   }
   const float rstd = 1.0f / sqrtf(ms + eps);
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i)
+  for (int i = 0; i < kRowPieces; ++i)
     if (i < nch) {
       const int c = (threadIdx.x + i * kNormThreads) * 4;
       float w[4];
@@ -192,7 +192,7 @@ hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const vo
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
                             hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
-  if (splits > kMaxSplits || H > 4 * kNormThreads * kMaxChunks || H % 4) return hipErrorInvalidValue;
+  if (splits > kMaxSplits || H > 4 * kNormThreads * kRowPieces || H % 4) return hipErrorInvalidValue;
   if (res_type == kF32 && out_type == kF32)
     return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, s);
   if (res_type == kBF16 && out_type == kBF16)

@@ -47,12 +47,12 @@ template <typename T>
 __global__ __launch_bounds__(256) void rope_append(const float *part, int splits, int rows_total,
                                                    T *q_out, int ld_q, float *qkv_dump,
                                                    const float2 *tab, int use_rope, int nh, int d,
-                                                   int row0, ChunkRef ch, DecodeGroup dg) {
+                                                   int row0, ChunkSet cs, DecodeGroup dg) {
   const int r = row0 + blockIdx.x;
   const int A = nh * d;
   const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= A) return;
-  const RowRef rr = row_ref(r, ch, dg);
+  const RowRef rr = row_ref(r, cs, dg);
   T *kc = reinterpret_cast<T *>(rr.k);
   T *vc = reinterpret_cast<T *>(rr.v);
   const size_t slice = (size_t)rows_total * 3 * A, src = (size_t)r * 3 * A;
@@ -71,12 +71,12 @@ __global__ __launch_bounds__(256) void rope_append(const float *part, int splits
     const float2 *t = tab + (size_t)rr.pos * (d / 2) + e0 / 2;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const float2 cs = t[u];
+      const float2 cz = t[u];
       const float q0 = q[2 * u], q1 = q[2 * u + 1], k0 = k[2 * u], k1 = k[2 * u + 1];
-      q[2 * u] = q0 * cs.x - q1 * cs.y;
-      q[2 * u + 1] = q0 * cs.y + q1 * cs.x;
-      k[2 * u] = k0 * cs.x - k1 * cs.y;
-      k[2 * u + 1] = k0 * cs.y + k1 * cs.x;
+      q[2 * u] = q0 * cz.x - q1 * cz.y;
+      q[2 * u + 1] = q0 * cz.y + q1 * cz.x;
+      k[2 * u] = k0 * cz.x - k1 * cz.y;
+      k[2 * u + 1] = k0 * cz.y + k1 * cz.x;
     }
   }
   put4<T>(q_out + (size_t)r * ld_q + c, q);
@@ -89,17 +89,17 @@ __global__ __launch_bounds__(256) void rope_append(const float *part, int splits
 
 hipError_t launch_rope_append(int type, const float *part, int splits, int rows_total, void *q_out,
                               int ld_q, float *qkv_dump, const float2 *tab, int use_rope, int nh,
-                              int d, int row0, int n_rows, const ChunkRef &ch, const DecodeGroup &dg,
+                              int d, int row0, int n_rows, const ChunkSet &cs, const DecodeGroup &dg,
                               hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(n_rows, (nh * d / 4 + 255) / 256);
   if (type == kF32)
     hipLaunchKernelGGL(rope_append<float>, grid, dim3(256), 0, s, part, splits, rows_total,
-                       static_cast<float *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, ch, dg);
+                       static_cast<float *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, cs, dg);
   else
     hipLaunchKernelGGL(rope_append<bf16_t>, grid, dim3(256), 0, s, part, splits, rows_total,
-                       static_cast<bf16_t *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, ch, dg);
+                       static_cast<bf16_t *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, cs, dg);
   return hipGetLastError();
 }
 

@@ -92,41 +92,97 @@ struct Range {
   int idx;
 };
 
+// The batch as the forward sees it, whichever entry point passed it: prefill chunks (rows first, in
+// order), then decodes.
+struct BatchView {
+  int n_chunks;
+  sarathi_chunk chunks[kMaxChunks];
+  int C;   // total chunk rows
+  int B;
+  const sarathi_kv *decode_kv;
+  const int32_t *decode_len;
+  const void *x;
+  void *y;
+};
+
+// Shape fields of a one-chunk batch; the rest is checked on the view.
+sarathi_status view_batch(const sarathi_batch *b, BatchView *v) {
+  if (!b) return fail(SARATHI_ERR_INVALID, "batch is null");
+  if (b->chunk_len < 0 || b->n_decodes < 0)
+    return fail(SARATHI_ERR_INVALID, "chunk_len and n_decodes must be >= 0");
+  if (b->reserved != 0) return fail(SARATHI_ERR_INVALID, "batch.reserved must be 0");
+  v->n_chunks = b->chunk_len > 0 ? 1 : 0;
+  if (v->n_chunks) {
+    v->chunks[0].len = b->chunk_len;
+    v->chunks[0].offset = b->chunk_offset;
+    v->chunks[0].kv = b->chunk_kv;
+  }
+  v->C = b->chunk_len;
+  v->B = b->n_decodes;
+  v->decode_kv = b->decode_kv;
+  v->decode_len = b->decode_len;
+  v->x = b->x;
+  v->y = b->y;
+  return SARATHI_OK;
+}
+
+sarathi_status view_multi(const sarathi_multi_batch *b, BatchView *v) {
+  if (!b) return fail(SARATHI_ERR_INVALID, "batch is null");
+  if (b->n_chunks < 0 || b->n_chunks > kMaxChunks)
+    return fail(SARATHI_ERR_INVALID, "n_chunks %d outside [0, %d]", b->n_chunks, kMaxChunks);
+  if (b->n_decodes < 0) return fail(SARATHI_ERR_INVALID, "n_decodes must be >= 0");
+  if (b->reserved != 0 || b->reserved2 != 0) return fail(SARATHI_ERR_INVALID, "reserved fields must be 0");
+  if (b->n_chunks > 0 && !b->chunks) return fail(SARATHI_ERR_INVALID, "chunks is null");
+  v->n_chunks = b->n_chunks;
+  long long rows = 0;
+  for (int j = 0; j < b->n_chunks; ++j) {
+    if (b->chunks[j].len < 1) return fail(SARATHI_ERR_INVALID, "chunk %d has len %d < 1", j, b->chunks[j].len);
+    v->chunks[j] = b->chunks[j];
+    rows += b->chunks[j].len;
+  }
+  if (rows > (1 << 30)) return fail(SARATHI_ERR_INVALID, "too many chunk rows");
+  v->C = (int)rows;
+  v->B = b->n_decodes;
+  v->decode_kv = b->decode_kv;
+  v->decode_len = b->decode_len;
+  v->x = b->x;
+  v->y = b->y;
+  return SARATHI_OK;
+}
+
 // need_xy: forward requires x and y; the attention-only entry does not.
-sarathi_status check_batch(const sarathi_layer_desc *d, const sarathi_batch *b, bool need_xy) {
+sarathi_status check_view(const sarathi_layer_desc *d, const BatchView &b, bool need_xy) {
   sarathi_status st = check_desc(d);
   if (st != SARATHI_OK) return st;
-  if (!b) return fail(SARATHI_ERR_INVALID, "batch is null");
-  const int C = b->chunk_len, B = b->n_decodes;
-  if (C < 0 || B < 0) return fail(SARATHI_ERR_INVALID, "chunk_len and n_decodes must be >= 0");
-  if (C + B < 1) return fail(SARATHI_ERR_INVALID, "empty batch (chunk_len + n_decodes == 0)");
-  if (C + B > d->max_tokens)
-    return fail(SARATHI_ERR_INVALID, "C+B = %d exceeds max_tokens %d", C + B, d->max_tokens);
-  if (b->reserved != 0) return fail(SARATHI_ERR_INVALID, "batch.reserved must be 0");
-  if (need_xy && (!b->x || !b->y)) return fail(SARATHI_ERR_INVALID, "x and y must be non-null");
+  const int C = b.C, B = b.B;
+  if (C + B < 1) return fail(SARATHI_ERR_INVALID, "empty batch (no chunk rows and no decodes)");
+  if ((long long)C + B > d->max_tokens)
+    return fail(SARATHI_ERR_INVALID, "C+B = %lld exceeds max_tokens %d", (long long)C + B, d->max_tokens);
+  if (need_xy && (!b.x || !b.y)) return fail(SARATHI_ERR_INVALID, "x and y must be non-null");
   const size_t el = elem_size(d->dtype);
   const size_t per_slot = (size_t)d->n_heads * d->head_dim * el;
   std::vector<Range> ranges;
-  if (C > 0) {
-    const sarathi_kv &kv = b->chunk_kv;
-    if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "chunk cache pointers are null");
-    if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "chunk_kv.reserved must be 0");
-    if (b->chunk_offset < 0) return fail(SARATHI_ERR_INVALID, "chunk_offset must be >= 0");
-    if (kv.capacity <= 0 || (long long)b->chunk_offset + C > kv.capacity)
-      return fail(SARATHI_ERR_CAPACITY, "chunk offset %d + C %d exceeds cache capacity %d",
-                  b->chunk_offset, C, kv.capacity);
-    if ((long long)b->chunk_offset + C > d->max_pos)
-      return fail(SARATHI_ERR_CAPACITY, "chunk positions reach %d >= max_pos %d",
-                  b->chunk_offset + C - 1, d->max_pos);
-    ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "chunk K", -1});
-    ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "chunk V", -1});
+  for (int j = 0; j < b.n_chunks; ++j) {
+    const sarathi_chunk &c = b.chunks[j];
+    const sarathi_kv &kv = c.kv;
+    if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "chunk %d cache pointers are null", j);
+    if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "chunk %d kv.reserved must be 0", j);
+    if (c.offset < 0) return fail(SARATHI_ERR_INVALID, "chunk %d offset must be >= 0", j);
+    if (kv.capacity <= 0 || (long long)c.offset + c.len > kv.capacity)
+      return fail(SARATHI_ERR_CAPACITY, "chunk %d: offset %d + len %d exceeds cache capacity %d", j,
+                  c.offset, c.len, kv.capacity);
+    if ((long long)c.offset + c.len > d->max_pos)
+      return fail(SARATHI_ERR_CAPACITY, "chunk %d positions reach %lld >= max_pos %d", j,
+                  (long long)c.offset + c.len - 1, d->max_pos);
+    ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "chunk K", j});
+    ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "chunk V", j});
   }
   if (B > 0) {
-    if (!b->decode_kv || !b->decode_len)
+    if (!b.decode_kv || !b.decode_len)
       return fail(SARATHI_ERR_INVALID, "decode_kv and decode_len must be non-null when n_decodes > 0");
     for (int i = 0; i < B; ++i) {
-      const sarathi_kv &kv = b->decode_kv[i];
-      const int L = b->decode_len[i];
+      const sarathi_kv &kv = b.decode_kv[i];
+      const int L = b.decode_len[i];
       if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "decode %d cache pointers are null", i);
       if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "decode_kv[%d].reserved must be 0", i);
       if (L < 0) return fail(SARATHI_ERR_INVALID, "decode_len[%d] = %d < 0", i, L);
@@ -141,9 +197,9 @@ sarathi_status check_batch(const sarathi_layer_desc *d, const sarathi_batch *b, 
   }
   if (need_xy) {
     const size_t rows = (size_t)(C + B) * d->hidden * el;
-    ranges.push_back({(uintptr_t)b->y, (uintptr_t)b->y + rows, "y", -1});
-    const uintptr_t xl = (uintptr_t)b->x, xh = xl + rows;
-    const uintptr_t yl = (uintptr_t)b->y, yh = yl + rows;
+    ranges.push_back({(uintptr_t)b.y, (uintptr_t)b.y + rows, "y", -1});
+    const uintptr_t xl = (uintptr_t)b.x, xh = xl + rows;
+    const uintptr_t yl = (uintptr_t)b.y, yh = yl + rows;
     if (xl < yh && yl < xh) return fail(SARATHI_ERR_INVALID, "y overlaps x");
   }
   std::sort(ranges.begin(), ranges.end(),
@@ -154,6 +210,7 @@ sarathi_status check_batch(const sarathi_layer_desc *d, const sarathi_batch *b, 
                   ranges[i].what, ranges[i].idx, ranges[i - 1].what, ranges[i - 1].idx);
   return SARATHI_OK;
 }
+
 
 // Workspace layout of one forward.  The GEMM plans are fixed by the shapes alone (planned for the
 // 256 compute units of an MI355X), so the workspace size depends only on the description and batch.
@@ -170,19 +227,38 @@ struct Plan {
 // decode rows, and the chunk rows too in float32 mode.
 bool chunk_uses_split(const sarathi_layer_desc *d) { return d->dtype != SARATHI_BF16; }
 
-int max_key_splits(const sarathi_layer_desc *d, const sarathi_batch *b, int chunk_splits) {
+ChunkSet chunk_set(const BatchView &b) {
+  ChunkSet cs{};
+  cs.n = b.n_chunks;
+  int row = 0;
+  for (int j = 0; j < b.n_chunks; ++j) {
+    const sarathi_chunk &c = b.chunks[j];
+    cs.k[j] = (uint64_t)c.kv.k;
+    cs.v[j] = (uint64_t)c.kv.v;
+    cs.cap[j] = c.kv.capacity;
+    cs.len[j] = c.len;
+    cs.off[j] = c.offset;
+    cs.row0[j] = row;
+    row += c.len;
+  }
+  cs.rows = row;
+  return cs;
+}
+
+int max_key_splits(const sarathi_layer_desc *d, const BatchView &b, int chunk_splits) {
   int ms = chunk_splits;
-  if (b->chunk_len > 0 && chunk_uses_split(d))
-    ms = std::max(ms, attn_splits(b->chunk_offset + b->chunk_len));
-  for (int i = 0; i < b->n_decodes; ++i) ms = std::max(ms, attn_splits(b->decode_len[i] + 1));
+  if (chunk_uses_split(d))
+    for (int j = 0; j < b.n_chunks; ++j)
+      ms = std::max(ms, attn_splits(b.chunks[j].offset + b.chunks[j].len));
+  for (int i = 0; i < b.B; ++i) ms = std::max(ms, attn_splits(b.decode_len[i] + 1));
   return ms;
 }
 
-Plan make_plan(const sarathi_layer_desc *d, const sarathi_batch *b) {
+Plan make_plan(const sarathi_layer_desc *d, const BatchView &b) {
   Plan p{};
-  p.T = b->chunk_len + b->n_decodes;
+  p.T = b.C + b.B;
   p.T_alloc = round_up(p.T, 64);
-  p.chunk_splits = chunk_uses_split(d) ? 1 : chunk_attn_splits(b->chunk_len, b->chunk_offset, d->n_heads);
+  p.chunk_splits = chunk_uses_split(d) ? 1 : chunk_attn_splits(chunk_set(b), d->n_heads);
   p.max_splits = max_key_splits(d, b, p.chunk_splits);
   const int ty = d->dtype;
   const size_t el = elem_size(ty), R = p.T_alloc;
@@ -211,28 +287,16 @@ Plan make_plan(const sarathi_layer_desc *d, const sarathi_batch *b) {
   return p;
 }
 
-ChunkRef chunk_ref(const sarathi_batch *b) {
-  ChunkRef c{};
-  c.len = b->chunk_len;
-  if (b->chunk_len > 0) {
-    c.k = (uint64_t)b->chunk_kv.k;
-    c.v = (uint64_t)b->chunk_kv.v;
-    c.cap = b->chunk_kv.capacity;
-    c.off = b->chunk_offset;
-  }
-  return c;
-}
-
-DecodeGroup decode_group(const sarathi_batch *b, int base) {
+DecodeGroup decode_group(const BatchView &b, int base) {
   DecodeGroup g{};
   g.base = base;
-  g.n = std::min(kMaxDecodesPerLaunch, b->n_decodes - base);
+  g.n = std::min(kMaxDecodesPerLaunch, b.B - base);
   if (g.n < 0) g.n = 0;
   for (int i = 0; i < g.n; ++i) {
-    g.k[i] = (uint64_t)b->decode_kv[base + i].k;
-    g.v[i] = (uint64_t)b->decode_kv[base + i].v;
-    g.len[i] = b->decode_len[base + i];
-    g.cap[i] = b->decode_kv[base + i].capacity;
+    g.k[i] = (uint64_t)b.decode_kv[base + i].k;
+    g.v[i] = (uint64_t)b.decode_kv[base + i].v;
+    g.len[i] = b.decode_len[base + i];
+    g.cap[i] = b.decode_kv[base + i].capacity;
   }
   return g;
 }
@@ -272,13 +336,14 @@ struct Marker {
   }
 };
 
-// Attention of all batch rows, split per request: chunk rows, then decode rows (64 per launch
-// group), then one merge of the split partials; writes out [T, A] (storage type).
-sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b, const Plan &p,
+// Attention of all batch rows, split per request: chunk rows (all chunks in one launch), then
+// decode rows (64 per launch group), then one merge of the split partials; writes out [T, A]
+// (storage type).
+sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, const Plan &p,
                              const void *q, void *out, char *ws, hipStream_t s, Marker &mk) {
   const int A = d->n_heads * d->head_dim;
-  const int C = b->chunk_len, B = b->n_decodes;
-  const ChunkRef ch = chunk_ref(b);
+  const int C = b.C, B = b.B;
+  const ChunkSet cs = chunk_set(b);
   float *po = reinterpret_cast<float *>(ws + p.part_o);
   float *pml = reinterpret_cast<float *>(ws + p.part_ml);
   const bool split_chunk = chunk_uses_split(d);
@@ -286,10 +351,10 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
   if (C > 0) {
     if (split_chunk) {
       const DecodeGroup none = decode_group(b, B);   // empty group
-      HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, ch, none,
+      HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, cs, none,
                                p.max_splits, po, pml, s));
     } else {
-      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, ch, out, A, p.chunk_splits,
+      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, cs, out, A, p.chunk_splits,
                                 p.max_splits, po, pml, s));
     }
   }
@@ -297,7 +362,7 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_DECODE));
   for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
     const DecodeGroup g = decode_group(b, base);
-    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, ch, g,
+    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, cs, g,
                              p.max_splits, po, pml, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
@@ -313,12 +378,11 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const sarathi_batch *b
   return SARATHI_OK;
 }
 
-sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *workspace,
-                            size_t ws_bytes, void *stream, const sarathi_debug_dump *dump,
-                            sarathi_timer *timer) {
+sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspace, size_t ws_bytes,
+                            void *stream, const sarathi_debug_dump *dump, sarathi_timer *timer) {
   if (!L) return fail(SARATHI_ERR_INVALID, "layer is null");
   const sarathi_layer_desc *d = &L->desc;
-  sarathi_status st = check_batch(d, b, true);
+  sarathi_status st = check_view(d, b, true);
   if (st != SARATHI_OK) return st;
   const Plan p = make_plan(d, b);
   if (!workspace) return fail(SARATHI_ERR_WORKSPACE, "workspace is null");
@@ -344,7 +408,7 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
 
   // 1. norm 1 over the C+B rows (pad rows zeroed)
   HIP_TRY(mk.start(SARATHI_STAGE_NORM1));
-  HIP_TRY(launch_norm_rows(ty, ty, !llama, b->x, nullptr, 0, nullptr, L->w.norm1_w, L->w.norm1_b, n1,
+  HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, nullptr, 0, nullptr, L->w.norm1_w, L->w.norm1_b, n1,
                            H, T, R, d->norm_eps, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM1, true));
   // 2. QKV projection: one GEMM over chunk and decode rows (float32 split partials)
@@ -354,20 +418,21 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.qkv, s));
   HIP_TRY(mk.end(SARATHI_STAGE_QKV, true));
-  // 3. sum of the partials + RoPE + KV append (per launch group of decodes)
-  const ChunkRef ch = chunk_ref(b);
+  // 3. sum of the partials + RoPE + KV append: the chunk rows with the first decode group, then the
+  // other decode groups
+  const ChunkSet cs = chunk_set(b);
   HIP_TRY(mk.start(SARATHI_STAGE_ROPE_APPEND));
   {
     int base = 0;
     do {
       const DecodeGroup dg = decode_group(b, base);
-      const int row0 = base == 0 ? 0 : b->chunk_len + base;
-      const int n_rows = (base == 0 ? b->chunk_len : 0) + dg.n;
+      const int row0 = base == 0 ? 0 : b.C + base;
+      const int n_rows = (base == 0 ? b.C : 0) + dg.n;
       HIP_TRY(launch_rope_append(ty, part, p.qkv.splits, T, q, A, dump ? dump->qkv : nullptr,
                                  L->rope_tab, llama ? 1 : 0, d->n_heads, d->head_dim, row0, n_rows,
-                                 ch, dg, s));
+                                 cs, dg, s));
       base += kMaxDecodesPerLaunch;
-    } while (base < b->n_decodes);
+    } while (base < b.B);
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ROPE_APPEND, true));
   // 4. attention, split per request
@@ -382,7 +447,7 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   HIP_TRY(mk.end(SARATHI_STAGE_O, true));
   // 6. h1 = x + sum of the O partials (kept in float32), then norm 2
   HIP_TRY(mk.start(SARATHI_STAGE_NORM2));
-  HIP_TRY(launch_norm_rows(ty, ty, !llama, b->x, part, p.o.splits, h1, L->w.norm2_w, L->w.norm2_b, n2,
+  HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, part, p.o.splits, h1, L->w.norm2_w, L->w.norm2_b, n2,
                            H, T, R, d->norm_eps, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM2, true));
   // 7. FFN up (+gate): activation fused into the GEMM, or split product + activation pass
@@ -406,7 +471,7 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   g.a = act; g.lda = F; g.w0 = L->w.w_down; g.ldw = F; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.down, s));
-  HIP_TRY(launch_resid_sum(ty, h1, part, p.down.splits, b->y, T, H, s));
+  HIP_TRY(launch_resid_sum(ty, h1, part, p.down.splits, b.y, T, H, s));
   HIP_TRY(mk.end(SARATHI_STAGE_FFN_DOWN, true));
   mk.commit();
 
@@ -420,6 +485,38 @@ sarathi_status forward_impl(sarathi_layer *L, const sarathi_batch *b, void *work
   }
   return SARATHI_OK;
 }
+
+sarathi_status make_view(const sarathi_batch *b, BatchView *v) { return view_batch(b, v); }
+sarathi_status make_view(const sarathi_multi_batch *b, BatchView *v) { return view_multi(b, v); }
+
+// Validation of a batch of either kind: the description first, then the batch.
+template <typename Batch>
+sarathi_status checked_view(const sarathi_layer_desc *d, const Batch *b, bool need_xy, BatchView *v) {
+  sarathi_status st = check_desc(d);
+  if (st != SARATHI_OK) return st;
+  st = make_view(b, v);
+  if (st != SARATHI_OK) return st;
+  return check_view(d, *v, need_xy);
+}
+
+template <typename Batch>
+size_t workspace_bytes(const sarathi_layer_desc *d, const Batch *b) {
+  BatchView v;
+  if (checked_view(d, b, false, &v) != SARATHI_OK) return 0;
+  return make_plan(d, v).total;
+}
+
+template <typename Batch>
+sarathi_status forward_entry(sarathi_layer *L, const Batch *b, void *workspace, size_t ws_bytes,
+                             void *stream, const sarathi_debug_dump *dump, sarathi_timer *timer) {
+  if (!L) return fail(SARATHI_ERR_INVALID, "layer is null");
+  BatchView v;
+  const sarathi_status st = checked_view(&L->desc, b, true, &v);
+  if (st != SARATHI_OK) return st;
+  return forward_impl(L, v, workspace, ws_bytes, stream, dump, timer);
+}
+
+static_assert(SARATHI_MAX_CHUNKS == kMaxChunks, "chunk table size");
 
 }  // namespace
 
@@ -482,23 +579,44 @@ void sarathi_layer_destroy(sarathi_layer *layer) {
 }
 
 sarathi_status sarathi_batch_check(const sarathi_layer_desc *desc, const sarathi_batch *batch) {
-  return check_batch(desc, batch, true);
+  BatchView v;
+  return checked_view(desc, batch, true, &v);
 }
 
 size_t sarathi_workspace_size(const sarathi_layer_desc *desc, const sarathi_batch *batch) {
-  if (check_batch(desc, batch, false) != SARATHI_OK) return 0;
-  return make_plan(desc, batch).total;
+  return workspace_bytes(desc, batch);
 }
 
 sarathi_status sarathi_layer_forward(sarathi_layer *layer, const sarathi_batch *batch,
                                      void *workspace, size_t ws_bytes, void *stream) {
-  return forward_impl(layer, batch, workspace, ws_bytes, stream, nullptr, nullptr);
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
 sarathi_status sarathi_layer_forward_debug(sarathi_layer *layer, const sarathi_batch *batch,
                                            void *workspace, size_t ws_bytes, void *stream,
                                            const sarathi_debug_dump *dump) {
-  return forward_impl(layer, batch, workspace, ws_bytes, stream, dump, nullptr);
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, dump, nullptr);
+}
+
+sarathi_status sarathi_multi_batch_check(const sarathi_layer_desc *desc,
+                                         const sarathi_multi_batch *batch) {
+  BatchView v;
+  return checked_view(desc, batch, true, &v);
+}
+
+size_t sarathi_multi_workspace_size(const sarathi_layer_desc *desc, const sarathi_multi_batch *batch) {
+  return workspace_bytes(desc, batch);
+}
+
+sarathi_status sarathi_multi_forward(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                     void *workspace, size_t ws_bytes, void *stream) {
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+sarathi_status sarathi_multi_forward_debug(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           const sarathi_debug_dump *dump) {
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, dump, nullptr);
 }
 
 sarathi_status sarathi_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a,
@@ -559,9 +677,10 @@ sarathi_status stack_plan(sarathi_layer *const *layers, int n, const sarathi_sta
       return report ? fail(SARATHI_ERR_INVALID, "layer %d: hidden size or storage type differs from layer 0", l)
                     : SARATHI_ERR_INVALID;
     const sarathi_batch bl = stack_layer_batch(b, l, b->x, b->y);
-    const sarathi_status st = check_batch(&d, &bl, report);
+    BatchView v;
+    const sarathi_status st = checked_view(&d, &bl, true, &v);
     if (st != SARATHI_OK) return st;
-    p.layer_ws = std::max(p.layer_ws, make_plan(&d, &bl).total);
+    p.layer_ws = std::max(p.layer_ws, make_plan(&d, v).total);
   }
   const size_t T = (size_t)b->chunk_len + b->n_decodes;
   p.act_bytes = n > 1 ? align256(T * d0.hidden * elem_size(d0.dtype)) : 0;
@@ -595,7 +714,7 @@ sarathi_status sarathi_stack_forward(sarathi_layer *const *layers, int32_t n_lay
     const void *x = l == 0 ? batch->x : act[(l - 1) & 1];
     void *y = l == n_layers - 1 ? batch->y : act[l & 1];
     const sarathi_batch bl = stack_layer_batch(batch, l, x, y);
-    st = forward_impl(layers[l], &bl, ws, p.layer_ws, stream, nullptr, nullptr);
+    st = forward_entry(layers[l], &bl, ws, p.layer_ws, stream, nullptr, nullptr);
     if (st != SARATHI_OK) return st;
   }
   return SARATHI_OK;
@@ -604,16 +723,17 @@ sarathi_status sarathi_stack_forward(sarathi_layer *const *layers, int32_t n_lay
 sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_batch *batch,
                                  const void *q, void *out, void *workspace, size_t ws_bytes,
                                  void *stream) {
-  sarathi_status st = check_batch(desc, batch, false);
+  BatchView v;
+  sarathi_status st = checked_view(desc, batch, false, &v);
   if (st != SARATHI_OK) return st;
   if (!q || !out) return fail(SARATHI_ERR_INVALID, "q and out must be non-null");
-  const Plan p = make_plan(desc, batch);
+  const Plan p = make_plan(desc, v);
   if (!workspace) return fail(SARATHI_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)workspace % 256) return fail(SARATHI_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (ws_bytes < p.total)
     return fail(SARATHI_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
   Marker none;
-  return run_attention(desc, batch, p, q, out, static_cast<char *>(workspace),
+  return run_attention(desc, v, p, q, out, static_cast<char *>(workspace),
                        static_cast<hipStream_t>(stream), none);
 }
 
@@ -655,7 +775,14 @@ sarathi_status sarathi_layer_forward_timed(sarathi_layer *layer, const sarathi_b
                                            void *workspace, size_t ws_bytes, void *stream,
                                            sarathi_timer *timer) {
   if (!timer) return fail(SARATHI_ERR_INVALID, "timer is null");
-  return forward_impl(layer, batch, workspace, ws_bytes, stream, nullptr, timer);
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, nullptr, timer);
+}
+
+sarathi_status sarathi_multi_forward_timed(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           sarathi_timer *timer) {
+  if (!timer) return fail(SARATHI_ERR_INVALID, "timer is null");
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, nullptr, timer);
 }
 
 sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_t *count) {

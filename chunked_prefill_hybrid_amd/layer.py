@@ -85,7 +85,41 @@ class HybridLayer:
                                _ptr(x, dt), _ptr(y, dt))
 
     def workspace_size(self, batch) -> int:
+        if isinstance(batch, _abi.sarathi_multi_batch):
+            return _abi.sarathi_multi_workspace_size(self.desc, batch)
         return _abi.sarathi_workspace_size(self.desc, batch)
+
+    def multi_batch(self, x: Optional[torch.Tensor], y: Optional[torch.Tensor],
+                    chunks: Sequence[Tuple[int, int, KV]], decode_kv: Sequence[KV],
+                    decode_len: Sequence[int]):
+        """(sarathi_multi_batch, keepalive).  chunks: list of (len, offset, (K, V)), rows in list
+        order, then the decodes."""
+        dt = self.dtype
+        ch = [(ln, off, _ptr(kv[0], dt), _ptr(kv[1], dt), kv[0].shape[1]) for ln, off, kv in chunks]
+        dkv = [(_ptr(k, dt), _ptr(v, dt), k.shape[1]) for k, v in decode_kv]
+        return _abi.make_multi_batch(ch, dkv, list(decode_len), _ptr(x, dt), _ptr(y, dt))
+
+    def forward_multi(self, x, y, chunks, decode_kv, decode_len, workspace: Optional[torch.Tensor] = None,
+                      stream=None, dump: Optional[dict] = None):
+        """Enqueue the layer over a batch with several prefill chunks (see multi_batch); y and the
+        caches are written in place.  dump as in forward."""
+        b, keep = self.multi_batch(x, y, chunks, decode_kv, decode_len)
+        need = _abi.sarathi_multi_workspace_size(self.desc, b)
+        if need == 0:
+            st = _abi.sarathi_multi_batch_check(self.desc, b)
+            raise _abi.SarathiError(st, "multi batch", _abi.sarathi_last_error())
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr = _ptr(workspace)
+        nbytes = workspace.numel() * workspace.element_size()
+        if dump:
+            d = _abi.sarathi_debug_dump(*[_ptr(dump.get(n), torch.float32) for n in
+                                          ("n1", "qkv", "q_rot", "attn", "h1", "n2", "act")])
+            _abi.sarathi_multi_forward_debug(self.handle, b, ws_ptr, nbytes, _stream(stream), d)
+        else:
+            _abi.sarathi_multi_forward(self.handle, b, ws_ptr, nbytes, _stream(stream))
+        del keep
+        return y
 
     def forward(self, x, y, chunk_len, chunk_offset, chunk_kv, decode_kv, decode_len,
                 workspace: Optional[torch.Tensor] = None, stream=None, dump: Optional[dict] = None):

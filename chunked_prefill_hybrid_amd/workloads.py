@@ -30,6 +30,7 @@ import numpy as np
 __all__ = [
     "LayerShape", "BatchSpec", "Workload", "SHAPES", "bf16_round", "bf16_bits",
     "make_weights", "make_batch", "workload", "sweep", "tiny_schedule", "WORKLOADS",
+    "MultiSpec", "budget_batch", "make_multi_batch", "chunks_of",
 ]
 
 
@@ -76,6 +77,37 @@ class BatchSpec:
     decode_len_range: Optional[Tuple[int, int]] = None
 
 
+@dataclass(frozen=True)
+class MultiSpec:
+    """Composition of one token-budget batch: `budget` tokens go to the decodes first, then to prefill
+    chunks cut from `prompts` in order (each (prompt_len, tokens already prefilled); a partially
+    prefilled prompt is listed first), the stall-free step composition of the Sarathi-Serve notes.
+    Decode lengths as in BatchSpec."""
+    budget: int
+    prompts: Tuple[Tuple[int, int], ...]
+    n_decodes: int
+    decode_lens: Optional[Tuple[int, ...]] = None
+    decode_len_range: Optional[Tuple[int, int]] = None
+
+
+def budget_batch(budget: int, n_decodes: int, prompts: Sequence[Tuple[int, int]]):
+    """One step of token-budget batching (junupark.xyz notes on Sarathi-Serve, "Stall Free Batching"):
+    the decodes are taken first, one token each; then each prompt in order gets
+    min(remaining budget, its remaining tokens), until the budget is spent.  Returns (decodes taken,
+    [(prompt index, chunk length, chunk offset)])."""
+    n_dec = min(n_decodes, budget)
+    left = budget - n_dec
+    chunks = []
+    for i, (plen, done) in enumerate(prompts):
+        if left <= 0:
+            break
+        n = min(left, plen - done)
+        if n > 0:
+            chunks.append((i, n, done))
+            left -= n
+    return n_dec, chunks
+
+
 SHAPES = {
     "tiny": LayerShape("tiny-llama", "llama", 256, 4, 64, 688, "f32", 1e-6, 10000.0, None),
     "llama13b": LayerShape("llama-13b", "llama", 5120, 40, 128, 13824, "bf16", 1e-6, 10000.0, 0.02),
@@ -105,7 +137,23 @@ WORKLOADS = {
                         BatchSpec(256, 0, 256, 64, decode_lens=(2048,) * 64)),
     "llama13b_long": Workload("llama13b_long", SHAPES["llama13b"],
                               BatchSpec(512, 7680, 8192, 48, decode_len_range=(2048, 8192))),
+    # Token-budget batch: 512 tokens = 18 decodes + the last 94 tokens of a 1024-token prompt + a whole
+    # 300-token prompt + the first 100 tokens of a new 1024-token prompt.
+    "llama13b_budget": Workload("llama13b_budget", SHAPES["llama13b"],
+                                MultiSpec(512, ((1024, 930), (300, 0), (1024, 0)), 18,
+                                          decode_lens=(1024,) * 18)),
 }
+
+
+def chunks_of(batch: dict):
+    """The prefill chunks of a generated batch as a list of dicts (len, offset, k, v), whichever kind
+    of batch it is (one chunk: chunk_len / chunk_offset / chunk_k / chunk_v; several: chunks)."""
+    if "chunks" in batch:
+        return list(batch["chunks"])
+    if batch["chunk_len"]:
+        return [{"len": batch["chunk_len"], "offset": batch["chunk_offset"], "k": batch["chunk_k"],
+                 "v": batch["chunk_v"]}]
+    return []
 
 
 def workload(key: str, **batch_changes) -> Workload:
@@ -250,14 +298,7 @@ def make_batch(shape: LayerShape, spec: BatchSpec, rng, fill_rest: float = 0.0) 
     x = _normal(rng, (C + B, shape.hidden), 1.0, shape.dtype)
     cap = max(spec.prompt_len, spec.chunk_offset + C, 1)
     ck, cv = _cache(rng, shape, cap, spec.chunk_offset, fill_rest)
-    if spec.decode_lens is not None:
-        lens = list(spec.decode_lens)[:B]
-        assert len(lens) == B, "decode_lens must list one length per decode"
-    elif B:
-        lo, hi = spec.decode_len_range
-        lens = [int(v) for v in rng.generator().integers(lo, hi, size=B, endpoint=True)]
-    else:
-        lens = []
+    lens = _decode_lens(spec, rng, B)
     dk, dv = [], []
     for L in lens:
         k, v = _cache(rng, shape, L + 1, L, fill_rest)
@@ -267,11 +308,47 @@ def make_batch(shape: LayerShape, spec: BatchSpec, rng, fill_rest: float = 0.0) 
             "decode_len": lens, "decode_k": dk, "decode_v": dv}
 
 
+def _decode_lens(spec, rng: Draws, B: int) -> List[int]:
+    if spec.decode_lens is not None:
+        lens = list(spec.decode_lens)[:B]
+        assert len(lens) == B, "decode_lens must list one length per decode"
+        return lens
+    if B:
+        lo, hi = spec.decode_len_range
+        return [int(v) for v in rng.generator().integers(lo, hi, size=B, endpoint=True)]
+    return []
+
+
+def make_multi_batch(shape: LayerShape, spec: MultiSpec, rng, fill_rest: float = 0.0) -> dict:
+    """Hidden states and caches of one token-budget batch (drawn after the weights).  The chunks come
+    from budget_batch; chunk j's request has a cache of capacity prompt_len holding N(0,1) entries in
+    its already-prefilled slots; decodes as in make_batch.  Draw order: X, each chunk's cache (K then
+    V) in chunk order, the decode lengths, each decode cache."""
+    rng = as_draws(rng)
+    B, picked = budget_batch(spec.budget, spec.n_decodes, spec.prompts)
+    C = sum(n for _, n, _ in picked)
+    x = _normal(rng, (C + B, shape.hidden), 1.0, shape.dtype)
+    chunks = []
+    for i, n, off in picked:
+        k, v = _cache(rng, shape, spec.prompts[i][0], off, fill_rest)
+        chunks.append({"len": n, "offset": off, "k": k, "v": v})
+    lens = _decode_lens(spec, rng, B)
+    dk, dv = [], []
+    for L in lens:
+        k, v = _cache(rng, shape, L + 1, L, fill_rest)
+        dk.append(k)
+        dv.append(v)
+    return {"x": x, "chunks": chunks, "decode_len": lens, "decode_k": dk, "decode_v": dv}
+
+
 def generate(w: Workload, fill_rest: float = 0.0) -> Tuple[dict, dict]:
     """(weights, batch) of a workload, drawn from its seed in the fixed order."""
     rng = Draws(w.seed)
     weights = make_weights(w.shape, rng)
-    batch = make_batch(w.shape, w.batch, rng, fill_rest)
+    if isinstance(w.batch, MultiSpec):
+        batch = make_multi_batch(w.shape, w.batch, rng, fill_rest)
+    else:
+        batch = make_batch(w.shape, w.batch, rng, fill_rest)
     return weights, batch
 
 

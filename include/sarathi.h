@@ -3,7 +3,8 @@
  *
  * The library runs the forward pass of one LLaMA-style (or GPT-style) decoder layer over a HYBRID
  * BATCH: one prefill chunk of C tokens from one request plus B single-token decodes, each decode
- * request with its own KV cache.  The linear ops (QKV, O, gate/up, down) run as single GEMMs over the
+ * request with its own KV cache (or, through the sarathi_multi_* entry points, several chunks of
+ * different requests plus decodes).  The linear ops (QKV, O, gate/up, down) run as single GEMMs over the
  * C+B concatenated rows, so the decodes share the chunk's weight fetches; attention is split per
  * request: causal attention of the chunk over its cached prefix plus itself, and single-query
  * attention of each decode over its own cache plus its own new token.
@@ -202,6 +203,54 @@ sarathi_status sarathi_stack_forward(sarathi_layer *const *layers, int32_t n_lay
                                      const sarathi_stack_batch *batch, void *workspace,
                                      size_t ws_bytes, void *stream);
 
+/* ---- Batches with several prefill chunks -------------------------------------------------------
+ * A token-budget batch: decodes plus SEVERAL prefill chunks, each from a different request (a
+ * partially prefilled prompt and new prompts cut to fit the budget; junupark.xyz notes on
+ * Sarathi-Serve, "Stall Free Batching" and its worked example 4 decodes + 30 + 66 tokens).  The
+ * linear ops still run as single GEMMs over all rows; each chunk attends causally to its own
+ * request's cached prefix plus itself, each decode to its own cache.  With one chunk (or none) the
+ * result is bitwise that of sarathi_layer_forward on the equivalent sarathi_batch. */
+#define SARATHI_MAX_CHUNKS 16
+
+typedef struct {
+    int32_t len;                /* rows of this chunk, >= 1 */
+    int32_t offset;             /* entries already in this request's cache = position of row 0 */
+    sarathi_kv kv;              /* device buffers; capacity >= offset + len */
+} sarathi_chunk;
+
+/* Rows of x: chunk 0's rows, then chunk 1's, ..., then decode 0..n_decodes-1.  Row r of chunk j
+ * (batch row sum_{i<j} chunks[i].len + r) sits at position chunks[j].offset + r and writes cache
+ * slot chunks[j].offset + r of chunks[j].kv. */
+typedef struct {
+    int32_t n_chunks;           /* 0 .. SARATHI_MAX_CHUNKS */
+    int32_t reserved;           /* must be 0 */
+    const sarathi_chunk *chunks;  /* HOST array [n_chunks]; may be NULL when n_chunks == 0 */
+    int32_t n_decodes;          /* B >= 0 */
+    int32_t reserved2;          /* must be 0 */
+    const sarathi_kv *decode_kv;  /* HOST array [n_decodes]; capacity >= decode_len[i] + 1 */
+    const int32_t *decode_len;    /* HOST array [n_decodes]; >= 0 */
+    const void *x;              /* device [T, H], T = total chunk rows + n_decodes */
+    void *y;                    /* device [T, H]; must not overlap x, caches or workspace */
+} sarathi_multi_batch;
+
+/* Host-only validation, as sarathi_batch_check, per chunk; also rejects n_chunks outside
+ * [0, SARATHI_MAX_CHUNKS], a chunk with len < 1, and two chunks (or a chunk and a decode) that share
+ * a cache.  Returns OK, INVALID or CAPACITY. */
+sarathi_status sarathi_multi_batch_check(const sarathi_layer_desc *desc, const sarathi_multi_batch *batch);
+
+/* Bytes of device workspace sarathi_multi_forward needs for this batch; 0 if the check fails. */
+size_t sarathi_multi_workspace_size(const sarathi_layer_desc *desc, const sarathi_multi_batch *batch);
+
+/* Enqueues the layer's forward over the batch (workspace rules as sarathi_layer_forward).
+ * Errors (all before any launch): everything sarathi_multi_batch_check reports, WORKSPACE, HIP. */
+sarathi_status sarathi_multi_forward(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                     void *workspace, size_t ws_bytes, void *stream);
+
+/* As sarathi_multi_forward plus the intermediates of sarathi_layer_forward_debug (dump may be NULL). */
+sarathi_status sarathi_multi_forward_debug(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           const sarathi_debug_dump *dump);
+
 /* ---- Per-stage timing (measurement only) ------------------------------------------------------
  * The layer's forward runs as the stages below, in this order (per-operation profile of a hybrid
  * iteration: preproj, attention, postproj, FFN; SARATHI: Efficient LLM Inference by Piggybacking
@@ -239,6 +288,11 @@ void sarathi_timer_destroy(sarathi_timer *timer);
  * Errors: as the forward; INVALID if the timer already holds `capacity` unread forwards (nothing is
  * enqueued then). */
 sarathi_status sarathi_layer_forward_timed(sarathi_layer *layer, const sarathi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           sarathi_timer *timer);
+
+/* As sarathi_multi_forward, recording the timer's events (see sarathi_layer_forward_timed). */
+sarathi_status sarathi_multi_forward_timed(sarathi_layer *layer, const sarathi_multi_batch *batch,
                                            void *workspace, size_t ws_bytes, void *stream,
                                            sarathi_timer *timer);
 

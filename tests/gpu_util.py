@@ -90,11 +90,15 @@ def new_rows_from_caches(db, C, off, lens):
 
 def compare(shape, b, ref, db, dd, tol=None, label=""):
     """Errors of every checked tensor; asserts each is within tolerance."""
-    tol = tol if tol is not None else TOL[shape.dtype]
     C, off, lens = b["chunk_len"], b["chunk_offset"], list(b["decode_len"])
-    y = db["y"].float().cpu().numpy()
-    x = np.asarray(b["x"], dtype=np.float64)
     nk, nv = new_rows_from_caches(db, C, off, lens)
+    return compare_rows(shape, b["x"], ref, db["y"], nk, nv, dd, tol, label)
+
+
+def compare_rows(shape, x, ref, y_dev, nk, nv, dd, tol=None, label=""):
+    tol = tol if tol is not None else TOL[shape.dtype]
+    y = y_dev.float().cpu().numpy()
+    x = np.asarray(x, dtype=np.float64)
     errs = {"y": rel(y, ref["y"]), "dy": rel(y - x, ref["y"] - x), "new_k": rel(nk, ref["new_k"]),
             "new_v": rel(nv, ref["new_v"])}
     if dd is not None:
@@ -104,6 +108,47 @@ def compare(shape, b, ref, db, dd, tol=None, label=""):
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     assert not bad, f"{label}: over tolerance {tol}: {bad}"
     return errs
+
+
+# ---- batches with several prefill chunks ----------------------------------------------------------
+
+def upload_multi(shape, b):
+    dt = tdtype(shape)
+    d = {"x": dev(b["x"], dt), "decode_len": list(b["decode_len"]),
+         "chunks": [(c["len"], c["offset"], (dev(c["k"], dt), dev(c["v"], dt))) for c in b["chunks"]],
+         "decode_kv": [(dev(k, dt), dev(v, dt)) for k, v in zip(b["decode_k"], b["decode_v"])]}
+    d["y"] = torch.empty_like(d["x"])
+    return d
+
+
+def run_multi(layer, db, dump=True, workspace=None):
+    shape = layer.shape
+    T = db["x"].shape[0]
+    A = shape.attn_width
+    widths = {"n1": shape.hidden, "qkv": 3 * A, "q_rot": A, "attn": A, "h1": shape.hidden,
+              "n2": shape.hidden, "act": shape.ffn}
+    dd = {k: torch.full((T, w), float("nan"), device=DEV) for k, w in widths.items()} if dump else None
+    layer.forward_multi(db["x"], db["y"], db["chunks"], db["decode_kv"], db["decode_len"],
+                        workspace=workspace, dump=dd)
+    torch.cuda.synchronize()
+    return dd
+
+
+def new_rows_multi(db):
+    """The K/V rows the step wrote, read back from the device caches: [T, nh, d] each."""
+    ks, vs = [], []
+    for n, off, (k, v) in db["chunks"]:
+        ks.append(k[:, off:off + n, :].permute(1, 0, 2).float().cpu().numpy())
+        vs.append(v[:, off:off + n, :].permute(1, 0, 2).float().cpu().numpy())
+    for (k, v), L in zip(db["decode_kv"], db["decode_len"]):
+        ks.append(k[:, L:L + 1, :].permute(1, 0, 2).float().cpu().numpy())
+        vs.append(v[:, L:L + 1, :].permute(1, 0, 2).float().cpu().numpy())
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+def compare_multi(shape, b, ref, db, dd, tol=None, label=""):
+    nk, nv = new_rows_multi(db)
+    return compare_rows(shape, b["x"], ref, db["y"], nk, nv, dd, tol, label)
 
 
 def oracle_ref(shape, w, b):

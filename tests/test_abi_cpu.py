@@ -44,6 +44,9 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(_abi.sarathi_debug_dump) == 56
     assert ctypes.sizeof(_abi.sarathi_stack_batch) == 56
     assert _abi.sarathi_stack_batch.decode_kv.offset == 24 and _abi.sarathi_stack_batch.x.offset == 40
+    assert ctypes.sizeof(_abi.sarathi_chunk) == 32
+    assert ctypes.sizeof(_abi.sarathi_multi_batch) == 56
+    assert _abi.sarathi_multi_batch.decode_kv.offset == 24 and _abi.sarathi_multi_batch.x.offset == 40
 
 
 def desc(**kw):
@@ -133,4 +136,66 @@ def test_stack_rejects_empty_or_null_before_any_hip_call(lib):
     assert _abi.sarathi_stack_workspace_size([None], b) == 0
     with pytest.raises(_abi.SarathiError) as e:
         _abi.sarathi_stack_forward([], b, addr(5), 1 << 20, 0)
+    assert e.value.status == _abi.SARATHI_ERR_INVALID
+
+
+# ---- batches with several prefill chunks ---------------------------------------------------------
+
+def multi(chunks=((8, 0, 64), (5, 30, 64), (1, 9, 16)), lens=(17,), x=addr(0), y=addr(1), share=None,
+          n_override=None):
+    """chunks: (len, offset, capacity); chunk j's cache at addr(40 + 2j)."""
+    ch = [(n, o, addr(40 + 2 * j), addr(41 + 2 * j), cap) for j, (n, o, cap) in enumerate(chunks)]
+    if share == "chunks":
+        ch[1] = (ch[1][0], ch[1][1], ch[0][2], ch[0][3], ch[1][4])
+    dkv = [(addr(10 + 2 * i), addr(11 + 2 * i), L + 1) for i, L in enumerate(lens)]
+    if share == "chunk_decode":
+        dkv[0] = (ch[0][2], ch[0][3], dkv[0][2])
+    b, keep = _abi.make_multi_batch(ch, dkv, list(lens), x, y)
+    if n_override is not None:
+        b.n_chunks = n_override
+    return b, keep
+
+
+def test_multi_valid_batches(lib):
+    for kw in (dict(), dict(lens=()), dict(chunks=()), dict(chunks=((4, 0, 8),) * 1)):
+        b, keep = multi(**kw)
+        assert _abi.sarathi_multi_batch_check(desc(), b) == _abi.SARATHI_OK, kw
+        assert _abi.sarathi_multi_workspace_size(desc(), b) % 256 == 0
+    chunks = tuple((2, 0, 4) for _ in range(_abi.SARATHI_MAX_CHUNKS))
+    b, keep = multi(chunks=chunks, lens=())
+    assert _abi.sarathi_multi_batch_check(desc(), b) == _abi.SARATHI_OK
+
+
+def test_multi_workspace_matches_single_chunk(lib):
+    """One chunk through either entry point plans the same workspace."""
+    b1, k1 = multi(chunks=((20, 7, 64),), lens=(17, 40))
+    b2, k2 = _abi.make_batch(20, 7, (addr(40), addr(41), 64), [(addr(10), addr(11), 18), (addr(12), addr(13), 41)],
+                             [17, 40], addr(0), addr(1))
+    assert _abi.sarathi_multi_workspace_size(desc(), b1) == _abi.sarathi_workspace_size(desc(), b2) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunks=(), lens=()), _abi.SARATHI_ERR_INVALID),                       # empty batch
+    (dict(chunks=((0, 0, 8),)), _abi.SARATHI_ERR_INVALID),                      # chunk of length 0
+    (dict(chunks=((4, 6, 8),)), _abi.SARATHI_ERR_CAPACITY),                     # chunk past its capacity
+    (dict(chunks=((4, 254, 300),)), _abi.SARATHI_ERR_CAPACITY),                 # position >= max_pos
+    (dict(share="chunks"), _abi.SARATHI_ERR_INVALID),                           # two chunks share a cache
+    (dict(share="chunk_decode"), _abi.SARATHI_ERR_INVALID),                     # chunk and decode share
+    (dict(n_override=17), _abi.SARATHI_ERR_INVALID),                            # more than 16 chunks
+    (dict(n_override=-1), _abi.SARATHI_ERR_INVALID),
+    (dict(chunks=((40, 0, 64), (30, 0, 64))), _abi.SARATHI_ERR_INVALID),        # rows > max_tokens
+    (dict(y=addr(0) + 64), _abi.SARATHI_ERR_INVALID),                           # y overlaps x
+])
+def test_multi_invalid_batches(lib, kw, status):
+    b, keep = multi(**kw)
+    assert _abi.sarathi_multi_batch_check(desc(), b) == status
+    assert _abi.sarathi_last_error() != ""
+    if "y" not in kw:
+        assert _abi.sarathi_multi_workspace_size(desc(), b) == 0
+
+
+def test_multi_forward_rejects_before_any_hip_call(lib):
+    b, keep = multi(chunks=((0, 0, 8),))
+    with pytest.raises(_abi.SarathiError) as e:
+        _abi.sarathi_multi_forward(None, b, addr(5), 1 << 20, 0)
     assert e.value.status == _abi.SARATHI_ERR_INVALID

@@ -46,3 +46,23 @@ def test_full_size_workload(key):
 ])
 def test_full_size_sweep_points(key, changes):
     run_full(wl.workload(key, **changes))
+
+
+def test_full_size_token_budget_batch():
+    """The llama13b_budget workload: 18 decodes plus three chunks (the end of a partly prefilled
+    prompt, a whole short prompt, the start of a new one) in one 512-token batch."""
+    wk = wl.workload("llama13b_budget")
+    t0 = time.time()
+    gu.say(f"case full-size {wk.key} budget={wk.batch.budget} B={wk.batch.n_decodes}")
+    w, b = wl.generate(wk)
+    shape = wk.shape
+    T = b["x"].shape[0]
+    max_pos = max([c["offset"] + c["len"] for c in b["chunks"]] + [L + 1 for L in b["decode_len"]])
+    layer = hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=T, max_pos=max_pos)
+    db = gu.upload_multi(shape, b)
+    dd = gu.run_multi(layer, db)
+    gu.say(f"  gpu done at {time.time() - t0:.1f}s")
+    ref = oracle.layer_forward_multi(shape, w, b)
+    gu.say(f"  oracle done at {time.time() - t0:.1f}s")
+    gu.compare_multi(shape, b, ref, db, dd, label=f"{wk.key} full")
+    layer.close()
