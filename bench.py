@@ -37,8 +37,10 @@ METRIC = "hybrid-batch layer tokens/s (chunk+decodes); % bf16 MFMA and HBM roofl
 from chunked_prefill_hybrid_amd.profiling import kernel_source_hash  # noqa: E402
 
 
-def stage_work(shape, C, off, lens):
-    """Algorithmic work of each stage: (flops, bytes).  GEMM flops use the unpadded row count."""
+def stage_work(shape, chunks, lens):
+    """Algorithmic work of each stage: (flops, bytes).  chunks: [(len, offset)] of the batch's prefill
+    chunks.  GEMM flops use the unpadded row count."""
+    C = sum(n for n, _ in chunks)
     T = C + len(lens)
     H, A, F = shape.hidden, shape.attn_width, shape.ffn
     el = 2 if shape.dtype == "bf16" else 4
@@ -50,7 +52,9 @@ def stage_work(shape, C, off, lens):
         "ffn_down": (2.0 * T * F * H, el * (H * F + T * F + T * H) + 4 * T * H),
         # decode attention streams each decode's K and V over its L_i + 1 keys, plus its query
         "attn_decode": (4.0 * A * sum(L + 1 for L in lens), el * sum(2 * A * (L + 1) + A for L in lens)),
-        "attn_chunk": (4.0 * A * (C * off + C * (C + 1) / 2), el * (2 * A * (off + C) + 2 * C * A)),
+        # each chunk reads its request's K/V over offset + len keys once, plus its q and output rows
+        "attn_chunk": (sum(4.0 * A * (n * o + n * (n + 1) / 2) for n, o in chunks),
+                       el * sum(2 * A * (o + n) + 2 * n * A for n, o in chunks)),
         "norm1": (0.0, el * 2 * T * H),
         "norm2": (0.0, (4 + el) * T * H),
         "rope_append": (0.0, el * 2 * T * 3 * A),
@@ -105,11 +109,14 @@ def cpu_baseline(wk, weights, batch, budget_s=25.0):
         t_start = time.perf_counter()
         while True:
             t0 = time.perf_counter()
-            oracle.layer_forward(wk.shape, weights, batch)
+            if "chunks" in batch:
+                oracle.layer_forward_multi(wk.shape, weights, batch)
+            else:
+                oracle.layer_forward(wk.shape, weights, batch)
             times.append(time.perf_counter() - t0)
             if time.perf_counter() - t_start + times[-1] > budget_s or len(times) >= 3:
                 break
-    T = batch["chunk_len"] + len(batch["decode_len"])
+    T = batch["x"].shape[0]
     t = statistics.median(times)
     return {"value": round(T / t, 2), "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"full batch ({T} rows, one layer, float64 NumPy), {len(times)} run(s), median {t:.2f} s"}
@@ -143,7 +150,10 @@ def main():
     wk = wl.workload(args.workload)
     shape = wk.shape
     weights, batch = wl.generate(wk)
-    C, off, lens = batch["chunk_len"], batch["chunk_offset"], list(batch["decode_len"])
+    chunks = wl.chunks_of(batch)            # [{len, offset, k, v}]: one chunk, several, or none
+    multi = "chunks" in batch               # token-budget workloads use the several-chunk entry point
+    lens = list(batch["decode_len"])
+    C = sum(c["len"] for c in chunks)
     T = C + len(lens)
     dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
 
@@ -151,9 +161,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
 
     wdev = {k: dev(v, torch.float32 if k.startswith("norm") else dt) for k, v in weights.items() if v is not None}
-    base = {"x": dev(batch["x"]), "ck": dev(batch["chunk_k"]), "cv": dev(batch["chunk_v"]),
+    base = {"x": dev(batch["x"]), "ck": [(dev(c["k"]), dev(c["v"])) for c in chunks],
             "dk": [dev(k) for k in batch["decode_k"]], "dv": [dev(v) for v in batch["decode_v"]]}
-    max_pos = max([off + C] + [L + 1 for L in lens])
+    max_pos = max([c["offset"] + c["len"] for c in chunks] + [L + 1 for L in lens])
     reps = []
     for r in range(args.replicas):
         cl = (lambda t: t) if r == 0 else (lambda t: t.clone())
@@ -161,27 +171,39 @@ def main():
         layer = hl.HybridLayer(shape, wr, max_tokens=T, max_pos=max_pos)
         x = cl(base["x"])
         y = torch.empty_like(x)
-        ck, cv = cl(base["ck"]), cl(base["cv"])
+        ckv = [(cl(k), cl(v)) for k, v in base["ck"]]
         dkv = [(cl(k), cl(v)) for k, v in zip(base["dk"], base["dv"])]
-        b, keep = layer.batch(x, y, C, off, (ck, cv), dkv, lens)
+        if multi:
+            spec = [(c["len"], c["offset"], kv) for c, kv in zip(chunks, ckv)]
+            b, keep = layer.multi_batch(x, y, spec, dkv, lens)
+        else:
+            spec = None
+            b, keep = layer.batch(x, y, C, chunks[0]["offset"] if chunks else 0, ckv[0] if ckv else None,
+                                  dkv, lens)
         ws = torch.empty(layer.workspace_size(b), dtype=torch.uint8, device="cuda")
         sub = {}
         if C > 0 and lens:
             # the same rows split into a chunk-only and a decode-only batch (same caches, same slots)
-            sub["chunk_only"] = layer.batch(x[:C], y[:C], C, off, (ck, cv), [], [])
-            sub["decode_only"] = layer.batch(x[C:], y[C:], 0, 0, None, dkv, lens)
+            if multi:
+                sub["chunk_only"] = layer.multi_batch(x[:C], y[:C], spec, [], [])
+                sub["decode_only"] = layer.multi_batch(x[C:], y[C:], [], dkv, lens)
+            else:
+                sub["chunk_only"] = layer.batch(x[:C], y[:C], C, chunks[0]["offset"], ckv[0], [], [])
+                sub["decode_only"] = layer.batch(x[C:], y[C:], 0, 0, None, dkv, lens)
             for name, (sb, _) in sub.items():
                 assert layer.workspace_size(sb) <= ws.numel(), name
-        reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, ck, cv, dkv, wr)))
+        reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, ckv, dkv, wr)))
     stream = torch.cuda.current_stream().cuda_stream
+    fwd = _abi.sarathi_multi_forward if multi else _abi.sarathi_layer_forward
+    fwd_timed = _abi.sarathi_multi_forward_timed if multi else _abi.sarathi_layer_forward_timed
 
     def step(i, timer=None):
         r = reps[i % len(reps)]
         nb = r["ws"].numel()
         if timer:
-            _abi.sarathi_layer_forward_timed(r["layer"].handle, r["b"], r["ws"].data_ptr(), nb, stream, timer)
+            fwd_timed(r["layer"].handle, r["b"], r["ws"].data_ptr(), nb, stream, timer)
         else:
-            _abi.sarathi_layer_forward(r["layer"].handle, r["b"], r["ws"].data_ptr(), nb, stream)
+            fwd(r["layer"].handle, r["b"], r["ws"].data_ptr(), nb, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -195,7 +217,7 @@ def main():
         step(i, timer)
     stages = _abi.sarathi_timer_read(timer)
     _abi.sarathi_timer_destroy(timer)
-    work = stage_work(shape, C, off, lens)
+    work = stage_work(shape, [(c["len"], c["offset"]) for c in chunks], lens)
     breakdown = {}
     for name, (tot, cnt) in stages.items():
         if cnt == 0:
@@ -251,14 +273,12 @@ def main():
         def time_batch(name):
             for i in range(5):
                 r = reps[i % len(reps)]
-                _abi.sarathi_layer_forward(r["layer"].handle, r["sub"][name][0], r["ws"].data_ptr(),
-                                           r["ws"].numel(), stream)
+                fwd(r["layer"].handle, r["sub"][name][0], r["ws"].data_ptr(), r["ws"].numel(), stream)
             torch.cuda.synchronize()
             t_0 = time.perf_counter()
             for i in range(n_sw):
                 r = reps[i % len(reps)]
-                _abi.sarathi_layer_forward(r["layer"].handle, r["sub"][name][0], r["ws"].data_ptr(),
-                                           r["ws"].numel(), stream)
+                fwd(r["layer"].handle, r["sub"][name][0], r["ws"].data_ptr(), r["ws"].numel(), stream)
             torch.cuda.synchronize()
             return (time.perf_counter() - t_0) / n_sw * 1e6
 
@@ -277,11 +297,16 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{shape.name} layer, chunk C={C} at offset {off} + {len(lens)} decodes "
+        "config": {"workload": f"{shape.name} layer, "
+                               + (" + ".join(f"chunk {c['len']} at offset {c['offset']}" for c in chunks)
+                                  or "no chunk")
+                               + f" + {len(lens)} decodes "
                                f"(KV lengths {min(lens) if lens else 0}..{max(lens) if lens else 0})",
                    "hidden": shape.hidden, "heads": shape.n_heads, "head_dim": shape.head_dim,
-                   "ffn": shape.ffn, "chunk": C, "chunk_offset": off, "decodes": len(lens),
-                   "rows": T, "replicas": args.replicas},
+                   "ffn": shape.ffn, "chunk": C,
+                   "chunk_offset": chunks[0]["offset"] if len(chunks) == 1 else None,
+                   "chunks": [[c["len"], c["offset"]] for c in chunks],
+                   "decodes": len(lens), "rows": T, "replicas": args.replicas},
         "roofline": roof,
         "stages": breakdown,
         "summary": summary,

@@ -7,7 +7,9 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -18,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsarathi.so")
+RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.json")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -36,13 +39,29 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
+def _resources(stderr: str) -> dict:
+    """Per-kernel register, scratch and occupancy figures from the compiler's resource remarks."""
+    out, cur = {}, None
+    for line in stderr.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|TotalSGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]"
+                      r"|LDS Size \[bytes/block\]): (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).split(" ")[0]] = int(m.group(2))
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
@@ -51,7 +70,13 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        done = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in done]
+    res = {}
+    for _, r in done:
+        res.update(r)
+    with open(RESOURCES, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kUnroll = 8;
 
-template <typename T, int D>
+template <typename T, int D, bool kChunkRows>
 __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int nh, int row0,
                                                        ChunkSet cs, DecodeGroup dg, int max_splits,
                                                        float *part_o, float *part_ml, float qscale) {
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
   constexpr int NIT = KPW / KPI;
   static_assert(NIT % kUnroll == 0, "whole unrolled steps");
   const int r = row0 + blockIdx.x, s = blockIdx.y, h = blockIdx.z;
-  const RowRef rr = row_ref(r, cs, dg);
+  const RowRef rr = row_ref<kChunkRows>(r, cs, dg);
   const int n_keys = rr.pos + 1;
   const int nsp = attn_splits(n_keys);
   const size_t pidx = ((size_t)r * nh + h) * max_splits + s;
@@ -223,8 +223,12 @@ template <typename T, int D>
 hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, const ChunkSet &cs,
                      const DecodeGroup &dg, int max_splits, float *po, float *pml, hipStream_t s) {
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_rows_split<T, D>), dim3(n_rows, max_splits, nh), dim3(256), 0, s,
-                     static_cast<const T *>(q), ld_q, nh, row0, cs, dg, max_splits, po, pml, qscale);
+  if (row0 < cs.rows)
+    hipLaunchKernelGGL((attn_rows_split<T, D, true>), dim3(n_rows, max_splits, nh), dim3(256), 0, s,
+                       static_cast<const T *>(q), ld_q, nh, row0, cs, dg, max_splits, po, pml, qscale);
+  else
+    hipLaunchKernelGGL((attn_rows_split<T, D, false>), dim3(n_rows, max_splits, nh), dim3(256), 0, s,
+                       static_cast<const T *>(q), ld_q, nh, row0, cs, dg, max_splits, po, pml, qscale);
   return hipGetLastError();
 }
 

@@ -145,9 +145,11 @@ struct RowRef {
 
 // Position, cache and key count of batch row r.  The chunk table is read at constant indices only
 // (a select per entry), which keeps the argument block out of per-lane scratch memory.
+// kChunkRows = false: the launch covers decode rows only, and the chunk table is never read.
+template <bool kChunkRows = true>
 __device__ __forceinline__ RowRef row_ref(int r, const ChunkSet &cs, const DecodeGroup &dg) {
   RowRef rr;
-  if (r < cs.rows) {
+  if (kChunkRows && r < cs.rows) {
     uint64_t k = cs.k[0], v = cs.v[0];
     int cap = cs.cap[0], pos = cs.off[0] + r;
 #pragma unroll

@@ -43,7 +43,7 @@ __device__ __forceinline__ void sum4(const float *part, int splits, size_t slice
 }
 
 // grid: (rows, column blocks of 1024); one 4-element chunk of q, k and v per thread.
-template <typename T>
+template <typename T, bool kChunkRows>
 __global__ __launch_bounds__(256) void rope_append(const float *part, int splits, int rows_total,
                                                    T *q_out, int ld_q, float *qkv_dump,
                                                    const float2 *tab, int use_rope, int nh, int d,
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void rope_append(const float *part, int splits
   const int A = nh * d;
   const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= A) return;
-  const RowRef rr = row_ref(r, cs, dg);
+  const RowRef rr = row_ref<kChunkRows>(r, cs, dg);
   T *kc = reinterpret_cast<T *>(rr.k);
   T *vc = reinterpret_cast<T *>(rr.v);
   const size_t slice = (size_t)rows_total * 3 * A, src = (size_t)r * 3 * A;
@@ -94,12 +94,16 @@ hipError_t launch_rope_append(int type, const float *part, int splits, int rows_
   if (n_rows <= 0) return hipSuccess;
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(n_rows, (nh * d / 4 + 255) / 256);
-  if (type == kF32)
-    hipLaunchKernelGGL(rope_append<float>, grid, dim3(256), 0, s, part, splits, rows_total,
-                       static_cast<float *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, cs, dg);
-  else
-    hipLaunchKernelGGL(rope_append<bf16_t>, grid, dim3(256), 0, s, part, splits, rows_total,
-                       static_cast<bf16_t *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, cs, dg);
+#define SARATHI_ROPE(T, CR)                                                                            \
+  hipLaunchKernelGGL((rope_append<T, CR>), grid, dim3(256), 0, s, part, splits, rows_total,            \
+                     static_cast<T *>(q_out), ld_q, qkv_dump, tab, use_rope, nh, d, row0, cs, dg)
+  const bool chunk_rows = row0 < cs.rows;
+  if (type == kF32) {
+    if (chunk_rows) SARATHI_ROPE(float, true); else SARATHI_ROPE(float, false);
+  } else {
+    if (chunk_rows) SARATHI_ROPE(bf16_t, true); else SARATHI_ROPE(bf16_t, false);
+  }
+#undef SARATHI_ROPE
   return hipGetLastError();
 }
 

@@ -64,18 +64,25 @@ def run(argv) -> int:
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
 
     wdev = {k: dev(v, torch.float32 if k.startswith("norm") else dt) for k, v in weights.items() if v is not None}
-    C, off, lens = batch["chunk_len"], batch["chunk_offset"], list(batch["decode_len"])
-    layer = hl.HybridLayer(shape, wdev, max_tokens=C + len(lens),
-                           max_pos=max([off + C] + [L + 1 for L in lens]))
+    chunks = wl.chunks_of(batch)
+    lens = list(batch["decode_len"])
+    T = sum(c["len"] for c in chunks) + len(lens)
+    layer = hl.HybridLayer(shape, wdev, max_tokens=T,
+                           max_pos=max([c["offset"] + c["len"] for c in chunks] + [L + 1 for L in lens]))
     x = dev(batch["x"])
     y = torch.empty_like(x)
-    ckv = (dev(batch["chunk_k"]), dev(batch["chunk_v"])) if C else None
+    ckv = [(dev(c["k"]), dev(c["v"])) for c in chunks]
     dkv = [(dev(k), dev(v)) for k, v in zip(batch["decode_k"], batch["decode_v"])]
-    b, keep = layer.batch(x, y, C, off, ckv, dkv, lens)
+    if "chunks" in batch:
+        b, keep = layer.multi_batch(x, y, [(c["len"], c["offset"], kv) for c, kv in zip(chunks, ckv)], dkv, lens)
+        fwd = _abi.sarathi_multi_forward
+    else:
+        b, keep = layer.batch(x, y, batch["chunk_len"], batch["chunk_offset"], ckv[0] if ckv else None, dkv, lens)
+        fwd = _abi.sarathi_layer_forward
     ws = torch.empty(layer.workspace_size(b), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(args.warmup + args.steps):
-        _abi.sarathi_layer_forward(layer.handle, b, ws.data_ptr(), ws.numel(), stream)
+        fwd(layer.handle, b, ws.data_ptr(), ws.numel(), stream)
     torch.cuda.synchronize()
     n = args.copy_mib << 20
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
