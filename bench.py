@@ -19,6 +19,7 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -129,6 +130,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--page-size", type=int, default=None,
+                    help="lay the caches out in a page pool with this many tokens per page "
+                         "(overrides the workload's own layout; 0 = contiguous caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the chunk-only / decode-only runs behind the decode-cost comparison")
@@ -148,6 +152,8 @@ def main():
 
     torch.cuda.set_device(0)
     wk = wl.workload(args.workload)
+    if args.page_size is not None:
+        wk = dataclasses.replace(wk, page_size=args.page_size or None)
     shape = wk.shape
     weights, batch = wl.generate(wk)
     chunks = wl.chunks_of(batch)            # [{len, offset, k, v}]: one chunk, several, or none
@@ -161,8 +167,17 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
 
     wdev = {k: dev(v, torch.float32 if k.startswith("norm") else dt) for k, v in weights.items() if v is not None}
-    base = {"x": dev(batch["x"]), "ck": [(dev(c["k"]), dev(c["v"])) for c in chunks],
-            "dk": [dev(k) for k in batch["decode_k"]], "dv": [dev(v) for v in batch["decode_v"]]}
+    paged = wk.page_size is not None
+    if paged:
+        # every request's cache in one pool of fixed-size pages, in a shuffled page order
+        caches = [(c["k"], c["v"]) for c in chunks] + list(zip(batch["decode_k"], batch["decode_v"]))
+        kp, vp, tables = wl.paginate(caches, wk.page_size, seed=wk.seed + 1)
+        base = {"x": dev(batch["x"]), "pool": (dev(kp), dev(vp)),
+                "tables": [torch.from_numpy(t).to("cuda") for t in tables]}
+        del kp, vp, caches
+    else:
+        base = {"x": dev(batch["x"]), "ck": [(dev(c["k"]), dev(c["v"])) for c in chunks],
+                "dk": [dev(k) for k in batch["decode_k"]], "dv": [dev(v) for v in batch["decode_v"]]}
     max_pos = max([c["offset"] + c["len"] for c in chunks] + [L + 1 for L in lens])
     reps = []
     for r in range(args.replicas):
@@ -171,6 +186,19 @@ def main():
         layer = hl.HybridLayer(shape, wr, max_tokens=T, max_pos=max_pos)
         x = cl(base["x"])
         y = torch.empty_like(x)
+        if paged:
+            pool = (cl(base["pool"][0]), cl(base["pool"][1]))
+            tbs = [cl(t) for t in base["tables"]]
+            nc = len(chunks)
+            spec = [(c["len"], c["offset"], t) for c, t in zip(chunks, tbs)]
+            b, keep = layer.paged_batch(x, y, pool, spec, tbs[nc:], lens)
+            ws = torch.empty(layer.workspace_size(b), dtype=torch.uint8, device="cuda")
+            sub = {}
+            if C > 0 and lens:
+                sub["chunk_only"] = layer.paged_batch(x[:C], y[:C], pool, spec, [], [])
+                sub["decode_only"] = layer.paged_batch(x[C:], y[C:], pool, [], tbs[nc:], lens)
+            reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, pool, tbs, wr)))
+            continue
         ckv = [(cl(k), cl(v)) for k, v in base["ck"]]
         dkv = [(cl(k), cl(v)) for k, v in zip(base["dk"], base["dv"])]
         if multi:
@@ -194,8 +222,12 @@ def main():
                 assert layer.workspace_size(sb) <= ws.numel(), name
         reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, ckv, dkv, wr)))
     stream = torch.cuda.current_stream().cuda_stream
-    fwd = _abi.sarathi_multi_forward if multi else _abi.sarathi_layer_forward
-    fwd_timed = _abi.sarathi_multi_forward_timed if multi else _abi.sarathi_layer_forward_timed
+    if paged:
+        fwd, fwd_timed = _abi.sarathi_paged_forward, _abi.sarathi_paged_forward_timed
+    elif multi:
+        fwd, fwd_timed = _abi.sarathi_multi_forward, _abi.sarathi_multi_forward_timed
+    else:
+        fwd, fwd_timed = _abi.sarathi_layer_forward, _abi.sarathi_layer_forward_timed
 
     def step(i, timer=None):
         r = reps[i % len(reps)]
@@ -301,12 +333,14 @@ def main():
                                + (" + ".join(f"chunk {c['len']} at offset {c['offset']}" for c in chunks)
                                   or "no chunk")
                                + f" + {len(lens)} decodes "
-                               f"(KV lengths {min(lens) if lens else 0}..{max(lens) if lens else 0})",
+                               f"(KV lengths {min(lens) if lens else 0}..{max(lens) if lens else 0})"
+                               + (f", paged KV ({wk.page_size}-token pages)" if paged else ""),
                    "hidden": shape.hidden, "heads": shape.n_heads, "head_dim": shape.head_dim,
                    "ffn": shape.ffn, "chunk": C,
                    "chunk_offset": chunks[0]["offset"] if len(chunks) == 1 else None,
                    "chunks": [[c["len"], c["offset"]] for c in chunks],
-                   "decodes": len(lens), "rows": T, "replicas": args.replicas},
+                   "decodes": len(lens), "rows": T, "replicas": args.replicas,
+                   "kv_page_size": wk.page_size},
         "roofline": roof,
         "stages": breakdown,
         "summary": summary,

@@ -33,6 +33,8 @@ EXPORTED = [
     "sarathi_layer_forward_timed", "sarathi_timer_read", "sarathi_stack_workspace_size",
     "sarathi_stack_forward", "sarathi_multi_batch_check", "sarathi_multi_workspace_size",
     "sarathi_multi_forward", "sarathi_multi_forward_debug", "sarathi_multi_forward_timed",
+    "sarathi_paged_batch_check", "sarathi_paged_workspace_size", "sarathi_paged_forward",
+    "sarathi_paged_forward_debug", "sarathi_paged_forward_timed",
 ]
 
 SARATHI_MAX_CHUNKS = 16
@@ -78,6 +80,25 @@ class sarathi_multi_batch(ctypes.Structure):
     _fields_ = [("n_chunks", c_int32), ("reserved", c_int32), ("chunks", POINTER(sarathi_chunk)),
                 ("n_decodes", c_int32), ("reserved2", c_int32), ("decode_kv", POINTER(sarathi_kv)),
                 ("decode_len", POINTER(c_int32)), ("x", c_void_p), ("y", c_void_p)]
+
+
+class sarathi_page_pool(ctypes.Structure):
+    _fields_ = [("k_pool", c_void_p), ("v_pool", c_void_p), ("n_pages", c_int32), ("page_size", c_int32)]
+
+
+class sarathi_page_table(ctypes.Structure):
+    _fields_ = [("pages", c_void_p), ("n_entries", c_int32), ("reserved", c_int32)]
+
+
+class sarathi_paged_chunk(ctypes.Structure):
+    _fields_ = [("len", c_int32), ("offset", c_int32), ("table", sarathi_page_table)]
+
+
+class sarathi_paged_batch(ctypes.Structure):
+    _fields_ = [("pool", sarathi_page_pool), ("n_chunks", c_int32), ("reserved", c_int32),
+                ("chunks", POINTER(sarathi_paged_chunk)), ("n_decodes", c_int32), ("reserved2", c_int32),
+                ("decode_tables", POINTER(sarathi_page_table)), ("decode_len", POINTER(c_int32)),
+                ("x", c_void_p), ("y", c_void_p)]
 
 
 class sarathi_debug_dump(ctypes.Structure):
@@ -146,6 +167,18 @@ def lib():
         L.sarathi_multi_forward_debug.restype = c_int32
         L.sarathi_multi_forward_timed.argtypes = [c_void_p, MB, c_void_p, c_size_t, c_void_p, c_void_p]
         L.sarathi_multi_forward_timed.restype = c_int32
+        PB = POINTER(sarathi_paged_batch)
+        L.sarathi_paged_batch_check.argtypes = [POINTER(sarathi_layer_desc), PB]
+        L.sarathi_paged_batch_check.restype = c_int32
+        L.sarathi_paged_workspace_size.argtypes = [POINTER(sarathi_layer_desc), PB]
+        L.sarathi_paged_workspace_size.restype = c_size_t
+        L.sarathi_paged_forward.argtypes = [c_void_p, PB, c_void_p, c_size_t, c_void_p]
+        L.sarathi_paged_forward.restype = c_int32
+        L.sarathi_paged_forward_debug.argtypes = [c_void_p, PB, c_void_p, c_size_t, c_void_p,
+                                                  POINTER(sarathi_debug_dump)]
+        L.sarathi_paged_forward_debug.restype = c_int32
+        L.sarathi_paged_forward_timed.argtypes = [c_void_p, PB, c_void_p, c_size_t, c_void_p, c_void_p]
+        L.sarathi_paged_forward_timed.restype = c_int32
         L.sarathi_status_str.argtypes = [c_int32]
         L.sarathi_status_str.restype = c_char_p
         L.sarathi_last_error.argtypes = []
@@ -333,3 +366,48 @@ def make_multi_batch(chunks, decode_kv, decode_len, x: int, y: int):
                             ctypes.cast(kv_arr, POINTER(sarathi_kv)) if B else None,
                             ctypes.cast(len_arr, POINTER(c_int32)), x or 0, y or 0)
     return b, (ch_arr, kv_arr, len_arr)
+
+
+def sarathi_paged_batch_check(desc: sarathi_layer_desc, batch: sarathi_paged_batch) -> int:
+    return lib().sarathi_paged_batch_check(byref(desc), byref(batch))
+
+
+def sarathi_paged_workspace_size(desc: sarathi_layer_desc, batch: sarathi_paged_batch) -> int:
+    return lib().sarathi_paged_workspace_size(byref(desc), byref(batch))
+
+
+def sarathi_paged_forward(handle: int, batch: sarathi_paged_batch, ws: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().sarathi_paged_forward(handle, byref(batch), ws, ws_bytes, stream), "sarathi_paged_forward")
+
+
+def sarathi_paged_forward_debug(handle: int, batch: sarathi_paged_batch, ws: int, ws_bytes: int, stream: int,
+                                dump: sarathi_debug_dump) -> None:
+    _check(lib().sarathi_paged_forward_debug(handle, byref(batch), ws, ws_bytes, stream, byref(dump)),
+           "sarathi_paged_forward_debug")
+
+
+def sarathi_paged_forward_timed(handle: int, batch: sarathi_paged_batch, ws: int, ws_bytes: int, stream: int,
+                                timer: int) -> None:
+    _check(lib().sarathi_paged_forward_timed(handle, byref(batch), ws, ws_bytes, stream, timer),
+           "sarathi_paged_forward_timed")
+
+
+def make_paged_batch(pool, chunks, decode_tables, decode_len, x: int, y: int):
+    """Build a sarathi_paged_batch.  pool: (k_pool_ptr, v_pool_ptr, n_pages, page_size); chunks: list
+    of (len, offset, table_ptr, n_entries); decode_tables: list of (table_ptr, n_entries); decode_len:
+    list of ints.  Returns (batch, keepalive) as make_batch."""
+    n = len(chunks)
+    ch_arr = (sarathi_paged_chunk * max(n, 1))()
+    for j, (ln, off, tp, ne) in enumerate(chunks):
+        ch_arr[j] = sarathi_paged_chunk(int(ln), int(off), sarathi_page_table(tp, int(ne), 0))
+    B = len(decode_len)
+    tb_arr = (sarathi_page_table * max(B, 1))()
+    len_arr = (c_int32 * max(B, 1))()
+    for i, ((tp, ne), L) in enumerate(zip(decode_tables, decode_len)):
+        tb_arr[i] = sarathi_page_table(tp, int(ne), 0)
+        len_arr[i] = int(L)
+    b = sarathi_paged_batch(sarathi_page_pool(pool[0], pool[1], int(pool[2]), int(pool[3])), n, 0,
+                            ctypes.cast(ch_arr, POINTER(sarathi_paged_chunk)) if n else None, B, 0,
+                            ctypes.cast(tb_arr, POINTER(sarathi_page_table)) if B else None,
+                            ctypes.cast(len_arr, POINTER(c_int32)), x or 0, y or 0)
+    return b, (ch_arr, tb_arr, len_arr)

@@ -26,6 +26,10 @@
 // The key range of each 64-query block can be split over several workgroups so that short chunks
 // still fill the GPU; a split writes (m, l, unnormalised O) partials for attn_combine.
 //
+// Paged KV caches (a pool of fixed-size pages per layer and a block table per request) change only
+// the DMA source addresses: each lane's key row is looked up in the chunk's block table, one tile
+// ahead of its loads.
+//
 // One launch serves every prefill chunk of the batch.  A batch may carry several partial prefills of
 // different requests next to its decodes, as in token-budget ("stall-free") batching (junupark.xyz
 // notes on Sarathi-Serve, "Stall Free Batching"); each chunk attends only to its own request's cache,
@@ -70,9 +74,9 @@ template <int D> __device__ __forceinline__ int v_slot(int r, int c) {
   return D == 128 ? c ^ ((r & 7) << 1) : c;
 }
 
-template <int D>
+template <int D, bool kPaged>
 __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q, int nh,
-                                                       ChunkSet cs, bf16_t *out, int ld_out,
+                                                       ChunkSet cs, PagePool pool, bf16_t *out, int ld_out,
                                                        float qscale_log2, int n_split, int stride,
                                                        float *part_o, float *part_ml, int per_xcd) {
   using G = TileGeom<D>;
@@ -110,8 +114,13 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
   const int nt = (n_keys + kBKV - 1) / kBKV;
   const int t_begin = (int)((long long)split * nt / n_split);
   const int t_end = (int)((long long)(split + 1) * nt / n_split);
-  const bf16_t *Kh = reinterpret_cast<const bf16_t *>(cs.k[cj]) + (size_t)h * cap * D;
-  const bf16_t *Vh = reinterpret_cast<const bf16_t *>(cs.v[cj]) + (size_t)h * cap * D;
+  // Contiguous caches: this head's [cap, D] slab.  Paged caches: the pools, addressed per key row
+  // through the chunk's block table.
+  const bf16_t *Kh = kPaged ? reinterpret_cast<const bf16_t *>(pool.k)
+                            : reinterpret_cast<const bf16_t *>(cs.k[cj]) + (size_t)h * cap * D;
+  const bf16_t *Vh = kPaged ? reinterpret_cast<const bf16_t *>(pool.v)
+                            : reinterpret_cast<const bf16_t *>(cs.v[cj]) + (size_t)h * cap * D;
+  const int32_t *table = reinterpret_cast<const int32_t *>(cs.k[cj]);
 
   // This lane's query (row of the wave's 16) and its fragments of q (B operand of S^T = K Q^T).
   const int my_q = q_first + wave * 16 + c16;
@@ -134,15 +143,27 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
     kc[i] = k_slot<D>(r, sl);   // the slot permutation is an involution
     vc[i] = v_slot<D>(r, sl);
   }
+  // Paged caches: pool pages of the rows this lane loads for a tile.  They are fetched one tile ahead
+  // (pages_of for the next tile is issued right after the current tile's DMA), so the table's latency
+  // hides behind a tile of work.
+  int pg_next[G::kLoadsPerWave] = {};
+  auto pages_of = [&](int t) {
+    if (!kPaged) return;
+    const int k0 = min(t, t_end - 1) * kBKV;
+#pragma unroll
+    for (int i = 0; i < G::kLoadsPerWave; ++i)
+      pg_next[i] = pool_page(table, min(k0 + lr[i], n_keys - 1) >> pool.shift, pool.n_pages);
+  };
   // Tile t (clamped to the split's last tile, so every step issues the same loads) into stage u.
   auto issue = [&](int u, int t) {
     const int k0 = min(t, t_end - 1) * kBKV;
 #pragma unroll
     for (int i = 0; i < G::kLoadsPerWave; ++i) {
-      const size_t key = (size_t)min(k0 + lr[i], n_keys - 1);
+      const int key = min(k0 + lr[i], n_keys - 1);
+      const size_t ro = kPaged ? paged_off(pg_next[i], h, key, nh, pool.shift, D) : (size_t)key * D;
       const int dst = G::kRPL * (wave + 4 * i) * D;
-      dma16(Kh + key * D + kc[i] * 8, kst(u) + dst);
-      dma16(Vh + key * D + vc[i] * 8, vst(u) + dst);
+      dma16(Kh + ro + kc[i] * 8, kst(u) + dst);
+      dma16(Vh + ro + vc[i] * 8, vst(u) + dst);
     }
   };
 
@@ -240,12 +261,17 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
     constexpr int kNSt = kChunkStages;
     auto step = [&](int u, int t) {
       issue((u + kNSt - 1) % kNSt, t + kNSt - 1);
+      pages_of(t + kNSt);
       compute(u, t);
       wait_vm_lgkm0<(kNSt - 2) * kL>();   // this wave's loads of tile t + 1 have landed
       stage_barrier();                    // ... and everyone's; stage u is free again
     };
 #pragma unroll
-    for (int u = 0; u < kNSt - 1; ++u) issue(u, t_begin + u);
+    for (int u = 0; u < kNSt - 1; ++u) {
+      pages_of(t_begin + u);
+      issue(u, t_begin + u);
+    }
+    pages_of(t_begin + kNSt - 1);
     wait_vm_lgkm0<(kNSt - 2) * kL>();
     stage_barrier();
     int t0 = t_begin;
@@ -288,15 +314,20 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q
 }
 
 template <int D>
-hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkSet &cs, void *out, int ld_out,
-                     int n_split, int stride, float *part_o, float *part_ml, hipStream_t s) {
+hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkSet &cs, const PagePool &pool, void *out,
+                     int ld_out, int n_split, int stride, float *part_o, float *part_ml, hipStream_t s) {
   int items = 0;
   for (int j = 0; j < cs.n; ++j) items += (cs.len[j] + kBQ - 1) / kBQ * n_split * nh;
   const int per_xcd = (items + 7) / 8;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(attn_chunk_mfma<D>, dim3(8 * per_xcd), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(q), ld_q, nh, cs, static_cast<bf16_t *>(out), ld_out,
-                     qscale, n_split, stride, part_o, part_ml, per_xcd);
+  if (pool.k)
+    hipLaunchKernelGGL((attn_chunk_mfma<D, true>), dim3(8 * per_xcd), dim3(256), 0, s,
+                       static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out),
+                       ld_out, qscale, n_split, stride, part_o, part_ml, per_xcd);
+  else
+    hipLaunchKernelGGL((attn_chunk_mfma<D, false>), dim3(8 * per_xcd), dim3(256), 0, s,
+                       static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out),
+                       ld_out, qscale, n_split, stride, part_o, part_ml, per_xcd);
   return hipGetLastError();
 }
 
@@ -320,15 +351,15 @@ int chunk_attn_splits(const ChunkSet &cs, int nh) {
   return max(1, min(min(want, kMaxChunkSplits), min(by_length, first_tiles)));
 }
 
-hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs, void *out,
-                             int ld_out, int n_split, int stride, float *part_o, float *part_ml,
-                             hipStream_t s) {
+hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
+                             const PagePool &pool, void *out, int ld_out, int n_split, int stride,
+                             float *part_o, float *part_ml, hipStream_t s) {
   if (cs.n <= 0 || cs.rows <= 0) return hipSuccess;
   if (cs.n > kMaxChunks) return hipErrorInvalidValue;
   if (n_split < 1 || n_split > stride || (n_split > 1 && (!part_o || !part_ml)))
     return hipErrorInvalidValue;
-  if (d == 128) return run_chunk<128>(q, ld_q, nh, cs, out, ld_out, n_split, stride, part_o, part_ml, s);
-  if (d == 64) return run_chunk<64>(q, ld_q, nh, cs, out, ld_out, n_split, stride, part_o, part_ml, s);
+  if (d == 128) return run_chunk<128>(q, ld_q, nh, cs, pool, out, ld_out, n_split, stride, part_o, part_ml, s);
+  if (d == 64) return run_chunk<64>(q, ld_q, nh, cs, pool, out, ld_out, n_split, stride, part_o, part_ml, s);
   return hipErrorInvalidValue;
 }
 

@@ -13,6 +13,9 @@
 // 4 bf16 keys of d=128 (1 KiB).  Each wave streams its keys in steps of 8 loads of K and 8 of V per
 // lane (an online softmax across steps), the four waves of a workgroup merge through LDS, and each
 // workgroup writes one split partial (max m and sum l in the log2 domain, unnormalised output).
+// With a paged cache a key row is located through the request's block table (one table entry per
+// page, held in a lane of the wave and shuffled to the lanes reading that page); a page's
+// [page_size, d] slab per head is contiguous, so each 16-byte load stays a full-row read.
 #include <math.h>
 
 #include "kernels.h"
@@ -22,9 +25,10 @@ namespace {
 
 constexpr int kUnroll = 8;
 
-template <typename T, int D, bool kChunkRows>
+template <typename T, int D, bool kChunkRows, bool kPaged>
 __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int nh, int row0,
-                                                       ChunkSet cs, DecodeGroup dg, int max_splits,
+                                                       ChunkSet cs, DecodeGroup dg, PagePool pool,
+                                                       int max_splits,
                                                        float *part_o, float *part_ml, float qscale) {
   constexpr int E = Packet<T>::E;      // elements per 16-byte packet
   constexpr int LPK = D / E;           // lanes per key row
@@ -53,9 +57,24 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
   unpack<T>(ld16(q + (size_t)r * ld_q + h * D + sub * E), qv);
 #pragma unroll
   for (int e = 0; e < E; ++e) qv[e] *= qscale;
-  const T *Kh = reinterpret_cast<const T *>(rr.k) + (size_t)h * rr.cap * D + sub * E;
-  const T *Vh = reinterpret_cast<const T *>(rr.v) + (size_t)h * rr.cap * D + sub * E;
+  const T *Kh = kPaged ? reinterpret_cast<const T *>(pool.k) + sub * E
+                      : reinterpret_cast<const T *>(rr.k) + (size_t)h * rr.cap * D + sub * E;
+  const T *Vh = kPaged ? reinterpret_cast<const T *>(pool.v) + sub * E
+                      : reinterpret_cast<const T *>(rr.v) + (size_t)h * rr.cap * D + sub * E;
   const int wbeg = k_begin + wave * KPW;
+  // Paged caches: lane i holds the pool page of the wave's i-th page (its keys wbeg .. wbeg + KPW - 1
+  // span at most KPW / page_size + 1 pages); a key's page is then one lane shuffle away.
+  int tbl = 0, pg0 = 0;
+  if (kPaged) {
+    pg0 = wbeg >> pool.shift;
+    const int n_ent = rr.cap >> pool.shift;
+    tbl = pool_page(reinterpret_cast<const int32_t *>(rr.k), min(pg0 + lane, n_ent - 1), pool.n_pages);
+  }
+  auto key_off = [&](int j) -> size_t {
+    if (!kPaged) return (size_t)j * D;
+    const int page = __shfl(tbl, min((j >> pool.shift) - pg0, kWave - 1), kWave);
+    return paged_off(page, h, j, nh, pool.shift, D);
+  };
 
   float m_run = -INFINITY, l_run = 0.f, o[E];
 #pragma unroll
@@ -65,17 +84,17 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
     if (wbeg + c0 * KPI >= k_end) break;
     uint4 kr[kUnroll], vr[kUnroll];
     bool ok[kUnroll];
+    size_t ko[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int j = wbeg + (c0 + u) * KPI + grp;
       ok[u] = j < k_end;
-      kr[u] = ok[u] ? ld16_stream(Kh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
+      ko[u] = key_off(j);
+      kr[u] = ok[u] ? ld16_stream(Kh + ko[u]) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int j = wbeg + (c0 + u) * KPI + grp;
-      vr[u] = ok[u] ? ld16_stream(Vh + (size_t)j * D) : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      vr[u] = ok[u] ? ld16_stream(Vh + ko[u]) : make_uint4(0, 0, 0, 0);
     float sc[kUnroll];
     float cmax = -INFINITY;
 #pragma unroll
@@ -221,14 +240,20 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
 
 template <typename T, int D>
 hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, const ChunkSet &cs,
-                     const DecodeGroup &dg, int max_splits, float *po, float *pml, hipStream_t s) {
+                     const DecodeGroup &dg, const PagePool &pool, int max_splits, float *po, float *pml,
+                     hipStream_t s) {
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  if (row0 < cs.rows)
-    hipLaunchKernelGGL((attn_rows_split<T, D, true>), dim3(n_rows, max_splits, nh), dim3(256), 0, s,
-                       static_cast<const T *>(q), ld_q, nh, row0, cs, dg, max_splits, po, pml, qscale);
-  else
-    hipLaunchKernelGGL((attn_rows_split<T, D, false>), dim3(n_rows, max_splits, nh), dim3(256), 0, s,
-                       static_cast<const T *>(q), ld_q, nh, row0, cs, dg, max_splits, po, pml, qscale);
+  const dim3 grid(n_rows, max_splits, nh);
+#define SARATHI_SPLIT(CR, PG)                                                                   \
+  hipLaunchKernelGGL((attn_rows_split<T, D, CR, PG>), grid, dim3(256), 0, s,                   \
+                     static_cast<const T *>(q), ld_q, nh, row0, cs, dg, pool, max_splits, po, pml, qscale)
+  const bool chunk_rows = row0 < cs.rows, paged = pool.k != 0;
+  if (chunk_rows) {
+    if (paged) SARATHI_SPLIT(true, true); else SARATHI_SPLIT(true, false);
+  } else {
+    if (paged) SARATHI_SPLIT(false, true); else SARATHI_SPLIT(false, false);
+  }
+#undef SARATHI_SPLIT
   return hipGetLastError();
 }
 
@@ -245,13 +270,13 @@ hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, int chunk_r
 }  // namespace
 
 hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
-                            const ChunkSet &cs, const DecodeGroup &dg, int max_splits,
-                            float *part_o, float *part_ml, hipStream_t s) {
+                            const ChunkSet &cs, const DecodeGroup &dg, const PagePool &pool,
+                            int max_splits, float *part_o, float *part_ml, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (type == kF32 && d == 64) return run_split<float, 64>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
-  if (type == kF32 && d == 128) return run_split<float, 128>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
-  if (type == kBF16 && d == 64) return run_split<bf16_t, 64>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
-  if (type == kBF16 && d == 128) return run_split<bf16_t, 128>(q, ld_q, nh, row0, n_rows, cs, dg, max_splits, part_o, part_ml, s);
+  if (type == kF32 && d == 64) return run_split<float, 64>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
+  if (type == kF32 && d == 128) return run_split<float, 128>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
+  if (type == kBF16 && d == 64) return run_split<bf16_t, 64>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
+  if (type == kBF16 && d == 128) return run_split<bf16_t, 128>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
   return hipErrorInvalidValue;
 }
 

@@ -72,12 +72,21 @@ __device__ __forceinline__ void st16(void *p, const uint4 &v) { *reinterpret_cas
 __device__ __forceinline__ void dma16(const bf16_t *src, bf16_t *lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
+// Global-memory view of a pointer.  Request descriptors carry cache pointers as integers, so the
+// compiler cannot tell which memory they point to and would emit flat_* accesses through them; a
+// flat access also counts against the LDS wait counter and checks the address space per lane.
+// Accesses through this view compile to global_* instructions.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *as_global(T *p) {
+  return (__attribute__((address_space(1))) T *)p;
+}
+
 // 16-byte load of data read once per forward (KV caches in decode attention): non-temporal, which
 // streams from HBM measurably faster (6.3 vs 5.6 TB/s in a plain read) than loads that allocate in
 // the caches.
 __device__ __forceinline__ uint4 ld16_stream(const void *p) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  const u32x4 v = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x4 *>(p)));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -136,6 +145,27 @@ struct DecodeGroup {
   int32_t cap[kMaxDecodesPerLaunch];
   int32_t n, base;                      // decodes base .. base+n-1 of the batch
 };
+
+// Paged KV caches: every request's K (and V) rows live in fixed-size pages of one pool per layer,
+// each pool [n_pages, nh, page_size, d] (a (page, head) slab of page_size rows is contiguous), and the
+// request's block table maps its logical page i (tokens i*page_size ...) to a pool page.  With a pool,
+// the k field of a request descriptor holds its block table (device int32 [cap / page_size]) and cap
+// is the request's capacity in tokens.  Table entries are clamped into [0, n_pages) before use, so a
+// bad entry can give wrong values but never an access outside the pool.
+struct PagePool {
+  uint64_t k, v;        // device pools (0: the requests use contiguous caches)
+  int32_t n_pages;
+  int32_t shift;        // page_size = 1 << shift
+};
+
+__device__ __forceinline__ int pool_page(const int32_t *table, int entry, int n_pages) {
+  return min(max(as_global(table)[entry], 0), n_pages - 1);
+}
+
+// Element offset of (head h, key j) in a paged pool, given key j's pool page.
+__device__ __forceinline__ size_t paged_off(int page, int h, int j, int nh, int shift, int d) {
+  return (((size_t)page * nh + h) << shift | (size_t)(j & ((1 << shift) - 1))) * d;
+}
 
 // Position, cache and key count of batch row r (keys 0..pos are attended; pos is the write slot).
 struct RowRef {

@@ -69,12 +69,12 @@ hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, 
 // RoPE + KV append: for rows [row0, row0+n_rows) of the batch, sums the QKV GEMM's split partials
 // (float32 [splits][rows_total][3A]), rotates q and k at the row's position (if use_rope) with the
 // float32 cos/sin table tab[pos * d/2 + j], writes q to q_out (storage, row stride ld_q) and k, v
-// into the row's caches at slot pos.  If qkv_dump is non-null it receives the summed, unrotated
+// into the row's caches at slot pos (with a page pool: into the pool page of the row's block table).  If qkv_dump is non-null it receives the summed, unrotated
 // q|k|v row (float32 [rows, 3A]).
 hipError_t launch_rope_append(int type, const float *part, int splits, int rows_total, void *q_out,
                               int ld_q, float *qkv_dump, const float2 *tab, int use_rope, int nh,
                               int d, int row0, int n_rows, const ChunkSet &cs, const DecodeGroup &dg,
-                              hipStream_t s);
+                              const PagePool &pool, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Split-KV single-query attention for rows [row0, row0+n_rows): each (row, head) attends over keys
@@ -86,8 +86,8 @@ __host__ __device__ inline int attn_splits(int n_keys) {
   return (n_keys + kAttnSplit - 1) / kAttnSplit;
 }
 hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
-                            const ChunkSet &cs, const DecodeGroup &dg, int max_splits,
-                            float *part_o, float *part_ml, hipStream_t s);
+                            const ChunkSet &cs, const DecodeGroup &dg, const PagePool &pool,
+                            int max_splits, float *part_o, float *part_ml, hipStream_t s);
 
 // Merges the split partials of rows [row0, row0+n_rows) into out[row, h*d + e] (storage type,
 // row stride ld_out).  Partials sit at ((row * nh + h) * max_splits + s); rows below chunk_rows
@@ -105,9 +105,9 @@ constexpr int kChunkTargetWorkgroups = 512;   // two workgroups per compute unit
 constexpr int kMinSplitTiles = 16;            // a split keeps at least 16 key tiles
 constexpr int kMaxChunkSplits = 16;
 int chunk_attn_splits(const ChunkSet &cs, int nh);
-hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs, void *out,
-                             int ld_out, int n_split, int stride, float *part_o, float *part_ml,
-                             hipStream_t s);
+hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
+                             const PagePool &pool, void *out, int ld_out, int n_split, int stride,
+                             float *part_o, float *part_ml, hipStream_t s);
 
 // Zero-fill rows [row0, row1) of a [*, cols] storage matrix (row stride ld).
 hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int row1, hipStream_t s);

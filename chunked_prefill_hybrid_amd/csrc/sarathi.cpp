@@ -94,6 +94,8 @@ struct Range {
 
 // The batch as the forward sees it, whichever entry point passed it: prefill chunks (rows first, in
 // order), then decodes.
+// With a page pool (paged == true), a chunk's kv.k holds its block table, kv.v is null and
+// kv.capacity is the table's token capacity; the decodes' tables are in decode_tables.
 struct BatchView {
   int n_chunks;
   sarathi_chunk chunks[kMaxChunks];
@@ -103,7 +105,17 @@ struct BatchView {
   const int32_t *decode_len;
   const void *x;
   void *y;
+  bool paged;
+  sarathi_page_pool pool;
+  int page_shift;
+  const sarathi_page_table *decode_tables;
 };
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return (1 << s) == v ? s : -1;
+}
 
 // Shape fields of a one-chunk batch; the rest is checked on the view.
 sarathi_status view_batch(const sarathi_batch *b, BatchView *v) {
@@ -111,6 +123,8 @@ sarathi_status view_batch(const sarathi_batch *b, BatchView *v) {
   if (b->chunk_len < 0 || b->n_decodes < 0)
     return fail(SARATHI_ERR_INVALID, "chunk_len and n_decodes must be >= 0");
   if (b->reserved != 0) return fail(SARATHI_ERR_INVALID, "batch.reserved must be 0");
+  v->paged = false;
+  v->decode_tables = nullptr;
   v->n_chunks = b->chunk_len > 0 ? 1 : 0;
   if (v->n_chunks) {
     v->chunks[0].len = b->chunk_len;
@@ -133,6 +147,8 @@ sarathi_status view_multi(const sarathi_multi_batch *b, BatchView *v) {
   if (b->n_decodes < 0) return fail(SARATHI_ERR_INVALID, "n_decodes must be >= 0");
   if (b->reserved != 0 || b->reserved2 != 0) return fail(SARATHI_ERR_INVALID, "reserved fields must be 0");
   if (b->n_chunks > 0 && !b->chunks) return fail(SARATHI_ERR_INVALID, "chunks is null");
+  v->paged = false;
+  v->decode_tables = nullptr;
   v->n_chunks = b->n_chunks;
   long long rows = 0;
   for (int j = 0; j < b->n_chunks; ++j) {
@@ -144,6 +160,64 @@ sarathi_status view_multi(const sarathi_multi_batch *b, BatchView *v) {
   v->C = (int)rows;
   v->B = b->n_decodes;
   v->decode_kv = b->decode_kv;
+  v->decode_len = b->decode_len;
+  v->x = b->x;
+  v->y = b->y;
+  return SARATHI_OK;
+}
+
+sarathi_status view_paged(const sarathi_paged_batch *b, BatchView *v) {
+  if (!b) return fail(SARATHI_ERR_INVALID, "batch is null");
+  if (b->n_chunks < 0 || b->n_chunks > kMaxChunks)
+    return fail(SARATHI_ERR_INVALID, "n_chunks %d outside [0, %d]", b->n_chunks, kMaxChunks);
+  if (b->n_decodes < 0) return fail(SARATHI_ERR_INVALID, "n_decodes must be >= 0");
+  if (b->reserved != 0 || b->reserved2 != 0) return fail(SARATHI_ERR_INVALID, "reserved fields must be 0");
+  if (b->n_chunks > 0 && !b->chunks) return fail(SARATHI_ERR_INVALID, "chunks is null");
+  const sarathi_page_pool &pl = b->pool;
+  if (!pl.k_pool || !pl.v_pool) return fail(SARATHI_ERR_INVALID, "page pool pointers are null");
+  if (pl.n_pages < 1) return fail(SARATHI_ERR_INVALID, "page pool has no pages");
+  const int shift = log2_exact(pl.page_size);
+  if (pl.page_size < 1 || pl.page_size > 65536 || shift < 0)
+    return fail(SARATHI_ERR_INVALID, "page_size %d is not a power of two in [1, 65536]", pl.page_size);
+  v->paged = true;
+  v->pool = pl;
+  v->page_shift = shift;
+  auto table_cap = [&](const sarathi_page_table &t, const char *what, int idx, int *cap) {
+    if (!t.pages) return fail(SARATHI_ERR_INVALID, "%s %d: block table is null", what, idx);
+    if (t.reserved != 0) return fail(SARATHI_ERR_INVALID, "%s %d: table.reserved must be 0", what, idx);
+    if (t.n_entries < 1 || (long long)t.n_entries << shift > (1ll << 30))
+      return fail(SARATHI_ERR_INVALID, "%s %d: block table size %d out of range", what, idx, t.n_entries);
+    *cap = t.n_entries << shift;
+    return SARATHI_OK;
+  };
+  v->n_chunks = b->n_chunks;
+  long long rows = 0;
+  for (int j = 0; j < b->n_chunks; ++j) {
+    const sarathi_paged_chunk &c = b->chunks[j];
+    if (c.len < 1) return fail(SARATHI_ERR_INVALID, "chunk %d has len %d < 1", j, c.len);
+    int cap = 0;
+    const sarathi_status st = table_cap(c.table, "chunk", j, &cap);
+    if (st != SARATHI_OK) return st;
+    v->chunks[j].len = c.len;
+    v->chunks[j].offset = c.offset;
+    v->chunks[j].kv.k = const_cast<int32_t *>(c.table.pages);
+    v->chunks[j].kv.v = nullptr;
+    v->chunks[j].kv.capacity = cap;
+    v->chunks[j].kv.reserved = 0;
+    rows += c.len;
+  }
+  if (b->n_decodes > 0 && (!b->decode_tables || !b->decode_len))
+    return fail(SARATHI_ERR_INVALID, "decode_tables and decode_len must be non-null when n_decodes > 0");
+  for (int i = 0; i < b->n_decodes; ++i) {
+    int cap = 0;
+    const sarathi_status st = table_cap(b->decode_tables[i], "decode", i, &cap);
+    if (st != SARATHI_OK) return st;
+  }
+  if (rows > (1 << 30)) return fail(SARATHI_ERR_INVALID, "too many chunk rows");
+  v->C = (int)rows;
+  v->B = b->n_decodes;
+  v->decode_kv = nullptr;
+  v->decode_tables = b->decode_tables;
   v->decode_len = b->decode_len;
   v->x = b->x;
   v->y = b->y;
@@ -162,11 +236,14 @@ sarathi_status check_view(const sarathi_layer_desc *d, const BatchView &b, bool 
   const size_t el = elem_size(d->dtype);
   const size_t per_slot = (size_t)d->n_heads * d->head_dim * el;
   std::vector<Range> ranges;
+  std::vector<uintptr_t> tables;   // paged: every request's block table, to reject shared ones
   for (int j = 0; j < b.n_chunks; ++j) {
     const sarathi_chunk &c = b.chunks[j];
     const sarathi_kv &kv = c.kv;
-    if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "chunk %d cache pointers are null", j);
-    if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "chunk %d kv.reserved must be 0", j);
+    if (!b.paged) {
+      if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "chunk %d cache pointers are null", j);
+      if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "chunk %d kv.reserved must be 0", j);
+    }
     if (c.offset < 0) return fail(SARATHI_ERR_INVALID, "chunk %d offset must be >= 0", j);
     if (kv.capacity <= 0 || (long long)c.offset + c.len > kv.capacity)
       return fail(SARATHI_ERR_CAPACITY, "chunk %d: offset %d + len %d exceeds cache capacity %d", j,
@@ -174,26 +251,45 @@ sarathi_status check_view(const sarathi_layer_desc *d, const BatchView &b, bool 
     if ((long long)c.offset + c.len > d->max_pos)
       return fail(SARATHI_ERR_CAPACITY, "chunk %d positions reach %lld >= max_pos %d", j,
                   (long long)c.offset + c.len - 1, d->max_pos);
-    ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "chunk K", j});
-    ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "chunk V", j});
+    if (b.paged) {
+      tables.push_back((uintptr_t)kv.k);
+    } else {
+      ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "chunk K", j});
+      ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "chunk V", j});
+    }
   }
   if (B > 0) {
-    if (!b.decode_kv || !b.decode_len)
+    if ((!b.paged && !b.decode_kv) || !b.decode_len)
       return fail(SARATHI_ERR_INVALID, "decode_kv and decode_len must be non-null when n_decodes > 0");
     for (int i = 0; i < B; ++i) {
-      const sarathi_kv &kv = b.decode_kv[i];
       const int L = b.decode_len[i];
-      if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "decode %d cache pointers are null", i);
-      if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "decode_kv[%d].reserved must be 0", i);
+      int cap;
+      if (b.paged) {
+        cap = b.decode_tables[i].n_entries << b.page_shift;
+        tables.push_back((uintptr_t)b.decode_tables[i].pages);
+      } else {
+        const sarathi_kv &kv = b.decode_kv[i];
+        if (!kv.k || !kv.v) return fail(SARATHI_ERR_INVALID, "decode %d cache pointers are null", i);
+        if (kv.reserved != 0) return fail(SARATHI_ERR_INVALID, "decode_kv[%d].reserved must be 0", i);
+        cap = kv.capacity;
+        ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "decode K", i});
+        ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "decode V", i});
+      }
       if (L < 0) return fail(SARATHI_ERR_INVALID, "decode_len[%d] = %d < 0", i, L);
-      if ((long long)L + 1 > kv.capacity)
-        return fail(SARATHI_ERR_CAPACITY, "decode %d: slot %d does not fit capacity %d", i, L,
-                    kv.capacity);
+      if ((long long)L + 1 > cap)
+        return fail(SARATHI_ERR_CAPACITY, "decode %d: slot %d does not fit capacity %d", i, L, cap);
       if (L >= d->max_pos)
         return fail(SARATHI_ERR_CAPACITY, "decode %d: position %d >= max_pos %d", i, L, d->max_pos);
-      ranges.push_back({(uintptr_t)kv.k, (uintptr_t)kv.k + per_slot * kv.capacity, "decode K", i});
-      ranges.push_back({(uintptr_t)kv.v, (uintptr_t)kv.v + per_slot * kv.capacity, "decode V", i});
     }
+  }
+  if (b.paged) {
+    std::sort(tables.begin(), tables.end());
+    for (size_t i = 1; i < tables.size(); ++i)
+      if (tables[i] == tables[i - 1])
+        return fail(SARATHI_ERR_INVALID, "two requests share one block table");
+    const size_t pool_bytes = (size_t)b.pool.n_pages * d->n_heads * b.pool.page_size * d->head_dim * el;
+    ranges.push_back({(uintptr_t)b.pool.k_pool, (uintptr_t)b.pool.k_pool + pool_bytes, "K pool", -1});
+    ranges.push_back({(uintptr_t)b.pool.v_pool, (uintptr_t)b.pool.v_pool + pool_bytes, "V pool", -1});
   }
   if (need_xy) {
     const size_t rows = (size_t)(C + B) * d->hidden * el;
@@ -287,16 +383,34 @@ Plan make_plan(const sarathi_layer_desc *d, const BatchView &b) {
   return p;
 }
 
+PagePool page_pool(const BatchView &b) {
+  PagePool p{};
+  if (b.paged) {
+    p.k = (uint64_t)b.pool.k_pool;
+    p.v = (uint64_t)b.pool.v_pool;
+    p.n_pages = b.pool.n_pages;
+    p.shift = b.page_shift;
+  }
+  return p;
+}
+
 DecodeGroup decode_group(const BatchView &b, int base) {
   DecodeGroup g{};
   g.base = base;
   g.n = std::min(kMaxDecodesPerLaunch, b.B - base);
   if (g.n < 0) g.n = 0;
   for (int i = 0; i < g.n; ++i) {
-    g.k[i] = (uint64_t)b.decode_kv[base + i].k;
-    g.v[i] = (uint64_t)b.decode_kv[base + i].v;
+    if (b.paged) {
+      const sarathi_page_table &t = b.decode_tables[base + i];
+      g.k[i] = (uint64_t)t.pages;
+      g.v[i] = 0;
+      g.cap[i] = t.n_entries << b.page_shift;
+    } else {
+      g.k[i] = (uint64_t)b.decode_kv[base + i].k;
+      g.v[i] = (uint64_t)b.decode_kv[base + i].v;
+      g.cap[i] = b.decode_kv[base + i].capacity;
+    }
     g.len[i] = b.decode_len[base + i];
-    g.cap[i] = b.decode_kv[base + i].capacity;
   }
   return g;
 }
@@ -344,6 +458,7 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   const int A = d->n_heads * d->head_dim;
   const int C = b.C, B = b.B;
   const ChunkSet cs = chunk_set(b);
+  const PagePool pool = page_pool(b);
   float *po = reinterpret_cast<float *>(ws + p.part_o);
   float *pml = reinterpret_cast<float *>(ws + p.part_ml);
   const bool split_chunk = chunk_uses_split(d);
@@ -351,10 +466,10 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   if (C > 0) {
     if (split_chunk) {
       const DecodeGroup none = decode_group(b, B);   // empty group
-      HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, cs, none,
+      HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, cs, none, pool,
                                p.max_splits, po, pml, s));
     } else {
-      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, cs, out, A, p.chunk_splits,
+      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, cs, pool, out, A, p.chunk_splits,
                                 p.max_splits, po, pml, s));
     }
   }
@@ -362,7 +477,7 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_DECODE));
   for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
     const DecodeGroup g = decode_group(b, base);
-    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, cs, g,
+    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, cs, g, pool,
                              p.max_splits, po, pml, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
@@ -421,6 +536,7 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   // 3. sum of the partials + RoPE + KV append: the chunk rows with the first decode group, then the
   // other decode groups
   const ChunkSet cs = chunk_set(b);
+  const PagePool pool = page_pool(b);
   HIP_TRY(mk.start(SARATHI_STAGE_ROPE_APPEND));
   {
     int base = 0;
@@ -430,7 +546,7 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
       const int n_rows = (base == 0 ? b.C : 0) + dg.n;
       HIP_TRY(launch_rope_append(ty, part, p.qkv.splits, T, q, A, dump ? dump->qkv : nullptr,
                                  L->rope_tab, llama ? 1 : 0, d->n_heads, d->head_dim, row0, n_rows,
-                                 cs, dg, s));
+                                 cs, dg, pool, s));
       base += kMaxDecodesPerLaunch;
     } while (base < b.B);
   }
@@ -488,6 +604,7 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
 
 sarathi_status make_view(const sarathi_batch *b, BatchView *v) { return view_batch(b, v); }
 sarathi_status make_view(const sarathi_multi_batch *b, BatchView *v) { return view_multi(b, v); }
+sarathi_status make_view(const sarathi_paged_batch *b, BatchView *v) { return view_paged(b, v); }
 
 // Validation of a batch of either kind: the description first, then the batch.
 template <typename Batch>
@@ -614,6 +731,27 @@ sarathi_status sarathi_multi_forward(sarathi_layer *layer, const sarathi_multi_b
 }
 
 sarathi_status sarathi_multi_forward_debug(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           const sarathi_debug_dump *dump) {
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, dump, nullptr);
+}
+
+sarathi_status sarathi_paged_batch_check(const sarathi_layer_desc *desc,
+                                         const sarathi_paged_batch *batch) {
+  BatchView v;
+  return checked_view(desc, batch, true, &v);
+}
+
+size_t sarathi_paged_workspace_size(const sarathi_layer_desc *desc, const sarathi_paged_batch *batch) {
+  return workspace_bytes(desc, batch);
+}
+
+sarathi_status sarathi_paged_forward(sarathi_layer *layer, const sarathi_paged_batch *batch,
+                                     void *workspace, size_t ws_bytes, void *stream) {
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+sarathi_status sarathi_paged_forward_debug(sarathi_layer *layer, const sarathi_paged_batch *batch,
                                            void *workspace, size_t ws_bytes, void *stream,
                                            const sarathi_debug_dump *dump) {
   return forward_entry(layer, batch, workspace, ws_bytes, stream, dump, nullptr);
@@ -779,6 +917,13 @@ sarathi_status sarathi_layer_forward_timed(sarathi_layer *layer, const sarathi_b
 }
 
 sarathi_status sarathi_multi_forward_timed(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           sarathi_timer *timer) {
+  if (!timer) return fail(SARATHI_ERR_INVALID, "timer is null");
+  return forward_entry(layer, batch, workspace, ws_bytes, stream, nullptr, timer);
+}
+
+sarathi_status sarathi_paged_forward_timed(sarathi_layer *layer, const sarathi_paged_batch *batch,
                                            void *workspace, size_t ws_bytes, void *stream,
                                            sarathi_timer *timer) {
   if (!timer) return fail(SARATHI_ERR_INVALID, "timer is null");

@@ -85,6 +85,8 @@ class HybridLayer:
                                _ptr(x, dt), _ptr(y, dt))
 
     def workspace_size(self, batch) -> int:
+        if isinstance(batch, _abi.sarathi_paged_batch):
+            return _abi.sarathi_paged_workspace_size(self.desc, batch)
         if isinstance(batch, _abi.sarathi_multi_batch):
             return _abi.sarathi_multi_workspace_size(self.desc, batch)
         return _abi.sarathi_workspace_size(self.desc, batch)
@@ -98,6 +100,41 @@ class HybridLayer:
         ch = [(ln, off, _ptr(kv[0], dt), _ptr(kv[1], dt), kv[0].shape[1]) for ln, off, kv in chunks]
         dkv = [(_ptr(k, dt), _ptr(v, dt), k.shape[1]) for k, v in decode_kv]
         return _abi.make_multi_batch(ch, dkv, list(decode_len), _ptr(x, dt), _ptr(y, dt))
+
+    def paged_batch(self, x: Optional[torch.Tensor], y: Optional[torch.Tensor], pool: Tuple[torch.Tensor, torch.Tensor],
+                    chunks: Sequence[Tuple[int, int, torch.Tensor]], decode_tables: Sequence[torch.Tensor],
+                    decode_len: Sequence[int]):
+        """(sarathi_paged_batch, keepalive).  pool: (K pool, V pool), each [n_pages, nh, page_size, d];
+        chunks: list of (len, offset, block table); decode_tables: one block table per decode.  Block
+        tables are int32 device tensors."""
+        dt = self.dtype
+        kp, vp = pool
+        n_pages, page = kp.shape[0], kp.shape[2]
+        ch = [(ln, off, _ptr(t, torch.int32), t.numel()) for ln, off, t in chunks]
+        tb = [(_ptr(t, torch.int32), t.numel()) for t in decode_tables]
+        return _abi.make_paged_batch((_ptr(kp, dt), _ptr(vp, dt), n_pages, page), ch, tb, list(decode_len),
+                                     _ptr(x, dt), _ptr(y, dt))
+
+    def forward_paged(self, x, y, pool, chunks, decode_tables, decode_len,
+                      workspace: Optional[torch.Tensor] = None, stream=None, dump: Optional[dict] = None):
+        """Enqueue the layer over a batch whose caches live in a page pool (see paged_batch)."""
+        b, keep = self.paged_batch(x, y, pool, chunks, decode_tables, decode_len)
+        need = _abi.sarathi_paged_workspace_size(self.desc, b)
+        if need == 0:
+            st = _abi.sarathi_paged_batch_check(self.desc, b)
+            raise _abi.SarathiError(st, "paged batch", _abi.sarathi_last_error())
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr = _ptr(workspace)
+        nbytes = workspace.numel() * workspace.element_size()
+        if dump:
+            d = _abi.sarathi_debug_dump(*[_ptr(dump.get(n), torch.float32) for n in
+                                          ("n1", "qkv", "q_rot", "attn", "h1", "n2", "act")])
+            _abi.sarathi_paged_forward_debug(self.handle, b, ws_ptr, nbytes, _stream(stream), d)
+        else:
+            _abi.sarathi_paged_forward(self.handle, b, ws_ptr, nbytes, _stream(stream))
+        del keep
+        return y
 
     def forward_multi(self, x, y, chunks, decode_kv, decode_len, workspace: Optional[torch.Tensor] = None,
                       stream=None, dump: Optional[dict] = None):

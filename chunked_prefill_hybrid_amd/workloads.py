@@ -30,7 +30,7 @@ import numpy as np
 __all__ = [
     "LayerShape", "BatchSpec", "Workload", "SHAPES", "bf16_round", "bf16_bits",
     "make_weights", "make_batch", "workload", "sweep", "tiny_schedule", "WORKLOADS",
-    "MultiSpec", "budget_batch", "make_multi_batch", "chunks_of",
+    "MultiSpec", "budget_batch", "make_multi_batch", "chunks_of", "paginate",
 ]
 
 
@@ -123,6 +123,7 @@ class Workload:
     batch: BatchSpec
     seed: int = 0
     note: str = ""
+    page_size: Optional[int] = None   # caches laid out in a page pool of this many tokens per page
 
 
 WORKLOADS = {
@@ -137,6 +138,9 @@ WORKLOADS = {
                         BatchSpec(256, 0, 256, 64, decode_lens=(2048,) * 64)),
     "llama13b_long": Workload("llama13b_long", SHAPES["llama13b"],
                               BatchSpec(512, 7680, 8192, 48, decode_len_range=(2048, 8192))),
+    # The llama13b batch with every cache in one pool of 16-token pages (shuffled page order).
+    "llama13b_paged": Workload("llama13b_paged", SHAPES["llama13b"],
+                               BatchSpec(256, 768, 1024, 18, decode_lens=(1024,) * 18), page_size=16),
     # Token-budget batch: 512 tokens = 18 decodes + the last 94 tokens of a 1024-token prompt + a whole
     # 300-token prompt + the first 100 tokens of a new 1024-token prompt.
     "llama13b_budget": Workload("llama13b_budget", SHAPES["llama13b"],
@@ -154,6 +158,33 @@ def chunks_of(batch: dict):
         return [{"len": batch["chunk_len"], "offset": batch["chunk_offset"], "k": batch["chunk_k"],
                  "v": batch["chunk_v"]}]
     return []
+
+
+def paginate(caches, page_size: int, seed: int = 0, extra_pages: int = 0, fill: float = 0.0):
+    """Lay requests' caches out in a page pool (input preparation for the paged-KV path).
+
+    caches: list of (K, V) arrays [nh, cap_i, d].  Request i gets ceil(cap_i / page_size) pages, at
+    pool positions drawn from a seeded random permutation (so logically adjacent pages are scattered);
+    extra_pages unused pages are added to the pool.  Slots past cap_i in a request's last page, and
+    unused pages, hold `fill`.  Returns (k_pool, v_pool, tables): pools [n_pages, nh, page_size, d],
+    tables a list of int32 arrays (request i's logical page -> pool page)."""
+    nh, d = caches[0][0].shape[0], caches[0][0].shape[2]
+    counts = [-(-k.shape[1] // page_size) for k, _ in caches]
+    n_pages = sum(counts) + extra_pages
+    perm = np.random.default_rng(seed).permutation(n_pages).astype(np.int32)
+    kp = np.full((n_pages, nh, page_size, d), fill, np.float32)
+    vp = np.full((n_pages, nh, page_size, d), fill, np.float32)
+    tables, start = [], 0
+    for (k, v), n in zip(caches, counts):
+        t = perm[start:start + n]
+        start += n
+        for i, page in enumerate(t):
+            rows = slice(i * page_size, min((i + 1) * page_size, k.shape[1]))
+            m = rows.stop - rows.start
+            kp[page, :, :m, :] = k[:, rows, :]
+            vp[page, :, :m, :] = v[:, rows, :]
+        tables.append(t.copy())
+    return kp, vp, tables
 
 
 def workload(key: str, **batch_changes) -> Workload:

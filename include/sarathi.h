@@ -251,6 +251,72 @@ sarathi_status sarathi_multi_forward_debug(sarathi_layer *layer, const sarathi_m
                                            void *workspace, size_t ws_bytes, void *stream,
                                            const sarathi_debug_dump *dump);
 
+/* ---- Paged KV caches ---------------------------------------------------------------------------
+ * Instead of one buffer per request allocated at maximum length, every request's K/V rows live in
+ * fixed-size pages of a pool shared by all requests of the layer, found through the request's block
+ * table.  The pages call dynamic (vLLM-style) KV allocation complementary: it raises the number of
+ * requests that fit, and so the number of decodes that can ride with each chunk (SARATHI: Efficient
+ * LLM Inference by Piggybacking Decodes with Chunked Prefills, "System Optimizations from Prior
+ * Work", memory management).  Everything else is as for sarathi_multi_forward.
+ *
+ * Layout: k_pool and v_pool are each [n_pages, n_heads, page_size, head_dim] in the layer's storage
+ * type: page p holds, per head, page_size consecutive rows.  Token t of a request lives in pool page
+ * pages[t / page_size] at row t % page_size.
+ *
+ * The block tables are DEVICE arrays the library only reads; their contents cannot be checked on the
+ * host.  Every entry is clamped into [0, n_pages) before use, so a bad entry yields wrong values but
+ * never an access outside the pools.  The pages a call WRITES (the slots of this step's rows) must
+ * not be shared between requests; pages it only reads (a common prefix) may be. */
+typedef struct {
+    void *k_pool;               /* device [n_pages, n_heads, page_size, head_dim] */
+    void *v_pool;               /* device, same shape; must not overlap k_pool */
+    int32_t n_pages;            /* >= 1 */
+    int32_t page_size;          /* tokens per page: a power of two in [1, 65536] (16 or 32 typical) */
+} sarathi_page_pool;
+
+typedef struct {
+    const int32_t *pages;       /* DEVICE int32 [n_entries]: logical page i -> pool page */
+    int32_t n_entries;          /* the request can hold n_entries * page_size tokens */
+    int32_t reserved;           /* must be 0 */
+} sarathi_page_table;
+
+typedef struct {
+    int32_t len;                /* rows of this chunk, >= 1 */
+    int32_t offset;             /* tokens of this request already cached */
+    sarathi_page_table table;   /* n_entries * page_size >= offset + len */
+} sarathi_paged_chunk;
+
+/* Rows of x as in sarathi_multi_batch: chunk rows in chunk order, then decodes. */
+typedef struct {
+    sarathi_page_pool pool;
+    int32_t n_chunks;           /* 0 .. SARATHI_MAX_CHUNKS */
+    int32_t reserved;           /* must be 0 */
+    const sarathi_paged_chunk *chunks;          /* HOST array [n_chunks] */
+    int32_t n_decodes;          /* >= 0 */
+    int32_t reserved2;          /* must be 0 */
+    const sarathi_page_table *decode_tables;    /* HOST array [n_decodes]; capacity > decode_len[i] */
+    const int32_t *decode_len;                  /* HOST array [n_decodes] */
+    const void *x;              /* device [T, H] */
+    void *y;                    /* device [T, H]; must not overlap x or the pools */
+} sarathi_paged_batch;
+
+/* Host-only validation: as sarathi_multi_batch_check, plus the pool (non-null, page_size a power of
+ * two, n_pages >= 1, K and V pools disjoint), each table (non-null, n_entries >= 1, capacity), and no
+ * two requests passing the same table.  Returns OK, INVALID or CAPACITY. */
+sarathi_status sarathi_paged_batch_check(const sarathi_layer_desc *desc, const sarathi_paged_batch *batch);
+
+/* Bytes of device workspace sarathi_paged_forward needs; 0 if the check fails. */
+size_t sarathi_paged_workspace_size(const sarathi_layer_desc *desc, const sarathi_paged_batch *batch);
+
+/* Enqueues the forward over a paged batch.  Errors: as sarathi_paged_batch_check, WORKSPACE, HIP. */
+sarathi_status sarathi_paged_forward(sarathi_layer *layer, const sarathi_paged_batch *batch,
+                                     void *workspace, size_t ws_bytes, void *stream);
+
+/* As sarathi_paged_forward plus the intermediates of sarathi_layer_forward_debug (dump may be NULL). */
+sarathi_status sarathi_paged_forward_debug(sarathi_layer *layer, const sarathi_paged_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           const sarathi_debug_dump *dump);
+
 /* ---- Per-stage timing (measurement only) ------------------------------------------------------
  * The layer's forward runs as the stages below, in this order (per-operation profile of a hybrid
  * iteration: preproj, attention, postproj, FFN; SARATHI: Efficient LLM Inference by Piggybacking
@@ -293,6 +359,11 @@ sarathi_status sarathi_layer_forward_timed(sarathi_layer *layer, const sarathi_b
 
 /* As sarathi_multi_forward, recording the timer's events (see sarathi_layer_forward_timed). */
 sarathi_status sarathi_multi_forward_timed(sarathi_layer *layer, const sarathi_multi_batch *batch,
+                                           void *workspace, size_t ws_bytes, void *stream,
+                                           sarathi_timer *timer);
+
+/* As sarathi_paged_forward, recording the timer's events (see sarathi_layer_forward_timed). */
+sarathi_status sarathi_paged_forward_timed(sarathi_layer *layer, const sarathi_paged_batch *batch,
                                            void *workspace, size_t ws_bytes, void *stream,
                                            sarathi_timer *timer);
 

@@ -47,6 +47,9 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(_abi.sarathi_chunk) == 32
     assert ctypes.sizeof(_abi.sarathi_multi_batch) == 56
     assert _abi.sarathi_multi_batch.decode_kv.offset == 24 and _abi.sarathi_multi_batch.x.offset == 40
+    assert ctypes.sizeof(_abi.sarathi_page_pool) == 24 and ctypes.sizeof(_abi.sarathi_page_table) == 16
+    assert ctypes.sizeof(_abi.sarathi_paged_chunk) == 24 and ctypes.sizeof(_abi.sarathi_paged_batch) == 80
+    assert _abi.sarathi_paged_batch.chunks.offset == 32 and _abi.sarathi_paged_batch.x.offset == 64
 
 
 def desc(**kw):
@@ -199,3 +202,48 @@ def test_multi_forward_rejects_before_any_hip_call(lib):
     with pytest.raises(_abi.SarathiError) as e:
         _abi.sarathi_multi_forward(None, b, addr(5), 1 << 20, 0)
     assert e.value.status == _abi.SARATHI_ERR_INVALID
+
+
+# ---- paged KV caches -------------------------------------------------------------------------------
+
+def paged(chunks=((8, 0, 2), (5, 30, 3)), lens=(17,), dec_entries=(2,), pool=(addr(60), addr(61), 64, 16),
+          x=addr(0), y=addr(1), same_table=False):
+    """chunks: (len, offset, n_entries); tables at addr(70 + j) / addr(80 + i)."""
+    ch = [(n, o, addr(70 + j), ne) for j, (n, o, ne) in enumerate(chunks)]
+    tb = [(addr(80 + i), ne) for i, ne in enumerate(dec_entries)]
+    if same_table:
+        tb[0] = (ch[0][2], tb[0][1])
+    return _abi.make_paged_batch(pool, ch, tb, list(lens), x, y)
+
+
+def test_paged_valid_batches(lib):
+    for kw in (dict(), dict(lens=(), dec_entries=()), dict(chunks=()),
+               dict(pool=(addr(60), addr(61), 8, 1), chunks=((8, 0, 8),), lens=(), dec_entries=())):
+        b, keep = paged(**kw)
+        assert _abi.sarathi_paged_batch_check(desc(), b) == _abi.SARATHI_OK, kw
+        assert _abi.sarathi_paged_workspace_size(desc(), b) % 256 == 0
+
+
+def test_paged_workspace_matches_multi(lib):
+    b1, k1 = paged(chunks=((20, 7, 2),), lens=(17, 40), dec_entries=(2, 3))
+    b2, k2 = _abi.make_multi_batch([(20, 7, addr(40), addr(41), 64)],
+                                   [(addr(10), addr(11), 18), (addr(12), addr(13), 41)], [17, 40], addr(0), addr(1))
+    assert _abi.sarathi_paged_workspace_size(desc(), b1) == _abi.sarathi_multi_workspace_size(desc(), b2) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pool=(addr(60), addr(61), 64, 12)), _abi.SARATHI_ERR_INVALID),        # page size not a power of 2
+    (dict(pool=(addr(60), addr(61), 0, 16)), _abi.SARATHI_ERR_INVALID),         # empty pool
+    (dict(pool=(0, addr(61), 64, 16)), _abi.SARATHI_ERR_INVALID),               # null pool
+    (dict(pool=(addr(60), addr(60) + 64, 64, 16)), _abi.SARATHI_ERR_INVALID),   # K and V pools overlap
+    (dict(chunks=((8, 0, 0),)), _abi.SARATHI_ERR_INVALID),                      # empty block table
+    (dict(chunks=((8, 30, 2),)), _abi.SARATHI_ERR_CAPACITY),                    # 38 tokens > 2 pages of 16
+    (dict(lens=(32,), dec_entries=(2,)), _abi.SARATHI_ERR_CAPACITY),            # slot 32 past 2 pages
+    (dict(same_table=True), _abi.SARATHI_ERR_INVALID),                          # two requests, one table
+    (dict(y=addr(60) + 4096), _abi.SARATHI_ERR_INVALID),                        # y inside the K pool
+    (dict(chunks=(), lens=(), dec_entries=()), _abi.SARATHI_ERR_INVALID),       # empty batch
+])
+def test_paged_invalid_batches(lib, kw, status):
+    b, keep = paged(**kw)
+    assert _abi.sarathi_paged_batch_check(desc(), b) == status
+    assert _abi.sarathi_last_error() != ""
