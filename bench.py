@@ -250,6 +250,9 @@ def main():
     stages = _abi.sarathi_timer_read(timer)
     _abi.sarathi_timer_destroy(timer)
     work = stage_work(shape, [(c["len"], c["offset"]) for c in chunks], lens)
+    if chunks and lens and stages["attn_chunk"][1] == 0:
+        # chunk and decode attention ran as one launch, recorded as the decode stage
+        work["attn_decode"] = tuple(a + b for a, b in zip(work["attn_decode"], work["attn_chunk"]))
     breakdown = {}
     for name, (tot, cnt) in stages.items():
         if cnt == 0:

@@ -18,6 +18,7 @@
 // [page_size, d] slab per head is contiguous, so each 16-byte load stays a full-row read.
 #include <math.h>
 
+#include "attn_chunk_body.h"
 #include "kernels.h"
 
 namespace sarathi {
@@ -25,18 +26,21 @@ namespace {
 
 constexpr int kUnroll = 8;
 
+// The work of one (row r, key split s, head h) item: the split's partial of row r's attention.  sm,
+// sl (4 floats each) and so (4 x D floats) are the caller's shared-memory arrays for the merge of the
+// four waves.
 template <typename T, int D, bool kChunkRows, bool kPaged>
-__global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int nh, int row0,
-                                                       ChunkSet cs, DecodeGroup dg, PagePool pool,
-                                                       int max_splits,
-                                                       float *part_o, float *part_ml, float qscale) {
+__device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q, int ld_q, int nh,
+                                                const ChunkSet &cs, const DecodeGroup &dg,
+                                                const PagePool &pool, int max_splits, float *part_o,
+                                                float *part_ml, float qscale, float *sm, float *sl,
+                                                float *so) {
   constexpr int E = Packet<T>::E;      // elements per 16-byte packet
   constexpr int LPK = D / E;           // lanes per key row
   constexpr int KPI = kWave / LPK;     // keys per wave load step
   constexpr int KPW = kAttnSplit / 4;  // keys per wave per split
   constexpr int NIT = KPW / KPI;
   static_assert(NIT % kUnroll == 0, "whole unrolled steps");
-  const int r = row0 + blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   const RowRef rr = row_ref<kChunkRows>(r, cs, dg);
   const int n_keys = rr.pos + 1;
   const int nsp = attn_splits(n_keys);
@@ -131,11 +135,9 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = wave_sum(o[e], LPK);
 
-  __shared__ float sm[4], sl[4];
-  __shared__ float so[4][D];
   if (grp == 0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) so[wave][sub * E + e] = o[e];
+    for (int e = 0; e < E; ++e) so[wave * D + sub * E + e] = o[e];
   }
   if (lane == 0) {
     sm[wave] = m_run;
@@ -148,12 +150,12 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       w[i] = (sm[i] == -INFINITY) ? 0.f : exp2f(sm[i] - M);
-      L += sl[i] * w[i];
+      L = fmaf(sl[i], w[i], L);
     }
     for (int c = lane; c < D; c += kWave) {
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc += (w[i] != 0.f) ? so[i][c] * w[i] : 0.f;
+      for (int i = 0; i < 4; ++i) acc = (w[i] != 0.f) ? fmaf(so[i * D + c], w[i], acc) : acc;
       part_o[pidx * D + c] = acc;
     }
     if (lane == 0) {
@@ -161,6 +163,61 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
       part_ml[2 * pidx + 1] = L;
     }
   }
+}
+
+template <typename T, int D, bool kChunkRows, bool kPaged>
+__global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int nh, int row0,
+                                                       ChunkSet cs, DecodeGroup dg, PagePool pool,
+                                                       int max_splits,
+                                                       float *part_o, float *part_ml, float qscale) {
+  __shared__ float sm[4], sl[4], so[4 * D];
+  split_attn_item<T, D, kChunkRows, kPaged>(row0 + blockIdx.x, blockIdx.y, blockIdx.z, q, ld_q, nh, cs,
+                                            dg, pool, max_splits, part_o, part_ml, qscale, sm, sl, so);
+}
+
+// Chunk and decode attention in one launch.  Workgroups [0, chunk_grid) run the chunk work items
+// (attn_chunk_body.h), the others the key splits of the decode rows [dec_row0, dec_row0 + dec_rows).
+// The chunk items are few and latency-bound (one 64-query block each, walking its key range tile by
+// tile) and leave most compute units idle; the memory-bound decode splits fill them, so the two kinds
+// of attention of a hybrid batch overlap instead of running one after the other.
+template <int D, bool kPaged>
+__global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int nh, ChunkSet cs,
+                                                  PagePool pool, bf16_t *out, int ld_out,
+                                                  float chunk_qscale, int n_split, int max_splits,
+                                                  float *part_o, float *part_ml, int per_xcd,
+                                                  int chunk_grid, DecodeGroup dg, int dec_row0,
+                                                  int dec_rows, float dec_qscale) {
+  SARATHI_CHUNK_LDS(D);
+  __shared__ float sm[4], sl[4], so[4 * D];
+  const int b = blockIdx.x;
+  if (b < chunk_grid) {
+    chunk_attn_item<D, kPaged>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, ld_out,
+                               chunk_qscale, n_split, max_splits, part_o, part_ml, k0s, v0s, k1s, v1s,
+                               k2s, v2s);
+  } else {
+    const int d = b - chunk_grid;
+    const int r = d % dec_rows, rest = d / dec_rows;
+    split_attn_item<bf16_t, D, false, kPaged>(dec_row0 + r, rest % max_splits, rest / max_splits, q, ld_q,
+                                              nh, cs, dg, pool, max_splits, part_o, part_ml, dec_qscale,
+                                              sm, sl, so);
+  }
+}
+
+template <int D, bool kPaged>
+hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const PagePool &pool, void *out,
+                     int ld_out, int n_split, int max_splits, float *po, float *pml,
+                     const DecodeGroup &dg, int dec_row0, int dec_rows, hipStream_t s) {
+  int items = 0;
+  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], n_split, nh);
+  const int per_xcd = (items + 7) / 8;
+  const int chunk_grid = 8 * per_xcd;
+  const int grid = chunk_grid + dec_rows * max_splits * nh;
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL((attn_fused<D, kPaged>), dim3(grid), dim3(256), 0, s,
+                     static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out),
+                     ld_out, qscale, n_split, max_splits, po, pml, per_xcd, chunk_grid, dg, dec_row0,
+                     dec_rows, qscale);
+  return hipGetLastError();
 }
 
 // One wave per (row, head), four per workgroup.  Lane l holds the (m, l) of splits l, l + 64, ...;
@@ -204,7 +261,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
 #pragma unroll
   for (int k = 0; k < kCombineSlots; ++k) {
     w[k] = l[k] > 0.f ? exp2f(m[k] - M) : 0.f;
-    L += l[k] * w[k];
+    L = fmaf(l[k], w[k], L);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, kWave);
@@ -229,7 +286,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
     for (int u = 0; u < kGroup; ++u)
       if (ws[u] != 0.f) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += ws[u] * v[u][i];
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(ws[u], v[u][i], acc[i]);
       }
   }
   const float inv = 1.0f / L;
@@ -293,6 +350,24 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
   if (type == kBF16 && d == 64) SARATHI_COMBINE(bf16_t, 64);
   if (type == kBF16 && d == 128) SARATHI_COMBINE(bf16_t, 128);
 #undef SARATHI_COMBINE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
+                             const PagePool &pool, void *out, int ld_out, int n_split, int max_splits,
+                             float *part_o, float *part_ml, const DecodeGroup &dg, int dec_row0,
+                             int dec_rows, hipStream_t s) {
+  if (cs.n <= 0 || cs.n > kMaxChunks || dec_rows <= 0 || dec_rows > kMaxDecodesPerLaunch)
+    return hipErrorInvalidValue;
+  if (n_split < 1 || n_split > max_splits || max_splits > kMaxKeySplits || !part_o || !part_ml)
+    return hipErrorInvalidValue;
+  const bool paged = pool.k != 0;
+  if (d == 128)
+    return paged ? run_fused<128, true>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s)
+                 : run_fused<128, false>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s);
+  if (d == 64)
+    return paged ? run_fused<64, true>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s)
+                 : run_fused<64, false>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s);
   return hipErrorInvalidValue;
 }
 

@@ -109,6 +109,15 @@ hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const Chunk
                              const PagePool &pool, void *out, int ld_out, int n_split, int stride,
                              float *part_o, float *part_ml, hipStream_t s);
 
+// The chunk attention of every chunk of the set and the split-KV attention of decode rows
+// [dec_row0, dec_row0 + dec_rows) (one decode group, dg) in one launch (bf16).  Chunk rows are
+// handled as by launch_attn_chunk with n_split key splits (partials when n_split > 1, stride
+// max_splits); decode rows write split partials as launch_attn_rows does.
+hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
+                             const PagePool &pool, void *out, int ld_out, int n_split, int max_splits,
+                             float *part_o, float *part_ml, const DecodeGroup &dg, int dec_row0,
+                             int dec_rows, hipStream_t s);
+
 // Zero-fill rows [row0, row1) of a [*, cols] storage matrix (row stride ld).
 hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int row1, hipStream_t s);
 

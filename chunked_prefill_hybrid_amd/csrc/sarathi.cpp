@@ -319,6 +319,11 @@ struct Plan {
   size_t n1, q, attn, h1, n2, act, part, part_o, part_ml, total;
 };
 
+#ifndef SARATHI_FUSED_ATTN
+#define SARATHI_FUSED_ATTN 1
+#endif
+constexpr bool kFusedAttention = SARATHI_FUSED_ATTN != 0;
+
 // bf16 chunk rows run the flash-style MFMA kernel; the split-KV kernel (and its partials) serves the
 // decode rows, and the chunk rows too in float32 mode.
 bool chunk_uses_split(const sarathi_layer_desc *d) { return d->dtype != SARATHI_BF16; }
@@ -462,8 +467,17 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   float *po = reinterpret_cast<float *>(ws + p.part_o);
   float *pml = reinterpret_cast<float *>(ws + p.part_ml);
   const bool split_chunk = chunk_uses_split(d);
+  // bf16 batches with chunk rows and decode rows run both attentions in one launch when the chunk
+  // work items are fewer than the compute units: the decode splits then fill the units the
+  // latency-bound chunk work leaves idle.  With more chunk items the shared launch's register and LDS
+  // footprint (that of the chunk work) halves the decode splits' occupancy, which costs more than the
+  // overlap gains (measured), so the two run as separate launches.  The fused launch's time is
+  // recorded as the decode stage.
+  int chunk_work = 0;
+  for (int j = 0; j < cs.n; ++j) chunk_work += (cs.len[j] + 63) / 64 * p.chunk_splits * d->n_heads;
+  const bool fused = kFusedAttention && !split_chunk && C > 0 && B > 0 && chunk_work <= kPlanCUs;
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_CHUNK));
-  if (C > 0) {
+  if (C > 0 && !fused) {
     if (split_chunk) {
       const DecodeGroup none = decode_group(b, B);   // empty group
       HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, cs, none, pool,
@@ -473,12 +487,16 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
                                 p.max_splits, po, pml, s));
     }
   }
-  HIP_TRY(mk.end(SARATHI_STAGE_ATTN_CHUNK, C > 0));
+  HIP_TRY(mk.end(SARATHI_STAGE_ATTN_CHUNK, C > 0 && !fused));
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_DECODE));
   for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
     const DecodeGroup g = decode_group(b, base);
-    HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, cs, g, pool,
-                             p.max_splits, po, pml, s));
+    if (fused && base == 0)
+      HIP_TRY(launch_attn_fused(d->head_dim, q, A, d->n_heads, cs, pool, out, A, p.chunk_splits,
+                                p.max_splits, po, pml, g, C, g.n, s));
+    else
+      HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, cs, g, pool,
+                               p.max_splits, po, pml, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_MERGE));

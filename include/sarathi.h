@@ -328,7 +328,9 @@ typedef enum {
     SARATHI_STAGE_QKV = 1,         /* QKV GEMM */
     SARATHI_STAGE_ROPE_APPEND = 2, /* RoPE + KV-cache append */
     SARATHI_STAGE_ATTN_CHUNK = 3,  /* chunk attention (prefix + causal chunk) */
-    SARATHI_STAGE_ATTN_DECODE = 4, /* decode attention (split-KV partials) */
+    SARATHI_STAGE_ATTN_DECODE = 4, /* decode attention (split-KV partials); when the batch's chunk and
+                                      decode attention run as one launch, that launch's time is
+                                      recorded here and the chunk stage does not run */
     SARATHI_STAGE_ATTN_MERGE = 5,  /* merge of split partials */
     SARATHI_STAGE_O = 6,           /* O GEMM + residual */
     SARATHI_STAGE_NORM2 = 7,
