@@ -9,7 +9,8 @@ Piggybacking Decodes with Chunked Prefills):
   batch (one 1024-token prompt), of a decode-only batch (4 decodes at 1024 cached tokens) and of a
   decode-maximal batch (a 1021-token chunk plus 3 decodes), with the stage split of the page's table
   (pre-projection = norm + QKV + RoPE/append, attention, post-projection = O, FFN = norm + up + down)
-  and the marginal time of a piggybacked decode: (t(1021 + 3 decodes) - t(1021 alone)) / 3.
+  and the marginal time of a piggybacked decode: (t(1021 + 3 decodes) - t(1021 alone)) / 3, from
+  alternating runs of the two batches (median of the paired differences).
 * Figure 8 analog (section 5, decode speedup vs batch size): for prompt and decode lengths
   L in {1K, 2K, 3K} and batch size B (1 prompt + B - 1 decodes), the whole L-token prompt runs in
   chunks of 256 with B - 1 decodes riding in every step, and again alone.  The marginal decode time
@@ -131,6 +132,25 @@ def timed(model, fn, reps: int, warmup: int = 1) -> float:
     return statistics.median(times)
 
 
+def timed_pair(model, fa, fb, reps: int):
+    """Times fa and fb alternately, reps times each; returns (median ms of fa, median ms of fb, median
+    of the per-repetition differences fb - fa).  Pairing the runs cancels slow drifts of the clock,
+    which matters when the difference is small next to the times."""
+    torch = model.torch
+    fa()
+    fb()
+    ta, tb = [], []
+    for _ in range(reps):
+        for f, out in ((fa, ta), (fb, tb)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            b.synchronize()
+            out.append(a.elapsed_time(b))
+    return statistics.median(ta), statistics.median(tb), statistics.median([y - x for x, y in zip(ta, tb)])
+
+
 def stage_split(model, C, off, chunk_kv0, decode_kv0, lens, reps: int):
     """Per-stage milliseconds of one stack step, from layer 0's stage timer times n_layers (all layers
     have the same shape and work)."""
@@ -175,7 +195,11 @@ def table2(model, reps: int):
     run("decode_only", 0, B, B)
     run("decode_maximal", P - 3, 3, P)
     run("chunk_1021_alone", P - 3, 0, P - 3)
-    marg = (rows["decode_maximal"]["ms"] - rows["chunk_1021_alone"]["ms"]) / 3
+    # the marginal decode time is a small difference of two ~35 ms runs: time them alternately
+    dkv3 = [row[:3] for row in dec_kv]
+    _, _, diff = timed_pair(model, model.prepare(P - 3, 0, chunk, [], []),
+                            model.prepare(P - 3, 0, chunk, dkv3, [P] * 3), max(reps, 15))
+    marg = diff / 3
     rows["marginal_decode_ms"] = marg
     rows["decode_speedup"] = rows["decode_only"]["ms_per_token"] / marg if marg > 0 else None
     say(f"  marginal decode: {marg * 1e3:.2f} us/token; decode-only {rows['decode_only']['ms_per_token'] * 1e3:.2f}"
