@@ -35,22 +35,38 @@ hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkSet &cs, const 
 
 }  // namespace
 
-// Splits of each query block's key range, one count for every chunk of the set: enough to reach
-// kChunkTargetWorkgroups workgroups, but only while every split keeps at least kMinSplitTiles tiles (a
-// split costs a partial write and a merge, which only pays off when the key ranges are long), and never
-// more than any chunk's first block has tiles (so no split is empty).
+// Splits of each query block's key range, one count for every chunk of the set.  The work items run
+// in rounds of kChunkTargetWorkgroups (two per compute unit); a round lasts about as long as its
+// longest item walks its key tiles, and each split beyond the first costs about kSplitCostTiles tile
+// times (its partial is written and merged).  The count with the shortest estimated makespan wins,
+// among those that keep every split at least kMinSplitTiles tiles long and never exceed the tiles of
+// any chunk's first block (so no split is empty).  Items that leave the last round mostly idle are
+// what this avoids: with 8 query blocks x 40 heads over an 8K-key prefix, two splits make 640 items,
+// a full round and a quarter of one, no faster than one split; three make 960 in two full rounds.
 int chunk_attn_splits(const ChunkSet &cs, int nh) {
   if (cs.n <= 0) return 1;
-  int q_blocks = 0, first_tiles = 1 << 30, by_length = 1 << 30;
+  int q_blocks = 0, first_tiles = 1 << 30, by_length = 1 << 30, max_tiles = 0;
   for (int j = 0; j < cs.n; ++j) {
     const int C = cs.len[j], off = cs.off[j];
     q_blocks += (C + kBQ - 1) / kBQ;
     first_tiles = min(first_tiles, (off + min(C, kBQ) + kBKV - 1) / kBKV);
     const int avg_tiles = (off + (C + 1) / 2 + kBKV - 1) / kBKV;
     by_length = min(by_length, max(1, avg_tiles / kMinSplitTiles));
+    max_tiles = max(max_tiles, (off + C + kBKV - 1) / kBKV);
   }
-  const int want = (kChunkTargetWorkgroups + q_blocks * nh - 1) / (q_blocks * nh);
-  return max(1, min(min(want, kMaxChunkSplits), min(by_length, first_tiles)));
+  const int s_max = max(1, min(kMaxChunkSplits, min(by_length, first_tiles)));
+  int best = 1;
+  long long best_t = -1;
+  for (int sp = 1; sp <= s_max; ++sp) {
+    const long long items = (long long)q_blocks * nh * sp;
+    const long long rounds = (items + kChunkTargetWorkgroups - 1) / kChunkTargetWorkgroups;
+    const long long t = rounds * ((max_tiles + sp - 1) / sp) + (long long)kSplitCostTiles * (sp - 1);
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,

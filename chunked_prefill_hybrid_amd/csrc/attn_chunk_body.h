@@ -56,6 +56,8 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 // 2^x for x <= 0 with the hardware exponential alone: results below the normal range flush to 0,
 // which is what a probability that small contributes anyway.
 __device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
+// Largest log2 gap between a tile's score maximum and the running exponent base before the base moves.
+constexpr float kRebase = 8.0f;
 
 template <int D> struct TileGeom {
   static constexpr int kChunks = D / 8;            // 16-byte chunks per row
@@ -207,18 +209,24 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    // A split that starts past a query's position leaves its row fully masked (m_new = -inf): then
-    // the exponent base is 0, every p is 0 and the row's partial stays empty (l = 0).
-    const float m_new = fmaxf(m_run, tmax * qscale_log2);
-    const float m_base = m_new == -INFINITY ? 0.f : m_new;
-    // Rescale the running sums only when some query of the wave found a larger maximum.
-    if (__any(m_new > m_run)) {
-      const float corr = exp2_nonpos(m_run - m_base);
+    // The exponent base m_run moves only when a tile's maximum exceeds it by more than kRebase (in
+    // log2 units): probabilities then stay below 2^kRebase, well inside float32 and bfloat16 range,
+    // and the running sums are rescaled on a few tiles instead of on every tile with a new maximum.
+    // Any base gives the same softmax, since O and l share it.  A split that starts past a query's
+    // position leaves its row fully masked (m_run stays -inf): the exponent base is then 0, every p is
+    // 0 and the row's partial stays empty (l = 0).
+    const float m_tile = tmax * qscale_log2;
+    const bool rebase = m_tile > m_run + kRebase;
+    if (__any(rebase)) {
+      const float m_new = rebase ? m_tile : m_run;
+      // 1 for a query whose base stays, 0 for one whose sums are still empty (m_run = -inf)
+      const float corr = exp2_nonpos(m_run - (m_new == -INFINITY ? 0.f : m_new));
       l_run *= corr;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= corr;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float m_base = m_run == -INFINITY ? 0.f : m_run;
     // P^T operands: k-step s holds keys s*32 + 4g + i (slots 0..3) and s*32 + 16 + 4g + i (4..7).
     bf16x8_t pf[2];
 #pragma unroll
@@ -227,7 +235,7 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2_nonpos(fmaf(sc[2 * s + hb][i], qscale_log2, -m_base));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * s + hb][i], qscale_log2, -m_base));
           l_run += p;
           pf[s][hb * 4 + i] = (__bf16)p;
         }

@@ -104,6 +104,7 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
 constexpr int kChunkTargetWorkgroups = 512;   // two workgroups per compute unit
 constexpr int kMinSplitTiles = 16;            // a split keeps at least 16 key tiles
 constexpr int kMaxChunkSplits = 16;
+constexpr int kSplitCostTiles = 3;            // makespan cost of one more split, in key-tile times
 int chunk_attn_splits(const ChunkSet &cs, int nh);
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
                              const PagePool &pool, void *out, int ld_out, int n_split, int stride,
