@@ -128,7 +128,8 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
     const int q = min(wave + kWaves * i, G::kLoadsA - 1);
     const int row = kRPL * q + lrow;
     const int gr = min(m0 + row, g.m_alloc - 1);
-    a_src[i] = A + (size_t)gr * g.lda + (size_t)kb * kBK + swz_slot(row, lslot) * 8;
+    const size_t a_row = g.a_kmajor ? ((size_t)kb * g.m_alloc + gr) * kBK : (size_t)gr * g.lda + (size_t)kb * kBK;
+    a_src[i] = A + a_row + swz_slot(row, lslot) * 8;
     a_lds[i] = kRPL * q * kLdsK;
   }
   const bf16_t *b_src[G::kBI];
@@ -155,11 +156,13 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   }
 
   // Loads of k-tile j (clamped to the last tile, so every wave issues the same loads every step)
-  // into LDS stage `st`.
+  // into LDS stage `st`.  A k-tile of a k-tile-major A lies m_alloc * 64 elements after the previous.
+  const int a_kstep = g.a_kmajor ? g.m_alloc * kBK : kBK;
   auto issue = [&](bf16_t *st, int j) {
     const int kofs = min(j, ntiles - 1) * kBK;
+    const int a_kofs = min(j, ntiles - 1) * a_kstep;
 #pragma unroll
-    for (int i = 0; i < G::kAI; ++i) dma16(a_src[i] + kofs, st + a_lds[i]);
+    for (int i = 0; i < G::kAI; ++i) dma16(a_src[i] + a_kofs, st + a_lds[i]);
 #pragma unroll
     for (int i = 0; i < G::kBI; ++i) {
       const int q = wave + kWaves * i;
@@ -421,6 +424,8 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
 }
 
 hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  // k-tile-major A: bf16 only, and its whole extent must be addressable with 32-bit offsets
+  if (g.a_kmajor && (type == kF32 || (long long)g.m_alloc * g.k >= (1ll << 31))) return hipErrorInvalidValue;
   if (type == kF32) {
     switch (epi) {
       case kEpiStore: return run_f32<kEpiStore>(g, s);

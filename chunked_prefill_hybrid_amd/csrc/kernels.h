@@ -15,11 +15,12 @@ enum StorageType { kF32 = 0, kBF16 = 1 };
 // Row norms.  v[r] = resid[r] + sum_{s < splits} part[s][r]  (resid in `res_type` storage, the
 // split partials of a GEMM in float32 with slice stride rows*H; splits may be 0).  If sum_out is
 // non-null it receives v (float32).  out[r] = RMSNorm(v) * g  or  LayerNorm(v) * g + b for r < rows;
-// rows rows..rows_alloc-1 of out are zero-filled.
+// rows rows..rows_alloc-1 of out are zero-filled.  out is row-major [rows_alloc, H], or with
+// kmajor k-tile-major [H/64][rows_alloc][64] (the layout the bf16 GEMM reads fastest; H % 64 == 0).
 hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
                             const float *part, int splits, float *sum_out, const float *g,
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                            hipStream_t s);
+                            bool kmajor, hipStream_t s);
 
 // FFN activation from split partials ([splits][rows][n_part] float32): gated (n_part = 2F):
 // out[r, j] = silu(sum_s part[s][r][j]) * sum_s part[s][r][F + j];  else (n_part = F):
@@ -53,6 +54,8 @@ struct GemmArgs {
   int n;              // output columns
   int k;              // multiple of 64 in bf16 mode
   int n_w0;           // kEpiPartial with w1: rows of the product taken from w0
+  int a_kmajor;       // bf16 only: a is k-tile-major, [k/64][m_alloc][64] (lda unused).  A k-tile of
+                      // 8 rows is then 1 KiB of consecutive bytes, which the LDS DMA fetches faster
 };
 
 // Launch shape of one GEMM: m_tiles x n_tiles output tiles, each k range cut into `splits`;
@@ -125,5 +128,8 @@ hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int r
 // Convert a [rows, cols] storage matrix (row stride ld_src) to float32 (row stride ld_dst).
 hipError_t launch_to_f32(int type, const void *src, int ld_src, float *dst, int ld_dst, int rows,
                          int cols, hipStream_t s);
+// The same from a k-tile-major [cols/64][rows_alloc][64] matrix.
+hipError_t launch_kmajor_to_f32(int type, const void *src, int rows_alloc, float *dst, int ld_dst,
+                                int rows, int cols, hipStream_t s);
 
 }  // namespace sarathi

@@ -19,6 +19,15 @@ __global__ __launch_bounds__(256) void widen_rows(const T *src, int ld_src, floa
   for (int c = threadIdx.x; c < cols; c += blockDim.x) d[c] = to_f32(s[c]);
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void widen_kmajor_rows(const T *src, int rows_alloc, float *dst,
+                                                     int ld_dst, int cols) {
+  const int r = blockIdx.x;
+  float *d = dst + (size_t)r * ld_dst;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x)
+    d[c] = to_f32(src[((size_t)(c >> 6) * rows_alloc + r) * 64 + (c & 63)]);
+}
+
 }  // namespace
 
 hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int row1, hipStream_t s) {
@@ -41,6 +50,19 @@ hipError_t launch_to_f32(int type, const void *src, int ld_src, float *dst, int 
   else
     hipLaunchKernelGGL(widen_rows<bf16_t>, dim3(rows), dim3(256), 0, s,
                        static_cast<const bf16_t *>(src), ld_src, dst, ld_dst, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmajor_to_f32(int type, const void *src, int rows_alloc, float *dst, int ld_dst,
+                                int rows, int cols, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (rows > rows_alloc || cols % 64) return hipErrorInvalidValue;
+  if (type == kF32)
+    hipLaunchKernelGGL(widen_kmajor_rows<float>, dim3(rows), dim3(256), 0, s,
+                       static_cast<const float *>(src), rows_alloc, dst, ld_dst, cols);
+  else
+    hipLaunchKernelGGL(widen_kmajor_rows<bf16_t>, dim3(rows), dim3(256), 0, s,
+                       static_cast<const bf16_t *>(src), rows_alloc, dst, ld_dst, cols);
   return hipGetLastError();
 }
 

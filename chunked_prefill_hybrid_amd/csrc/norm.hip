@@ -77,13 +77,16 @@ template <typename Tres, typename Tout, bool LN>
 __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, const float *part,
                                                       int splits, float *sum_out, const float *g,
                                                       const float *b, Tout *out, int H, int rows,
-                                                      float eps) {
+                                                      float eps, int kmajor_rows) {
   __shared__ float red[kNormThreads / 64];
   const int r = blockIdx.x;
-  Tout *o = out + (size_t)r * H;
+  // Element c of this row: row-major, or k-tile-major (64-column tiles of kmajor_rows rows each).
+  auto at = [&](int c) -> Tout * {
+    return kmajor_rows ? out + ((size_t)(c >> 6) * kmajor_rows + r) * 64 + (c & 63) : out + (size_t)r * H + c;
+  };
   if (r >= rows) {
     const float z[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c = threadIdx.x * 4; c < H; c += kNormThreads * 4) store4<Tout>(o + c, z);
+    for (int c = threadIdx.x * 4; c < H; c += kNormThreads * 4) store4<Tout>(at(c), z);
     return;
   }
   const size_t slice = (size_t)rows * H, row_off = (size_t)r * H;
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, con
         w[e] = (v[i][e] - mean) * rstd * g[c + e];
         if (LN) w[e] += b[c + e];
       }
-      store4<Tout>(o + c, w);
+      store4<Tout>(at(c), w);
     }
 }
 
@@ -173,15 +176,15 @@ __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int split
 template <typename Tres, typename Tout>
 hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, float *sum_out,
                     const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
-                    float eps, hipStream_t s) {
+                    float eps, int kmajor_rows, hipStream_t s) {
   if (ln)
     hipLaunchKernelGGL((norm_rows<Tres, Tout, true>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
                        static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
-                       static_cast<Tout *>(out), H, rows, eps);
+                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows);
   else
     hipLaunchKernelGGL((norm_rows<Tres, Tout, false>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
                        static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
-                       static_cast<Tout *>(out), H, rows, eps);
+                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows);
   return hipGetLastError();
 }
 
@@ -190,13 +193,15 @@ hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, f
 hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
                             const float *part, int splits, float *sum_out, const float *g,
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                            hipStream_t s) {
+                            bool kmajor, hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
   if (splits > kMaxSplits || H > 4 * kNormThreads * kRowPieces || H % 4) return hipErrorInvalidValue;
+  if (kmajor && H % 64) return hipErrorInvalidValue;
+  const int km = kmajor ? rows_alloc : 0;
   if (res_type == kF32 && out_type == kF32)
-    return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, s);
+    return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, s);
   if (res_type == kBF16 && out_type == kBF16)
-    return run_norm<bf16_t, bf16_t>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, s);
+    return run_norm<bf16_t, bf16_t>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, s);
   return hipErrorInvalidValue;
 }
 

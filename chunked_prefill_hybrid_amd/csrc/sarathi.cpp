@@ -538,16 +538,18 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   float *h1 = reinterpret_cast<float *>(ws + p.h1);
   float *part = reinterpret_cast<float *>(ws + p.part);
   void *n2 = ws + p.n2, *act = ws + p.act;
+  // bf16: the norms write the QKV and gate/up GEMMs' inputs k-tile-major ([H/64][R][64])
+  const bool kmajor = ty == kBF16;
 
   // 1. norm 1 over the C+B rows (pad rows zeroed)
   HIP_TRY(mk.start(SARATHI_STAGE_NORM1));
   HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, nullptr, 0, nullptr, L->w.norm1_w, L->w.norm1_b, n1,
-                           H, T, R, d->norm_eps, s));
+                           H, T, R, d->norm_eps, kmajor, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM1, true));
   // 2. QKV projection: one GEMM over chunk and decode rows (float32 split partials)
   HIP_TRY(mk.start(SARATHI_STAGE_QKV));
   GemmArgs g{};
-  g.a = n1; g.lda = H; g.w0 = L->w.w_qkv; g.ldw = H; g.part = part;
+  g.a = n1; g.lda = H; g.a_kmajor = kmajor; g.w0 = L->w.w_qkv; g.ldw = H; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.qkv, s));
   HIP_TRY(mk.end(SARATHI_STAGE_QKV, true));
@@ -582,12 +584,12 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   // 6. h1 = x + sum of the O partials (kept in float32), then norm 2
   HIP_TRY(mk.start(SARATHI_STAGE_NORM2));
   HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, part, p.o.splits, h1, L->w.norm2_w, L->w.norm2_b, n2,
-                           H, T, R, d->norm_eps, s));
+                           H, T, R, d->norm_eps, kmajor, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM2, true));
   // 7. FFN up (+gate): activation fused into the GEMM, or split product + activation pass
   HIP_TRY(mk.start(SARATHI_STAGE_FFN_UP));
   g = GemmArgs{};
-  g.a = n2; g.lda = H; g.ldw = H; g.m_alloc = R; g.m_store = T; g.k = H;
+  g.a = n2; g.lda = H; g.a_kmajor = kmajor; g.ldw = H; g.m_alloc = R; g.m_store = T; g.k = H;
   g.w0 = llama ? L->w.w_gate : L->w.w_up;
   g.w1 = llama ? L->w.w_up : nullptr;
   if (p.up.epi == kEpiPartial) {
@@ -610,11 +612,15 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   mk.commit();
 
   if (dump) {
-    if (dump->n1) HIP_TRY(launch_to_f32(ty, n1, H, dump->n1, H, T, H, s));
+    if (dump->n1)
+      HIP_TRY(kmajor ? launch_kmajor_to_f32(ty, n1, R, dump->n1, H, T, H, s)
+                     : launch_to_f32(ty, n1, H, dump->n1, H, T, H, s));
     if (dump->q_rot) HIP_TRY(launch_to_f32(ty, q, A, dump->q_rot, A, T, A, s));
     if (dump->attn) HIP_TRY(launch_to_f32(ty, attn, A, dump->attn, A, T, A, s));
     if (dump->h1) HIP_TRY(launch_to_f32(kF32, h1, H, dump->h1, H, T, H, s));
-    if (dump->n2) HIP_TRY(launch_to_f32(ty, n2, H, dump->n2, H, T, H, s));
+    if (dump->n2)
+      HIP_TRY(kmajor ? launch_kmajor_to_f32(ty, n2, R, dump->n2, H, T, H, s)
+                     : launch_to_f32(ty, n2, H, dump->n2, H, T, H, s));
     if (dump->act) HIP_TRY(launch_to_f32(ty, act, F, dump->act, F, T, F, s));
   }
   return SARATHI_OK;
