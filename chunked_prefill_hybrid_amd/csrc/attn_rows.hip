@@ -24,12 +24,17 @@
 namespace sarathi {
 namespace {
 
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 8;       // keys per lane and online-softmax step
+// Steps whose K/V loads the fused kernel issues together.  Its occupancy is set by the chunk work's
+// registers and LDS, so its decode waves are fewer; each keeps two steps of loads in flight.  The
+// arithmetic is the same step by step, so a decode row's result does not depend on which kernel
+// served it.
+constexpr int kPrefetchFused = 2;
 
 // The work of one (row r, key split s, head h) item: the split's partial of row r's attention.  sm,
 // sl (4 floats each) and so (4 x D floats) are the caller's shared-memory arrays for the merge of the
 // four waves.
-template <typename T, int D, bool kChunkRows, bool kPaged>
+template <typename T, int D, bool kChunkRows, bool kPaged, int kPre = 1>
 __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q, int ld_q, int nh,
                                                 const ChunkSet &cs, const DecodeGroup &dg,
                                                 const PagePool &pool, int max_splits, float *part_o,
@@ -41,6 +46,8 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
   constexpr int KPW = kAttnSplit / 4;  // keys per wave per split
   constexpr int NIT = KPW / KPI;
   static_assert(NIT % kUnroll == 0, "whole unrolled steps");
+  constexpr int P = (kPre * kUnroll <= NIT && NIT % (kPre * kUnroll) == 0) ? kPre : 1;
+  constexpr int U = P * kUnroll;   // loads per lane issued together
   const RowRef rr = row_ref<kChunkRows>(r, cs, dg);
   const int n_keys = rr.pos + 1;
   const int nsp = attn_splits(n_keys);
@@ -84,51 +91,55 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
 
-  for (int c0 = 0; c0 < NIT; c0 += kUnroll) {
+  for (int c0 = 0; c0 < NIT; c0 += U) {
     if (wbeg + c0 * KPI >= k_end) break;
-    uint4 kr[kUnroll], vr[kUnroll];
-    bool ok[kUnroll];
-    size_t ko[kUnroll];
+    uint4 kr[U], vr[U];
+    bool ok[U];
+    size_t ko[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int j = wbeg + (c0 + u) * KPI + grp;
       ok[u] = j < k_end;
       ko[u] = key_off(j);
       kr[u] = ok[u] ? ld16_stream(Kh + ko[u]) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
       vr[u] = ok[u] ? ld16_stream(Vh + ko[u]) : make_uint4(0, 0, 0, 0);
-    float sc[kUnroll];
-    float cmax = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float kv[E];
-      unpack<T>(kr[u], kv);
-      float dot = 0.f;
+    for (int h = 0; h < P; ++h) {
+      if (h > 0 && wbeg + (c0 + h * kUnroll) * KPI >= k_end) break;   // the steps one at a time
+      float sc[kUnroll];
+      float cmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
+      for (int u = 0; u < kUnroll; ++u) {
+        float kv[E];
+        unpack<T>(kr[h * kUnroll + u], kv);
+        float dot = 0.f;
 #pragma unroll
-      for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
-      sc[u] = ok[u] ? dot : -INFINITY;
-      cmax = fmaxf(cmax, sc[u]);
+        for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
+#pragma unroll
+        for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
+        sc[u] = ok[h * kUnroll + u] ? dot : -INFINITY;
+        cmax = fmaxf(cmax, sc[u]);
+      }
+      cmax = wave_max(cmax, LPK);
+      const float m_new = fmaxf(m_run, cmax);
+      const float corr = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] *= corr;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float p = ok[h * kUnroll + u] ? exp2f(sc[u] - m_new) : 0.f;
+        l_run += p;
+        float vv[E];
+        unpack<T>(vr[h * kUnroll + u], vv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[e], o[e]);
+      }
+      m_run = m_new;
     }
-    cmax = wave_max(cmax, LPK);
-    const float m_new = fmaxf(m_run, cmax);
-    const float corr = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-    l_run *= corr;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] *= corr;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float p = ok[u] ? exp2f(sc[u] - m_new) : 0.f;
-      l_run += p;
-      float vv[E];
-      unpack<T>(vr[u], vv);
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[e], o[e]);
-    }
-    m_run = m_new;
   }
   // Sum over the key groups of the wave (lanes with equal `sub`); scores were replicated per group.
   l_run = wave_sum(l_run, LPK);
@@ -197,7 +208,8 @@ __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int
   } else {
     const int d = b - chunk_grid;
     const int r = d % dec_rows, rest = d / dec_rows;
-    split_attn_item<bf16_t, D, false, kPaged>(dec_row0 + r, rest % max_splits, rest / max_splits, q, ld_q,
+    split_attn_item<bf16_t, D, false, kPaged, kPrefetchFused>(dec_row0 + r, rest % max_splits,
+                                                              rest / max_splits, q, ld_q,
                                               nh, cs, dg, pool, max_splits, part_o, part_ml, dec_qscale,
                                               sm, sl, so);
   }
