@@ -78,8 +78,15 @@ def roofline_entry(stage, avg_ms, flops, nbytes, dtype):
         achieved = nbytes / (avg_ms * 1e-3) / 1e9
         peak = PEAK_HBM_GBS
         unit = "GB/s"
-    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4)}
+    e = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4)}
+    if bound == "mfma" and nbytes > 0:
+        # A contraction whose arithmetic intensity lies below the ridge point (peak flops / peak HBM
+        # bandwidth, 312 FLOP/B for bf16) has the HBM line as its roofline ceiling: its algorithmic
+        # bytes over the duration, against 8 TB/s, are reported beside the MFMA fraction.
+        e["intensity"] = round(flops / nbytes, 1)
+        e["hbm_frac"] = round(nbytes / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    return e
 
 
 def load_traffic(stage, workload_key):
