@@ -103,9 +103,10 @@ def load_traffic(stage, workload_key):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wk, weights, batch, budget_s=25.0):
-    """The CPU oracle (as it is, float64 NumPy) on the full batch, repeated while it stays within the
-    time budget; BLAS threads capped at 16 (one GPU's share of host cores)."""
+def cpu_baseline(wk, weights, batch, budget_s=25.0, target_s=10.0):
+    """The CPU oracle (as it is, float64 NumPy) on the full batch, repeated until about target_s of
+    CPU work (at least 3 runs) while it stays within the time budget; BLAS threads capped at 16 (one
+    GPU's share of host cores)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -122,7 +123,8 @@ def cpu_baseline(wk, weights, batch, budget_s=25.0):
             else:
                 oracle.layer_forward(wk.shape, weights, batch)
             times.append(time.perf_counter() - t0)
-            if time.perf_counter() - t_start + times[-1] > budget_s or len(times) >= 3:
+            spent = time.perf_counter() - t_start
+            if spent + times[-1] > budget_s or (len(times) >= 3 and spent >= target_s):
                 break
     T = batch["x"].shape[0]
     t = statistics.median(times)
