@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "hybrid-batch layer tokens/s (chunk+decodes); % bf16 MFMA and HBM roofline"
 
 
-from chunked_prefill_hybrid_amd.profiling import kernel_source_hash  # noqa: E402
+from chunked_prefill_hybrid_amd.profiling import kernel_source_hash, stage_source_hash  # noqa: E402
 
 
 def stage_work(shape, chunks, lens):
@@ -98,7 +98,7 @@ def load_traffic(stage, workload_key):
         rec = json.load(open(path)).get(f"{workload_key}:{stage}")
     except Exception:
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != stage_source_hash(stage):
         return None
     return rec.get("bytes_per_launch")
 

@@ -10,8 +10,8 @@ layer's kernels.
 
 Summary mode (CPU only): reads the two counter CSVs, scales each kernel's average per-dispatch count
 by the copy's calibration factor, prints a markdown table, and records the bytes per launch of one
-stage's kernel in a JSON file keyed "<workload>:<stage>" together with a hash of the kernel sources,
-so that a reader can tell when the figure no longer describes the code.
+stage's kernel in a JSON file keyed "<workload>:<stage>" together with a hash of the sources that
+kernel is compiled from, so that a reader can tell when the figure no longer describes the code.
 
     python -m chunked_prefill_hybrid_amd.profiling summarize --fetch <fetch.csv> --write <write.csv> \\
         --workload llama13b --stage ffn_up --kernel 'gemm_bf16_rows<4, 9, 2>' --json profiles/traffic.json
@@ -31,13 +31,31 @@ import sys
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
-def kernel_source_hash() -> str:
-    """SHA-1 (12 hex digits) over the HIP/C++ sources, in file-name order."""
+def kernel_source_hash(files=None) -> str:
+    """SHA-1 (12 hex digits) over the HIP/C++ sources (all of them, or the named ones), in file-name
+    order."""
     h = hashlib.sha1()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    paths = sorted(glob.glob(os.path.join(CSRC, "*"))) if files is None else \
+        sorted(os.path.join(CSRC, f) for f in files)
+    for p in paths:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:12]
+
+
+# The sources each stage's kernels are compiled from: a stage's traffic record stays valid while
+# these files are unchanged.
+_GEMM_SOURCES = ("common.h", "gemm.hip", "kernels.h")
+STAGE_SOURCES = {
+    "qkv": _GEMM_SOURCES, "o": _GEMM_SOURCES, "ffn_up": _GEMM_SOURCES, "ffn_down": _GEMM_SOURCES,
+    "attn_decode": ("attn_chunk_body.h", "attn_rows.hip", "common.h", "kernels.h"),
+    "attn_chunk": ("attn_chunk.hip", "attn_chunk_body.h", "common.h", "kernels.h"),
+}
+
+
+def stage_source_hash(stage) -> str:
+    """Hash of the sources of one stage's kernels (all sources for a stage not listed)."""
+    return kernel_source_hash(STAGE_SOURCES.get(stage))
 
 
 def run(argv) -> int:
@@ -145,7 +163,8 @@ def summarize(argv) -> int:
         if args.kernel and k == args.kernel:
             rec = {"kernel": k, "bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb),
                    "write_bytes": round(wb), "fetch_factor": round(f_fetch, 4),
-                   "write_factor": round(f_write, 4), "source_hash": kernel_source_hash()}
+                   "write_factor": round(f_write, 4), "source_hash": stage_source_hash(args.stage),
+                   "sources": list(STAGE_SOURCES.get(args.stage, ["*"]))}
     if args.json and args.stage:
         if rec is None:
             raise SystemExit(f"kernel {args.kernel!r} not in the CSVs")
