@@ -25,7 +25,7 @@ kernel's work is fixed by the shapes).  Every time is a median over --reps repet
 stack, measured with HIP events on the launch stream.
 
     python -m chunked_prefill_hybrid_amd.stack_bench --workload llama13b --layers 40 \\
-        --json gpurun_out/stack_llama13b.json
+        --json stack_llama13b.json
 """
 from __future__ import annotations
 

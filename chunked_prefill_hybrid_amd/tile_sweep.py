@@ -8,7 +8,7 @@ decodes) for T = t0..t1 and records the per-stage times of the four GEMMs (QKV, 
 with the library's stage timer, in their layer configuration (split-K partials, fused SwiGLU).
 
     python -m chunked_prefill_hybrid_amd.tile_sweep --workload llama13b --t0 1 --t1 1024 \\
-        --csv gpurun_out/tile_sweep.csv
+        --csv tile_sweep.csv
 
 Prints one CSV line per T (stage averages in microseconds) and, at the end, the steps: the values of T
 at which a stage's time rises by more than --step-frac over its time at T - 1.
