@@ -19,7 +19,7 @@ template <int D>
 hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkSet &cs, const PagePool &pool, void *out,
                      int ld_out, int n_split, int stride, float *part_o, float *part_ml, hipStream_t s) {
   int items = 0;
-  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], n_split, nh);
+  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh);
   const int per_xcd = (items + 7) / 8;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   if (pool.k)
@@ -35,38 +35,54 @@ hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkSet &cs, const 
 
 }  // namespace
 
-// Splits of each query block's key range, one count for every chunk of the set.  The work items run
-// in rounds of kChunkTargetWorkgroups (two per compute unit); a round lasts about as long as its
-// longest item walks its key tiles, and each split beyond the first costs about kSplitCostTiles tile
-// times (its partial is written and merged).  The count with the shortest estimated makespan wins,
-// among those that keep every split at least kMinSplitTiles tiles long and never exceed the tiles of
-// any chunk's first block (so no split is empty).  Items that leave the last round mostly idle are
-// what this avoids: with 8 query blocks x 40 heads over an 8K-key prefix, two splits make 640 items,
-// a full round and a quarter of one, no faster than one split; three make 960 in two full rounds.
-int chunk_attn_splits(const ChunkSet &cs, int nh) {
-  if (cs.n <= 0) return 1;
-  int q_blocks = 0, first_tiles = 1 << 30, by_length = 1 << 30, max_tiles = 0;
+// Splits of each chunk's query-block key ranges, chosen per chunk and written to cs.split; returns
+// the largest.  The work items run in rounds of kChunkTargetWorkgroups (two per compute unit); a
+// round lasts about as long as its longest item walks its key tiles, and each split beyond the first
+// costs about kSplitCostTiles tile times (its partial is written and merged).  For a target item
+// length of T tiles every chunk takes the splits that bring its longest block under T, within its
+// limit: splits of at least kMinSplitTiles tiles, and never more than its first block has tiles (so
+// no split is empty).  The T with the shortest estimated makespan wins.  Two cases this serves: a
+// long prefix chunk next to short new prompts in a token-budget batch is split while the short ones
+// are not, so it stops setting the makespan alone; and with 8 query blocks x 40 heads over an
+// 8K-key prefix, two splits make 640 items (a full round and a quarter of one, no faster than one
+// split) while three make 960 in two full rounds.
+int chunk_attn_splits(ChunkSet &cs, int nh) {
+  int cap[kMaxChunks], tiles[kMaxChunks], blocks[kMaxChunks];
+  int max_tiles = 1;
   for (int j = 0; j < cs.n; ++j) {
     const int C = cs.len[j], off = cs.off[j];
-    q_blocks += (C + kBQ - 1) / kBQ;
-    first_tiles = min(first_tiles, (off + min(C, kBQ) + kBKV - 1) / kBKV);
+    blocks[j] = (C + kBQ - 1) / kBQ;
+    tiles[j] = (off + C + kBKV - 1) / kBKV;
+    const int first_tiles = (off + min(C, kBQ) + kBKV - 1) / kBKV;
     const int avg_tiles = (off + (C + 1) / 2 + kBKV - 1) / kBKV;
-    by_length = min(by_length, max(1, avg_tiles / kMinSplitTiles));
-    max_tiles = max(max_tiles, (off + C + kBKV - 1) / kBKV);
+    cap[j] = max(1, min(kMaxChunkSplits, min(first_tiles, avg_tiles / kMinSplitTiles)));
+    max_tiles = max(max_tiles, tiles[j]);
+    cs.split[j] = 1;
   }
-  const int s_max = max(1, min(kMaxChunkSplits, min(by_length, first_tiles)));
-  int best = 1;
   long long best_t = -1;
-  for (int sp = 1; sp <= s_max; ++sp) {
-    const long long items = (long long)q_blocks * nh * sp;
+  int best_T = max_tiles;
+  for (int T = max_tiles; T >= 1; --T) {
+    long long items = 0;
+    int longest = 0, most = 1;
+    for (int j = 0; j < cs.n; ++j) {
+      const int sp = min(cap[j], (tiles[j] + T - 1) / T);
+      items += (long long)blocks[j] * sp * nh;
+      longest = max(longest, (tiles[j] + sp - 1) / sp);
+      most = max(most, sp);
+    }
     const long long rounds = (items + kChunkTargetWorkgroups - 1) / kChunkTargetWorkgroups;
-    const long long t = rounds * ((max_tiles + sp - 1) / sp) + (long long)kSplitCostTiles * (sp - 1);
+    const long long t = rounds * longest + (long long)kSplitCostTiles * (most - 1);
     if (best_t < 0 || t < best_t) {
       best_t = t;
-      best = sp;
+      best_T = T;
     }
   }
-  return best;
+  int most = 1;
+  for (int j = 0; j < cs.n; ++j) {
+    cs.split[j] = min(cap[j], (tiles[j] + best_T - 1) / best_T);
+    most = max(most, cs.split[j]);
+  }
+  return most;
 }
 
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
@@ -76,6 +92,8 @@ hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const Chunk
   if (cs.n > kMaxChunks) return hipErrorInvalidValue;
   if (n_split < 1 || n_split > stride || (n_split > 1 && (!part_o || !part_ml)))
     return hipErrorInvalidValue;
+  for (int j = 0; j < cs.n; ++j)
+    if (cs.split[j] < 1 || cs.split[j] > n_split) return hipErrorInvalidValue;
   if (d == 128) return run_chunk<128>(q, ld_q, nh, cs, pool, out, ld_out, n_split, stride, part_o, part_ml, s);
   if (d == 64) return run_chunk<64>(q, ld_q, nh, cs, pool, out, ld_out, n_split, stride, part_o, part_ml, s);
   return hipErrorInvalidValue;

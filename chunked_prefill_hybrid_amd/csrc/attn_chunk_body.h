@@ -77,6 +77,11 @@ template <int D> __device__ __forceinline__ int v_slot(int r, int c) {
   return D == 128 ? c ^ ((r & 7) << 1) : c;
 }
 
+// Work items of a chunk of `len` rows: 64-query blocks x key splits x heads.
+__host__ __device__ inline int chunk_items(int len, int n_split, int nh) {
+  return (len + kBQ - 1) / kBQ * n_split * nh;
+}
+
 // The work of one chunk work item (chunk, head, key split, 64-query block), for the chunk kernel and
 // for the chunk part of the fused attention kernel.  The LDS stages are the caller's
 // shared-memory arrays (separate arrays, so the compiler can tell the stages apart).
@@ -95,7 +100,7 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
   // Items are numbered chunk by chunk; the scan over the chunks is uniform across the workgroup.
   int cj = 0, first_item = 0;
   for (; cj < cs.n; ++cj) {
-    const int n_items = (cs.len[cj] + kBQ - 1) / kBQ * n_split * nh;
+    const int n_items = chunk_items(cs.len[cj], cs.split[cj], nh);
     if (item < first_item + n_items) break;
     first_item += n_items;
   }
@@ -103,7 +108,8 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
   const int C = cs.len[cj], off = cs.off[cj], row0 = cs.row0[cj], cap = cs.cap[cj];
   const int q_blocks = (C + kBQ - 1) / kBQ;
   const int local = item - first_item;
-  const int qb = local % q_blocks, split = (local / q_blocks) % n_split, h = local / (q_blocks * n_split);
+  const int ns = cs.split[cj];   // this chunk's splits (n_split is the largest of the set)
+  const int qb = local % q_blocks, split = (local / q_blocks) % ns, h = local / (q_blocks * ns);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
@@ -111,8 +117,8 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
   const int q_last = min(C, q_first + kBQ) - 1;          // last query of the workgroup
   const int n_keys = off + q_last + 1;                    // keys any of its queries sees
   const int nt = (n_keys + kBKV - 1) / kBKV;
-  const int t_begin = (int)((long long)split * nt / n_split);
-  const int t_end = (int)((long long)(split + 1) * nt / n_split);
+  const int t_begin = (int)((long long)split * nt / ns);
+  const int t_end = (int)((long long)(split + 1) * nt / ns);
   // Contiguous caches: this head's [cap, D] slab.  Paged caches: the pools, addressed per key row
   // through the chunk's block table.
   const bf16_t *Kh = kPaged ? reinterpret_cast<const bf16_t *>(pool.k)
@@ -293,7 +299,7 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
   // Row sums over the four lane groups of the query, then O[q][d] = O^T[d][q] / l.
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
-  if (n_split > 1) {
+  if (ns > 1) {   // a split chunk: partials for attn_combine (an unsplit one writes its rows)
     if (my_q < C) {
       const size_t pidx = ((size_t)(row0 + my_q) * nh + h) * stride + split;
       if (g == 0) {
@@ -325,10 +331,6 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
   __shared__ __attribute__((aligned(1024))) bf16_t k2s[kChunkStages > 2 ? TileGeom<D>::kElems : 8];    \
   __shared__ __attribute__((aligned(1024))) bf16_t v2s[kChunkStages > 2 ? TileGeom<D>::kElems : 8]
 
-// Work items of a chunk of `len` rows: 64-query blocks x key splits x heads.
-__host__ __device__ inline int chunk_items(int len, int n_split, int nh) {
-  return (len + kBQ - 1) / kBQ * n_split * nh;
-}
 
 // Chunk work item of workgroup b: XCD-aware, workgroup b runs on XCD b % 8 and the items of XCD x are
 // the consecutive range [x per_xcd, (x + 1) per_xcd), so the query blocks and splits of a head share

@@ -220,7 +220,7 @@ hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const 
                      int ld_out, int n_split, int max_splits, float *po, float *pml,
                      const DecodeGroup &dg, int dec_row0, int dec_rows, hipStream_t s) {
   int items = 0;
-  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], n_split, nh);
+  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh);
   const int per_xcd = (items + 7) / 8;
   const int chunk_grid = 8 * per_xcd;
   const int grid = chunk_grid + dec_rows * max_splits * nh;
@@ -242,6 +242,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int row0, int n_rows,
                                                                    int max_splits, int chunk_rows,
                                                                    int chunk_splits,
+                                                                   ChunkSplits table,
                                                                    const float *part_o,
                                                                    const float *part_ml, T *out,
                                                                    int ld_out) {
@@ -250,7 +251,19 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
   if (pair >= n_rows * nh) return;
   const int r = row0 + pair / nh, h = pair % nh;
   const size_t base = ((size_t)r * nh + h) * max_splits;
-  const int n_used = r < chunk_rows ? chunk_splits : max_splits;
+  int n_used = max_splits;
+  if (r < chunk_rows) {
+    n_used = chunk_splits;
+    if (chunk_splits == 0) {
+      // The row's chunk, found with constant-index selects (the table is a by-value argument).
+      int ns = table.split[0];
+#pragma unroll
+      for (int i = 1; i < kMaxChunks; ++i)
+        if (i < table.n && r >= table.row0[i]) ns = table.split[i];
+      if (ns <= 1) return;   // written by the chunk kernel
+      n_used = ns;
+    }
+  }
   float m[kCombineSlots], l[kCombineSlots], w[kCombineSlots];
   float M = -INFINITY;
 #pragma unroll
@@ -328,11 +341,12 @@ hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, cons
 
 template <typename T, int D>
 hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, int chunk_rows, int chunk_splits,
-                       const float *po, const float *pml, void *out, int ld_out, hipStream_t s) {
+                       const ChunkSplits &table, const float *po, const float *pml, void *out,
+                       int ld_out, hipStream_t s) {
   const int pairs = n_rows * nh;
   hipLaunchKernelGGL((attn_combine<T, D>), dim3((pairs + kCombineWaves - 1) / kCombineWaves),
                      dim3(64 * kCombineWaves), 0, s, nh, row0, n_rows, max_splits, chunk_rows,
-                     chunk_splits, po, pml, static_cast<T *>(out), ld_out);
+                     chunk_splits, table, po, pml, static_cast<T *>(out), ld_out);
   return hipGetLastError();
 }
 
@@ -350,13 +364,19 @@ hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, in
 }
 
 hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int max_splits,
-                               int chunk_rows, int chunk_splits, const float *part_o,
-                               const float *part_ml, void *out, int ld_out, hipStream_t s) {
+                               int chunk_rows, int chunk_splits, const ChunkSplits &table,
+                               const float *part_o, const float *part_ml, void *out, int ld_out,
+                               hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (chunk_splits < 1 || chunk_splits > max_splits || max_splits > kMaxKeySplits)
+  if (chunk_splits < 0 || chunk_splits > max_splits || max_splits > kMaxKeySplits)
     return hipErrorInvalidValue;
+  if (chunk_splits == 0 && row0 < chunk_rows) {   // some merged rows are chunk rows: the table serves
+    if (table.n < 1 || table.n > kMaxChunks) return hipErrorInvalidValue;
+    for (int j = 0; j < table.n; ++j)
+      if (table.split[j] < 1 || table.split[j] > max_splits) return hipErrorInvalidValue;
+  }
 #define SARATHI_COMBINE(T, D) \
-  return run_combine<T, D>(nh, row0, n_rows, max_splits, chunk_rows, chunk_splits, part_o, part_ml, out, ld_out, s)
+  return run_combine<T, D>(nh, row0, n_rows, max_splits, chunk_rows, chunk_splits, table, part_o, part_ml, out, ld_out, s)
   if (type == kF32 && d == 64) SARATHI_COMBINE(float, 64);
   if (type == kF32 && d == 128) SARATHI_COMBINE(float, 128);
   if (type == kBF16 && d == 64) SARATHI_COMBINE(bf16_t, 64);
@@ -373,6 +393,8 @@ hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const Chunk
     return hipErrorInvalidValue;
   if (n_split < 1 || n_split > max_splits || max_splits > kMaxKeySplits || !part_o || !part_ml)
     return hipErrorInvalidValue;
+  for (int j = 0; j < cs.n; ++j)
+    if (cs.split[j] < 1 || cs.split[j] > n_split) return hipErrorInvalidValue;
   const bool paged = pool.k != 0;
   if (d == 128)
     return paged ? run_fused<128, true>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s)

@@ -135,6 +135,7 @@ struct ChunkSet {
   int32_t len[kMaxChunks];                 // chunk rows (>= 1)
   int32_t off[kMaxChunks];                 // entries already cached = position of the first row
   int32_t row0[kMaxChunks];                // first batch row
+  int32_t split[kMaxChunks];               // key-range splits of the chunk's query blocks (>= 1)
   int32_t n, rows;                         // chunks; total chunk rows
 };
 

@@ -92,23 +92,34 @@ hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, in
                             const ChunkSet &cs, const DecodeGroup &dg, const PagePool &pool,
                             int max_splits, float *part_o, float *part_ml, hipStream_t s);
 
+// Partial counts of the chunk rows for the merge: chunk i owns rows row0[i].. (up to the next
+// chunk's first row) and left split[i] partials per row and head; split[i] == 1 means the chunk
+// kernel wrote those rows itself.
+struct ChunkSplits {
+  int32_t row0[kMaxChunks];
+  int32_t split[kMaxChunks];
+  int32_t n;
+};
 // Merges the split partials of rows [row0, row0+n_rows) into out[row, h*d + e] (storage type,
-// row stride ld_out).  Partials sit at ((row * nh + h) * max_splits + s); rows below chunk_rows
-// have chunk_splits of them, the others max_splits.
+// row stride ld_out).  Partials sit at ((row * nh + h) * max_splits + s).  Rows at or past
+// chunk_rows have max_splits of them.  Rows below it have chunk_splits of them when chunk_splits > 0;
+// with chunk_splits == 0 they have their chunk's count from `table`, and the rows of chunks with one
+// split are left as they are.
 hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int max_splits,
-                               int chunk_rows, int chunk_splits, const float *part_o,
-                               const float *part_ml, void *out, int ld_out, hipStream_t s);
+                               int chunk_rows, int chunk_splits, const ChunkSplits &table,
+                               const float *part_o, const float *part_ml, void *out, int ld_out,
+                               hipStream_t s);
 
 // Flash-style causal chunk attention (bf16, MFMA) over every chunk of the set: row row0[j] + t of
 // chunk j attends to keys 0..off[j]+t of chunk j's cache.  q and out are batch-row indexed (row
-// strides ld_q, ld_out).  With n_split > 1 each 64-query block's key tiles are split n_split ways
-// and the splits write partials (stride `stride` splits per row and head) for launch_attn_combine
-// instead of out.
+// strides ld_q, ld_out).  Chunk j's 64-query blocks split their key tiles cs.split[j] ways; n_split
+// is the largest of these.  With n_split > 1 every chunk writes partials (stride `stride` splits per
+// row and head; slots past its own count marked empty) for launch_attn_combine instead of out.
 constexpr int kChunkTargetWorkgroups = 512;   // two workgroups per compute unit
-constexpr int kMinSplitTiles = 16;            // a split keeps at least 16 key tiles
+constexpr int kMinSplitTiles = 4;             // a split keeps at least 4 key tiles
 constexpr int kMaxChunkSplits = 16;
 constexpr int kSplitCostTiles = 3;            // makespan cost of one more split, in key-tile times
-int chunk_attn_splits(const ChunkSet &cs, int nh);
+int chunk_attn_splits(ChunkSet &cs, int nh);
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
                              const PagePool &pool, void *out, int ld_out, int n_split, int stride,
                              float *part_o, float *part_ml, hipStream_t s);

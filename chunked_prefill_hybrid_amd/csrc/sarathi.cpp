@@ -340,6 +340,7 @@ ChunkSet chunk_set(const BatchView &b) {
     cs.len[j] = c.len;
     cs.off[j] = c.offset;
     cs.row0[j] = row;
+    cs.split[j] = 1;
     row += c.len;
   }
   cs.rows = row;
@@ -355,11 +356,42 @@ int max_key_splits(const sarathi_layer_desc *d, const BatchView &b, int chunk_sp
   return ms;
 }
 
+// Whether a batch runs its chunk and decode attention in one fused launch: bf16, both kinds of rows,
+// and at most one 64-query chunk block per compute unit and head with unsplit key ranges.  With more
+// chunk items the shared launch's register and LDS footprint (that of the chunk work) lowers the
+// decode splits' occupancy by more than the overlap gains (measured).
+bool fused_attention(const sarathi_layer_desc *d, const BatchView &b, const ChunkSet &cs) {
+  if (!kFusedAttention || chunk_uses_split(d) || b.C <= 0 || b.B <= 0) return false;
+  int work = 0;
+  for (int j = 0; j < cs.n; ++j) work += (cs.len[j] + 63) / 64 * d->n_heads;
+  return work <= kPlanCUs;
+}
+
+// Key-range splits of every chunk for the MFMA chunk kernel, written to cs.split; returns the
+// largest.  A fused launch takes them only while its chunk items stay within one per compute unit;
+// otherwise its chunks run unsplit.
+int plan_chunk_splits(const sarathi_layer_desc *d, const BatchView &b, ChunkSet &cs) {
+  for (int j = 0; j < cs.n; ++j) cs.split[j] = 1;
+  if (chunk_uses_split(d) || cs.n <= 0) return 1;
+  const bool fused = fused_attention(d, b, cs);
+  const int most = chunk_attn_splits(cs, d->n_heads);
+  if (fused) {
+    int items = 0;
+    for (int j = 0; j < cs.n; ++j) items += (cs.len[j] + 63) / 64 * cs.split[j] * d->n_heads;
+    if (items > kPlanCUs) {
+      for (int j = 0; j < cs.n; ++j) cs.split[j] = 1;
+      return 1;
+    }
+  }
+  return most;
+}
+
 Plan make_plan(const sarathi_layer_desc *d, const BatchView &b) {
   Plan p{};
   p.T = b.C + b.B;
   p.T_alloc = round_up(p.T, 64);
-  p.chunk_splits = chunk_uses_split(d) ? 1 : chunk_attn_splits(chunk_set(b), d->n_heads);
+  ChunkSet cs = chunk_set(b);
+  p.chunk_splits = plan_chunk_splits(d, b, cs);
   p.max_splits = max_key_splits(d, b, p.chunk_splits);
   const int ty = d->dtype;
   const size_t el = elem_size(ty), R = p.T_alloc;
@@ -462,20 +494,16 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
                              const void *q, void *out, char *ws, hipStream_t s, Marker &mk) {
   const int A = d->n_heads * d->head_dim;
   const int C = b.C, B = b.B;
-  const ChunkSet cs = chunk_set(b);
+  ChunkSet cs = chunk_set(b);
+  plan_chunk_splits(d, b, cs);   // the same counts as p.chunk_splits (their largest)
   const PagePool pool = page_pool(b);
   float *po = reinterpret_cast<float *>(ws + p.part_o);
   float *pml = reinterpret_cast<float *>(ws + p.part_ml);
   const bool split_chunk = chunk_uses_split(d);
-  // bf16 batches with chunk rows and decode rows run both attentions in one launch when the chunk
-  // work items are fewer than the compute units: the decode splits then fill the units the
-  // latency-bound chunk work leaves idle.  With more chunk items the shared launch's register and LDS
-  // footprint (that of the chunk work) halves the decode splits' occupancy, which costs more than the
-  // overlap gains (measured), so the two run as separate launches.  The fused launch's time is
-  // recorded as the decode stage.
-  int chunk_work = 0;
-  for (int j = 0; j < cs.n; ++j) chunk_work += (cs.len[j] + 63) / 64 * p.chunk_splits * d->n_heads;
-  const bool fused = kFusedAttention && !split_chunk && C > 0 && B > 0 && chunk_work <= kPlanCUs;
+  // Batches with chunk rows and decode rows run both attentions in one launch when fused_attention
+  // says so (few chunk items): the decode splits then fill the units the latency-bound chunk work
+  // leaves idle.  The fused launch's time is recorded as the decode stage.
+  const bool fused = fused_attention(d, b, cs);
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_CHUNK));
   if (C > 0 && !fused) {
     if (split_chunk) {
@@ -500,13 +528,21 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_MERGE));
-  // Chunk rows need merging when the split-KV kernel served them or the MFMA kernel was split.
+  // Chunk rows need merging when the split-KV kernel served them (all of them, max_splits partials
+  // each) or their chunk was split by the MFMA kernel (the merge reads each chunk's count from the
+  // table and leaves the rows of unsplit chunks alone).
   const bool merge_chunk = split_chunk || p.chunk_splits > 1;
   const int merge_row0 = merge_chunk ? 0 : C;
-  const int chunk_splits = split_chunk ? p.max_splits : p.chunk_splits;
+  const int chunk_splits = split_chunk ? p.max_splits : 0;
+  ChunkSplits table{};
+  table.n = cs.n;
+  for (int j = 0; j < cs.n; ++j) {
+    table.row0[j] = cs.row0[j];
+    table.split[j] = cs.split[j];
+  }
   if (C + B > merge_row0)
     HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, merge_row0, C + B - merge_row0,
-                                p.max_splits, C, chunk_splits, po, pml, out, A, s));
+                                p.max_splits, C, chunk_splits, table, po, pml, out, A, s));
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_MERGE, C + B > merge_row0));
   return SARATHI_OK;
 }

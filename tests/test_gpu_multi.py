@@ -63,6 +63,8 @@ def run_case(shape, chunk_specs, dec_lens, seed=0, label=None):
     (MID_GPT, [(33, 0), (65, 128)], [17]),
     (MID_D64, [(17, 3), (80, 100)], []),
     (MID, [(64, 2100), (40, 2500)], [30]),                         # long prefixes: split key ranges
+    (MID, [(64, 2100), (100, 0), (30, 50)], []),                   # per-chunk splits 3, 1, 1
+    (MID, [(64, 2100), (100, 0), (30, 50)], [40, 900]),            # the same in the fused launch
     (MID, [(n, 7 * n) for n in range(1, 17)], [3]),                # sixteen chunks of 1..16 rows
     (MID, [], [9, 300]),                                           # no chunk at all
 ])
