@@ -74,6 +74,7 @@ def test_paged_bf16_page_sizes(page):
     (MID_GPT, [(65, 128)], [17], 16),
     (MID_D64, [(17, 3), (80, 100)], [9], 32),
     (MID, [(64, 2100), (40, 2500)], [30], 16),      # split key ranges of the chunk kernel
+    (MID, [(64, 2100), (100, 0), (30, 50)], [], 8), # per-chunk split counts 3, 1, 1
     (MID, [], [1, 40, 1023], 16),                   # decodes only
     (MID, [(200, 0)], [], 1),                       # one-token pages
 ])
