@@ -35,6 +35,7 @@ EXPORTED = [
     "sarathi_multi_forward", "sarathi_multi_forward_debug", "sarathi_multi_forward_timed",
     "sarathi_paged_batch_check", "sarathi_paged_workspace_size", "sarathi_paged_forward",
     "sarathi_paged_forward_debug", "sarathi_paged_forward_timed",
+    "sarathi_plan_describe", "sarathi_multi_plan_describe", "sarathi_paged_plan_describe",
 ]
 
 SARATHI_MAX_CHUNKS = 16
@@ -99,6 +100,18 @@ class sarathi_paged_batch(ctypes.Structure):
                 ("chunks", POINTER(sarathi_paged_chunk)), ("n_decodes", c_int32), ("reserved2", c_int32),
                 ("decode_tables", POINTER(sarathi_page_table)), ("decode_len", POINTER(c_int32)),
                 ("x", c_void_p), ("y", c_void_p)]
+
+
+class sarathi_gemm_plan(ctypes.Structure):
+    _fields_ = [("epilogue", c_int32), ("row_tiles", c_int32), ("col_tiles", c_int32), ("k_splits", c_int32)]
+
+
+class sarathi_plan_info(ctypes.Structure):
+    _fields_ = [("rows", c_int32), ("rows_alloc", c_int32), ("n_chunks", c_int32),
+                ("fused_attention", c_int32), ("chunk_splits", c_int32 * SARATHI_MAX_CHUNKS),
+                ("max_key_splits", c_int32), ("reserved", c_int32),
+                ("qkv", sarathi_gemm_plan), ("o", sarathi_gemm_plan), ("up", sarathi_gemm_plan),
+                ("down", sarathi_gemm_plan), ("workspace_bytes", ctypes.c_uint64)]
 
 
 class sarathi_debug_dump(ctypes.Structure):
@@ -179,6 +192,13 @@ def lib():
         L.sarathi_paged_forward_debug.restype = c_int32
         L.sarathi_paged_forward_timed.argtypes = [c_void_p, PB, c_void_p, c_size_t, c_void_p, c_void_p]
         L.sarathi_paged_forward_timed.restype = c_int32
+        PI = POINTER(sarathi_plan_info)
+        L.sarathi_plan_describe.argtypes = [POINTER(sarathi_layer_desc), POINTER(sarathi_batch), PI]
+        L.sarathi_plan_describe.restype = c_int32
+        L.sarathi_multi_plan_describe.argtypes = [POINTER(sarathi_layer_desc), MB, PI]
+        L.sarathi_multi_plan_describe.restype = c_int32
+        L.sarathi_paged_plan_describe.argtypes = [POINTER(sarathi_layer_desc), PB, PI]
+        L.sarathi_paged_plan_describe.restype = c_int32
         L.sarathi_status_str.argtypes = [c_int32]
         L.sarathi_status_str.restype = c_char_p
         L.sarathi_last_error.argtypes = []
@@ -411,3 +431,16 @@ def make_paged_batch(pool, chunks, decode_tables, decode_len, x: int, y: int):
                             ctypes.cast(tb_arr, POINTER(sarathi_page_table)) if B else None,
                             ctypes.cast(len_arr, POINTER(c_int32)), x or 0, y or 0)
     return b, (ch_arr, tb_arr, len_arr)
+
+
+def plan_describe(desc: sarathi_layer_desc, batch) -> sarathi_plan_info:
+    """The launch plan of a forward over a single-chunk, multi-chunk or paged batch (host only)."""
+    info = sarathi_plan_info()
+    if isinstance(batch, sarathi_multi_batch):
+        st = lib().sarathi_multi_plan_describe(byref(desc), byref(batch), byref(info))
+    elif isinstance(batch, sarathi_paged_batch):
+        st = lib().sarathi_paged_plan_describe(byref(desc), byref(batch), byref(info))
+    else:
+        st = lib().sarathi_plan_describe(byref(desc), byref(batch), byref(info))
+    _check(st, "plan_describe")
+    return info

@@ -683,6 +683,40 @@ size_t workspace_bytes(const sarathi_layer_desc *d, const Batch *b) {
   return make_plan(d, v).total;
 }
 
+sarathi_gemm_plan gemm_info(const GemmPlan &g) {
+  sarathi_gemm_plan out{};
+  out.epilogue = g.epi;
+  out.row_tiles = g.m_tiles;
+  out.col_tiles = g.n_tiles;
+  out.k_splits = g.splits;
+  return out;
+}
+
+template <typename Batch>
+sarathi_status describe_entry(const sarathi_layer_desc *d, const Batch *b, sarathi_plan_info *info) {
+  if (!info) return fail(SARATHI_ERR_INVALID, "info is null");
+  BatchView v;
+  const sarathi_status st = checked_view(d, b, false, &v);
+  if (st != SARATHI_OK) return st;
+  const Plan p = make_plan(d, v);
+  ChunkSet cs = chunk_set(v);
+  plan_chunk_splits(d, v, cs);
+  sarathi_plan_info out{};
+  out.rows = p.T;
+  out.rows_alloc = p.T_alloc;
+  out.n_chunks = cs.n;
+  out.fused_attention = fused_attention(d, v, cs) ? 1 : 0;
+  for (int j = 0; j < cs.n; ++j) out.chunk_splits[j] = cs.split[j];
+  out.max_key_splits = p.max_splits;
+  out.qkv = gemm_info(p.qkv);
+  out.o = gemm_info(p.o);
+  out.up = gemm_info(p.up);
+  out.down = gemm_info(p.down);
+  out.workspace_bytes = p.total;
+  *info = out;
+  return SARATHI_OK;
+}
+
 template <typename Batch>
 sarathi_status forward_entry(sarathi_layer *L, const Batch *b, void *workspace, size_t ws_bytes,
                              void *stream, const sarathi_debug_dump *dump, sarathi_timer *timer) {
@@ -1027,5 +1061,20 @@ const char *sarathi_status_str(sarathi_status status) {
 }
 
 const char *sarathi_last_error(void) { return g_last_error.c_str(); }
+
+sarathi_status sarathi_plan_describe(const sarathi_layer_desc *desc, const sarathi_batch *batch,
+                                     sarathi_plan_info *info) {
+  return describe_entry(desc, batch, info);
+}
+
+sarathi_status sarathi_multi_plan_describe(const sarathi_layer_desc *desc,
+                                           const sarathi_multi_batch *batch, sarathi_plan_info *info) {
+  return describe_entry(desc, batch, info);
+}
+
+sarathi_status sarathi_paged_plan_describe(const sarathi_layer_desc *desc,
+                                           const sarathi_paged_batch *batch, sarathi_plan_info *info) {
+  return describe_entry(desc, batch, info);
+}
 
 }  // extern "C"

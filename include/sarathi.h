@@ -375,6 +375,40 @@ sarathi_status sarathi_paged_forward_timed(sarathi_layer *layer, const sarathi_p
  * timer.  Errors: INVALID, HIP. */
 sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_t *count);
 
+/* ---- Launch plan (inspection) -------------------------------------------------------------------
+ * How a forward over a batch would run, computed on the host exactly as the forward computes it, with
+ * no device work: for tests and tools.  The four linear ops run as one GEMM each over all C+B rows
+ * and attention is split per request (SARATHI: Efficient LLM Inference by Piggybacking Decodes with
+ * Chunked Prefills, "Decode-Maximal Batching"); the row tiles of those GEMMs are what the
+ * same page's tile-quantization discussion ("Identifying the Ideal Chunk Size", Figure 7) is about. */
+typedef struct {
+    int32_t epilogue;    /* 0 bf16/f32 store, 1 float32 split-K partials, 2 SiLU*mul, 3 GELU */
+    int32_t row_tiles;   /* workgroup tiles along the batch rows */
+    int32_t col_tiles;   /* workgroup tiles along the output columns */
+    int32_t k_splits;    /* split-K factor (partials summed in split order by the next kernel) */
+} sarathi_gemm_plan;     /* 16 bytes */
+
+typedef struct {
+    int32_t rows;                                /* C + B */
+    int32_t rows_alloc;                          /* rows of the activation buffers (multiple of 64) */
+    int32_t n_chunks;
+    int32_t fused_attention;                     /* 1: chunk and decode attention in one launch */
+    int32_t chunk_splits[SARATHI_MAX_CHUNKS];    /* key-range splits of each chunk's query blocks */
+    int32_t max_key_splits;                      /* split partials per row and head */
+    int32_t reserved;
+    sarathi_gemm_plan qkv, o, up, down;          /* up: gate|up for LLAMA, up for GPT */
+    uint64_t workspace_bytes;                    /* as the matching *_workspace_size */
+} sarathi_plan_info;     /* 160 bytes */
+
+/* Fill *info for a forward over `batch`.  Errors: as the matching *_batch_check (without the x/y
+ * requirement), or INVALID for a null info; *info is left unchanged then. */
+sarathi_status sarathi_plan_describe(const sarathi_layer_desc *desc, const sarathi_batch *batch,
+                                     sarathi_plan_info *info);
+sarathi_status sarathi_multi_plan_describe(const sarathi_layer_desc *desc,
+                                           const sarathi_multi_batch *batch, sarathi_plan_info *info);
+sarathi_status sarathi_paged_plan_describe(const sarathi_layer_desc *desc,
+                                           const sarathi_paged_batch *batch, sarathi_plan_info *info);
+
 /* Static description of a status code. */
 const char *sarathi_status_str(sarathi_status status);
 

@@ -247,3 +247,100 @@ def test_paged_invalid_batches(lib, kw, status):
     b, keep = paged(**kw)
     assert _abi.sarathi_paged_batch_check(desc(), b) == status
     assert _abi.sarathi_last_error() != ""
+
+
+# ---- launch plans (host only) ----------------------------------------------------------------------
+
+def desc13b(**kw):
+    """The llama-13b layer in bf16."""
+    return desc(hidden=5120, n_heads=40, head_dim=128, ffn=13824, dtype=_abi.SARATHI_BF16, max_tokens=1024,
+                max_pos=8192, **kw)
+
+
+def gemms(info):
+    return [getattr(info, g) for g in ("qkv", "o", "up", "down")]
+
+
+def test_plan_info_layout():
+    assert ctypes.sizeof(_abi.sarathi_gemm_plan) == 16
+    assert ctypes.sizeof(_abi.sarathi_plan_info) == 160
+    assert _abi.sarathi_plan_info.chunk_splits.offset == 16
+    assert _abi.sarathi_plan_info.qkv.offset == 88 and _abi.sarathi_plan_info.workspace_bytes.offset == 152
+
+
+def test_plan_of_hybrid_batch(lib):
+    """C = 256 at offset 768 with 18 decodes of 1024: 4 query blocks x 40 heads = 160 chunk items fit
+    one pass of the chip, so the chunk and the decodes share one attention launch, unsplit."""
+    d = desc13b()
+    b, keep = batch(C=256, off=768, cap=1024, lens=(1024,) * 18, caps=[1025] * 18)
+    info = _abi.plan_describe(d, b)
+    assert info.rows == 274 and info.rows_alloc >= 274 and info.n_chunks == 1
+    assert info.fused_attention == 1 and list(info.chunk_splits) == [1] + [0] * 15
+    assert info.max_key_splits >= 1
+    assert [g.epilogue for g in gemms(info)] == [1, 1, 2, 1]          # partials except SiLU*up
+    assert [g.col_tiles for g in gemms(info)] == [3 * 5120 // 128, 5120 // 128, 13824 // 64, 5120 // 128]
+    assert all(g.row_tiles == 1 and g.k_splits >= 1 for g in gemms(info))
+    assert info.workspace_bytes == _abi.sarathi_workspace_size(d, b)
+
+
+def test_gemm_plan_independent_of_batch_rows(lib):
+    """Split-K counts and epilogues depend on the weight shape alone, so a row's k-sum is cut at the
+    same points in a one-decode batch and in a hybrid batch of several hundred rows."""
+    d = desc13b()
+    plans = []
+    for kw in (dict(C=0, lens=(10,)), dict(C=0, cap=8192, lens=(4000,) * 48),
+               dict(C=256, off=768, cap=1024, lens=(1024,) * 18), dict(C=512, off=7680, cap=8192, lens=(4000,) * 48)):
+        b, keep = batch(**kw)
+        info = _abi.plan_describe(d, b)
+        assert info.rows == kw["C"] + len(kw["lens"])
+        plans.append([(g.epilogue, g.k_splits, g.col_tiles) for g in gemms(info)])
+    assert all(p == plans[0] for p in plans)
+
+
+def test_plan_splits_long_chunk(lib):
+    """C = 512 at offset 7680: 320 chunk items exceed one pass, so attention runs as separate chunk
+    and decode launches, and the chunk's 8192-key range is cut into several splits."""
+    b, keep = batch(C=512, off=7680, cap=8192, lens=(4000,) * 48)
+    info = _abi.plan_describe(desc13b(), b)
+    assert info.fused_attention == 0 and info.n_chunks == 1
+    assert 1 < info.chunk_splits[0] <= info.max_key_splits
+    assert list(info.chunk_splits)[1:] == [0] * 15
+
+
+def test_plan_of_decode_only_batch(lib):
+    b, keep = batch(C=0, lens=(10, 700))
+    info = _abi.plan_describe(desc13b(), b)
+    assert info.n_chunks == 0 and info.fused_attention == 0 and list(info.chunk_splits) == [0] * 16
+    assert info.rows == 2
+
+
+def test_plan_of_token_budget_batch(lib):
+    """Three chunks (94 tokens at offset 930, a whole 300-token prompt, 100 tokens of a new prompt):
+    the chunk with the longest key range gets the most splits."""
+    b, keep = multi(chunks=((94, 930, 1024), (300, 0, 300), (100, 0, 1024)), lens=(1024,) * 12)
+    info = _abi.plan_describe(desc13b(), b)
+    assert info.rows == 506 and info.n_chunks == 3 and info.fused_attention == 0
+    s = list(info.chunk_splits)
+    assert all(x >= 1 for x in s[:3]) and s[3:] == [0] * 13
+    assert s[0] == max(s[:3]) and s[0] > 1
+    assert info.workspace_bytes == _abi.sarathi_multi_workspace_size(desc13b(), b)
+
+
+def test_paged_plan_matches_multi(lib):
+    """Paging changes where keys live, not the launch plan."""
+    d = desc13b()
+    b1, k1 = paged(chunks=((94, 930, 64), (300, 0, 19)), lens=(1000,), dec_entries=(64,),
+                   pool=(addr(60), addr(61), 4096, 16))
+    b2, k2 = _abi.make_multi_batch([(94, 930, addr(40), addr(41), 1024), (300, 0, addr(42), addr(43), 300)],
+                                   [(addr(10), addr(11), 1001)], [1000], addr(0), addr(1))
+    p1, p2 = _abi.plan_describe(d, b1), _abi.plan_describe(d, b2)
+    assert bytes(p1) == bytes(p2)
+
+
+def test_plan_describe_rejects_invalid(lib):
+    b, keep = multi(chunks=((0, 0, 8),))
+    with pytest.raises(_abi.SarathiError) as e:
+        _abi.plan_describe(desc(), b)
+    assert e.value.status == _abi.SARATHI_ERR_INVALID
+    b, keep = batch()
+    assert lib.sarathi_plan_describe(ctypes.byref(desc()), ctypes.byref(b), None) == _abi.SARATHI_ERR_INVALID
