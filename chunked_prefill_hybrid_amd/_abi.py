@@ -109,7 +109,7 @@ class sarathi_gemm_plan(ctypes.Structure):
 class sarathi_plan_info(ctypes.Structure):
     _fields_ = [("rows", c_int32), ("rows_alloc", c_int32), ("n_chunks", c_int32),
                 ("fused_attention", c_int32), ("chunk_splits", c_int32 * SARATHI_MAX_CHUNKS),
-                ("max_key_splits", c_int32), ("reserved", c_int32),
+                ("max_key_splits", c_int32), ("chunk_query_blocks", c_int32),
                 ("qkv", sarathi_gemm_plan), ("o", sarathi_gemm_plan), ("up", sarathi_gemm_plan),
                 ("down", sarathi_gemm_plan), ("workspace_bytes", ctypes.c_uint64)]
 

@@ -6,18 +6,20 @@
 // "Chunked-Prefills", attention mask construction and Figure 6).  The prefix is re-read from HBM by
 // every chunk of the request, the overhead the same page discusses under "Overhead 2".
 //
-// Flash-style design for gfx950.  A workgroup takes one head and 64 queries (16 per wave) and streams
-// a range of the request's keys in tiles of 64 through a 2- or 3-stage LDS ring filled by LDS DMA
+// Flash-style design for gfx950.  A workgroup takes one head and 64 RB queries (16 RB per wave, in RB
+// blocks of 16) and streams a range of the request's keys in tiles of 64 through a 2- or 3-stage LDS ring filled by LDS DMA
 // (global_load_lds_dwordx4: no staging registers, no LDS store instructions).  Per wave and tile:
-//   S^T = K Q^T   (16 x v_mfma_f32_16x16x32_bf16 for d = 128): lane l then holds the scores of query
-//                 l % 16 for 16 of the tile's keys, so a query's row max / sum need only in-lane work
-//                 and two butterfly steps;
+//   S^T = K Q^T   (16 x v_mfma_f32_16x16x32_bf16 per block for d = 128): lane l then holds the
+//                 scores of query l % 16 of each block for 16 of the tile's keys, so a query's row
+//                 max / sum need only in-lane work and two butterfly steps;
 //   online softmax in float32 (log2 domain, scale folded into the exponent);
 //   O^T += V^T P^T (16 more MFMAs): P^T is taken straight from the S^T registers, and V^T's operand
 //                 comes from the row-major V tile through transposing LDS reads (ds_read_b64_tr_b16:
 //                 in each group of 16 lanes, lane j addresses row j/4, columns 4(j%4)..4(j%4)+3, and
 //                 lane i receives column i of those 4 rows), so the keys of a lane's k-slots match
 //                 the keys of its P^T values without any register shuffling.
+// Each K and V fragment read from LDS feeds the MFMAs of all RB query blocks of the wave, so RB = 2
+// halves the LDS reads per score and doubles the independent MFMA chains per wave.
 // K rows are stored with their 16-byte chunks permuted (slot = chunk ^ f(row)) so the 16 rows of a
 // fragment read hit distinct banks; V rows likewise for the transposing reads.  Only tiles that cross
 // the diagonal are masked.  Rows past the last key any query of the block needs are loaded as copies
@@ -42,7 +44,7 @@
 namespace sarathi {
 namespace {
 
-constexpr int kBQ = 64;         // queries per workgroup (16 per wave)
+constexpr int kBQ = 64;         // queries per workgroup at one 16-query block per wave
 constexpr int kBKV = 64;        // keys per tile
 #ifndef SARATHI_CHUNK_STAGES
 #define SARATHI_CHUNK_STAGES 2
@@ -77,15 +79,15 @@ template <int D> __device__ __forceinline__ int v_slot(int r, int c) {
   return D == 128 ? c ^ ((r & 7) << 1) : c;
 }
 
-// Work items of a chunk of `len` rows: 64-query blocks x key splits x heads.
-__host__ __device__ inline int chunk_items(int len, int n_split, int nh) {
-  return (len + kBQ - 1) / kBQ * n_split * nh;
+// Work items of a chunk of `len` rows: bq-query blocks x key splits x heads.
+__host__ __device__ inline int chunk_items(int len, int n_split, int nh, int bq) {
+  return (len + bq - 1) / bq * n_split * nh;
 }
 
 // The work of one chunk work item (chunk, head, key split, 64-query block), for the chunk kernel and
 // for the chunk part of the fused attention kernel.  The LDS stages are the caller's
 // shared-memory arrays (separate arrays, so the compiler can tell the stages apart).
-template <int D, bool kPaged>
+template <int D, bool kPaged, int RB>
 __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int ld_q, int nh,
                                                 const ChunkSet &cs, const PagePool &pool, bf16_t *out,
                                                 int ld_out, float qscale_log2, int n_split, int stride,
@@ -94,27 +96,30 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
   using G = TileGeom<D>;
   constexpr int KS = D / 32;             // k-steps of the score MFMA
   constexpr int DB = D / 16;             // 16-row blocks of O^T
+  constexpr int BQ = kBQ * RB;           // queries of the workgroup
+  static_assert(RB == 1 || RB == 2, "query blocks per wave");
   auto kst = [&](int u) -> bf16_t * { return u == 0 ? k0s : u == 1 ? k1s : k2s; };
   auto vst = [&](int u) -> bf16_t * { return u == 0 ? v0s : u == 1 ? v1s : v2s; };
 
   // Items are numbered chunk by chunk; the scan over the chunks is uniform across the workgroup.
   int cj = 0, first_item = 0;
   for (; cj < cs.n; ++cj) {
-    const int n_items = chunk_items(cs.len[cj], cs.split[cj], nh);
+    const int n_items = chunk_items(cs.len[cj], cs.split[cj], nh, BQ);
     if (item < first_item + n_items) break;
     first_item += n_items;
   }
   if (cj >= cs.n) return;
   const int C = cs.len[cj], off = cs.off[cj], row0 = cs.row0[cj], cap = cs.cap[cj];
-  const int q_blocks = (C + kBQ - 1) / kBQ;
+  const int q_blocks = (C + BQ - 1) / BQ;
   const int local = item - first_item;
   const int ns = cs.split[cj];   // this chunk's splits (n_split is the largest of the set)
   const int qb = local % q_blocks, split = (local / q_blocks) % ns, h = local / (q_blocks * ns);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  const int q_first = qb * kBQ;
-  const int q_last = min(C, q_first + kBQ) - 1;          // last query of the workgroup
+  const int q_first = qb * BQ;
+  const int q_last = min(C, q_first + BQ) - 1;           // last query of the workgroup
+  const int q_wave = q_first + wave * 16 * RB;            // first query of this wave
   const int n_keys = off + q_last + 1;                    // keys any of its queries sees
   const int nt = (n_keys + kBKV - 1) / kBKV;
   const int t_begin = (int)((long long)split * nt / ns);
@@ -127,15 +132,18 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
                             : reinterpret_cast<const bf16_t *>(cs.v[cj]) + (size_t)h * cap * D;
   const int32_t *table = reinterpret_cast<const int32_t *>(cs.k[cj]);
 
-  // This lane's query (row of the wave's 16) and its fragments of q (B operand of S^T = K Q^T).
-  const int my_q = q_first + wave * 16 + c16;
-  const int my_pos = off + min(my_q, C - 1);
-  bf16x8_t qf[KS];
-  {
-    const bf16_t *qr = q + (size_t)(row0 + min(my_q, C - 1)) * ld_q + h * D;
+  // This lane's query in each of the wave's blocks (row c16 of block rb) and its fragments of q
+  // (B operand of S^T = K Q^T).
+  int my_q[RB], my_pos[RB];
+  bf16x8_t qf[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    my_q[rb] = q_wave + rb * 16 + c16;
+    my_pos[rb] = off + min(my_q[rb], C - 1);
+    const bf16_t *qr = q + (size_t)(row0 + min(my_q[rb], C - 1)) * ld_q + h * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8_t *>(qr + ks * 32 + g * 8);
+      qf[rb][ks] = *reinterpret_cast<const bf16x8_t *>(qr + ks * 32 + g * 8);
   }
 
   // DMA sources: load i of this wave fills tile rows kRPL (wave + 4 i) .. + kRPL - 1; lane l lands
@@ -172,80 +180,92 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
     }
   };
 
-  f32x4_t o[DB];
+  f32x4_t o[RB][DB];
+  float m_run[RB], l_run[RB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
 
   auto compute = [&](int u, int t) {
     const bf16_t *Ks = kst(u), *Vs = vst(u);
-    // S^T for the tile: 4 key blocks of 16.
-    f32x4_t sacc[4];
+    // S^T for the tile: 4 key blocks of 16, each K fragment shared by the wave's query blocks.
+    f32x4_t sacc[RB][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int r = kb * 16 + c16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Ks[r * D + k_slot<D>(r, ks * 4 + g) * 8]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ks], sacc[rb][kb], 0, 0, 0);
       }
     }
     // Raw scores, masked past each query's position; only tiles that reach past the wave's first
     // query need the mask (a wave-uniform test).  The log2-domain scale (positive) is applied to the
     // maximum and inside each exponent's multiply-add.
     const int k0 = t * kBKV;
-    const bool diag = k0 + kBKV - 1 > off + q_first + wave * 16;
-    float sc[4][4];
+    const bool diag = k0 + kBKV - 1 > off + q_wave;
+    bf16x8_t pf[RB][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[kb][i] = sacc[kb][i];
-    if (diag) {
+    for (int rb = 0; rb < RB; ++rb) {
+      float sc[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + kb * 16 + g * 4 + i > my_pos) sc[kb][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) sc[kb][i] = sacc[rb][kb][i];
+      if (diag) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + kb * 16 + g * 4 + i > my_pos[rb]) sc[kb][i] = -INFINITY;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      // The exponent base m_run moves only when a tile's maximum exceeds it by more than kRebase (in
+      // log2 units): probabilities then stay below 2^kRebase, well inside float32 and bfloat16
+      // range, and the running sums are rescaled on a few tiles instead of on every tile with a new
+      // maximum.  Any base gives the same softmax, since O and l share it.  A split that starts past
+      // a query's position leaves its row fully masked (m_run stays -inf): the exponent base is then
+      // 0, every p is 0 and the row's partial stays empty (l = 0).
+      const float m_tile = tmax * qscale_log2;
+      const bool rebase = m_tile > m_run[rb] + kRebase;
+      if (__any(rebase)) {
+        const float m_new = rebase ? m_tile : m_run[rb];
+        // 1 for a query whose base stays, 0 for one whose sums are still empty (m_run = -inf)
+        const float corr = exp2_nonpos(m_run[rb] - (m_new == -INFINITY ? 0.f : m_new));
+        l_run[rb] *= corr;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= corr;
+        m_run[rb] = m_new;
+      }
+      const float m_base = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+      // P^T operands: k-step s holds keys s*32 + 4g + i (slots 0..3) and s*32 + 16 + 4g + i (4..7).
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * s + hb][i], qscale_log2, -m_base));
+            l_run[rb] += p;
+            pf[rb][s][hb * 4 + i] = (__bf16)p;
+          }
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    // The exponent base m_run moves only when a tile's maximum exceeds it by more than kRebase (in
-    // log2 units): probabilities then stay below 2^kRebase, well inside float32 and bfloat16 range,
-    // and the running sums are rescaled on a few tiles instead of on every tile with a new maximum.
-    // Any base gives the same softmax, since O and l share it.  A split that starts past a query's
-    // position leaves its row fully masked (m_run stays -inf): the exponent base is then 0, every p is
-    // 0 and the row's partial stays empty (l = 0).
-    const float m_tile = tmax * qscale_log2;
-    const bool rebase = m_tile > m_run + kRebase;
-    if (__any(rebase)) {
-      const float m_new = rebase ? m_tile : m_run;
-      // 1 for a query whose base stays, 0 for one whose sums are still empty (m_run = -inf)
-      const float corr = exp2_nonpos(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      l_run *= corr;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= corr;
-      m_run = m_new;
-    }
-    const float m_base = m_run == -INFINITY ? 0.f : m_run;
-    // P^T operands: k-step s holds keys s*32 + 4g + i (slots 0..3) and s*32 + 16 + 4g + i (4..7).
-    bf16x8_t pf[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * s + hb][i], qscale_log2, -m_base));
-          l_run += p;
-          pf[s][hb * 4 + i] = (__bf16)p;
-        }
-    // O^T += V^T P^T; V^T fragments by transposing reads of rows s*32 + 4g + (0..3) and + 16.
+    // O^T += V^T P^T; V^T fragments by transposing reads of rows s*32 + 4g + (0..3) and + 16, each
+    // shared by the wave's query blocks.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int col = db * 16 + 4 * (c16 & 3);          // this lane's 4 addressed columns
@@ -261,8 +281,10 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
         }
         const s16x8_t vv = {half[0][0], half[0][1], half[0][2], half[0][3],
                             half[1][0], half[1][1], half[1][2], half[1][3]};
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[s], o[db],
-                                                         0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[rb][s],
+                                                              o[rb][db], 0, 0, 0);
       }
     }
   };
@@ -297,29 +319,35 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
   }
 
   // Row sums over the four lane groups of the query, then O[q][d] = O^T[d][q] / l.
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
-  if (ns > 1) {   // a split chunk: partials for attn_combine (an unsplit one writes its rows)
-    if (my_q < C) {
-      const size_t pidx = ((size_t)(row0 + my_q) * nh + h) * stride + split;
-      if (g == 0) {
-        part_ml[2 * pidx] = m_run;
-        part_ml[2 * pidx + 1] = l_run;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float l = l_run[rb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int qr = my_q[rb];
+    if (ns > 1) {   // a split chunk: partials for attn_combine (an unsplit one writes its rows)
+      if (qr < C) {
+        const size_t pidx = ((size_t)(row0 + qr) * nh + h) * stride + split;
+        if (g == 0) {
+          part_ml[2 * pidx] = m_run[rb];
+          part_ml[2 * pidx + 1] = l;
+        }
+        float *po = part_o + pidx * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<float4 *>(&po[db * 16 + g * 4]) =
+              make_float4(o[rb][db][0], o[rb][db][1], o[rb][db][2], o[rb][db][3]);
       }
-      float *po = part_o + pidx * D;
+    } else if (qr < C) {
+      const float inv = 1.0f / l;
+      bf16_t *orow = out + (size_t)(row0 + qr) * ld_out + h * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<float4 *>(&po[db * 16 + g * 4]) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-    }
-  } else if (my_q < C) {
-    const float inv = 1.0f / l_run;
-    bf16_t *orow = out + (size_t)(row0 + my_q) * ld_out + h * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      uint2 u;
-      u.x = (uint32_t)f32_to_bf16(o[db][0] * inv) | ((uint32_t)f32_to_bf16(o[db][1] * inv) << 16);
-      u.y = (uint32_t)f32_to_bf16(o[db][2] * inv) | ((uint32_t)f32_to_bf16(o[db][3] * inv) << 16);
-      *reinterpret_cast<uint2 *>(&orow[db * 16 + g * 4]) = u;
+      for (int db = 0; db < DB; ++db) {
+        uint2 u;
+        u.x = (uint32_t)f32_to_bf16(o[rb][db][0] * inv) | ((uint32_t)f32_to_bf16(o[rb][db][1] * inv) << 16);
+        u.y = (uint32_t)f32_to_bf16(o[rb][db][2] * inv) | ((uint32_t)f32_to_bf16(o[rb][db][3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(&orow[db * 16 + g * 4]) = u;
+      }
     }
   }
 }

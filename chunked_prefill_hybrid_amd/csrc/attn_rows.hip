@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int
   __shared__ float sm[4], sl[4], so[4 * D];
   const int b = blockIdx.x;
   if (b < chunk_grid) {
-    chunk_attn_item<D, kPaged>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, ld_out,
+    chunk_attn_item<D, kPaged, 1>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, ld_out,
                                chunk_qscale, n_split, max_splits, part_o, part_ml, k0s, v0s, k1s, v1s,
                                k2s, v2s);
   } else {
@@ -220,7 +220,7 @@ hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const 
                      int ld_out, int n_split, int max_splits, float *po, float *pml,
                      const DecodeGroup &dg, int dec_row0, int dec_rows, hipStream_t s) {
   int items = 0;
-  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh);
+  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh, kBQ);
   const int per_xcd = (items + 7) / 8;
   const int chunk_grid = 8 * per_xcd;
   const int grid = chunk_grid + dec_rows * max_splits * nh;

@@ -137,6 +137,7 @@ struct ChunkSet {
   int32_t row0[kMaxChunks];                // first batch row
   int32_t split[kMaxChunks];               // key-range splits of the chunk's query blocks (>= 1)
   int32_t n, rows;                         // chunks; total chunk rows
+  int32_t qblocks;                         // chunk kernel: 16-query blocks per wave (1 or 2)
 };
 
 struct DecodeGroup {

@@ -112,14 +112,21 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
 
 // Flash-style causal chunk attention (bf16, MFMA) over every chunk of the set: row row0[j] + t of
 // chunk j attends to keys 0..off[j]+t of chunk j's cache.  q and out are batch-row indexed (row
-// strides ld_q, ld_out).  Chunk j's 64-query blocks split their key tiles cs.split[j] ways; n_split
-// is the largest of these.  With n_split > 1 every chunk writes partials (stride `stride` splits per
-// row and head; slots past its own count marked empty) for launch_attn_combine instead of out.
-constexpr int kChunkTargetWorkgroups = 512;   // two workgroups per compute unit
+// strides ld_q, ld_out).  Chunk j's query blocks (64 queries; 128 with cs.qblocks = 2, two 16-query
+// blocks per wave, contiguous caches only) split their key tiles cs.split[j] ways; n_split is the
+// largest of these.  A chunk with cs.split[j] > 1 writes partials (stride `stride` splits per row and
+// head) for launch_attn_combine instead of out.
+constexpr int kChunkResident = 512;           // chunk-kernel workgroups resident at once (two per CU)
+constexpr int kFusedChunkResident = 512;      // fused-kernel workgroups resident at once (two per CU)
+// Time of one key tile of a chunk-kernel item with two 16-query blocks per wave, in units of the
+// one-block item's tile time (measured on the llama-13b shape over an 8K-key prefix: 2.44 against
+// 1.51 microseconds per tile).
+constexpr double kTwoBlockTileCost = 1.62;
 constexpr int kMinSplitTiles = 4;             // a split keeps at least 4 key tiles
 constexpr int kMaxChunkSplits = 16;
 constexpr int kSplitCostTiles = 3;            // makespan cost of one more split, in key-tile times
-int chunk_attn_splits(ChunkSet &cs, int nh);
+int chunk_attn_splits(ChunkSet &cs, int nh, int bq, int resident, long long *cost);
+int chunk_attn_plan(ChunkSet &cs, int nh, bool paged);
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
                              const PagePool &pool, void *out, int ld_out, int n_split, int stride,
                              float *part_o, float *part_ml, hipStream_t s);

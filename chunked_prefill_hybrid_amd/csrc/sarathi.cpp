@@ -344,6 +344,7 @@ ChunkSet chunk_set(const BatchView &b) {
     row += c.len;
   }
   cs.rows = row;
+  cs.qblocks = 1;
   return cs;
 }
 
@@ -374,7 +375,9 @@ int plan_chunk_splits(const sarathi_layer_desc *d, const BatchView &b, ChunkSet 
   for (int j = 0; j < cs.n; ++j) cs.split[j] = 1;
   if (chunk_uses_split(d) || cs.n <= 0) return 1;
   const bool fused = fused_attention(d, b, cs);
-  const int most = chunk_attn_splits(cs, d->n_heads);
+  long long cost;
+  const int most = fused ? chunk_attn_splits(cs, d->n_heads, 64, kFusedChunkResident, &cost)
+                         : chunk_attn_plan(cs, d->n_heads, b.paged);
   if (fused) {
     int items = 0;
     for (int j = 0; j < cs.n; ++j) items += (cs.len[j] + 63) / 64 * cs.split[j] * d->n_heads;
@@ -708,6 +711,7 @@ sarathi_status describe_entry(const sarathi_layer_desc *d, const Batch *b, sarat
   out.fused_attention = fused_attention(d, v, cs) ? 1 : 0;
   for (int j = 0; j < cs.n; ++j) out.chunk_splits[j] = cs.split[j];
   out.max_key_splits = p.max_splits;
+  out.chunk_query_blocks = cs.qblocks;
   out.qkv = gemm_info(p.qkv);
   out.o = gemm_info(p.o);
   out.up = gemm_info(p.up);

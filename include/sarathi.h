@@ -395,7 +395,7 @@ typedef struct {
     int32_t fused_attention;                     /* 1: chunk and decode attention in one launch */
     int32_t chunk_splits[SARATHI_MAX_CHUNKS];    /* key-range splits of each chunk's query blocks */
     int32_t max_key_splits;                      /* split partials per row and head */
-    int32_t reserved;
+    int32_t chunk_query_blocks;                  /* 16-query blocks per wave of the chunk attention (1 or 2; 1 when fused) */
     sarathi_gemm_plan qkv, o, up, down;          /* up: gate|up for LLAMA, up for GPT */
     uint64_t workspace_bytes;                    /* as the matching *_workspace_size */
 } sarathi_plan_info;     /* 160 bytes */

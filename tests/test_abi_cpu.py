@@ -307,6 +307,30 @@ def test_plan_splits_long_chunk(lib):
     assert list(info.chunk_splits)[1:] == [0] * 15
 
 
+def test_plan_two_query_blocks_per_wave(lib):
+    """A separate chunk launch takes two 16-query blocks per wave when its items would otherwise need
+    more than one round of the resident workgroups: the 13B long-context chunk and the 20-head GPU
+    test batches do; fused launches, short chunks and paged caches keep one."""
+    b, keep = batch(C=512, off=7680, cap=8192, lens=(4000,) * 48)
+    assert _abi.plan_describe(desc13b(), b).chunk_query_blocks == 2
+    for hd in (128, 64):
+        d = desc(hidden=20 * hd, n_heads=20, head_dim=hd, ffn=1024, dtype=_abi.SARATHI_BF16, max_tokens=4096,
+                 max_pos=4096)
+        for chunks, lens in ((((1024, 2000, 3032),), (30,)), (((1000, 2000, 3008), (37, 100, 145)), ()),
+                             (((1000, 2000, 3008), (37, 100, 145)), (30,))):
+            b, keep = multi(chunks=chunks, lens=lens)
+            info = _abi.plan_describe(d, b)
+            assert info.fused_attention == 0 and info.chunk_query_blocks == 2, (hd, chunks, lens)
+            assert info.chunk_splits[0] == 3
+    b, keep = batch(C=256, off=768, cap=1024, lens=(1024,) * 18, caps=[1025] * 18)
+    assert _abi.plan_describe(desc13b(), b).chunk_query_blocks == 1                 # fused
+    b, keep = multi(chunks=((94, 930, 1024), (300, 0, 300), (100, 0, 1024)), lens=(1024,) * 12)
+    assert _abi.plan_describe(desc13b(), b).chunk_query_blocks == 1                 # short chunks
+    b, keep = paged(chunks=((512, 7680, 512),), lens=(), dec_entries=(), pool=(addr(60), addr(61), 1000, 16))
+    info = _abi.plan_describe(desc13b(), b)
+    assert info.fused_attention == 0 and info.chunk_query_blocks == 1               # paged
+
+
 def test_plan_of_decode_only_batch(lib):
     b, keep = batch(C=0, lens=(10, 700))
     info = _abi.plan_describe(desc13b(), b)

@@ -35,4 +35,5 @@ def test_hot_kernels_fit_their_occupancy_targets():
     chunk = {k: v for k, v in res.items() if "attn_chunk_mfma" in k}
     assert gemm and chunk
     assert all(v["Occupancy"] >= 2 for v in gemm.values()), gemm
+    assert len(chunk) == 6, chunk   # d in {64, 128} x (contiguous: one or two query blocks; paged: one)
     assert all(v["Occupancy"] >= 2 for v in chunk.values()), chunk

@@ -19,6 +19,10 @@ pytestmark = pytest.mark.gpu
 MID = wl.LayerShape("mid-llama", "llama", 512, 4, 128, 1408, "bf16", 1e-6, 10000.0, None)
 MID_GPT = wl.LayerShape("mid-gpt", "gpt", 512, 4, 128, 1024, "bf16", 1e-5, 10000.0, None)
 MID_D64 = wl.LayerShape("mid-llama-d64", "llama", 256, 4, 64, 704, "bf16", 1e-6, 10000.0, None)
+# 20 heads: enough chunk work items that the planner runs a long chunk with two 16-query blocks per
+# wave (pinned in test_abi_cpu.py)
+WIDE = wl.LayerShape("wide-llama", "llama", 2560, 20, 128, 1024, "bf16", 1e-6, 10000.0, None)
+WIDE_D64 = wl.LayerShape("wide-llama-d64", "llama", 1280, 20, 64, 1024, "bf16", 1e-6, 10000.0, None)
 
 
 def make(shape, chunk_specs, dec_lens, seed, extra=3):
@@ -67,6 +71,9 @@ def run_case(shape, chunk_specs, dec_lens, seed=0, label=None):
     (MID, [(64, 2100), (100, 0), (30, 50)], [40, 900]),            # the same in the fused launch
     (MID, [(n, 7 * n) for n in range(1, 17)], [3]),                # sixteen chunks of 1..16 rows
     (MID, [], [9, 300]),                                           # no chunk at all
+    (WIDE, [(1024, 2000)], [30]),                                  # 128-query blocks, 3 key splits
+    (WIDE, [(1000, 2000), (37, 100)], []),                         # the same, ragged, splits 3 and 1
+    (WIDE_D64, [(1000, 2000), (37, 100)], [30]),                   # d = 64
 ])
 def test_multi_bf16(shape, chunks, lens):
     run_case(shape, chunks, lens)
