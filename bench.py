@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--page-size", type=int, default=None,
                     help="lay the caches out in a page pool with this many tokens per page "
                          "(overrides the workload's own layout; 0 = contiguous caches)")
+    ap.add_argument("--batch", default=None,
+                    help="replace fields of the workload's batch composition, a JSON object such as "
+                         "'{\"n_decodes\": 4, \"decode_lens\": [2048, 2048, 2048, 2048]}' (sweep points)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the chunk-only / decode-only runs behind the decode-cost comparison")
@@ -160,7 +163,8 @@ def main():
     from chunked_prefill_hybrid_amd import workloads as wl
 
     torch.cuda.set_device(0)
-    wk = wl.workload(args.workload)
+    changes = {k: tuple(v) if isinstance(v, list) else v for k, v in json.loads(args.batch or "{}").items()}
+    wk = wl.workload(args.workload, **changes)
     if args.page_size is not None:
         wk = dataclasses.replace(wk, page_size=args.page_size or None)
     shape = wk.shape

@@ -195,6 +195,20 @@ def workload(key: str, **batch_changes) -> Workload:
     return w
 
 
+def sweep_changes(key: str) -> List[dict]:
+    """The C or B sweep a workload is measured on, as BatchSpec field changes: chunk length C for
+    llama33b (tile quantization, with C = 257 one row past a tile), the number of piggybacked decodes B
+    for gpt3tp8 (the P:D sweep) and llama13b."""
+    b = WORKLOADS[key].batch
+    if key == "llama33b":
+        return [dict(chunk_len=c, prompt_len=max(c, b.chunk_offset + c)) for c in (128, 256, 257, 512)]
+    if key == "gpt3tp8":
+        return [dict(n_decodes=n, decode_lens=(2048,) * n) for n in (1, 2, 4, 8, 16, 32, 64)]
+    if key == "llama13b":
+        return [dict(n_decodes=n, decode_lens=(1024,) * n) for n in (1, 4, 8, 18, 32, 64)]
+    return []
+
+
 def sweep(key: str) -> List[Workload]:
     """Sweep points of a workload: the hybrid batch, its chunk-only (B=0) and decode-only (C=0) parts,
     and the C or B sweep the workload is measured on."""
@@ -202,12 +216,7 @@ def sweep(key: str) -> List[Workload]:
     b = w.batch
     pts: List[Workload] = [w, workload(key, n_decodes=0, decode_lens=() if b.decode_lens else None),
                            workload(key, chunk_len=0)]
-    if key == "llama33b":
-        for c in (128, 256, 257):
-            pts.append(workload(key, chunk_len=c, prompt_len=max(c, 1)))
-    if key == "gpt3tp8":
-        for nd in (1, 2, 4, 8, 16, 32):
-            pts.append(workload(key, n_decodes=nd, decode_lens=(2048,) * nd))
+    pts += [workload(key, **ch) for ch in sweep_changes(key)]
     return pts
 
 
