@@ -94,3 +94,61 @@ def test_planted_mistake_is_caught(name, monkeypatch, golden_dir):
             except (AssertionError, FloatingPointError, ValueError):
                 failed += 1
     assert failed >= 1, f"no pin caught the planted mistake {name}"
+
+
+# ------------------------------------------------------------------------------------------------
+# Planted mistakes in the layer stack's chaining.
+# ------------------------------------------------------------------------------------------------
+
+def _stack_layer_batch(batch, l, x):
+    return {"x": x, "chunk_len": batch["chunk_len"], "chunk_offset": batch["chunk_offset"],
+            "decode_len": batch["decode_len"],
+            "chunk_k": batch["chunk_k"][l] if batch["chunk_len"] else None,
+            "chunk_v": batch["chunk_v"][l] if batch["chunk_len"] else None,
+            "decode_k": batch["decode_k"][l], "decode_v": batch["decode_v"][l]}
+
+
+def _stack_input_to_every_layer(shape, layer_weights, batch, dtype=np.float64):
+    outs = [L.layer_forward(shape, w, _stack_layer_batch(batch, l, batch["x"]), dtype)
+            for l, w in enumerate(layer_weights)]
+    return {"y": outs[-1]["y"], "layers": outs}
+
+
+def _stack_weights_reversed(shape, layer_weights, batch, dtype=np.float64):
+    x, outs = batch["x"], []
+    for l, w in enumerate(reversed(list(layer_weights))):
+        outs.append(L.layer_forward(shape, w, _stack_layer_batch(batch, l, x), dtype))
+        x = outs[-1]["y"]
+    return {"y": x, "layers": outs}
+
+
+def _stack_first_layer_caches(shape, layer_weights, batch, dtype=np.float64):
+    x, outs = batch["x"], []
+    for w in layer_weights:
+        outs.append(L.layer_forward(shape, w, _stack_layer_batch(batch, 0, x), dtype))
+        x = outs[-1]["y"]
+    return {"y": x, "layers": outs}
+
+
+STACK_MUTATIONS = {
+    "stack_input_to_every_layer": _stack_input_to_every_layer,
+    "stack_weights_reversed": _stack_weights_reversed,
+    "stack_first_layer_caches": _stack_first_layer_caches,
+}
+
+
+@pytest.mark.parametrize("name", sorted(STACK_MUTATIONS))
+def test_planted_stack_mistake_is_caught(name, monkeypatch):
+    import oracle
+    import tests.test_oracle_stack as stack_pins
+    monkeypatch.setattr(L, "stack_forward", STACK_MUTATIONS[name])
+    monkeypatch.setattr(oracle, "stack_forward", STACK_MUTATIONS[name])
+    failed = 0
+    for pin in (stack_pins.test_stack_chunked_prompt_equals_monolithic_and_decodes_are_independent,
+                stack_pins.test_stack_of_one_layer_is_the_layer,
+                stack_pins.test_stack_chains_layers_in_order_closed_form):
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin caught the planted mistake {name}"
