@@ -2,19 +2,25 @@
 
 One step = one forward of one decoder layer over one hybrid batch: a prefill chunk plus piggybacked
 decodes (SARATHI: Efficient LLM Inference by Piggybacking Decodes with Chunked Prefills, section 3,
-"Decode-Maximal Batching").  Default workload: LLaMA-13B layer shape in bf16, chunk C=256 at offset
-768 of a 1024-token prompt plus B=18 decodes with 1024 cached entries each.  Inputs are seeded and
-synthetic and already resident in HBM when timing starts.  Three replicas of the weights, caches and
-activations are rotated step by step so that the 256 MB last-level cache cannot hold a step's data.
+"Decode-Maximal Batching").  Default workload: the largest single-GPU batch of the measured set, the
+LLaMA-13B layer shape in bf16 with a chunk C=512 at offset 7680 of an 8192-token prompt plus B=48
+decodes whose KV lengths are uniform in [2048, 8192] (560 rows, about 5 GB of KV per step; the
+attention-dominated regime that section 6 of the same page, "Limitations and Trade-offs", points to).
+The C=256 + 18-decode LLaMA-13B batch is measured in the same run and reported under `secondary`.
 
-Passes: W warmup steps; a breakdown pass in which the library records HIP events around every stage
-(this perturbs the step time, so it is not the timed region); then exactly K timed steps in which
-events are recorded on the launch stream only around the dominant kernel's stage, giving that
-kernel's live average duration for the roofline.  Prints ONE JSON line: tokens/s over the K timed
-steps, the roofline of the dominant kernel, the per-stage breakdown, the layer's roofline fraction,
-the piggybacking comparison (the same rows run as a chunk-only and a decode-only batch, giving the
-marginal cost of a decode that rides with the chunk), and the CPU oracle's throughput on a bounded
-sample of the same workload.
+Inputs are seeded and synthetic, drawn on the GPU (workloads.generate(..., device="cuda")) and
+already resident in HBM when timing starts.  Three replicas of the weights, caches and activations
+are rotated step by step so that the 256 MB last-level cache cannot hold a step's data.
+
+Passes per workload: W warmup steps; a breakdown pass in which the library records HIP events around
+every stage (this perturbs the step time, so it is not the timed region); then exactly K timed steps
+in which events are recorded on the launch stream only around the dominant kernel's stage, giving
+that kernel's live average duration for the roofline, while a host thread samples the GPU's clock
+and power.  Prints ONE JSON line: tokens/s over the K timed steps, the roofline of the dominant
+kernel, the per-stage breakdown, the layer's roofline fraction, the piggybacking comparison (the same
+rows run as a chunk-only and a decode-only batch, giving the marginal cost of a decode that rides
+with the chunk), the GPU clock during the timed steps, and the CPU oracle's throughput on the same
+inputs (float32, on the host cores given to this process, plus a one-thread run).
 """
 from __future__ import annotations
 
@@ -24,6 +30,7 @@ import json
 import os
 import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -33,19 +40,32 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "hybrid-batch layer tokens/s (chunk+decodes); % bf16 MFMA and HBM roofline"
+DEFAULT_WORKLOAD = "llama13b_long"
+DEFAULT_SECONDARY = "llama13b"
 
 
 from chunked_prefill_hybrid_amd.profiling import kernel_source_hash, stage_source_hash  # noqa: E402
 
 
-def stage_work(shape, chunks, lens):
+def _split_count(n_keys):
+    return (n_keys + 255) // 256   # key splits of the split-KV attention (256 keys each)
+
+
+def stage_work(shape, chunks, lens, chunk_splits=None):
     """Algorithmic work of each stage: (flops, bytes).  chunks: [(len, offset)] of the batch's prefill
-    chunks.  GEMM flops use the unpadded row count."""
+    chunks; chunk_splits: key splits of each chunk (the merge reads the partials of split chunks).
+    GEMM flops use the unpadded row count."""
     C = sum(n for n, _ in chunks)
     T = C + len(lens)
     H, A, F = shape.hidden, shape.attn_width, shape.ffn
+    nh, d = shape.n_heads, shape.head_dim
     el = 2 if shape.dtype == "bf16" else 4
     up_n = 2 * F if shape.gated else F
+    splits = chunk_splits or [1] * len(chunks)
+    # the merge reads each split partial (d floats of o plus m and l) of the rows that have several,
+    # and writes those rows' attention output
+    merge_rows = [(n, s) for (n, _), s in zip(chunks, splits) if s > 1] + \
+                 [(1, _split_count(L + 1)) for L in lens]
     w = {
         "qkv": (2.0 * T * H * 3 * A, el * (3 * A * H + T * H + T * 3 * A)),
         "o": (2.0 * T * A * H, el * (H * A + T * A + T * H) + 4 * T * H),
@@ -59,13 +79,17 @@ def stage_work(shape, chunks, lens):
         "norm1": (0.0, el * 2 * T * H),
         "norm2": (0.0, (4 + el) * T * H),
         "rope_append": (0.0, el * 2 * T * 3 * A),
-        "attn_merge": (0.0, 0.0),
+        "attn_merge": (0.0, sum(n * (nh * s * (d + 2) * 4 + A * el) for n, s in merge_rows)),
     }
     return w
 
 
 BOUND = {"qkv": "mfma", "o": "mfma", "ffn_up": "mfma", "ffn_down": "mfma", "attn_chunk": "mfma",
          "attn_decode": "hbm", "norm1": "hbm", "norm2": "hbm", "rope_append": "hbm", "attn_merge": "hbm"}
+# Stages whose work is the method's own (the floor of the layer); the merge of split partials is a
+# cost of this design's key splits, reported but not counted in the floor.
+FLOOR_STAGES = ("qkv", "o", "ffn_up", "ffn_down", "attn_decode", "attn_chunk", "norm1", "norm2",
+                "rope_append")
 
 
 def roofline_entry(stage, avg_ms, flops, nbytes, dtype):
@@ -103,72 +127,148 @@ def load_traffic(stage, workload_key):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wk, weights, batch, budget_s=25.0, target_s=10.0):
-    """The CPU oracle (as it is, float64 NumPy) on the full batch, repeated until about target_s of
-    CPU work (at least 3 runs) while it stays within the time budget; BLAS threads capped at 16 (one
-    GPU's share of host cores)."""
+class ClockSampler:
+    """Samples the GPU's graphics clock and socket power from a host thread (AMD SMI) while it runs.
+    The device is matched by PCI address to torch's device 0; on any failure the summary says why."""
+
+    def __init__(self, period_s=0.005):
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+        try:
+            import amdsmi
+            import torch
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            p = torch.cuda.get_device_properties(0)
+            want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower().startswith(want):
+                    self._h = h
+            if self._h is None:
+                self.error = f"no AMD SMI device at PCI {want}"
+        except Exception as e:   # no SMI library, no permission, no driver
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+        w = None
+        try:
+            pw = self._smi.amdsmi_get_power_info(self._h)
+            w = pw.get("current_socket_power")
+            if not isinstance(w, (int, float)):
+                w = pw.get("average_socket_power")
+        except Exception:
+            pass
+        return c.get("clk"), (w if isinstance(w, (int, float)) else None)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._h is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": "amdsmi", "samples": 0, "error": self.error or "no samples"}
+        mhz = [c for c, _ in self.samples if isinstance(c, (int, float))]
+        w = [p for _, p in self.samples if isinstance(p, (int, float))]
+        out = {"source": "amdsmi", "samples": len(self.samples)}
+        if mhz:
+            out.update(gfx_mhz_median=statistics.median(mhz), gfx_mhz_min=min(mhz), gfx_mhz_max=max(mhz))
+        if w:
+            out["socket_power_w_median"] = statistics.median(w)
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
+def host_cpu():
+    """CPU model and the host threads this process may use (its affinity, capped by OMP_NUM_THREADS)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    threads = min(avail, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else avail
+    return model, threads, os.cpu_count()
+
+
+def cpu_baseline(wk, weights, batch):
+    """The CPU oracle as it is (plain NumPy, float32 arithmetic) on one full step of the same inputs
+    the GPU ran: once with BLAS on the host threads given to this process, once on one thread."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
-    cores = min(16, os.cpu_count() or 1)
-    times = []
-    with threadpool_limits(limits=cores, user_api="blas"):
-        used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-        t_start = time.perf_counter()
-        while True:
+
+    def host(a):
+        if a is None or isinstance(a, (int, float, list, tuple, dict)) or isinstance(a, np.ndarray):
+            return a
+        return a.float().cpu().numpy()
+
+    hw = {k: host(v) for k, v in weights.items()}
+    hb = {k: (host(v) if not isinstance(v, list) else [host(t) for t in v]) for k, v in batch.items()}
+    if "chunks" in hb:
+        hb["chunks"] = [{kk: host(vv) for kk, vv in c.items()} for c in batch["chunks"]]
+    fwd = oracle.layer_forward_multi if "chunks" in hb else oracle.layer_forward
+    model, threads, ncpu = host_cpu()
+    blas = [{"api": i.get("internal_api"), "version": i.get("version"), "threads": i.get("num_threads")}
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    T = hb["x"].shape[0]
+
+    def timed(n_threads):
+        with threadpool_limits(limits=n_threads, user_api="blas"):
+            used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
             t0 = time.perf_counter()
-            if "chunks" in batch:
-                oracle.layer_forward_multi(wk.shape, weights, batch)
-            else:
-                oracle.layer_forward(wk.shape, weights, batch)
-            times.append(time.perf_counter() - t0)
-            spent = time.perf_counter() - t_start
-            if spent + times[-1] > budget_s or (len(times) >= 3 and spent >= target_s):
-                break
-    T = batch["x"].shape[0]
-    t = statistics.median(times)
-    return {"value": round(T / t, 2), "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": f"full batch ({T} rows, one layer, float64 NumPy), {len(times)} run(s), median {t:.2f} s"}
+            fwd(wk.shape, hw, hb, dtype=np.float32)
+            return time.perf_counter() - t0, used
+
+    t_all, used = timed(threads)
+    t_one, _ = timed(1)
+    return {"value": round(T / t_all, 2), "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"one full step ({T} rows, one layer), float32 NumPy on the inputs the GPU ran",
+            "seconds": round(t_all, 2),
+            "one_thread": {"value": round(T / t_one, 2), "unit": "tokens/s", "seconds": round(t_one, 2)},
+            "cpu_model": model, "host_cpus": ncpu, "blas": blas}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama13b")
-    ap.add_argument("--replicas", type=int, default=3)
-    ap.add_argument("--page-size", type=int, default=None,
-                    help="lay the caches out in a page pool with this many tokens per page "
-                         "(overrides the workload's own layout; 0 = contiguous caches)")
-    ap.add_argument("--batch", default=None,
-                    help="replace fields of the workload's batch composition, a JSON object such as "
-                         "'{\"n_decodes\": 4, \"decode_lens\": [2048, 2048, 2048, 2048]}' (sweep points)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the chunk-only / decode-only runs behind the decode-cost comparison")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build measures a single MI355X "
-              f"(got --gpus {args.gpus}); multi-GPU sharding is described in the design notes.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def measure(key, args, changes=None, page_size=None, sweep=True):
+    """Runs one workload: warmup, stage breakdown, exactly args.steps timed steps, the piggyback
+    comparison.  Returns (report dict, workload, device weights, device batch)."""
     import torch
 
     from chunked_prefill_hybrid_amd import _abi
     from chunked_prefill_hybrid_amd import layer as hl
     from chunked_prefill_hybrid_amd import workloads as wl
 
-    torch.cuda.set_device(0)
-    changes = {k: tuple(v) if isinstance(v, list) else v for k, v in json.loads(args.batch or "{}").items()}
-    wk = wl.workload(args.workload, **changes)
-    if args.page_size is not None:
-        wk = dataclasses.replace(wk, page_size=args.page_size or None)
+    wk = wl.workload(key, **(changes or {}))
+    if page_size is not None:
+        wk = dataclasses.replace(wk, page_size=page_size or None)
     shape = wk.shape
-    weights, batch = wl.generate(wk)
+    weights, batch = wl.generate(wk, device="cuda")
     chunks = wl.chunks_of(batch)            # [{len, offset, k, v}]: one chunk, several, or none
     multi = "chunks" in batch               # token-budget workloads use the several-chunk entry point
     lens = list(batch["decode_len"])
@@ -177,13 +277,18 @@ def main():
     dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
 
     def dev(a, t=dt):
+        if isinstance(a, torch.Tensor):
+            return a.to(t)
+        import numpy as np
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
 
     wdev = {k: dev(v, torch.float32 if k.startswith("norm") else dt) for k, v in weights.items() if v is not None}
     paged = wk.page_size is not None
     if paged:
         # every request's cache in one pool of fixed-size pages, in a shuffled page order
-        caches = [(c["k"], c["v"]) for c in chunks] + list(zip(batch["decode_k"], batch["decode_v"]))
+        caches = [(c["k"].float().cpu().numpy(), c["v"].float().cpu().numpy()) for c in chunks] + \
+                 [(k.float().cpu().numpy(), v.float().cpu().numpy())
+                  for k, v in zip(batch["decode_k"], batch["decode_v"])]
         kp, vp, tables = wl.paginate(caches, wk.page_size, seed=wk.seed + 1)
         base = {"x": dev(batch["x"]), "pool": (dev(kp), dev(vp)),
                 "tables": [torch.from_numpy(t).to("cuda") for t in tables]}
@@ -234,6 +339,8 @@ def main():
             for name, (sb, _) in sub.items():
                 assert layer.workspace_size(sb) <= ws.numel(), name
         reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, ckv, dkv, wr)))
+    info = _abi.plan_describe(reps[0]["layer"].desc, reps[0]["b"])
+    chunk_splits = [int(info.chunk_splits[j]) for j in range(len(chunks))]
     stream = torch.cuda.current_stream().cuda_stream
     if paged:
         fwd, fwd_timed = _abi.sarathi_paged_forward, _abi.sarathi_paged_forward_timed
@@ -262,10 +369,12 @@ def main():
         step(i, timer)
     stages = _abi.sarathi_timer_read(timer)
     _abi.sarathi_timer_destroy(timer)
-    work = stage_work(shape, [(c["len"], c["offset"]) for c in chunks], lens)
-    if chunks and lens and stages["attn_chunk"][1] == 0:
+    work = stage_work(shape, [(c["len"], c["offset"]) for c in chunks], lens, chunk_splits)
+    fused = chunks and lens and stages["attn_chunk"][1] == 0
+    if fused:
         # chunk and decode attention ran as one launch, recorded as the decode stage
         work["attn_decode"] = tuple(a + b for a, b in zip(work["attn_decode"], work["attn_chunk"]))
+        work["attn_chunk"] = (0.0, 0.0)
     breakdown = {}
     for name, (tot, cnt) in stages.items():
         if cnt == 0:
@@ -275,17 +384,21 @@ def main():
         e = roofline_entry(name, avg, fl, by, shape.dtype)
         breakdown[name] = {"avg_us": round(avg * 1e3, 2), "frac": e["frac"], "bound": e["bound"],
                            "achieved": e["achieved"], "unit": e["unit"]}
+        if "hbm_frac" in e:
+            breakdown[name]["hbm_frac"] = e["hbm_frac"]
     dominant = max(breakdown, key=lambda n: breakdown[n]["avg_us"])
 
     # Timed region: exactly K steps; HIP events on the launch stream only around the dominant
-    # kernel's stage give its live average duration.
+    # kernel's stage give its live average duration; a host thread samples the GPU clock.
     timer = _abi.sarathi_timer_create(args.steps, _abi.stage_mask(dominant))
+    clocks = ClockSampler()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, timer)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, timer)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     live = _abi.sarathi_timer_read(timer)
     _abi.sarathi_timer_destroy(timer)
     tot, cnt = live[dominant]
@@ -294,28 +407,30 @@ def main():
     roof["traffic"] = load_traffic(dominant, wk.key)
     roof["kernel"] = dominant
     roof["avg_us"] = round(dom_avg_ms * 1e3, 2)
-    gemm_ms = sum(breakdown[n]["avg_us"] for n in ("qkv", "o", "ffn_up", "ffn_down")) / 1e3
-    gemm_flops = sum(work[n][0] for n in ("qkv", "o", "ffn_up", "ffn_down"))
+    gemms = [n for n in ("qkv", "o", "ffn_up", "ffn_down") if n in breakdown]
+    gemm_ms = sum(breakdown[n]["avg_us"] for n in gemms) / 1e3
+    gemm_flops = sum(work[n][0] for n in gemms)
+    peak_c = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
     summary = {
-        "gemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_c, 4) if gemm_ms else None,
         "decode_attn_hbm_frac": breakdown.get("attn_decode", {}).get("frac"),
+        "decode_attn_includes_chunk": bool(fused),
         "sum_of_stages_us": round(sum(v["avg_us"] for v in breakdown.values()), 2),
         "breakdown_note": "per-stage times from a separate pass with events around every stage",
     }
-
     ms_per_step = elapsed / args.steps * 1e3
-    # Layer roofline fraction: sum over stages of the time each would take at its own bound, over the
-    # measured step time.
-    peak_c = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
-    floor_us = sum(max(fl / (peak_c * 1e12), by / (PEAK_HBM_GBS * 1e9)) for fl, by in work.values()) * 1e6
+    # Layer roofline fraction: sum over the method's stages of the time each would take at its own
+    # bound, over the measured step time.
+    floor_us = sum(max(work[n][0] / (peak_c * 1e12), work[n][1] / (PEAK_HBM_GBS * 1e9))
+                   for n in FLOOR_STAGES) * 1e6
     summary["layer_floor_us"] = round(floor_us, 2)
     summary["layer_roofline_frac"] = round(floor_us / (ms_per_step * 1e3), 4)
 
     # Piggybacking comparison (SARATHI page, "Experiments", decode speedup): the marginal cost of a
     # decode riding with the chunk, (t(C,B) - t(C,0)) / B, against a decode in a decode-only batch,
     # t(0,B) / B.
-    sweep = None
-    if not args.no_sweep and reps[0]["sub"]:
+    pig = None
+    if sweep and reps[0]["sub"]:
         n_sw = max(20, min(args.steps, 100))
 
         def time_batch(name):
@@ -335,41 +450,105 @@ def main():
         B = len(lens)
         marginal = (t_h - t_c) / B
         alone = t_d / B
-        sweep = {"steps": n_sw, "t_hybrid_us": round(t_h, 2), "t_chunk_only_us": round(t_c, 2),
-                 "t_decode_only_us": round(t_d, 2), "marginal_decode_us": round(marginal, 3),
-                 "decode_only_per_decode_us": round(alone, 3),
-                 "decode_speedup": round(alone / marginal, 2) if marginal > 0 else None}
-    value = T * args.steps / elapsed
+        pig = {"steps": n_sw, "t_hybrid_us": round(t_h, 2), "t_chunk_only_us": round(t_c, 2),
+               "t_decode_only_us": round(t_d, 2), "marginal_decode_us": round(marginal, 3),
+               "decode_only_per_decode_us": round(alone, 3),
+               "decode_speedup": round(alone / marginal, 2) if marginal > 0 else None}
+    config = {"workload": f"{shape.name} layer, "
+                          + (" + ".join(f"chunk {c['len']} at offset {c['offset']}" for c in chunks)
+                             or "no chunk")
+                          + f" + {len(lens)} decodes "
+                          f"(KV lengths {min(lens) if lens else 0}..{max(lens) if lens else 0})"
+                          + (f", paged KV ({wk.page_size}-token pages)" if paged else ""),
+              "key": wk.key, "hidden": shape.hidden, "heads": shape.n_heads, "head_dim": shape.head_dim,
+              "ffn": shape.ffn, "chunk": C,
+              "chunk_offset": chunks[0]["offset"] if len(chunks) == 1 else None,
+              "chunks": [[c["len"], c["offset"]] for c in chunks],
+              "decodes": len(lens), "rows": T, "replicas": args.replicas, "kv_page_size": wk.page_size,
+              "kv_bytes": int(sum(2 * shape.attn_width * (2 if shape.dtype == "bf16" else 4) * (L + 1)
+                                  for L in lens))}
+    report = {"value": round(T * args.steps / elapsed, 1), "ms_per_step": round(ms_per_step, 4),
+              "dtype": shape.dtype, "config": config, "roofline": roof, "stages": breakdown,
+              "summary": summary, "piggyback": pig, "gpu_clock": clocks.summary(),
+              "plan": {"chunk_splits": chunk_splits, "fused_attention": int(info.fused_attention),
+                       "workspace_bytes": int(info.workspace_bytes)}}
+    for r in reps:
+        r["layer"].close()
+    reps.clear()
+    del base
+    return report, wk, weights, batch
+
+
+def note(msg):
+    """Progress on stderr (the JSON line is the only stdout output)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--secondary", default=None,
+                    help="comma-separated workloads measured after the headline and reported under "
+                         f"`secondary` (default: {DEFAULT_SECONDARY} when the headline is the default "
+                         "workload and its batch is unchanged; '' for none)")
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--page-size", type=int, default=None,
+                    help="lay the caches out in a page pool with this many tokens per page "
+                         "(overrides the workload's own layout; 0 = contiguous caches)")
+    ap.add_argument("--batch", default=None,
+                    help="replace fields of the workload's batch composition, a JSON object such as "
+                         "'{\"n_decodes\": 4, \"decode_lens\": [2048, 2048, 2048, 2048]}' (sweep points)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the chunk-only / decode-only runs behind the decode-cost comparison")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build measures a single MI355X "
+              f"(got --gpus {args.gpus}); multi-GPU sharding is described in the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    torch.cuda.set_device(0)
+    changes = {k: tuple(v) if isinstance(v, list) else v for k, v in json.loads(args.batch or "{}").items()}
+    if args.secondary is None:
+        plain = args.workload == DEFAULT_WORKLOAD and not changes and args.page_size is None
+        secondary = [DEFAULT_SECONDARY] if plain else []
+    else:
+        secondary = [s for s in args.secondary.split(",") if s]
+
+    rep, wk, weights, batch = measure(args.workload, args, changes, args.page_size, sweep=not args.no_sweep)
+    note(f"{args.workload}: {rep['value']:.0f} tokens/s, {rep['ms_per_step']:.4f} ms/step")
+    torch.cuda.empty_cache()
+    extra = {}
+    for key in secondary:
+        r2, *_ = measure(key, args, sweep=not args.no_sweep)
+        note(f"{key}: {r2['value']:.0f} tokens/s, {r2['ms_per_step']:.4f} ms/step")
+        torch.cuda.empty_cache()
+        extra[key] = r2
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype,
-        "data": "synthetic",
-        "config": {"workload": f"{shape.name} layer, "
-                               + (" + ".join(f"chunk {c['len']} at offset {c['offset']}" for c in chunks)
-                                  or "no chunk")
-                               + f" + {len(lens)} decodes "
-                               f"(KV lengths {min(lens) if lens else 0}..{max(lens) if lens else 0})"
-                               + (f", paged KV ({wk.page_size}-token pages)" if paged else ""),
-                   "hidden": shape.hidden, "heads": shape.n_heads, "head_dim": shape.head_dim,
-                   "ffn": shape.ffn, "chunk": C,
-                   "chunk_offset": chunks[0]["offset"] if len(chunks) == 1 else None,
-                   "chunks": [[c["len"], c["offset"]] for c in chunks],
-                   "decodes": len(lens), "rows": T, "replicas": args.replicas,
-                   "kv_page_size": wk.page_size},
-        "roofline": roof,
-        "stages": breakdown,
-        "summary": summary,
-        "piggyback": sweep,
+        "metric": METRIC, "value": rep["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rep["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rep["dtype"],
+        "data": "synthetic (seeded, drawn on the GPU; random-init weights of the layer shape)",
+        "config": rep["config"],
+        "roofline": rep["roofline"],
+        "stages": rep["stages"],
+        "summary": rep["summary"],
+        "piggyback": rep["piggyback"],
+        "gpu_clock": rep["gpu_clock"],
+        "plan": rep["plan"],
+        "secondary": extra or None,
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wk, weights, batch)
-    else:
-        out["cpu_baseline"] = None
+        note("CPU oracle baseline")
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wk, weights, batch)
     print(json.dumps(out), flush=True)
-    for r in reps:
-        r["layer"].close()
 
 
 if __name__ == "__main__":

@@ -37,9 +37,9 @@ constexpr int kPrefetchFused = 2;
 template <typename T, int D, bool kChunkRows, bool kPaged, int kPre = 1>
 __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q, int ld_q, int nh,
                                                 const ChunkSet &cs, const DecodeGroup &dg,
-                                                const PagePool &pool, int max_splits, float *part_o,
-                                                float *part_ml, float qscale, float *sm, float *sl,
-                                                float *so) {
+                                                const PagePool &pool, int stride, int prow0,
+                                                float *part_o, float *part_ml, float qscale, float *sm,
+                                                float *sl, float *so) {
   constexpr int E = Packet<T>::E;      // elements per 16-byte packet
   constexpr int LPK = D / E;           // lanes per key row
   constexpr int KPI = kWave / LPK;     // keys per wave load step
@@ -51,7 +51,7 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
   const RowRef rr = row_ref<kChunkRows>(r, cs, dg);
   const int n_keys = rr.pos + 1;
   const int nsp = attn_splits(n_keys);
-  const size_t pidx = ((size_t)r * nh + h) * max_splits + s;
+  const size_t pidx = ((size_t)(r - prow0) * nh + h) * stride + s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (s >= nsp) {  // no keys for this split: an empty partial
     if (tid == 0) {
@@ -179,11 +179,12 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
 template <typename T, int D, bool kChunkRows, bool kPaged>
 __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int nh, int row0,
                                                        ChunkSet cs, DecodeGroup dg, PagePool pool,
-                                                       int max_splits,
+                                                       int stride, int prow0,
                                                        float *part_o, float *part_ml, float qscale) {
   __shared__ float sm[4], sl[4], so[4 * D];
   split_attn_item<T, D, kChunkRows, kPaged>(row0 + blockIdx.x, blockIdx.y, blockIdx.z, q, ld_q, nh, cs,
-                                            dg, pool, max_splits, part_o, part_ml, qscale, sm, sl, so);
+                                            dg, pool, stride, prow0, part_o, part_ml, qscale, sm, sl,
+                                            so);
 }
 
 // Chunk and decode attention in one launch.  Workgroups [0, chunk_grid) run the chunk work items
@@ -194,41 +195,39 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
 template <int D, bool kPaged>
 __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int nh, ChunkSet cs,
                                                   PagePool pool, bf16_t *out, int ld_out,
-                                                  float chunk_qscale, int n_split, int max_splits,
-                                                  float *part_o, float *part_ml, int per_xcd,
-                                                  int chunk_grid, DecodeGroup dg, int dec_row0,
-                                                  int dec_rows, float dec_qscale) {
+                                                  float chunk_qscale, int n_split, AttnParts parts,
+                                                  int per_xcd, int chunk_grid, DecodeGroup dg,
+                                                  int dec_row0, int dec_rows, float dec_qscale) {
   SARATHI_CHUNK_LDS(D);
   __shared__ float sm[4], sl[4], so[4 * D];
   const int b = blockIdx.x;
   if (b < chunk_grid) {
     chunk_attn_item<D, kPaged, 1>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, ld_out,
-                               chunk_qscale, n_split, max_splits, part_o, part_ml, k0s, v0s, k1s, v1s,
-                               k2s, v2s);
+                               chunk_qscale, n_split, parts.stride_c, parts.o_c, parts.ml_c, k0s, v0s,
+                               k1s, v1s, k2s, v2s);
   } else {
     const int d = b - chunk_grid;
     const int r = d % dec_rows, rest = d / dec_rows;
-    split_attn_item<bf16_t, D, false, kPaged, kPrefetchFused>(dec_row0 + r, rest % max_splits,
-                                                              rest / max_splits, q, ld_q,
-                                              nh, cs, dg, pool, max_splits, part_o, part_ml, dec_qscale,
-                                              sm, sl, so);
+    split_attn_item<bf16_t, D, false, kPaged, kPrefetchFused>(
+        dec_row0 + r, rest % parts.stride_d, rest / parts.stride_d, q, ld_q, nh, cs, dg, pool,
+        parts.stride_d, cs.rows, parts.o_d, parts.ml_d, dec_qscale, sm, sl, so);
   }
 }
 
 template <int D, bool kPaged>
 hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const PagePool &pool, void *out,
-                     int ld_out, int n_split, int max_splits, float *po, float *pml,
-                     const DecodeGroup &dg, int dec_row0, int dec_rows, hipStream_t s) {
+                     int ld_out, int n_split, const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
+                     int dec_rows, hipStream_t s) {
   int items = 0;
   for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh, kBQ);
   const int per_xcd = (items + 7) / 8;
   const int chunk_grid = 8 * per_xcd;
-  const int grid = chunk_grid + dec_rows * max_splits * nh;
+  const int grid = chunk_grid + dec_rows * parts.stride_d * nh;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((attn_fused<D, kPaged>), dim3(grid), dim3(256), 0, s,
                      static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out),
-                     ld_out, qscale, n_split, max_splits, po, pml, per_xcd, chunk_grid, dg, dec_row0,
-                     dec_rows, qscale);
+                     ld_out, qscale, n_split, parts, per_xcd, chunk_grid, dg, dec_row0, dec_rows,
+                     qscale);
   return hipGetLastError();
 }
 
@@ -240,19 +239,21 @@ constexpr int kCombineWaves = 4;
 constexpr int kCombineSlots = kMaxKeySplits / kWave;   // splits per lane
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int row0, int n_rows,
-                                                                   int max_splits, int chunk_rows,
-                                                                   int chunk_splits,
+                                                                   int chunk_rows, int chunk_splits,
                                                                    ChunkSplits table,
-                                                                   const float *part_o,
-                                                                   const float *part_ml, T *out,
+                                                                   AttnParts parts, T *out,
                                                                    int ld_out) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);   // (row, head) index
   if (pair >= n_rows * nh) return;
   const int r = row0 + pair / nh, h = pair % nh;
-  const size_t base = ((size_t)r * nh + h) * max_splits;
-  int n_used = max_splits;
+  size_t base;
+  int n_used;
+  const float *part_o, *part_ml;
   if (r < chunk_rows) {
+    base = ((size_t)r * nh + h) * parts.stride_c;
+    part_o = parts.o_c;
+    part_ml = parts.ml_c;
     n_used = chunk_splits;
     if (chunk_splits == 0) {
       // The row's chunk, found with constant-index selects (the table is a by-value argument).
@@ -263,6 +264,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
       if (ns <= 1) return;   // written by the chunk kernel
       n_used = ns;
     }
+  } else {
+    base = ((size_t)(r - chunk_rows) * nh + h) * parts.stride_d;
+    part_o = parts.o_d;
+    part_ml = parts.ml_d;
+    n_used = parts.stride_d;
   }
   float m[kCombineSlots], l[kCombineSlots], w[kCombineSlots];
   float M = -INFINITY;
@@ -282,6 +288,15 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  // A row's non-empty splits come first (l >= 1 for each: its largest score contributes 2^0); the
+  // empty ones after them hold no output, so only the leading non-empty splits are read.
+  int n_keyed = 0;
+#pragma unroll
+  for (int k = 0; k < kCombineSlots; ++k)
+    if (l[k] > 0.f) n_keyed = lane + k * kWave + 1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) n_keyed = max(n_keyed, __shfl_xor(n_keyed, o, kWave));
+  n_used = n_keyed;
   float L = 0.f;
 #pragma unroll
   for (int k = 0; k < kCombineSlots; ++k) {
@@ -322,13 +337,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
 
 template <typename T, int D>
 hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, const ChunkSet &cs,
-                     const DecodeGroup &dg, const PagePool &pool, int max_splits, float *po, float *pml,
-                     hipStream_t s) {
+                     const DecodeGroup &dg, const PagePool &pool, int stride, int prow0, float *po,
+                     float *pml, hipStream_t s) {
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  const dim3 grid(n_rows, max_splits, nh);
+  const dim3 grid(n_rows, stride, nh);
 #define SARATHI_SPLIT(CR, PG)                                                                   \
   hipLaunchKernelGGL((attn_rows_split<T, D, CR, PG>), grid, dim3(256), 0, s,                   \
-                     static_cast<const T *>(q), ld_q, nh, row0, cs, dg, pool, max_splits, po, pml, qscale)
+                     static_cast<const T *>(q), ld_q, nh, row0, cs, dg, pool, stride, prow0, po, pml, qscale)
   const bool chunk_rows = row0 < cs.rows, paged = pool.k != 0;
   if (chunk_rows) {
     if (paged) SARATHI_SPLIT(true, true); else SARATHI_SPLIT(true, false);
@@ -340,13 +355,13 @@ hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, cons
 }
 
 template <typename T, int D>
-hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, int chunk_rows, int chunk_splits,
-                       const ChunkSplits &table, const float *po, const float *pml, void *out,
-                       int ld_out, hipStream_t s) {
+hipError_t run_combine(int nh, int row0, int n_rows, int chunk_rows, int chunk_splits,
+                       const ChunkSplits &table, const AttnParts &parts, void *out, int ld_out,
+                       hipStream_t s) {
   const int pairs = n_rows * nh;
   hipLaunchKernelGGL((attn_combine<T, D>), dim3((pairs + kCombineWaves - 1) / kCombineWaves),
-                     dim3(64 * kCombineWaves), 0, s, nh, row0, n_rows, max_splits, chunk_rows,
-                     chunk_splits, table, po, pml, static_cast<T *>(out), ld_out);
+                     dim3(64 * kCombineWaves), 0, s, nh, row0, n_rows, chunk_rows, chunk_splits,
+                     table, parts, static_cast<T *>(out), ld_out);
   return hipGetLastError();
 }
 
@@ -354,29 +369,38 @@ hipError_t run_combine(int nh, int row0, int n_rows, int max_splits, int chunk_r
 
 hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
                             const ChunkSet &cs, const DecodeGroup &dg, const PagePool &pool,
-                            int max_splits, float *part_o, float *part_ml, hipStream_t s) {
+                            int stride, int prow0, float *part_o, float *part_ml, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (type == kF32 && d == 64) return run_split<float, 64>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
-  if (type == kF32 && d == 128) return run_split<float, 128>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
-  if (type == kBF16 && d == 64) return run_split<bf16_t, 64>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
-  if (type == kBF16 && d == 128) return run_split<bf16_t, 128>(q, ld_q, nh, row0, n_rows, cs, dg, pool, max_splits, part_o, part_ml, s);
+  if (stride < 1 || stride > kMaxKeySplits || prow0 > row0 || !part_o || !part_ml) return hipErrorInvalidValue;
+#define SARATHI_ROWS(T, D) \
+  return run_split<T, D>(q, ld_q, nh, row0, n_rows, cs, dg, pool, stride, prow0, part_o, part_ml, s)
+  if (type == kF32 && d == 64) SARATHI_ROWS(float, 64);
+  if (type == kF32 && d == 128) SARATHI_ROWS(float, 128);
+  if (type == kBF16 && d == 64) SARATHI_ROWS(bf16_t, 64);
+  if (type == kBF16 && d == 128) SARATHI_ROWS(bf16_t, 128);
+#undef SARATHI_ROWS
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int max_splits,
-                               int chunk_rows, int chunk_splits, const ChunkSplits &table,
-                               const float *part_o, const float *part_ml, void *out, int ld_out,
-                               hipStream_t s) {
+hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int chunk_rows,
+                               int chunk_splits, const ChunkSplits &table, const AttnParts &parts,
+                               void *out, int ld_out, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (chunk_splits < 0 || chunk_splits > max_splits || max_splits > kMaxKeySplits)
+  if (row0 + n_rows > chunk_rows &&
+      (parts.stride_d < 1 || parts.stride_d > kMaxKeySplits || !parts.o_d || !parts.ml_d))
     return hipErrorInvalidValue;
-  if (chunk_splits == 0 && row0 < chunk_rows) {   // some merged rows are chunk rows: the table serves
-    if (table.n < 1 || table.n > kMaxChunks) return hipErrorInvalidValue;
-    for (int j = 0; j < table.n; ++j)
-      if (table.split[j] < 1 || table.split[j] > max_splits) return hipErrorInvalidValue;
+  if (row0 < chunk_rows) {   // some merged rows are chunk rows
+    if (parts.stride_c < 1 || parts.stride_c > kMaxKeySplits || !parts.o_c || !parts.ml_c)
+      return hipErrorInvalidValue;
+    if (chunk_splits < 0 || chunk_splits > parts.stride_c) return hipErrorInvalidValue;
+    if (chunk_splits == 0) {   // the table serves
+      if (table.n < 1 || table.n > kMaxChunks) return hipErrorInvalidValue;
+      for (int j = 0; j < table.n; ++j)
+        if (table.split[j] < 1 || table.split[j] > parts.stride_c) return hipErrorInvalidValue;
+    }
   }
 #define SARATHI_COMBINE(T, D) \
-  return run_combine<T, D>(nh, row0, n_rows, max_splits, chunk_rows, chunk_splits, table, part_o, part_ml, out, ld_out, s)
+  return run_combine<T, D>(nh, row0, n_rows, chunk_rows, chunk_splits, table, parts, out, ld_out, s)
   if (type == kF32 && d == 64) SARATHI_COMBINE(float, 64);
   if (type == kF32 && d == 128) SARATHI_COMBINE(float, 128);
   if (type == kBF16 && d == 64) SARATHI_COMBINE(bf16_t, 64);
@@ -386,22 +410,29 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
 }
 
 hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
-                             const PagePool &pool, void *out, int ld_out, int n_split, int max_splits,
-                             float *part_o, float *part_ml, const DecodeGroup &dg, int dec_row0,
+                             const PagePool &pool, void *out, int ld_out, int n_split,
+                             const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
                              int dec_rows, hipStream_t s) {
   if (cs.n <= 0 || cs.n > kMaxChunks || dec_rows <= 0 || dec_rows > kMaxDecodesPerLaunch)
     return hipErrorInvalidValue;
-  if (n_split < 1 || n_split > max_splits || max_splits > kMaxKeySplits || !part_o || !part_ml)
+  if (dec_row0 < cs.rows || parts.stride_d < 1 || parts.stride_d > kMaxKeySplits || !parts.o_d || !parts.ml_d)
+    return hipErrorInvalidValue;
+  if (n_split < 1 || (n_split > 1 && (parts.stride_c != n_split || !parts.o_c || !parts.ml_c)))
     return hipErrorInvalidValue;
   for (int j = 0; j < cs.n; ++j)
     if (cs.split[j] < 1 || cs.split[j] > n_split) return hipErrorInvalidValue;
   const bool paged = pool.k != 0;
-  if (d == 128)
-    return paged ? run_fused<128, true>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s)
-                 : run_fused<128, false>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s);
-  if (d == 64)
-    return paged ? run_fused<64, true>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s)
-                 : run_fused<64, false>(q, ld_q, nh, cs, pool, out, ld_out, n_split, max_splits, part_o, part_ml, dg, dec_row0, dec_rows, s);
+#define SARATHI_FUSED(D, P) \
+  return run_fused<D, P>(q, ld_q, nh, cs, pool, out, ld_out, n_split, parts, dg, dec_row0, dec_rows, s)
+  if (d == 128) {
+    if (paged) SARATHI_FUSED(128, true);
+    SARATHI_FUSED(128, false);
+  }
+  if (d == 64) {
+    if (paged) SARATHI_FUSED(64, true);
+    SARATHI_FUSED(64, false);
+  }
+#undef SARATHI_FUSED
   return hipErrorInvalidValue;
 }
 

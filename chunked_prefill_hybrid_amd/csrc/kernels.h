@@ -17,6 +17,7 @@ enum StorageType { kF32 = 0, kBF16 = 1 };
 // non-null it receives v (float32).  out[r] = RMSNorm(v) * g  or  LayerNorm(v) * g + b for r < rows;
 // rows rows..rows_alloc-1 of out are zero-filled.  out is row-major [rows_alloc, H], or with
 // kmajor k-tile-major [H/64][rows_alloc][64] (the layout the bf16 GEMM reads fastest; H % 64 == 0).
+constexpr int kMaxHidden = 16384;   // widest row a norm workgroup holds (1024 threads x 16 elements)
 hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
                             const float *part, int splits, float *sum_out, const float *g,
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
@@ -82,7 +83,9 @@ hipError_t launch_rope_append(int type, const float *part, int splits, int rows_
 // ---------------------------------------------------------------------------------------------
 // Split-KV single-query attention for rows [row0, row0+n_rows): each (row, head) attends over keys
 // 0..pos of its cache in balanced splits of at most kAttnSplit keys; each split writes its partial
-// (running max m and sum l in the log2 domain, unnormalised output o) to part_ml / part_o.
+// (running max m and sum l in the log2 domain, unnormalised output o) to part_ml / part_o, at slot
+// ((r - prow0) * nh + h) * stride + s (stride >= the row's split count; splits past a row's count
+// are written as empty partials).
 constexpr int kAttnSplit = 256;
 constexpr int kMaxKeySplits = 256;   // split partials per (row, head): keys up to 65536
 __host__ __device__ inline int attn_splits(int n_keys) {
@@ -90,7 +93,16 @@ __host__ __device__ inline int attn_splits(int n_keys) {
 }
 hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
                             const ChunkSet &cs, const DecodeGroup &dg, const PagePool &pool,
-                            int max_splits, float *part_o, float *part_ml, hipStream_t s);
+                            int stride, int prow0, float *part_o, float *part_ml, hipStream_t s);
+
+// Where the attention split partials of a forward live: chunk rows (batch rows below the merge's
+// chunk_rows) in region c, `stride_c` partials per (row, head), slot (r * nh + h) * stride_c + s;
+// decode rows in region d, slot ((r - chunk_rows) * nh + h) * stride_d + s.
+struct AttnParts {
+  float *o_c, *ml_c;   // [chunk rows][nh][stride_c] x (D floats | (m, l)), or null without chunk partials
+  float *o_d, *ml_d;   // [decode rows][nh][stride_d] x (D floats | (m, l))
+  int stride_c, stride_d;
+};
 
 // Partial counts of the chunk rows for the merge: chunk i owns rows row0[i].. (up to the next
 // chunk's first row) and left split[i] partials per row and head; split[i] == 1 means the chunk
@@ -101,14 +113,13 @@ struct ChunkSplits {
   int32_t n;
 };
 // Merges the split partials of rows [row0, row0+n_rows) into out[row, h*d + e] (storage type,
-// row stride ld_out).  Partials sit at ((row * nh + h) * max_splits + s).  Rows at or past
-// chunk_rows have max_splits of them.  Rows below it have chunk_splits of them when chunk_splits > 0;
-// with chunk_splits == 0 they have their chunk's count from `table`, and the rows of chunks with one
-// split are left as they are.
-hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int max_splits,
-                               int chunk_rows, int chunk_splits, const ChunkSplits &table,
-                               const float *part_o, const float *part_ml, void *out, int ld_out,
-                               hipStream_t s);
+// row stride ld_out).  Rows at or past chunk_rows merge their stride_d partials of region d.  Rows
+// below it merge chunk_splits partials of region c when chunk_splits > 0; with chunk_splits == 0
+// they merge their chunk's count from `table`, and the rows of chunks with one split are left as
+// they are.
+hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int chunk_rows,
+                               int chunk_splits, const ChunkSplits &table, const AttnParts &parts,
+                               void *out, int ld_out, hipStream_t s);
 
 // Flash-style causal chunk attention (bf16, MFMA) over every chunk of the set: row row0[j] + t of
 // chunk j attends to keys 0..off[j]+t of chunk j's cache.  q and out are batch-row indexed (row
@@ -133,11 +144,12 @@ hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const Chunk
 
 // The chunk attention of every chunk of the set and the split-KV attention of decode rows
 // [dec_row0, dec_row0 + dec_rows) (one decode group, dg) in one launch (bf16).  Chunk rows are
-// handled as by launch_attn_chunk with n_split key splits (partials when n_split > 1, stride
-// max_splits); decode rows write split partials as launch_attn_rows does.
+// handled as by launch_attn_chunk with n_split key splits (partials in region c of `parts` when
+// n_split > 1, stride_c = n_split); decode rows write split partials to region d as
+// launch_attn_rows does (stride_d, first row of the region = cs.rows).
 hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
-                             const PagePool &pool, void *out, int ld_out, int n_split, int max_splits,
-                             float *part_o, float *part_ml, const DecodeGroup &dg, int dec_row0,
+                             const PagePool &pool, void *out, int ld_out, int n_split,
+                             const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
                              int dec_rows, hipStream_t s);
 
 // Zero-fill rows [row0, row1) of a [*, cols] storage matrix (row stride ld).

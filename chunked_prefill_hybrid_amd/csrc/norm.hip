@@ -54,6 +54,7 @@ constexpr int kMaxSplits = 8;   // split partials a consumer sums (the planner n
 // a batch still keep several waves of memory requests per SIMD in flight).
 constexpr int kNormThreads = 1024;
 constexpr int kRowPieces = 4;   // 4-element pieces per thread: rows up to 16384 wide
+static_assert(4 * kNormThreads * kRowPieces == kMaxHidden, "row width limit");
 
 // v[0..3] += sum_s part[s][off..off+3] in split order; every split's load is issued before its add
 // so a thread keeps several loads in flight.
@@ -195,7 +196,7 @@ hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const vo
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
                             bool kmajor, hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
-  if (splits > kMaxSplits || H > 4 * kNormThreads * kRowPieces || H % 4) return hipErrorInvalidValue;
+  if (splits > kMaxSplits || H > kMaxHidden || H % 4) return hipErrorInvalidValue;
   if (kmajor && H % 64) return hipErrorInvalidValue;
   const int km = kmajor ? rows_alloc : 0;
   if (res_type == kF32 && out_type == kF32)

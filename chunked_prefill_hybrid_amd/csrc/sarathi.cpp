@@ -81,6 +81,11 @@ sarathi_status check_desc(const sarathi_layer_desc *d) {
     return fail(SARATHI_ERR_UNSUPPORTED, "hidden and n_heads*head_dim must be multiples of 64");
   if (d->dtype == SARATHI_BF16 && d->ffn % 64)
     return fail(SARATHI_ERR_UNSUPPORTED, "ffn must be a multiple of 64 in bf16 mode");
+  if (d->dtype == SARATHI_F32 && d->ffn % 16)
+    return fail(SARATHI_ERR_UNSUPPORTED, "ffn must be a multiple of 16 in f32 mode");
+  if (d->hidden > kMaxHidden)
+    return fail(SARATHI_ERR_UNSUPPORTED, "hidden %d > %d (a norm row is held by one workgroup)",
+                d->hidden, kMaxHidden);
   if ((long long)d->max_tokens * 3 * d->n_heads * d->head_dim > (1ll << 31))
     return fail(SARATHI_ERR_UNSUPPORTED, "max_tokens too large");
   return SARATHI_OK;
@@ -313,10 +318,12 @@ sarathi_status check_view(const sarathi_layer_desc *d, const BatchView &b, bool 
 constexpr int kPlanCUs = 256;
 
 struct Plan {
-  int T, T_alloc, max_splits;
+  int T, T_alloc, max_splits;   // max_splits: the most key splits of any row (reported by plan_describe)
   int chunk_splits;   // key-range splits of the MFMA chunk kernel (1: it writes the output itself)
+  int stride_c;       // attention partials per (chunk row, head): 0 when no chunk row leaves partials
+  int stride_d;       // attention partials per (decode row, head)
   GemmPlan qkv, o, up, down;
-  size_t n1, q, attn, h1, n2, act, part, part_o, part_ml, total;
+  size_t n1, q, attn, h1, n2, act, part, part_o_c, part_ml_c, part_o_d, part_ml_d, total;
 };
 
 #ifndef SARATHI_FUSED_ATTN
@@ -348,11 +355,19 @@ ChunkSet chunk_set(const BatchView &b) {
   return cs;
 }
 
-int max_key_splits(const sarathi_layer_desc *d, const BatchView &b, int chunk_splits) {
-  int ms = chunk_splits;
-  if (chunk_uses_split(d))
-    for (int j = 0; j < b.n_chunks; ++j)
-      ms = std::max(ms, attn_splits(b.chunks[j].offset + b.chunks[j].len));
+// Attention split partials per (row, head) of the chunk rows: with the split-KV kernel serving them
+// (float32) the most splits of any chunk row; with the MFMA kernel the chunk splits when there are
+// several, else none (the chunk kernel writes its rows itself).
+int chunk_partial_stride(const sarathi_layer_desc *d, const BatchView &b, int chunk_splits) {
+  if (!chunk_uses_split(d)) return chunk_splits > 1 ? chunk_splits : 0;
+  int ms = 0;
+  for (int j = 0; j < b.n_chunks; ++j) ms = std::max(ms, attn_splits(b.chunks[j].offset + b.chunks[j].len));
+  return ms;
+}
+
+// ... and of the decode rows: the most splits of any decode.
+int decode_partial_stride(const BatchView &b) {
+  int ms = 1;
   for (int i = 0; i < b.B; ++i) ms = std::max(ms, attn_splits(b.decode_len[i] + 1));
   return ms;
 }
@@ -395,7 +410,9 @@ Plan make_plan(const sarathi_layer_desc *d, const BatchView &b) {
   p.T_alloc = round_up(p.T, 64);
   ChunkSet cs = chunk_set(b);
   p.chunk_splits = plan_chunk_splits(d, b, cs);
-  p.max_splits = max_key_splits(d, b, p.chunk_splits);
+  p.stride_c = chunk_partial_stride(d, b, p.chunk_splits);
+  p.stride_d = decode_partial_stride(b);
+  p.max_splits = std::max({p.chunk_splits, p.stride_c, b.B > 0 ? p.stride_d : 1});
   const int ty = d->dtype;
   const size_t el = elem_size(ty), R = p.T_alloc;
   const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
@@ -417,8 +434,14 @@ Plan make_plan(const sarathi_layer_desc *d, const BatchView &b) {
   p.n2 = take(R * H * el);
   p.act = take(R * F * el);
   p.part = take(part_elems * 4);
-  p.part_o = take((size_t)p.T * d->n_heads * p.max_splits * d->head_dim * 4);
-  p.part_ml = take((size_t)p.T * d->n_heads * p.max_splits * 2 * 4);
+  // attention split partials: only the rows the merge reads (decode rows, and chunk rows when they
+  // leave partials)
+  const size_t slots_c = (size_t)b.C * d->n_heads * p.stride_c;
+  const size_t slots_d = (size_t)b.B * d->n_heads * p.stride_d;
+  p.part_o_c = take(slots_c * d->head_dim * 4);
+  p.part_ml_c = take(slots_c * 2 * 4);
+  p.part_o_d = take(slots_d * d->head_dim * 4);
+  p.part_ml_d = take(slots_d * 2 * 4);
   p.total = off;
   return p;
 }
@@ -500,8 +523,15 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   ChunkSet cs = chunk_set(b);
   plan_chunk_splits(d, b, cs);   // the same counts as p.chunk_splits (their largest)
   const PagePool pool = page_pool(b);
-  float *po = reinterpret_cast<float *>(ws + p.part_o);
-  float *pml = reinterpret_cast<float *>(ws + p.part_ml);
+  AttnParts parts{};
+  if (p.stride_c > 0) {
+    parts.o_c = reinterpret_cast<float *>(ws + p.part_o_c);
+    parts.ml_c = reinterpret_cast<float *>(ws + p.part_ml_c);
+    parts.stride_c = p.stride_c;
+  }
+  parts.o_d = reinterpret_cast<float *>(ws + p.part_o_d);
+  parts.ml_d = reinterpret_cast<float *>(ws + p.part_ml_d);
+  parts.stride_d = p.stride_d;
   const bool split_chunk = chunk_uses_split(d);
   // Batches with chunk rows and decode rows run both attentions in one launch when fused_attention
   // says so (few chunk items): the decode splits then fill the units the latency-bound chunk work
@@ -512,10 +542,10 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
     if (split_chunk) {
       const DecodeGroup none = decode_group(b, B);   // empty group
       HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, cs, none, pool,
-                               p.max_splits, po, pml, s));
+                               p.stride_c, 0, parts.o_c, parts.ml_c, s));
     } else {
       HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, cs, pool, out, A, p.chunk_splits,
-                                p.max_splits, po, pml, s));
+                                std::max(p.stride_c, 1), parts.o_c, parts.ml_c, s));
     }
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_CHUNK, C > 0 && !fused));
@@ -523,20 +553,20 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
     const DecodeGroup g = decode_group(b, base);
     if (fused && base == 0)
-      HIP_TRY(launch_attn_fused(d->head_dim, q, A, d->n_heads, cs, pool, out, A, p.chunk_splits,
-                                p.max_splits, po, pml, g, C, g.n, s));
+      HIP_TRY(launch_attn_fused(d->head_dim, q, A, d->n_heads, cs, pool, out, A, p.chunk_splits, parts,
+                                g, C, g.n, s));
     else
       HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, cs, g, pool,
-                               p.max_splits, po, pml, s));
+                               p.stride_d, C, parts.o_d, parts.ml_d, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_DECODE, B > 0));
   HIP_TRY(mk.start(SARATHI_STAGE_ATTN_MERGE));
-  // Chunk rows need merging when the split-KV kernel served them (all of them, max_splits partials
-  // each) or their chunk was split by the MFMA kernel (the merge reads each chunk's count from the
-  // table and leaves the rows of unsplit chunks alone).
-  const bool merge_chunk = split_chunk || p.chunk_splits > 1;
+  // Chunk rows need merging when the split-KV kernel served them (all their splits) or their chunk
+  // was split by the MFMA kernel (the merge reads each chunk's count from the table and leaves the
+  // rows of unsplit chunks alone).
+  const bool merge_chunk = p.stride_c > 0;
   const int merge_row0 = merge_chunk ? 0 : C;
-  const int chunk_splits = split_chunk ? p.max_splits : 0;
+  const int chunk_splits = split_chunk ? p.stride_c : 0;
   ChunkSplits table{};
   table.n = cs.n;
   for (int j = 0; j < cs.n; ++j) {
@@ -544,8 +574,8 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
     table.split[j] = cs.split[j];
   }
   if (C + B > merge_row0)
-    HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, merge_row0, C + B - merge_row0,
-                                p.max_splits, C, chunk_splits, table, po, pml, out, A, s));
+    HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, merge_row0, C + B - merge_row0, C,
+                                chunk_splits, table, parts, out, A, s));
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_MERGE, C + B > merge_row0));
   return SARATHI_OK;
 }

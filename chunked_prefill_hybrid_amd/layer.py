@@ -31,6 +31,17 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _hold_for(t: torch.Tensor, stream) -> None:
+    """Tell torch's caching allocator that `t` (a workspace this module allocated on the current
+    stream) is in use by the work just enqueued on `stream`, so its memory is not handed to another
+    allocation before that work ends.  Nothing to do when the work runs on the current stream."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream(stream))
+    if s.cuda_stream != torch.cuda.current_stream().cuda_stream:
+        t.record_stream(s)
+
+
 def make_desc(shape, max_tokens: int, max_pos: int) -> _abi.sarathi_layer_desc:
     return _abi.sarathi_layer_desc(
         shape.hidden, shape.n_heads, shape.head_dim, shape.ffn,
@@ -123,7 +134,8 @@ class HybridLayer:
         if need == 0:
             st = _abi.sarathi_paged_batch_check(self.desc, b)
             raise _abi.SarathiError(st, "paged batch", _abi.sarathi_last_error())
-        if workspace is None:
+        own_ws = workspace is None
+        if own_ws:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
         ws_ptr = _ptr(workspace)
         nbytes = workspace.numel() * workspace.element_size()
@@ -133,6 +145,8 @@ class HybridLayer:
             _abi.sarathi_paged_forward_debug(self.handle, b, ws_ptr, nbytes, _stream(stream), d)
         else:
             _abi.sarathi_paged_forward(self.handle, b, ws_ptr, nbytes, _stream(stream))
+        if own_ws:
+            _hold_for(workspace, stream)
         del keep
         return y
 
@@ -145,7 +159,8 @@ class HybridLayer:
         if need == 0:
             st = _abi.sarathi_multi_batch_check(self.desc, b)
             raise _abi.SarathiError(st, "multi batch", _abi.sarathi_last_error())
-        if workspace is None:
+        own_ws = workspace is None
+        if own_ws:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
         ws_ptr = _ptr(workspace)
         nbytes = workspace.numel() * workspace.element_size()
@@ -155,6 +170,8 @@ class HybridLayer:
             _abi.sarathi_multi_forward_debug(self.handle, b, ws_ptr, nbytes, _stream(stream), d)
         else:
             _abi.sarathi_multi_forward(self.handle, b, ws_ptr, nbytes, _stream(stream))
+        if own_ws:
+            _hold_for(workspace, stream)
         del keep
         return y
 
@@ -168,7 +185,8 @@ class HybridLayer:
         if need == 0:
             st = _abi.sarathi_batch_check(self.desc, b)
             raise _abi.SarathiError(st, "batch", _abi.sarathi_last_error())
-        if workspace is None:
+        own_ws = workspace is None
+        if own_ws:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
         ws_ptr = _ptr(workspace)
         nbytes = workspace.numel() * workspace.element_size()
@@ -178,6 +196,8 @@ class HybridLayer:
             _abi.sarathi_layer_forward_debug(self.handle, b, ws_ptr, nbytes, _stream(stream), d)
         else:
             _abi.sarathi_layer_forward(self.handle, b, ws_ptr, nbytes, _stream(stream))
+        if own_ws:
+            _hold_for(workspace, stream)
         del keep
         return y
 
@@ -209,6 +229,7 @@ def attention(shape, q: torch.Tensor, out: torch.Tensor, chunk_len: int, chunk_o
         raise _abi.SarathiError(_abi.sarathi_batch_check(desc, b), "batch", _abi.sarathi_last_error())
     ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     _abi.sarathi_attention(desc, b, _ptr(q, dt), _ptr(out, dt), _ptr(ws), need, _stream(stream))
+    _hold_for(ws, stream)
     del keep
     return out
 
@@ -261,12 +282,15 @@ class HybridStack:
             # Re-run with reporting so the error names the offending layer and field.
             _abi.sarathi_stack_forward(handles, b, 0, 0, _stream(stream))
             raise RuntimeError("stack batch rejected")
-        if workspace is None:
+        own_ws = workspace is None
+        if own_ws:
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
             workspace = self._ws
         _abi.sarathi_stack_forward(handles, b, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream))
+        if own_ws:
+            _hold_for(workspace, stream)
         del keep
         return y
 

@@ -263,8 +263,27 @@ def as_draws(rng) -> Draws:
     return Draws(int(rng))
 
 
+# Where _normal draws: None = host numpy arrays (PCG64 blocks, as described above); a torch device
+# string = tensors drawn on that device (see generate(..., device=...)).
+_DEVICE = None
+
+
+def _normal_device(seq: np.random.SeedSequence, shape, std: float, dtype: str):
+    """N(0, std^2) values drawn on _DEVICE by torch's generator, seeded from the tensor's stream; stored
+    as bfloat16 (round to nearest even) for the bf16 workloads, else float32."""
+    import torch
+    g = torch.Generator(device=_DEVICE)
+    g.manual_seed(int(seq.generate_state(1, np.uint64)[0] >> np.uint64(1)))
+    t = torch.randn(tuple(int(v) for v in shape), generator=g, device=_DEVICE, dtype=torch.float32)
+    if std != 1.0:
+        t *= std
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
 def _normal(draws: Draws, shape, std: float, dtype: str) -> np.ndarray:
     """float32 N(0, std^2) values of the given shape from the next stream, bf16-rounded if asked."""
+    if _DEVICE is not None:
+        return _normal_device(draws.next(), shape, std, dtype)
     n = int(np.prod(shape))
     out = np.empty(n, np.float32)
     seeds = draws.next().spawn(max(1, -(-n // _BLOCK)))
@@ -317,6 +336,12 @@ def _cache(draws: Draws, shape: LayerShape, cap: int, filled: int, fill_rest: fl
         vals = _normal(draws, (nh, filled, d), 1.0, shape.dtype) if filled else None
         if filled == cap:
             c = vals
+        elif _DEVICE is not None:
+            import torch
+            c = torch.full((nh, cap, d), fill_rest, device=_DEVICE,
+                           dtype=torch.bfloat16 if shape.dtype == "bf16" else torch.float32)
+            if filled:
+                c[:, :filled, :] = vals
         else:
             c = np.empty((nh, cap, d), np.float32)
             c[:, filled:, :] = fill_rest
@@ -381,14 +406,25 @@ def make_multi_batch(shape: LayerShape, spec: MultiSpec, rng, fill_rest: float =
     return {"x": x, "chunks": chunks, "decode_len": lens, "decode_k": dk, "decode_v": dv}
 
 
-def generate(w: Workload, fill_rest: float = 0.0) -> Tuple[dict, dict]:
-    """(weights, batch) of a workload, drawn from its seed in the fixed order."""
+def generate(w: Workload, fill_rest: float = 0.0, device: Optional[str] = None) -> Tuple[dict, dict]:
+    """(weights, batch) of a workload, drawn from its seed in the fixed order.
+
+    device=None: host numpy float32 arrays (bf16-rounded values for the bf16 workloads), the inputs
+    of the parity tests.  device='cuda' (throughput runs): the same streams in the same order, but
+    every normal tensor is drawn on the GPU by torch's generator seeded from its stream and kept in
+    the storage type (bfloat16 or float32); lengths and compositions are the same as on the host,
+    the values are not.  Norm gains and biases stay host arrays in both cases."""
+    global _DEVICE
     rng = Draws(w.seed)
-    weights = make_weights(w.shape, rng)
-    if isinstance(w.batch, MultiSpec):
-        batch = make_multi_batch(w.shape, w.batch, rng, fill_rest)
-    else:
-        batch = make_batch(w.shape, w.batch, rng, fill_rest)
+    _DEVICE = device
+    try:
+        weights = make_weights(w.shape, rng)
+        if isinstance(w.batch, MultiSpec):
+            batch = make_multi_batch(w.shape, w.batch, rng, fill_rest)
+        else:
+            batch = make_batch(w.shape, w.batch, rng, fill_rest)
+    finally:
+        _DEVICE = None
     return weights, batch
 
 

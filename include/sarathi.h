@@ -59,7 +59,7 @@ typedef enum { SARATHI_F32 = 0, SARATHI_BF16 = 1 } sarathi_dtype;
 typedef enum { SARATHI_ARCH_LLAMA = 0, SARATHI_ARCH_GPT = 1 } sarathi_arch;
 
 typedef struct {
-    int32_t hidden;      /* H: model width; multiple of 64 */
+    int32_t hidden;      /* H: model width; multiple of 64, at most 16384 */
     int32_t n_heads;     /* nh */
     int32_t head_dim;    /* d: 64 or 128.  Attention width A = nh*d; multiple of 64 */
     int32_t ffn;         /* F: FFN width; multiple of 64 in bf16 mode, of 16 in f32 mode */
@@ -121,7 +121,8 @@ typedef struct sarathi_layer sarathi_layer;   /* opaque, immutable after create 
 /* Creates a layer handle for the current HIP device.  Copies *desc; keeps the weight pointers (does
  * not copy weights).  Allocates only the device RoPE cos/sin table [max_pos, head_dim/2] (LLAMA),
  * built on the host in float64.  Errors: INVALID (null pointers, non-positive sizes), UNSUPPORTED
- * (head_dim not 64/128, widths not multiples of 64), NOMEM, HIP.  On error *out is set to NULL. */
+ * (head_dim not 64/128, widths not multiples of 64, ffn not a multiple of 16 in f32 mode, hidden
+ * above 16384), NOMEM, HIP.  On error *out is set to NULL. */
 sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarathi_weights *weights,
                                     sarathi_layer **out);
 

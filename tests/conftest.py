@@ -15,3 +15,17 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """After a GPU session: the per-tensor parity errors of every comparison against the oracle."""
+    gu = sys.modules.get("tests.gpu_util")
+    if gu is None or not getattr(gu, "RECORDS", None):
+        return
+    table = gu.parity_table()
+    terminalreporter.write_sep("-", "parity errors against the oracle (rel = max|gpu-ref| / max|ref|)")
+    terminalreporter.write_line(table)
+    path = os.environ.get("SARATHI_PARITY_TABLE")
+    if path:
+        with open(path, "w") as f:
+            f.write(table + "\n")

@@ -18,6 +18,9 @@ from chunked_prefill_hybrid_amd import layer as hl
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 DEV = "cuda"
+# Every comparison of a session: (label, tolerance, {tensor: rel error}); the test session's summary
+# prints them as a table (and writes it to $SARATHI_PARITY_TABLE when set).
+RECORDS = []
 
 
 def say(*a):
@@ -105,6 +108,7 @@ def compare_rows(shape, x, ref, y_dev, nk, nv, dd, tol=None, label=""):
         for k in ("n1", "qkv", "q_rot", "attn", "h1", "n2", "act"):
             errs[k] = rel(dd[k].cpu().numpy(), ref[k])
     say(f"[{label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    RECORDS.append((label, tol, dict(errs)))
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     assert not bad, f"{label}: over tolerance {tol}: {bad}"
     return errs
@@ -153,3 +157,19 @@ def compare_multi(shape, b, ref, db, dd, tol=None, label=""):
 
 def oracle_ref(shape, w, b):
     return oracle.layer_forward(shape, w, b)
+
+
+PARITY_COLUMNS = ("y", "dy", "attn", "q_rot", "new_k", "new_v", "n1", "h1", "n2", "act")
+
+
+def parity_table(records=None):
+    """Markdown table of recorded comparisons: per tensor, rel = max|gpu - ref| / max|ref|, and the
+    margin (tolerance / worst error)."""
+    records = RECORDS if records is None else records
+    head = "| case | tol | " + " | ".join(PARITY_COLUMNS) + " | worst / tol |"
+    lines = [head, "|" + "---|" * (len(PARITY_COLUMNS) + 3)]
+    for label, tol, errs in records:
+        worst = max(errs.values()) if errs else 0.0
+        cells = [f"{errs[c]:.2e}" if c in errs else "" for c in PARITY_COLUMNS]
+        lines.append(f"| {label} | {tol:g} | " + " | ".join(cells) + f" | {worst / tol:.3f} |")
+    return "\n".join(lines)

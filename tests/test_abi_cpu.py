@@ -107,6 +107,8 @@ def test_invalid_batches(lib, kw, status):
     (dict(head_dim=96), _abi.SARATHI_ERR_UNSUPPORTED),
     (dict(hidden=200), _abi.SARATHI_ERR_UNSUPPORTED),
     (dict(dtype=1, ffn=688), _abi.SARATHI_ERR_UNSUPPORTED),   # bf16 needs ffn % 64 == 0
+    (dict(ffn=680), _abi.SARATHI_ERR_UNSUPPORTED),            # f32 needs ffn % 16 == 0
+    (dict(hidden=20480), _abi.SARATHI_ERR_UNSUPPORTED),       # a norm row holds at most 16384
     (dict(arch=7), _abi.SARATHI_ERR_INVALID),
     (dict(max_pos=0), _abi.SARATHI_ERR_INVALID),
 ])
