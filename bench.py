@@ -128,7 +128,8 @@ def load_traffic(stage, workload_key):
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock and socket power from a host thread (AMD SMI) while it runs.
+    """Samples the GPU's graphics clock and socket power from a host thread (AMD SMI GPU metrics)
+    while it runs.
     The device is matched by PCI address to torch's device 0; on any failure the summary says why."""
 
     def __init__(self, period_s=0.005):
@@ -154,16 +155,18 @@ class ClockSampler:
             self.error = f"{type(e).__name__}: {e}"
 
     def _read(self):
-        c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-        w = None
-        try:
-            pw = self._smi.amdsmi_get_power_info(self._h)
-            w = pw.get("current_socket_power")
-            if not isinstance(w, (int, float)):
-                w = pw.get("average_socket_power")
-        except Exception:
-            pass
-        return c.get("clk"), (w if isinstance(w, (int, float)) else None)
+        # The SMU's metrics table (refreshed by the firmware every few milliseconds): the current
+        # graphics clock of each XCD (their mean; unset entries read as 0xFFFF or "N/A") and the
+        # socket power.
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+
+        def num(v):
+            return v if isinstance(v, (int, float)) and 0 < v < 0xFFFF else None
+        clks = [num(c) for c in (m.get("current_gfxclks") or []) if num(c)]
+        mhz = sum(clks) / len(clks) if clks else (num(m.get("current_gfxclk")) or
+                                                   num(m.get("average_gfxclk_frequency")))
+        w = num(m.get("current_socket_power")) or num(m.get("average_socket_power"))
+        return mhz, w
 
     def _loop(self):
         while not self._stop.is_set():
@@ -187,10 +190,10 @@ class ClockSampler:
 
     def summary(self):
         if not self.samples:
-            return {"source": "amdsmi", "samples": 0, "error": self.error or "no samples"}
+            return {"source": "amdsmi gpu_metrics", "samples": 0, "error": self.error or "no samples"}
         mhz = [c for c, _ in self.samples if isinstance(c, (int, float))]
         w = [p for _, p in self.samples if isinstance(p, (int, float))]
-        out = {"source": "amdsmi", "samples": len(self.samples)}
+        out = {"source": "amdsmi gpu_metrics", "samples": len(self.samples)}
         if mhz:
             out.update(gfx_mhz_median=statistics.median(mhz), gfx_mhz_min=min(mhz), gfx_mhz_max=max(mhz))
         if w:
@@ -310,11 +313,12 @@ def measure(key, args, changes=None, page_size=None, sweep=True):
             nc = len(chunks)
             spec = [(c["len"], c["offset"], t) for c, t in zip(chunks, tbs)]
             b, keep = layer.paged_batch(x, y, pool, spec, tbs[nc:], lens)
-            ws = torch.empty(layer.workspace_size(b), dtype=torch.uint8, device="cuda")
             sub = {}
             if C > 0 and lens:
                 sub["chunk_only"] = layer.paged_batch(x[:C], y[:C], pool, spec, [], [])
                 sub["decode_only"] = layer.paged_batch(x[C:], y[C:], pool, [], tbs[nc:], lens)
+            need = max([layer.workspace_size(b)] + [layer.workspace_size(sb) for sb, _ in sub.values()])
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
             reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, pool, tbs, wr)))
             continue
         ckv = [(cl(k), cl(v)) for k, v in base["ck"]]
@@ -326,7 +330,6 @@ def measure(key, args, changes=None, page_size=None, sweep=True):
             spec = None
             b, keep = layer.batch(x, y, C, chunks[0]["offset"] if chunks else 0, ckv[0] if ckv else None,
                                   dkv, lens)
-        ws = torch.empty(layer.workspace_size(b), dtype=torch.uint8, device="cuda")
         sub = {}
         if C > 0 and lens:
             # the same rows split into a chunk-only and a decode-only batch (same caches, same slots)
@@ -336,8 +339,11 @@ def measure(key, args, changes=None, page_size=None, sweep=True):
             else:
                 sub["chunk_only"] = layer.batch(x[:C], y[:C], C, chunks[0]["offset"], ckv[0], [], [])
                 sub["decode_only"] = layer.batch(x[C:], y[C:], 0, 0, None, dkv, lens)
-            for name, (sb, _) in sub.items():
-                assert layer.workspace_size(sb) <= ws.numel(), name
+        # one workspace serves the batch and its chunk-only and decode-only parts (a part's plan can
+        # need more: a chunk alone may split its key ranges where the hybrid batch's fused launch
+        # does not)
+        need = max([layer.workspace_size(b)] + [layer.workspace_size(sb) for sb, _ in sub.values()])
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         reps.append(dict(layer=layer, b=b, keep=keep, ws=ws, sub=sub, bufs=(x, y, ckv, dkv, wr)))
     info = _abi.plan_describe(reps[0]["layer"].desc, reps[0]["b"])
     chunk_splits = [int(info.chunk_splits[j]) for j in range(len(chunks))]

@@ -75,10 +75,12 @@ def run(argv) -> int:
     torch.cuda.set_device(0)
     wk = wl.workload(args.workload)
     shape = wk.shape
-    weights, batch = wl.generate(wk)
+    weights, batch = wl.generate(wk, device="cuda")
     dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
 
     def dev(a, t=dt):
+        if isinstance(a, torch.Tensor):
+            return a.to(t)
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
 
     wdev = {k: dev(v, torch.float32 if k.startswith("norm") else dt) for k, v in weights.items() if v is not None}
