@@ -28,7 +28,8 @@ SARATHI_ARCH_GPT = 1
 
 EXPORTED = [
     "sarathi_layer_create", "sarathi_layer_destroy", "sarathi_batch_check", "sarathi_workspace_size",
-    "sarathi_layer_forward", "sarathi_layer_forward_debug", "sarathi_gemm", "sarathi_attention",
+    "sarathi_layer_forward", "sarathi_layer_forward_debug", "sarathi_layer_forward_noalloc",
+    "sarathi_gemm", "sarathi_attention",
     "sarathi_status_str", "sarathi_last_error", "sarathi_timer_create", "sarathi_timer_destroy",
     "sarathi_layer_forward_timed", "sarathi_timer_read", "sarathi_stack_workspace_size",
     "sarathi_stack_forward", "sarathi_multi_batch_check", "sarathi_multi_workspace_size",
@@ -146,6 +147,8 @@ def lib():
         L.sarathi_workspace_size.restype = c_size_t
         L.sarathi_layer_forward.argtypes = [c_void_p, POINTER(sarathi_batch), c_void_p, c_size_t, c_void_p]
         L.sarathi_layer_forward.restype = c_int32
+        L.sarathi_layer_forward_noalloc.argtypes = [c_void_p, POINTER(sarathi_batch), c_void_p]
+        L.sarathi_layer_forward_noalloc.restype = c_int32
         L.sarathi_layer_forward_debug.argtypes = [c_void_p, POINTER(sarathi_batch), c_void_p, c_size_t,
                                                   c_void_p, POINTER(sarathi_debug_dump)]
         L.sarathi_layer_forward_debug.restype = c_int32
@@ -240,6 +243,14 @@ def sarathi_workspace_size(desc: sarathi_layer_desc, batch: sarathi_batch) -> in
 
 def sarathi_layer_forward(handle: int, batch: sarathi_batch, ws: int, ws_bytes: int, stream: int) -> None:
     _check(lib().sarathi_layer_forward(handle, byref(batch), ws, ws_bytes, stream), "sarathi_layer_forward")
+
+
+def sarathi_layer_forward_noalloc(handle: int, batch: sarathi_batch, stream: int) -> None:
+    """The layer forward on the library's fixed 128 MiB device scratch (no workspace argument)."""
+    _check(lib().sarathi_layer_forward_noalloc(handle, byref(batch), stream), "sarathi_layer_forward_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def sarathi_layer_forward_debug(handle: int, batch: sarathi_batch, ws: int, ws_bytes: int, stream: int,

@@ -152,6 +152,12 @@ hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const Chunk
                              const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
                              int dec_rows, hipStream_t s);
 
+// Device address of the current device's copy of the library's fixed scratch (kNoAllocScratchBytes,
+// 256-byte aligned), the workspace of the no-allocation forward.  Looked up once per device (the
+// device must be the current one then) and cached; later calls return the cached address.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(int device, void **out);
+
 // Zero-fill rows [row0, row1) of a [*, cols] storage matrix (row stride ld).
 hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int row1, hipStream_t s);
 

@@ -813,6 +813,10 @@ sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarath
       return fail(SARATHI_ERR_HIP, "copying the RoPE table failed: %s", hipGetErrorString(e));
     }
   }
+  // Set-up of the no-allocation forward: find this device's copy of the fixed scratch now, with the
+  // device current.  A failure here only matters to that entry point, which looks it up again.
+  void *scratch = nullptr;
+  (void)noalloc_scratch(L->device, &scratch);
   *out = L;
   return SARATHI_OK;
 }
@@ -835,6 +839,28 @@ size_t sarathi_workspace_size(const sarathi_layer_desc *desc, const sarathi_batc
 sarathi_status sarathi_layer_forward(sarathi_layer *layer, const sarathi_batch *batch,
                                      void *workspace, size_t ws_bytes, void *stream) {
   return forward_entry(layer, batch, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+sarathi_status sarathi_layer_forward_noalloc(sarathi_layer *layer, const sarathi_batch *batch,
+                                             void *stream) {
+  if (!layer) return fail(SARATHI_ERR_INVALID, "layer is null");
+  BatchView v;
+  const sarathi_status st = checked_view(&layer->desc, batch, true, &v);
+  if (st != SARATHI_OK) return st;
+  const size_t need = make_plan(&layer->desc, v).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(SARATHI_ERR_WORKSPACE,
+                "batch needs %zu bytes of workspace, more than the %zu-byte fixed scratch of the "
+                "no-allocation forward (use sarathi_layer_forward with a workspace)",
+                need, kNoAllocScratchBytes);
+  int device = -1;
+  HIP_TRY(hipGetDevice(&device));
+  if (device != layer->device)
+    return fail(SARATHI_ERR_INVALID, "current device %d is not the layer's device %d", device,
+                layer->device);
+  void *scratch = nullptr;
+  HIP_TRY(noalloc_scratch(device, &scratch));
+  return forward_impl(layer, v, scratch, kNoAllocScratchBytes, stream, nullptr, nullptr);
 }
 
 sarathi_status sarathi_layer_forward_debug(sarathi_layer *layer, const sarathi_batch *batch,

@@ -147,6 +147,21 @@ size_t sarathi_workspace_size(const sarathi_layer_desc *desc, const sarathi_batc
 sarathi_status sarathi_layer_forward(sarathi_layer *layer, const sarathi_batch *batch,
                                      void *workspace, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): sarathi_layer_forward without a workspace argument.  It
+ * runs the same kernels on a fixed scratch of 128 MiB (134217728 bytes) that the library holds in
+ * device memory on every GPU it runs on until the process ends; it calls no allocating routine.
+ * Batches whose sarathi_workspace_size exceeds 128 MiB are rejected with WORKSPACE before any
+ * launch (with the llama-13b shape, a 512-row chunk plus 48 decodes of 1K context needs 119 MiB and
+ * fits; a 512-row chunk at offset 7680 plus 48 decodes of 2K-8K context needs 176 MiB and does not:
+ * use sarathi_layer_forward with a workspace there).  The scratch keeps the last call's contents;
+ * no kernel needs it cleared.  Every call on one GPU uses that GPU's one scratch, so calls that
+ * overlap on the same GPU (other streams, other threads, other layers) race: serialise them.  The
+ * current device must be the layer's.  Errors (all before any launch): everything
+ * sarathi_batch_check reports, WORKSPACE, INVALID (wrong device), HIP. */
+sarathi_status sarathi_layer_forward_noalloc(sarathi_layer *layer, const sarathi_batch *batch,
+                                             void *stream);
+
 /* As sarathi_layer_forward, then also copies the intermediates named in *dump (float32 device
  * buffers of C+B rows) on the same stream.  dump may be NULL. */
 sarathi_status sarathi_layer_forward_debug(sarathi_layer *layer, const sarathi_batch *batch,
