@@ -7,24 +7,24 @@ namespace {
 
 template <int D, bool kPaged, int RB>
 __global__ __launch_bounds__(256) void attn_chunk_mfma(const bf16_t *q, int ld_q, int nh,
-                                                       ChunkSet cs, PagePool pool, bf16_t *out, int ld_out,
+                                                       ChunkSet cs, PagePool pool, bf16_t *out, OutLayout olay,
                                                        float qscale_log2, int n_split, int stride,
                                                        float *part_o, float *part_ml, int per_xcd) {
   SARATHI_CHUNK_LDS(D);
-  chunk_attn_item<D, kPaged, RB>(chunk_item_of(blockIdx.x, per_xcd), q, ld_q, nh, cs, pool, out, ld_out,
+  chunk_attn_item<D, kPaged, RB>(chunk_item_of(blockIdx.x, per_xcd), q, ld_q, nh, cs, pool, out, olay,
                                  qscale_log2, n_split, stride, part_o, part_ml, k0s, v0s, k1s, v1s, k2s,
                                  v2s);
 }
 
 template <int D, bool kPaged, int RB>
 hipError_t run_chunk(const void *q, int ld_q, int nh, const ChunkSet &cs, const PagePool &pool, void *out,
-                     int ld_out, int n_split, int stride, float *part_o, float *part_ml, hipStream_t s) {
+                     OutLayout olay, int n_split, int stride, float *part_o, float *part_ml, hipStream_t s) {
   int items = 0;
   for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh, kBQ * RB);
   const int per_xcd = (items + 7) / 8;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((attn_chunk_mfma<D, kPaged, RB>), dim3(8 * per_xcd), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out), ld_out,
+                     static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out), olay,
                      qscale, n_split, stride, part_o, part_ml, per_xcd);
   return hipGetLastError();
 }
@@ -105,7 +105,7 @@ int chunk_attn_plan(ChunkSet &cs, int nh, bool paged) {
 }
 
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
-                             const PagePool &pool, void *out, int ld_out, int n_split, int stride,
+                             const PagePool &pool, void *out, OutLayout olay, int n_split, int stride,
                              float *part_o, float *part_ml, hipStream_t s) {
   if (cs.n <= 0 || cs.rows <= 0) return hipSuccess;
   if (cs.n > kMaxChunks) return hipErrorInvalidValue;
@@ -116,7 +116,7 @@ hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const Chunk
   // two 16-query blocks per wave: contiguous caches only
   if (cs.qblocks != 1 && !(cs.qblocks == 2 && !pool.k)) return hipErrorInvalidValue;
 #define SARATHI_RUN_CHUNK(D, P, RB) \
-  run_chunk<D, P, RB>(q, ld_q, nh, cs, pool, out, ld_out, n_split, stride, part_o, part_ml, s)
+  run_chunk<D, P, RB>(q, ld_q, nh, cs, pool, out, olay, n_split, stride, part_o, part_ml, s)
   if (d == 128)
     return pool.k ? SARATHI_RUN_CHUNK(128, true, 1)
                   : cs.qblocks == 2 ? SARATHI_RUN_CHUNK(128, false, 2) : SARATHI_RUN_CHUNK(128, false, 1);

@@ -90,7 +90,7 @@ __host__ __device__ inline int chunk_items(int len, int n_split, int nh, int bq)
 template <int D, bool kPaged, int RB>
 __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int ld_q, int nh,
                                                 const ChunkSet &cs, const PagePool &pool, bf16_t *out,
-                                                int ld_out, float qscale_log2, int n_split, int stride,
+                                                OutLayout olay, float qscale_log2, int n_split, int stride,
                                                 float *part_o, float *part_ml, bf16_t *k0s, bf16_t *v0s,
                                                 bf16_t *k1s, bf16_t *v1s, bf16_t *k2s, bf16_t *v2s) {
   using G = TileGeom<D>;
@@ -340,13 +340,13 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
       }
     } else if (qr < C) {
       const float inv = 1.0f / l;
-      bf16_t *orow = out + (size_t)(row0 + qr) * ld_out + h * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         uint2 u;
         u.x = (uint32_t)f32_to_bf16(o[rb][db][0] * inv) | ((uint32_t)f32_to_bf16(o[rb][db][1] * inv) << 16);
         u.y = (uint32_t)f32_to_bf16(o[rb][db][2] * inv) | ((uint32_t)f32_to_bf16(o[rb][db][3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(&orow[db * 16 + g * 4]) = u;
+        // 4 consecutive columns, within one k-tile of a k-tile-major output
+        *reinterpret_cast<uint2 *>(&out[out_index(olay, row0 + qr, h * D + db * 16 + g * 4)]) = u;
       }
     }
   }

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
 // of attention of a hybrid batch overlap instead of running one after the other.
 template <int D, bool kPaged>
 __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int nh, ChunkSet cs,
-                                                  PagePool pool, bf16_t *out, int ld_out,
+                                                  PagePool pool, bf16_t *out, OutLayout olay,
                                                   float chunk_qscale, int n_split, AttnParts parts,
                                                   int per_xcd, int chunk_grid, DecodeGroup dg,
                                                   int dec_row0, int dec_rows, float dec_qscale) {
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int
   __shared__ float sm[4], sl[4], so[4 * D];
   const int b = blockIdx.x;
   if (b < chunk_grid) {
-    chunk_attn_item<D, kPaged, 1>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, ld_out,
+    chunk_attn_item<D, kPaged, 1>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, olay,
                                chunk_qscale, n_split, parts.stride_c, parts.o_c, parts.ml_c, k0s, v0s,
                                k1s, v1s, k2s, v2s);
   } else {
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int
 
 template <int D, bool kPaged>
 hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const PagePool &pool, void *out,
-                     int ld_out, int n_split, const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
+                     OutLayout olay, int n_split, const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
                      int dec_rows, hipStream_t s) {
   int items = 0;
   for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh, kBQ);
@@ -226,7 +226,7 @@ hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const 
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((attn_fused<D, kPaged>), dim3(grid), dim3(256), 0, s,
                      static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out),
-                     ld_out, qscale, n_split, parts, per_xcd, chunk_grid, dg, dec_row0, dec_rows,
+                     olay, qscale, n_split, parts, per_xcd, chunk_grid, dg, dec_row0, dec_rows,
                      qscale);
   return hipGetLastError();
 }
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
                                                                    int chunk_rows, int chunk_splits,
                                                                    ChunkSplits table,
                                                                    AttnParts parts, T *out,
-                                                                   int ld_out) {
+                                                                   OutLayout olay) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);   // (row, head) index
   if (pair >= n_rows * nh) return;
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
   const float inv = 1.0f / L;
 #pragma unroll
   for (int i = 0; i < PER; ++i)
-    out[(size_t)r * ld_out + h * D + lane + i * kWave] = from_f32<T>(acc[i] * inv);
+    out[out_index(olay, r, h * D + lane + i * kWave)] = from_f32<T>(acc[i] * inv);
 }
 
 template <typename T, int D>
@@ -356,12 +356,12 @@ hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, cons
 
 template <typename T, int D>
 hipError_t run_combine(int nh, int row0, int n_rows, int chunk_rows, int chunk_splits,
-                       const ChunkSplits &table, const AttnParts &parts, void *out, int ld_out,
+                       const ChunkSplits &table, const AttnParts &parts, void *out, OutLayout olay,
                        hipStream_t s) {
   const int pairs = n_rows * nh;
   hipLaunchKernelGGL((attn_combine<T, D>), dim3((pairs + kCombineWaves - 1) / kCombineWaves),
                      dim3(64 * kCombineWaves), 0, s, nh, row0, n_rows, chunk_rows, chunk_splits,
-                     table, parts, static_cast<T *>(out), ld_out);
+                     table, parts, static_cast<T *>(out), olay);
   return hipGetLastError();
 }
 
@@ -384,7 +384,7 @@ hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, in
 
 hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int chunk_rows,
                                int chunk_splits, const ChunkSplits &table, const AttnParts &parts,
-                               void *out, int ld_out, hipStream_t s) {
+                               void *out, OutLayout olay, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
   if (row0 + n_rows > chunk_rows &&
       (parts.stride_d < 1 || parts.stride_d > kMaxKeySplits || !parts.o_d || !parts.ml_d))
@@ -400,7 +400,7 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
     }
   }
 #define SARATHI_COMBINE(T, D) \
-  return run_combine<T, D>(nh, row0, n_rows, chunk_rows, chunk_splits, table, parts, out, ld_out, s)
+  return run_combine<T, D>(nh, row0, n_rows, chunk_rows, chunk_splits, table, parts, out, olay, s)
   if (type == kF32 && d == 64) SARATHI_COMBINE(float, 64);
   if (type == kF32 && d == 128) SARATHI_COMBINE(float, 128);
   if (type == kBF16 && d == 64) SARATHI_COMBINE(bf16_t, 64);
@@ -410,7 +410,7 @@ hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, in
 }
 
 hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
-                             const PagePool &pool, void *out, int ld_out, int n_split,
+                             const PagePool &pool, void *out, OutLayout olay, int n_split,
                              const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
                              int dec_rows, hipStream_t s) {
   if (cs.n <= 0 || cs.n > kMaxChunks || dec_rows <= 0 || dec_rows > kMaxDecodesPerLaunch)
@@ -423,7 +423,7 @@ hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const Chunk
     if (cs.split[j] < 1 || cs.split[j] > n_split) return hipErrorInvalidValue;
   const bool paged = pool.k != 0;
 #define SARATHI_FUSED(D, P) \
-  return run_fused<D, P>(q, ld_q, nh, cs, pool, out, ld_out, n_split, parts, dg, dec_row0, dec_rows, s)
+  return run_fused<D, P>(q, ld_q, nh, cs, pool, out, olay, n_split, parts, dg, dec_row0, dec_rows, s)
   if (d == 128) {
     if (paged) SARATHI_FUSED(128, true);
     SARATHI_FUSED(128, false);

@@ -107,6 +107,22 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Element (r, c) of a [rows, cols] matrix stored row-major (kw = 0, row stride ld) or k-tile-major,
+// [cols / kw][rows_alloc][kw] with kw = 32 or 64 (the layout a GEMM with kw-deep LDS stages reads as
+// contiguous blocks).
+__host__ __device__ __forceinline__ size_t mat_index(int r, int c, int ld, int kw, int rows_alloc) {
+  return kw ? ((size_t)(c / kw) * rows_alloc + r) * kw + (c % kw) : (size_t)r * ld + c;
+}
+
+// Where a kernel writes element (r, c) of its [rows, cols] output: row-major with row stride ld
+// (kw = 0), or k-tile-major over rows_alloc rows (kw = 32 or 64), as mat_index.
+struct OutLayout {
+  int ld, kw, rows_alloc;
+};
+__host__ __device__ __forceinline__ size_t out_index(const OutLayout &o, int r, int c) {
+  return mat_index(r, c, o.ld, o.kw, o.rows_alloc);
+}
+
 // Butterfly reductions over the lanes whose index differs only in the bits of [lo_mask, 32].
 __device__ __forceinline__ float wave_sum(float v, int from = 1) {
 #pragma unroll

@@ -7,12 +7,12 @@
 // is padded only to 32 rows; rows past C+B are never stored (the tile-quantization point of the same
 // page, "Identifying the Ideal Chunk Size", Figure 7, restated for 16-row MFMA blocks).
 //
-// bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 288; larger batches
+// bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 576; larger batches
 // take a few row tiles) and a 128-column stripe of the weights, so a weight tile is read once for
-// the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 144 rows x 32 columns.  A and W
-// k-tiles (64 deep) travel from global memory straight into LDS (global_load_lds_dwordx4: no
-// staging registers, no LDS store instructions) through a ring of up to 3 stages, so the loads of
-// tile j + 2 are in flight while tile j is multiplied.  The loads are what bounds this kernel at
+// the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 288 rows x 32 columns.  A and W
+// k-tiles (64 deep for tiles of up to 288 rows, 32 deep above) travel from global memory straight
+// into LDS (global_load_lds_dwordx4: no staging registers, no LDS store instructions) through a ring
+// of up to 3 stages, so the loads of tile j + 2 are in flight while tile j is multiplied.  The loads are what bounds this kernel at
 // small batches: a compute unit keeps only ~10 KB of reads in flight, so its fetch rate is set by
 // memory latency, and the A tile is fetched by every workgroup.  When the weight stripes alone do
 // not fill the 256 compute units, the k range is split: each split writes a float32 partial and the
@@ -26,26 +26,44 @@
 namespace sarathi {
 namespace {
 
-constexpr int kBK = 64;         // k extent of one LDS stage (bf16 elements): two MFMA k-steps
-constexpr int kLdsK = kBK;      // LDS row: 128 bytes = 8 chunks of 16 bytes, stored swizzled
-constexpr int kChunks = kBK / 8;
-// Chunk c of LDS row r is stored in slot c ^ ((r >> 1) & 7).  A fragment read takes one chunk of 16
-// consecutive rows; those land in 16 distinct 4-bank groups, so fragment reads have no bank conflicts.
-__device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// Stage depth.  A workgroup tile of up to 288 rows takes 64-deep k-tiles (an LDS row of 128 bytes =
+// 8 chunks of 16 bytes, two MFMA k-steps per stage).  Taller tiles (up to 576 rows, so batches of up
+// to 576 rows stream each weight stripe once) take 32-deep k-tiles (64-byte LDS rows, one k-step per
+// stage): three stages of 576 + 128 rows then still fit in LDS.
+template <int BK> struct KGeom {
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static constexpr int kChunks = BK / 8;          // 16-byte chunks per LDS row
+  static constexpr int kRPL = 1024 / (BK * 2);    // LDS rows per 1 KiB load
+  static constexpr int kSteps = BK / 32;          // MFMA k-steps per stage
+};
+// Chunk c of LDS row r is stored in slot c ^ f(r).  A fragment read takes one chunk of 16 consecutive
+// rows (rows 16q .. 16q + 15).  f = (r >> 1) & 7 with 128-byte rows and f = (r >> 1) & 3 with 64-byte
+// rows make those reads free of bank conflicts (both measured with the LDS bank-conflict counter on
+// this access pattern; with 64-byte rows, f = (r >> 2) & 3, r & 3, (r >> 3) & 3 or no swizzle give
+// four conflict cycles per read).
+template <int BK> __device__ __forceinline__ int swz_slot(int row, int chunk) {
+  return BK == 64 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 1) & 3);
+}
 constexpr int kMaxStages = 3;
 constexpr int kPlanWaveCols = 4;   // wave columns of a workgroup (8 waves: 2 rows x 4 columns)
 constexpr int kWM = 2;             // wave rows of a workgroup
 constexpr int kWaves = kWM * kPlanWaveCols;
-// Max 16-row blocks per wave row: 288 rows per tile.  A 320-row tile would leave room for only two
-// LDS stages, which measured as slow as two 160-row tiles (and slower than three 200-row tiles at
-// 577..640 rows), so batches past 288 rows take several row tiles.
-constexpr int kMBW = 9;
+// 16-row blocks per wave row: up to 9 (288-row tiles) with 64-deep stages, up to 18 (576-row tiles)
+// with 32-deep stages.  A 320-row tile with 64-deep stages would leave room for only two stages (it
+// measured as slow as two 160-row tiles).
+constexpr int kMBW64 = 9;
+constexpr int kMBW = 18;
 #ifndef SARATHI_GEMM_BN
 #define SARATHI_GEMM_BN 128
 #endif
 constexpr int kBN = SARATHI_GEMM_BN;   // columns per tile (weight rows per stripe)
 constexpr int kBMX = 16 * kMBW * kWM;
 constexpr int kLdsBudget = 160 * 1024;
+// Split-K boundaries lie on multiples of 64 k whatever a tile's stage depth, so a row's k-sum is cut
+// at the same points in a 288-row tile and in a 576-row one.
+constexpr int kSplitK = 64;
+
+__host__ __device__ constexpr int stage_depth(int mb) { return mb > kMBW64 ? 32 : 64; }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 // SiLU for the bf16 epilogue: z / (1 + 2^(-z log2 e)) with the hardware exponential and reciprocal,
@@ -62,18 +80,19 @@ __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erf
 // weight rows kBN / kRPL, dealt round-robin to the 8 waves.  As many stages as fit in LDS (up to
 // kMaxStages) are kept in flight: the loads of a tile are issued that many steps before its use,
 // which is what hides the memory latency.
-constexpr int kRPL = 1024 / (kBK * 2);   // LDS rows per load
 template <int MB> struct StageGeom {
+  static constexpr int kBK = stage_depth(MB);
+  using K = KGeom<kBK>;
   static constexpr int kRowsA = 32 * MB;
-  static constexpr int kElems = (kRowsA + kBN) * kLdsK;
+  static constexpr int kElems = (kRowsA + kBN) * kBK;
   static constexpr int kFit = kLdsBudget / (kElems * 2);
   static constexpr int kStages = kFit < kMaxStages ? kFit : kMaxStages;
   static_assert(kStages >= 2, "two stages fit in LDS");
-  static constexpr int kLoadsA = kRowsA / kRPL;
+  static constexpr int kLoadsA = kRowsA / K::kRPL;
   static constexpr int kAI = (kLoadsA + kWaves - 1) / kWaves;   // A loads per wave (some repeated)
-  static constexpr int kBI = kBN / kRPL / kWaves;               // weight loads per wave
-  static_assert(kRowsA % kRPL == 0, "whole loads of A rows");
-  static_assert(kBN % (kRPL * kWaves) == 0, "weight rows split evenly over the waves");
+  static constexpr int kBI = kBN / K::kRPL / kWaves;            // weight loads per wave
+  static_assert(kRowsA % K::kRPL == 0, "whole loads of A rows");
+  static_assert(kBN % (K::kRPL * kWaves) == 0, "weight rows split evenly over the waves");
   static_assert((kStages - 2) * (kAI + kBI) < 64, "loads in flight fit the wait counter");
 };
 
@@ -82,6 +101,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
 void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   static_assert(MB >= 1 && MB <= kMBW, "16-row blocks per wave row");
   using G = StageGeom<MB>;
+  constexpr int BK = G::kBK;
+  using K = KGeom<BK>;
   constexpr int WN = kPlanWaveCols;
   constexpr int kNB = kBN / (16 * WN);  // 16-column blocks per wave
   constexpr bool kGlu = EPI == kEpiSwiGLU;
@@ -91,13 +112,8 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   __shared__ __attribute__((aligned(1024))) bf16_t st0[G::kElems];
   __shared__ __attribute__((aligned(1024))) bf16_t st1[G::kElems];
   __shared__ __attribute__((aligned(1024))) bf16_t st2[kNSt > 2 ? G::kElems : 8];
-  __shared__ __attribute__((aligned(1024))) bf16_t st3[kNSt > 3 ? G::kElems : 8];
-  __shared__ __attribute__((aligned(1024))) bf16_t st4[kNSt > 4 ? G::kElems : 8];
-  __shared__ __attribute__((aligned(1024))) bf16_t st5[kNSt > 5 ? G::kElems : 8];
-  static_assert(kNSt <= 6, "stage arrays");
-  auto stage = [&](int u) -> bf16_t * {
-    return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : u == 3 ? st3 : u == 4 ? st4 : st5;
-  };
+  static_assert(kNSt <= 3, "stage arrays");
+  auto stage = [&](int u) -> bf16_t * { return u == 0 ? st0 : u == 1 ? st1 : st2; };
 
   // Tile of this workgroup (XCD-aware order: slot s of XCD x takes tile x * per_xcd + s).
   const int bid = blockIdx.x;
@@ -109,9 +125,9 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   const int n_tile = rest / p.splits;
   const int m0 = m_tile * G::kRowsA;
   const int n0 = n_tile * (kGlu ? kBN / 2 : kBN);
-  const int nk = g.k / kBK;
-  const int kb = (int)((long long)split * nk / p.splits);
-  const int ke = (int)((long long)(split + 1) * nk / p.splits);
+  const int nk = g.k / kSplitK;
+  const int kb = (int)((long long)split * nk / p.splits) * (kSplitK / BK);   // in BK-deep k-tiles
+  const int ke = (int)((long long)(split + 1) * nk / p.splits) * (kSplitK / BK);
   const int ntiles = ke - kb;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -127,22 +143,22 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   // then the same immediate for all waves): a wave whose round-robin share of A loads is one short
   // repeats the last A load, writing the same bytes to the same rows.  Rows are clamped into the
   // matrices: rows past the batch fill LDS rows whose products are never stored.
-  const int lrow = lane / kChunks, lslot = lane % kChunks;
+  const int lrow = lane / K::kChunks, lslot = lane % K::kChunks;
   const bf16_t *a_src[G::kAI];
   int a_lds[G::kAI];
 #pragma unroll
   for (int i = 0; i < G::kAI; ++i) {
     const int q = min(wave + kWaves * i, G::kLoadsA - 1);
-    const int row = kRPL * q + lrow;
+    const int row = K::kRPL * q + lrow;
     const int gr = min(m0 + row, g.m_alloc - 1);
-    const size_t a_row = g.a_kmajor ? ((size_t)kb * g.m_alloc + gr) * kBK : (size_t)gr * g.lda + (size_t)kb * kBK;
-    a_src[i] = A + a_row + swz_slot(row, lslot) * 8;
-    a_lds[i] = kRPL * q * kLdsK;
+    const size_t a_row = g.a_kmajor ? ((size_t)kb * g.m_alloc + gr) * BK : (size_t)gr * g.lda + (size_t)kb * BK;
+    a_src[i] = A + a_row + swz_slot<BK>(row, lslot) * 8;
+    a_lds[i] = K::kRPL * q * BK;
   }
   const bf16_t *b_src[G::kBI];
 #pragma unroll
   for (int i = 0; i < G::kBI; ++i) {
-    const int row = kRPL * (wave + kWaves * i) + lrow;   // weight row within the stripe's LDS block
+    const int row = K::kRPL * (wave + kWaves * i) + lrow;   // weight row within the stripe's LDS block
     int src_row;
     const bf16_t *Wp = W0;
     if (kGlu) {
@@ -159,21 +175,21 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
       }
     }
     // kRowsA is a multiple of 16, so the weight block's rows swizzle like rows 0..kBN-1
-    b_src[i] = Wp + (size_t)src_row * g.ldw + (size_t)kb * kBK + swz_slot(row, lslot) * 8;
+    b_src[i] = Wp + (size_t)src_row * g.ldw + (size_t)kb * BK + swz_slot<BK>(row, lslot) * 8;
   }
 
   // Loads of k-tile j (clamped to the last tile, so every wave issues the same loads every step)
-  // into LDS stage `st`.  A k-tile of a k-tile-major A lies m_alloc * 64 elements after the previous.
-  const int a_kstep = g.a_kmajor ? g.m_alloc * kBK : kBK;
+  // into LDS stage `st`.  A k-tile of a k-tile-major A lies m_alloc * BK elements after the previous.
+  const int a_kstep = g.a_kmajor ? g.m_alloc * BK : BK;
   auto issue = [&](bf16_t *st, int j) {
-    const int kofs = min(j, ntiles - 1) * kBK;
+    const int kofs = min(j, ntiles - 1) * BK;
     const int a_kofs = min(j, ntiles - 1) * a_kstep;
 #pragma unroll
     for (int i = 0; i < G::kAI; ++i) dma16(a_src[i] + a_kofs, st + a_lds[i]);
 #pragma unroll
     for (int i = 0; i < G::kBI; ++i) {
       const int q = wave + kWaves * i;
-      dma16(b_src[i] + kofs, st + (G::kRowsA + kRPL * q) * kLdsK);
+      dma16(b_src[i] + kofs, st + (G::kRowsA + K::kRPL * q) * BK);
     }
   };
 
@@ -184,28 +200,29 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
     for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Fragment rows start at multiples of 16, so a lane's swizzle term depends on lane & 15 only.
-  // Both k-steps' fragments of a tile are read before its MFMAs, so the MFMAs of k-step 0 run while
-  // the reads of k-step 1 are in flight.
+  // Both k-steps' fragments of a 64-deep tile are read before its MFMAs, so the MFMAs of k-step 0
+  // run while the reads of k-step 1 are in flight; a 32-deep tile of a tall workgroup tile (one
+  // k-step, up to 18 A fragments per wave) leaves the read order to the compiler's scheduler.
   const int frag_row = lane & 15;
-  const int frag_k0 = swz_slot(frag_row, (lane >> 4) + 0) * 8;   // k-step 0: chunks 0..3
-  const int frag_k1 = swz_slot(frag_row, (lane >> 4) + 4) * 8;   // k-step 1: chunks 4..7
+  int frag_k[K::kSteps];
+#pragma unroll
+  for (int ks = 0; ks < K::kSteps; ++ks) frag_k[ks] = swz_slot<BK>(frag_row, (lane >> 4) + 4 * ks) * 8;
   const int a_row0 = wm * 16 * MB;
   auto compute = [&](const bf16_t *L) {
-    bf16x8_t fa[2][MB], fb[2][kNB];
+    bf16x8_t fa[K::kSteps][MB], fb[K::kSteps][kNB];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int fk = ks == 0 ? frag_k0 : frag_k1;
+    for (int ks = 0; ks < K::kSteps; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
         fb[ks][nb] = *reinterpret_cast<const bf16x8_t *>(
-            &L[(G::kRowsA + wn * 16 * kNB + nb * 16 + frag_row) * kLdsK + fk]);
+            &L[(G::kRowsA + wn * 16 * kNB + nb * 16 + frag_row) * BK + frag_k[ks]]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        fa[ks][mb] = *reinterpret_cast<const bf16x8_t *>(&L[(a_row0 + mb * 16 + frag_row) * kLdsK + fk]);
+        fa[ks][mb] = *reinterpret_cast<const bf16x8_t *>(&L[(a_row0 + mb * 16 + frag_row) * BK + frag_k[ks]]);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (K::kSteps > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < K::kSteps; ++ks)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -252,7 +269,8 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
           const int n = n0 + (wn * (kNB / 2) + nb) * 16 + (lane & 15);
           if (n >= g.n) continue;
           const float gt = acc[mb][nb][i], up = acc[mb][nb + kNB / 2][i];
-          static_cast<bf16_t *>(g.out)[(size_t)m * g.ldo + n] = f32_to_bf16(silu_bf16_epilogue(gt) * up);
+          static_cast<bf16_t *>(g.out)[mat_index(m, n, g.ldo, g.out_kmajor, g.m_alloc)] =
+              f32_to_bf16(silu_bf16_epilogue(gt) * up);
         } else {
           const int n = n0 + wn * 16 * kNB + nb * 16 + (lane & 15);
           if (n >= g.n) continue;
@@ -262,7 +280,8 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
           } else if (EPI == kEpiStore) {
             static_cast<bf16_t *>(g.out)[(size_t)m * g.ldo + n] = f32_to_bf16(v);
           } else {  // kEpiGelu
-            static_cast<bf16_t *>(g.out)[(size_t)m * g.ldo + n] = f32_to_bf16(gelu_f(v));
+            static_cast<bf16_t *>(g.out)[mat_index(m, n, g.ldo, g.out_kmajor, g.m_alloc)] =
+                f32_to_bf16(gelu_f(v));
           }
         }
       }
@@ -353,6 +372,15 @@ hipError_t run_bf16(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
     case 7: return run_bf16_mb<7, EPI>(g, p, s);
     case 8: return run_bf16_mb<8, EPI>(g, p, s);
     case 9: return run_bf16_mb<9, EPI>(g, p, s);
+    case 10: return run_bf16_mb<10, EPI>(g, p, s);
+    case 11: return run_bf16_mb<11, EPI>(g, p, s);
+    case 12: return run_bf16_mb<12, EPI>(g, p, s);
+    case 13: return run_bf16_mb<13, EPI>(g, p, s);
+    case 14: return run_bf16_mb<14, EPI>(g, p, s);
+    case 15: return run_bf16_mb<15, EPI>(g, p, s);
+    case 16: return run_bf16_mb<16, EPI>(g, p, s);
+    case 17: return run_bf16_mb<17, EPI>(g, p, s);
+    case 18: return run_bf16_mb<18, EPI>(g, p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -376,18 +404,15 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
     p.grid = p.m_tiles * p.n_tiles;
     return p;
   }
-  p.m_tiles = (m + kBMX - 1) / kBMX;
-  const int rows = (m + p.m_tiles - 1) / p.m_tiles;
-  p.mbw = (rows + 31) / 32;
   p.wn = kPlanWaveCols;
-  const int nk = k / kBK;
+  const int nk = k / kSplitK;
   // The split count and the epilogue form depend on the weight shape only, never on the number of
   // batch rows: a row's k-sum is then cut at the same points whatever else is in the batch, so a
   // decode run alone and the same decode inside a hybrid batch give bitwise-equal results.
   // Time model for one 256-row tile: whole rounds of `cus` workgroups, each k-tile at ~half of a
   // CU's MFMA rate, plus the float32 partials written and read back at ~5 TB/s.
   const double m_ref = 256.0;
-  const double t_k = 2.0 * m_ref * kBN * kBK / 5.0e12;
+  const double t_k = 2.0 * m_ref * kBN * kSplitK / 5.0e12;
   auto est = [&](int tiles, int sp, double part_cols) {
     const int rounds = (tiles * sp + cus - 1) / cus;
     return rounds * (double)((nk + sp - 1) / sp) * t_k + (double)sp * m_ref * part_cols * 8.0 / 5.0e12;
@@ -424,15 +449,50 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
       p.splits = 1;
     }
   }
+  // Row tiles: as few 576-row tiles (32-deep stages) as hold the batch, or 288-row ones (64-deep
+  // stages), whichever gives the shorter estimate of whole rounds of `cus` workgroups times one
+  // workgroup's time.  A workgroup's time grows with its rows from its weight stream (about 0.55 of
+  // a 288-row workgroup, measured at 1 row) up to 1.0 at 288 rows (64-deep) and 1.6 at 576 rows
+  // (32-deep), measured on the llama-13b gate/up product.  The rows of a batch never change its
+  // split count, so either choice gives a row the same k-sum.
+  auto wg_time = [](int rows) {
+    return stage_depth((rows + 31) / 32) == 64 ? 0.55 + 0.45 * rows / 288.0 : 0.55 + 0.525 * rows / 288.0;
+  };
+  auto plan_rows = [&](int tile_rows, int *m_tiles, int *mbw) {
+    *m_tiles = (m + tile_rows - 1) / tile_rows;
+    const int rows = (m + *m_tiles - 1) / *m_tiles;
+    *mbw = (rows + 31) / 32;
+    const int wgs = *m_tiles * p.n_tiles * p.splits;
+    return (double)((wgs + cus - 1) / cus) * wg_time(rows);
+  };
+  int mt_tall, mb_tall, mt_short, mb_short;
+  const double t_tall = plan_rows(kBMX, &mt_tall, &mb_tall);
+  const double t_short = plan_rows(16 * kMBW64 * kWM, &mt_short, &mb_short);
+  if (t_tall <= t_short) {
+    p.m_tiles = mt_tall;
+    p.mbw = mb_tall;
+  } else {
+    p.m_tiles = mt_short;
+    p.mbw = mb_short;
+  }
   const int total = p.m_tiles * p.n_tiles * p.splits;
   p.per_xcd = (total + 7) / 8;
   p.grid = 8 * p.per_xcd;
   return p;
 }
 
+int gemm_stage_depth(const GemmPlan &p) { return stage_depth(p.mbw); }
+
 hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  // k-tile-major A: bf16 only, and its whole extent must be addressable with 32-bit offsets
-  if (g.a_kmajor && (type == kF32 || (long long)g.m_alloc * g.k >= (1ll << 31))) return hipErrorInvalidValue;
+  // k-tile-major A: bf16 only, tiles as wide as the plan's stage depth, and its whole extent
+  // addressable with 32-bit offsets
+  if (g.a_kmajor && (type == kF32 || g.a_kmajor != stage_depth(p.mbw) ||
+                     (long long)g.m_alloc * g.k >= (1ll << 31)))
+    return hipErrorInvalidValue;
+  if (type == kBF16 && (g.k % kSplitK || p.mbw < 1 || p.mbw > kMBW)) return hipErrorInvalidValue;
+  if (g.out_kmajor && (type == kF32 || (epi != kEpiSwiGLU && epi != kEpiGelu) ||
+                       (g.out_kmajor != 32 && g.out_kmajor != 64) || g.n % g.out_kmajor))
+    return hipErrorInvalidValue;
   if (type == kF32) {
     switch (epi) {
       case kEpiStore: return run_f32<kEpiStore>(g, s);

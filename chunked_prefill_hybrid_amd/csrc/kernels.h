@@ -15,19 +15,21 @@ enum StorageType { kF32 = 0, kBF16 = 1 };
 // Row norms.  v[r] = resid[r] + sum_{s < splits} part[s][r]  (resid in `res_type` storage, the
 // split partials of a GEMM in float32 with slice stride rows*H; splits may be 0).  If sum_out is
 // non-null it receives v (float32).  out[r] = RMSNorm(v) * g  or  LayerNorm(v) * g + b for r < rows;
-// rows rows..rows_alloc-1 of out are zero-filled.  out is row-major [rows_alloc, H], or with
-// kmajor k-tile-major [H/64][rows_alloc][64] (the layout the bf16 GEMM reads fastest; H % 64 == 0).
+// rows rows..rows_alloc-1 of out are zero-filled.  out is row-major [rows_alloc, H] (kmajor = 0), or
+// k-tile-major [H/w][rows_alloc][w] with w = kmajor, 32 or 64 (the layout the bf16 GEMM reads
+// fastest: w = its stage depth; H % 64 == 0).
 constexpr int kMaxHidden = 16384;   // widest row a norm workgroup holds (1024 threads x 16 elements)
 hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
                             const float *part, int splits, float *sum_out, const float *g,
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                            bool kmajor, hipStream_t s);
+                            int kmajor, hipStream_t s);
 
 // FFN activation from split partials ([splits][rows][n_part] float32): gated (n_part = 2F):
 // out[r, j] = silu(sum_s part[s][r][j]) * sum_s part[s][r][F + j];  else (n_part = F):
-// out[r, j] = gelu(sum_s part[s][r][j]).  out is storage type [rows, F].
+// out[r, j] = gelu(sum_s part[s][r][j]).  out is storage type [rows, F] row-major (kmajor = 0), or
+// k-tile-major [F/w][rows_alloc][w] with w = kmajor (32 or 64, F % w == 0).
 hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int splits, void *out,
-                          int rows, int F, hipStream_t s);
+                          int rows, int F, int kmajor, int rows_alloc, hipStream_t s);
 
 // out[r, c] = resid[r, c] + sum_{s < splits} part[s][r][c]  (resid float32, out storage type).
 hipError_t launch_resid_sum(int out_type, const float *resid, const float *part, int splits,
@@ -47,7 +49,8 @@ struct GemmArgs {
   const void *w0;     // [n, k] row stride ldw (rows 0..n_w0-1 when w1 continues it)
   const void *w1;     // SwiGLU: the up weight.  kEpiPartial: rows n_w0..n-1 of the product's
                       // weight (the up half of a gate|up product), else null
-  void *out;          // row stride ldo (kEpiStore / kEpiSwiGLU / kEpiGelu)
+  void *out;          // row stride ldo (kEpiStore / kEpiSwiGLU / kEpiGelu); with out_kmajor = w
+                      // (32 or 64; kEpiSwiGLU / kEpiGelu only) k-tile-major [n/w][m_alloc][w]
   float *part;        // [splits][m_store][n] (kEpiPartial)
   int lda, ldw, ldo;
   int m_alloc;        // rows of a that may be read
@@ -55,8 +58,10 @@ struct GemmArgs {
   int n;              // output columns
   int k;              // multiple of 64 in bf16 mode
   int n_w0;           // kEpiPartial with w1: rows of the product taken from w0
-  int a_kmajor;       // bf16 only: a is k-tile-major, [k/64][m_alloc][64] (lda unused).  A k-tile of
-                      // 8 rows is then 1 KiB of consecutive bytes, which the LDS DMA fetches faster
+  int out_kmajor;     // 0 or the k-tile width of out (see out)
+  int a_kmajor;       // 0: a is row-major.  bf16 only, w = 32 or 64 (the plan's stage depth): a is
+                      // k-tile-major, [k/w][m_alloc][w] (lda unused).  A k-tile of 1024 / (2 w) rows
+                      // is then 1 KiB of consecutive bytes, which the LDS DMA fetches faster
 };
 
 // Launch shape of one GEMM: m_tiles x n_tiles output tiles, each k range cut into `splits`;
@@ -67,6 +72,8 @@ struct GemmPlan { int epi, m_tiles, n_tiles, splits, mbw, wn, per_xcd, grid; };
 // product plus a separate activation pass is estimated faster; n is then the product width:
 // 2F for SwiGLU).  n_out is the output width of the epilogue (F for the FFN up products).
 GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus);
+// k depth of one LDS stage of a bf16 plan (32 or 64): the k-tile width of a k-tile-major A.
+int gemm_stage_depth(const GemmPlan &p);
 hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
@@ -112,18 +119,18 @@ struct ChunkSplits {
   int32_t split[kMaxChunks];
   int32_t n;
 };
-// Merges the split partials of rows [row0, row0+n_rows) into out[row, h*d + e] (storage type,
-// row stride ld_out).  Rows at or past chunk_rows merge their stride_d partials of region d.  Rows
+// Merges the split partials of rows [row0, row0+n_rows) into out[row, h*d + e] (storage type, laid
+// out as olay says).  Rows at or past chunk_rows merge their stride_d partials of region d.  Rows
 // below it merge chunk_splits partials of region c when chunk_splits > 0; with chunk_splits == 0
 // they merge their chunk's count from `table`, and the rows of chunks with one split are left as
 // they are.
 hipError_t launch_attn_combine(int type, int d, int nh, int row0, int n_rows, int chunk_rows,
                                int chunk_splits, const ChunkSplits &table, const AttnParts &parts,
-                               void *out, int ld_out, hipStream_t s);
+                               void *out, OutLayout olay, hipStream_t s);
 
 // Flash-style causal chunk attention (bf16, MFMA) over every chunk of the set: row row0[j] + t of
-// chunk j attends to keys 0..off[j]+t of chunk j's cache.  q and out are batch-row indexed (row
-// strides ld_q, ld_out).  Chunk j's query blocks (64 queries; 128 with cs.qblocks = 2, two 16-query
+// chunk j attends to keys 0..off[j]+t of chunk j's cache.  q and out are batch-row indexed (q row
+// stride ld_q; out laid out as olay says).  Chunk j's query blocks (64 queries; 128 with cs.qblocks = 2, two 16-query
 // blocks per wave, contiguous caches only) split their key tiles cs.split[j] ways; n_split is the
 // largest of these.  A chunk with cs.split[j] > 1 writes partials (stride `stride` splits per row and
 // head) for launch_attn_combine instead of out.
@@ -139,7 +146,7 @@ constexpr int kSplitCostTiles = 3;            // makespan cost of one more split
 int chunk_attn_splits(ChunkSet &cs, int nh, int bq, int resident, long long *cost);
 int chunk_attn_plan(ChunkSet &cs, int nh, bool paged);
 hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
-                             const PagePool &pool, void *out, int ld_out, int n_split, int stride,
+                             const PagePool &pool, void *out, OutLayout olay, int n_split, int stride,
                              float *part_o, float *part_ml, hipStream_t s);
 
 // The chunk attention of every chunk of the set and the split-KV attention of decode rows
@@ -148,7 +155,7 @@ hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const Chunk
 // n_split > 1, stride_c = n_split); decode rows write split partials to region d as
 // launch_attn_rows does (stride_d, first row of the region = cs.rows).
 hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
-                             const PagePool &pool, void *out, int ld_out, int n_split,
+                             const PagePool &pool, void *out, OutLayout olay, int n_split,
                              const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
                              int dec_rows, hipStream_t s);
 
@@ -164,8 +171,8 @@ hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int r
 // Convert a [rows, cols] storage matrix (row stride ld_src) to float32 (row stride ld_dst).
 hipError_t launch_to_f32(int type, const void *src, int ld_src, float *dst, int ld_dst, int rows,
                          int cols, hipStream_t s);
-// The same from a k-tile-major [cols/64][rows_alloc][64] matrix.
-hipError_t launch_kmajor_to_f32(int type, const void *src, int rows_alloc, float *dst, int ld_dst,
-                                int rows, int cols, hipStream_t s);
+// The same from a k-tile-major [cols/w][rows_alloc][w] matrix (w = 32 or 64).
+hipError_t launch_kmajor_to_f32(int type, const void *src, int w, int rows_alloc, float *dst,
+                                int ld_dst, int rows, int cols, hipStream_t s);
 
 }  // namespace sarathi

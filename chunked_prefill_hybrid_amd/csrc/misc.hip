@@ -20,12 +20,12 @@ __global__ __launch_bounds__(256) void widen_rows(const T *src, int ld_src, floa
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void widen_kmajor_rows(const T *src, int rows_alloc, float *dst,
-                                                     int ld_dst, int cols) {
+__global__ __launch_bounds__(256) void widen_kmajor_rows(const T *src, int w, int rows_alloc,
+                                                     float *dst, int ld_dst, int cols) {
   const int r = blockIdx.x;
   float *d = dst + (size_t)r * ld_dst;
   for (int c = threadIdx.x; c < cols; c += blockDim.x)
-    d[c] = to_f32(src[((size_t)(c >> 6) * rows_alloc + r) * 64 + (c & 63)]);
+    d[c] = to_f32(src[((size_t)(c / w) * rows_alloc + r) * w + (c % w)]);
 }
 
 }  // namespace
@@ -53,16 +53,16 @@ hipError_t launch_to_f32(int type, const void *src, int ld_src, float *dst, int 
   return hipGetLastError();
 }
 
-hipError_t launch_kmajor_to_f32(int type, const void *src, int rows_alloc, float *dst, int ld_dst,
-                                int rows, int cols, hipStream_t s) {
+hipError_t launch_kmajor_to_f32(int type, const void *src, int w, int rows_alloc, float *dst,
+                                int ld_dst, int rows, int cols, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (rows > rows_alloc || cols % 64) return hipErrorInvalidValue;
+  if (rows > rows_alloc || (w != 32 && w != 64) || cols % w) return hipErrorInvalidValue;
   if (type == kF32)
     hipLaunchKernelGGL(widen_kmajor_rows<float>, dim3(rows), dim3(256), 0, s,
-                       static_cast<const float *>(src), rows_alloc, dst, ld_dst, cols);
+                       static_cast<const float *>(src), w, rows_alloc, dst, ld_dst, cols);
   else
     hipLaunchKernelGGL(widen_kmajor_rows<bf16_t>, dim3(rows), dim3(256), 0, s,
-                       static_cast<const bf16_t *>(src), rows_alloc, dst, ld_dst, cols);
+                       static_cast<const bf16_t *>(src), w, rows_alloc, dst, ld_dst, cols);
   return hipGetLastError();
 }
 

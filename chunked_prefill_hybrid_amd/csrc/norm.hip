@@ -78,12 +78,15 @@ template <typename Tres, typename Tout, bool LN>
 __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, const float *part,
                                                       int splits, float *sum_out, const float *g,
                                                       const float *b, Tout *out, int H, int rows,
-                                                      float eps, int kmajor_rows) {
+                                                      float eps, int kmajor_rows, int kmajor_shift) {
   __shared__ float red[kNormThreads / 64];
   const int r = blockIdx.x;
-  // Element c of this row: row-major, or k-tile-major (64-column tiles of kmajor_rows rows each).
+  // Element c of this row: row-major, or k-tile-major (tiles of 2^kmajor_shift columns by
+  // kmajor_rows rows each).
   auto at = [&](int c) -> Tout * {
-    return kmajor_rows ? out + ((size_t)(c >> 6) * kmajor_rows + r) * 64 + (c & 63) : out + (size_t)r * H + c;
+    return kmajor_rows ? out + (((size_t)(c >> kmajor_shift) * kmajor_rows + r) << kmajor_shift) +
+                             (c & ((1 << kmajor_shift) - 1))
+                       : out + (size_t)r * H + c;
   };
   if (r >= rows) {
     const float z[4] = {0.f, 0.f, 0.f, 0.f};
@@ -158,7 +161,7 @@ __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erf
 
 template <typename Tout, bool GATED>
 __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int splits, Tout *out,
-                                                    int rows, int F) {
+                                                    int rows, int F, int kmajor, int rows_alloc) {
   const size_t n4 = (size_t)rows * F / 4;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= n4) return;
@@ -171,21 +174,21 @@ __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int split
   float v[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = GATED ? silu_f(a[e]) * u[e] : gelu_f(a[e]);
-  store4<Tout>(out + (size_t)r * F + c, v);
+  store4<Tout>(out + mat_index(r, c, F, kmajor, rows_alloc), v);   // 4 columns within one k-tile
 }
 
 template <typename Tres, typename Tout>
 hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, float *sum_out,
                     const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
-                    float eps, int kmajor_rows, hipStream_t s) {
+                    float eps, int kmajor_rows, int kmajor_shift, hipStream_t s) {
   if (ln)
     hipLaunchKernelGGL((norm_rows<Tres, Tout, true>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
                        static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
-                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows);
+                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows, kmajor_shift);
   else
     hipLaunchKernelGGL((norm_rows<Tres, Tout, false>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
                        static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
-                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows);
+                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows, kmajor_shift);
   return hipGetLastError();
 }
 
@@ -194,30 +197,35 @@ hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, f
 hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
                             const float *part, int splits, float *sum_out, const float *g,
                             const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                            bool kmajor, hipStream_t s) {
+                            int kmajor, hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
   if (splits > kMaxSplits || H > kMaxHidden || H % 4) return hipErrorInvalidValue;
+  if (kmajor != 0 && kmajor != 32 && kmajor != 64) return hipErrorInvalidValue;
   if (kmajor && H % 64) return hipErrorInvalidValue;
-  const int km = kmajor ? rows_alloc : 0;
+  const int km = kmajor ? rows_alloc : 0, ks = kmajor == 32 ? 5 : 6;
   if (res_type == kF32 && out_type == kF32)
-    return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, s);
+    return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, ks, s);
   if (res_type == kBF16 && out_type == kBF16)
-    return run_norm<bf16_t, bf16_t>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, s);
+    return run_norm<bf16_t, bf16_t>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, ks, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int splits, void *out,
-                          int rows, int F, hipStream_t s) {
+                          int rows, int F, int kmajor, int rows_alloc, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (splits > kMaxSplits) return hipErrorInvalidValue;
+  if (splits > kMaxSplits || F % 4) return hipErrorInvalidValue;
+  if (kmajor && ((kmajor != 32 && kmajor != 64) || F % kmajor || rows > rows_alloc))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)(((size_t)rows * F / 4 + kThreads - 1) / kThreads));
+#define SARATHI_ACT(T, GT) \
+  hipLaunchKernelGGL((ffn_act<T, GT>), grid, dim3(kThreads), 0, s, part, splits, static_cast<T *>(out), \
+                     rows, F, kmajor, rows_alloc)
   if (out_type == kF32) {
-    if (gated) hipLaunchKernelGGL((ffn_act<float, true>), grid, dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
-    else hipLaunchKernelGGL((ffn_act<float, false>), grid, dim3(kThreads), 0, s, part, splits, static_cast<float *>(out), rows, F);
+    if (gated) SARATHI_ACT(float, true); else SARATHI_ACT(float, false);
   } else {
-    if (gated) hipLaunchKernelGGL((ffn_act<bf16_t, true>), grid, dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
-    else hipLaunchKernelGGL((ffn_act<bf16_t, false>), grid, dim3(kThreads), 0, s, part, splits, static_cast<bf16_t *>(out), rows, F);
+    if (gated) SARATHI_ACT(bf16_t, true); else SARATHI_ACT(bf16_t, false);
   }
+#undef SARATHI_ACT
   return hipGetLastError();
 }
 

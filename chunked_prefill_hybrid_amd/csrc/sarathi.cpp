@@ -517,7 +517,8 @@ struct Marker {
 // decode rows (64 per launch group), then one merge of the split partials; writes out [T, A]
 // (storage type).
 sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, const Plan &p,
-                             const void *q, void *out, char *ws, hipStream_t s, Marker &mk) {
+                             const void *q, void *out, const OutLayout &olay, char *ws, hipStream_t s,
+                             Marker &mk) {
   const int A = d->n_heads * d->head_dim;
   const int C = b.C, B = b.B;
   ChunkSet cs = chunk_set(b);
@@ -544,7 +545,7 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
       HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, 0, C, cs, none, pool,
                                p.stride_c, 0, parts.o_c, parts.ml_c, s));
     } else {
-      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, cs, pool, out, A, p.chunk_splits,
+      HIP_TRY(launch_attn_chunk(d->head_dim, q, A, d->n_heads, cs, pool, out, olay, p.chunk_splits,
                                 std::max(p.stride_c, 1), parts.o_c, parts.ml_c, s));
     }
   }
@@ -553,7 +554,7 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   for (int base = 0; base < B; base += kMaxDecodesPerLaunch) {
     const DecodeGroup g = decode_group(b, base);
     if (fused && base == 0)
-      HIP_TRY(launch_attn_fused(d->head_dim, q, A, d->n_heads, cs, pool, out, A, p.chunk_splits, parts,
+      HIP_TRY(launch_attn_fused(d->head_dim, q, A, d->n_heads, cs, pool, out, olay, p.chunk_splits, parts,
                                 g, C, g.n, s));
     else
       HIP_TRY(launch_attn_rows(d->dtype, d->head_dim, q, A, d->n_heads, C + base, g.n, cs, g, pool,
@@ -575,7 +576,7 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   }
   if (C + B > merge_row0)
     HIP_TRY(launch_attn_combine(d->dtype, d->head_dim, d->n_heads, merge_row0, C + B - merge_row0, C,
-                                chunk_splits, table, parts, out, A, s));
+                                chunk_splits, table, parts, out, olay, s));
   HIP_TRY(mk.end(SARATHI_STAGE_ATTN_MERGE, C + B > merge_row0));
   return SARATHI_OK;
 }
@@ -607,18 +608,24 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   float *h1 = reinterpret_cast<float *>(ws + p.h1);
   float *part = reinterpret_cast<float *>(ws + p.part);
   void *n2 = ws + p.n2, *act = ws + p.act;
-  // bf16: the norms write the QKV and gate/up GEMMs' inputs k-tile-major ([H/64][R][64])
-  const bool kmajor = ty == kBF16;
+  // bf16: the norms write the QKV and gate/up GEMMs' inputs k-tile-major ([H/w][R][w], w = the
+  // consuming GEMM's stage depth)
+  const int kmajor1 = ty == kBF16 ? gemm_stage_depth(p.qkv) : 0;
+  const int kmajor2 = ty == kBF16 ? gemm_stage_depth(p.up) : 0;
+  // ... and the FFN activation k-tile-major for a down GEMM with 32-deep stages (its rows are then
+  // whole 64-byte blocks; with 64-deep stages row-major rows are whole 128-byte lines already)
+  const int kmajor_act = ty == kBF16 && gemm_stage_depth(p.down) == 32 ? 32 : 0;
+  const int kmajor_attn = ty == kBF16 && gemm_stage_depth(p.o) == 32 ? 32 : 0;   // same, O GEMM input
 
   // 1. norm 1 over the C+B rows (pad rows zeroed)
   HIP_TRY(mk.start(SARATHI_STAGE_NORM1));
   HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, nullptr, 0, nullptr, L->w.norm1_w, L->w.norm1_b, n1,
-                           H, T, R, d->norm_eps, kmajor, s));
+                           H, T, R, d->norm_eps, kmajor1, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM1, true));
   // 2. QKV projection: one GEMM over chunk and decode rows (float32 split partials)
   HIP_TRY(mk.start(SARATHI_STAGE_QKV));
   GemmArgs g{};
-  g.a = n1; g.lda = H; g.a_kmajor = kmajor; g.w0 = L->w.w_qkv; g.ldw = H; g.part = part;
+  g.a = n1; g.lda = H; g.a_kmajor = kmajor1; g.w0 = L->w.w_qkv; g.ldw = H; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.qkv, s));
   HIP_TRY(mk.end(SARATHI_STAGE_QKV, true));
@@ -641,39 +648,39 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   }
   HIP_TRY(mk.end(SARATHI_STAGE_ROPE_APPEND, true));
   // 4. attention, split per request
-  st = run_attention(d, b, p, q, attn, ws, s, mk);
+  st = run_attention(d, b, p, q, attn, OutLayout{A, kmajor_attn, R}, ws, s, mk);
   if (st != SARATHI_OK) return st;
   // 5. O projection (float32 split partials)
   HIP_TRY(mk.start(SARATHI_STAGE_O));
   g = GemmArgs{};
-  g.a = attn; g.lda = A; g.w0 = L->w.w_o; g.ldw = A; g.part = part;
+  g.a = attn; g.lda = A; g.a_kmajor = kmajor_attn; g.w0 = L->w.w_o; g.ldw = A; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = A;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.o, s));
   HIP_TRY(mk.end(SARATHI_STAGE_O, true));
   // 6. h1 = x + sum of the O partials (kept in float32), then norm 2
   HIP_TRY(mk.start(SARATHI_STAGE_NORM2));
   HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, part, p.o.splits, h1, L->w.norm2_w, L->w.norm2_b, n2,
-                           H, T, R, d->norm_eps, kmajor, s));
+                           H, T, R, d->norm_eps, kmajor2, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM2, true));
   // 7. FFN up (+gate): activation fused into the GEMM, or split product + activation pass
   HIP_TRY(mk.start(SARATHI_STAGE_FFN_UP));
   g = GemmArgs{};
-  g.a = n2; g.lda = H; g.a_kmajor = kmajor; g.ldw = H; g.m_alloc = R; g.m_store = T; g.k = H;
+  g.a = n2; g.lda = H; g.a_kmajor = kmajor2; g.ldw = H; g.m_alloc = R; g.m_store = T; g.k = H;
   g.w0 = llama ? L->w.w_gate : L->w.w_up;
   g.w1 = llama ? L->w.w_up : nullptr;
   if (p.up.epi == kEpiPartial) {
     g.part = part; g.n = llama ? 2 * F : F; g.n_w0 = F;
     HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.up, s));
-    HIP_TRY(launch_ffn_act(ty, llama, part, p.up.splits, act, T, F, s));
+    HIP_TRY(launch_ffn_act(ty, llama, part, p.up.splits, act, T, F, kmajor_act, R, s));
   } else {
-    g.out = act; g.ldo = F; g.n = F;
+    g.out = act; g.ldo = F; g.n = F; g.out_kmajor = kmajor_act;
     HIP_TRY(launch_gemm(ty, p.up.epi, g, p.up, s));
   }
   HIP_TRY(mk.end(SARATHI_STAGE_FFN_UP, true));
   // 8. down projection (split partials), y = h1 + sum of the partials
   HIP_TRY(mk.start(SARATHI_STAGE_FFN_DOWN));
   g = GemmArgs{};
-  g.a = act; g.lda = F; g.w0 = L->w.w_down; g.ldw = F; g.part = part;
+  g.a = act; g.lda = F; g.a_kmajor = kmajor_act; g.w0 = L->w.w_down; g.ldw = F; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.down, s));
   HIP_TRY(launch_resid_sum(ty, h1, part, p.down.splits, b.y, T, H, s));
@@ -682,15 +689,19 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
 
   if (dump) {
     if (dump->n1)
-      HIP_TRY(kmajor ? launch_kmajor_to_f32(ty, n1, R, dump->n1, H, T, H, s)
+      HIP_TRY(kmajor1 ? launch_kmajor_to_f32(ty, n1, kmajor1, R, dump->n1, H, T, H, s)
                      : launch_to_f32(ty, n1, H, dump->n1, H, T, H, s));
     if (dump->q_rot) HIP_TRY(launch_to_f32(ty, q, A, dump->q_rot, A, T, A, s));
-    if (dump->attn) HIP_TRY(launch_to_f32(ty, attn, A, dump->attn, A, T, A, s));
+    if (dump->attn)
+      HIP_TRY(kmajor_attn ? launch_kmajor_to_f32(ty, attn, kmajor_attn, R, dump->attn, A, T, A, s)
+                          : launch_to_f32(ty, attn, A, dump->attn, A, T, A, s));
     if (dump->h1) HIP_TRY(launch_to_f32(kF32, h1, H, dump->h1, H, T, H, s));
     if (dump->n2)
-      HIP_TRY(kmajor ? launch_kmajor_to_f32(ty, n2, R, dump->n2, H, T, H, s)
+      HIP_TRY(kmajor2 ? launch_kmajor_to_f32(ty, n2, kmajor2, R, dump->n2, H, T, H, s)
                      : launch_to_f32(ty, n2, H, dump->n2, H, T, H, s));
-    if (dump->act) HIP_TRY(launch_to_f32(ty, act, F, dump->act, F, T, F, s));
+    if (dump->act)
+      HIP_TRY(kmajor_act ? launch_kmajor_to_f32(ty, act, kmajor_act, R, dump->act, F, T, F, s)
+                         : launch_to_f32(ty, act, F, dump->act, F, T, F, s));
   }
   return SARATHI_OK;
 }
@@ -1025,7 +1036,8 @@ sarathi_status sarathi_attention(const sarathi_layer_desc *desc, const sarathi_b
   if (ws_bytes < p.total)
     return fail(SARATHI_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
   Marker none;
-  return run_attention(desc, v, p, q, out, static_cast<char *>(workspace),
+  const int A = desc->n_heads * desc->head_dim;
+  return run_attention(desc, v, p, q, out, OutLayout{A, 0, p.T}, static_cast<char *>(workspace),
                        static_cast<hipStream_t>(stream), none);
 }
 

@@ -19,6 +19,9 @@ MID = wl.LayerShape("mid-llama", "llama", 512, 4, 128, 1408, "bf16", 1e-6, 10000
 MID_GPT = wl.LayerShape("mid-gpt", "gpt", 512, 4, 128, 1024, "bf16", 1e-5, 10000.0, None)
 MID_F32 = wl.LayerShape("mid-llama-f32", "llama", 512, 4, 128, 1408, "f32", 1e-6, 10000.0, None)
 MID_D64 = wl.LayerShape("mid-llama-d64", "llama", 256, 4, 64, 704, "bf16", 1e-6, 10000.0, None)
+# A llama-7b-sized layer: at 400+ rows every one of its GEMMs takes one 576-row tile per column
+# stripe (32-deep stages)
+BIG = wl.LayerShape("big-llama", "llama", 4096, 32, 128, 11008, "bf16", 1e-6, 10000.0, None)
 
 
 def pad_caches(b, extra):
@@ -67,7 +70,9 @@ def run_case(shape, C, off, lens, seed=0, label=None, max_pos=None):
 # ------------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (17, 384, 320), (36, 768, 256), (105, 1536, 512),
-                                   (274, 640, 5120), (289, 192, 1408), (560, 256, 640)])
+                                   (274, 640, 5120), (289, 192, 1408), (560, 256, 640),
+                                   # enough columns for one round of 576-row tiles (32-deep stages)
+                                   (300, 30720, 256), (560, 30720, 512)])
 def test_gemm_bf16(m, n, k):
     gu.say(f"gemm bf16 m={m} n={n} k={k}")
     rng = np.random.default_rng(m * 7 + n)
@@ -186,20 +191,24 @@ def test_edge_batches(C, off, lens):
 # Invariants on the GPU
 # ------------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", [MID, MID_F32], ids=["bf16", "f32"])
-def test_decode_row_alone_equals_in_batch(shape):
-    gu.say(f"case decode alone vs in batch {shape.name}")
-    w, b = case(shape, 60, 9, [4, 250, 31], seed=3)
-    layer = hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=63, max_pos=512)
+@pytest.mark.parametrize("shape,C", [(MID, 60), (MID_F32, 60), (BIG, 400)],
+                         ids=["bf16", "f32", "bf16-tall-tiles"])
+def test_decode_row_alone_equals_in_batch(shape, C):
+    """A decode row run alone (one GEMM row, 288-row tiles with 64-deep stages) equals the same
+    decode inside a batch, bit for bit; with C = 400 the batch's GEMMs take 576-row tiles with
+    32-deep stages, whose k-sums must be cut at the same points."""
+    gu.say(f"case decode alone vs in batch {shape.name} C={C}")
+    w, b = case(shape, C, 9, [4, 250, 31], seed=3)
+    layer = hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=C + 3, max_pos=512)
     db = gu.upload_batch(shape, b)
     gu.run(layer, db, dump=False)
     y_full = db["y"].clone()
     for i, L in enumerate(b["decode_len"]):
-        db2 = gu.upload_batch(shape, {**b, "x": b["x"][60 + i:61 + i], "chunk_len": 0,
+        db2 = gu.upload_batch(shape, {**b, "x": b["x"][C + i:C + i + 1], "chunk_len": 0,
                                       "decode_len": [L], "decode_k": [b["decode_k"][i]],
                                       "decode_v": [b["decode_v"][i]]})
         gu.run(layer, db2, dump=False)
-        assert torch.equal(db2["y"][0], y_full[60 + i]), f"decode {i} differs alone vs in batch"
+        assert torch.equal(db2["y"][0], y_full[C + i]), f"decode {i} differs alone vs in batch"
     layer.close()
 
 
