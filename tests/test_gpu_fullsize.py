@@ -29,7 +29,8 @@ def run_full(wk):
     gu.say(f"  gpu done at {time.time() - t0:.1f}s")
     ref = oracle.layer_forward(shape, w, b)
     gu.say(f"  oracle done at {time.time() - t0:.1f}s")
-    gu.compare(shape, b, ref, db, dd, label=f"{wk.key} full")
+    gu.compare(shape, b, ref, db, dd, label=f"{wk.key} C={b['chunk_len']} off={b['chunk_offset']} "
+                                               f"B={len(b['decode_len'])} full")
     layer.close()
 
 
