@@ -15,9 +15,9 @@ are rotated step by step so that the 256 MB last-level cache cannot hold a step'
 Passes per workload: W warmup steps; a breakdown pass in which the library records HIP events around
 every stage (this perturbs the step time, so it is not the timed region); then exactly K timed steps
 in which events are recorded on the launch stream only around the dominant kernel's stage, giving
-that kernel's live average duration for the roofline, while a host thread samples the GPU's clock
-and power.  Prints ONE JSON line: tokens/s over the K timed steps, the roofline of the dominant
-kernel, the per-stage breakdown, the layer's roofline fraction, the piggybacking comparison (the same
+that kernel's live average duration for the roofline, and two one-thread kernels around them sample
+the shader clock counter, giving the average GPU clock over the timed steps.  Prints ONE JSON line:
+tokens/s over the K timed steps, the roofline of the dominant kernel, the per-stage breakdown, the layer's roofline fraction, the piggybacking comparison (the same
 rows run as a chunk-only and a decode-only batch, giving the marginal cost of a decode that rides
 with the chunk), the GPU clock during the timed steps, and the CPU oracle's throughput on the same
 inputs (float32, on the host cores given to this process, plus a one-thread run).
@@ -30,7 +30,6 @@ import json
 import os
 import statistics
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -127,80 +126,32 @@ def load_traffic(stage, workload_key):
     return rec.get("bytes_per_launch")
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock and socket power from a host thread (AMD SMI GPU metrics)
-    while it runs.
-    The device is matched by PCI address to torch's device 0; on any failure the summary says why."""
+class DeviceClock:
+    """Average shader clock over enqueued work: one single-thread kernel before and one after it each
+    sample the shader-clock timestamp counter (s_memtime) and the 100 MHz real-time counter
+    (s_memrealtime); the clock is 100 MHz x (timestamp delta) / (real-time delta)."""
 
-    def __init__(self, period_s=0.005):
-        self.period = period_s
-        self.samples = []
-        self.error = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._h = None
-        try:
-            import amdsmi
-            import torch
-            self._smi = amdsmi
-            amdsmi.amdsmi_init()
-            p = torch.cuda.get_device_properties(0)
-            want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
-            for h in amdsmi.amdsmi_get_processor_handles():
-                if str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower().startswith(want):
-                    self._h = h
-            if self._h is None:
-                self.error = f"no AMD SMI device at PCI {want}"
-        except Exception as e:   # no SMI library, no permission, no driver
-            self.error = f"{type(e).__name__}: {e}"
+    def __init__(self, stream):
+        import torch
 
-    def _read(self):
-        # The SMU's metrics table (refreshed by the firmware every few milliseconds): the current
-        # graphics clock of each XCD (their mean; unset entries read as 0xFFFF or "N/A") and the
-        # socket power.
-        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        from chunked_prefill_hybrid_amd import _abi
+        self._abi = _abi
+        self.stream = stream
+        self.buf = torch.zeros(4, dtype=torch.int64, device="cuda")
 
-        def num(v):
-            return v if isinstance(v, (int, float)) and 0 < v < 0xFFFF else None
-        clks = [num(c) for c in (m.get("current_gfxclks") or []) if num(c)]
-        mhz = sum(clks) / len(clks) if clks else (num(m.get("current_gfxclk")) or
-                                                   num(m.get("average_gfxclk_frequency")))
-        w = num(m.get("current_socket_power")) or num(m.get("average_socket_power"))
-        return mhz, w
+    def start(self):
+        self._abi.sarathi_clock_sample(self.buf.data_ptr(), self.stream)
 
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._read())
-            except Exception as e:
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        if self._h is not None:
-            self._thread = threading.Thread(target=self._loop, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread:
-            self._thread.join()
+    def stop(self):
+        self._abi.sarathi_clock_sample(self.buf.data_ptr() + 16, self.stream)
 
     def summary(self):
-        if not self.samples:
-            return {"source": "amdsmi gpu_metrics", "samples": 0, "error": self.error or "no samples"}
-        mhz = [c for c, _ in self.samples if isinstance(c, (int, float))]
-        w = [p for _, p in self.samples if isinstance(p, (int, float))]
-        out = {"source": "amdsmi gpu_metrics", "samples": len(self.samples)}
-        if mhz:
-            out.update(gfx_mhz_median=statistics.median(mhz), gfx_mhz_min=min(mhz), gfx_mhz_max=max(mhz))
-        if w:
-            out["socket_power_w_median"] = statistics.median(w)
-        if self.error:
-            out["error"] = self.error
-        return out
+        t0, r0, t1, r1 = [int(v) for v in self.buf.cpu().tolist()]
+        if r1 <= r0:
+            return {"source": "s_memtime / s_memrealtime", "error": "no real-time interval"}
+        return {"source": "s_memtime / s_memrealtime around the timed steps",
+                "gfx_mhz_avg": round(100.0 * (t1 - t0) / (r1 - r0), 1),
+                "interval_ms": round((r1 - r0) / 1e5, 3)}
 
 
 def host_cpu():
@@ -397,14 +348,15 @@ def measure(key, args, changes=None, page_size=None, sweep=True):
     # Timed region: exactly K steps; HIP events on the launch stream only around the dominant
     # kernel's stage give its live average duration; a host thread samples the GPU clock.
     timer = _abi.sarathi_timer_create(args.steps, _abi.stage_mask(dominant))
-    clocks = ClockSampler()
+    clocks = DeviceClock(stream)
     torch.cuda.synchronize()
-    with clocks:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(i, timer)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+    clocks.start()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, timer)
+    clocks.stop()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     live = _abi.sarathi_timer_read(timer)
     _abi.sarathi_timer_destroy(timer)
     tot, cnt = live[dominant]

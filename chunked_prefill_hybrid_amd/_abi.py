@@ -29,7 +29,7 @@ SARATHI_ARCH_GPT = 1
 EXPORTED = [
     "sarathi_layer_create", "sarathi_layer_destroy", "sarathi_batch_check", "sarathi_workspace_size",
     "sarathi_layer_forward", "sarathi_layer_forward_debug", "sarathi_layer_forward_noalloc",
-    "sarathi_gemm", "sarathi_attention",
+    "sarathi_gemm", "sarathi_attention", "sarathi_clock_sample",
     "sarathi_status_str", "sarathi_last_error", "sarathi_timer_create", "sarathi_timer_destroy",
     "sarathi_layer_forward_timed", "sarathi_timer_read", "sarathi_stack_workspace_size",
     "sarathi_stack_forward", "sarathi_multi_batch_check", "sarathi_multi_workspace_size",
@@ -202,12 +202,19 @@ def lib():
         L.sarathi_multi_plan_describe.restype = c_int32
         L.sarathi_paged_plan_describe.argtypes = [POINTER(sarathi_layer_desc), PB, PI]
         L.sarathi_paged_plan_describe.restype = c_int32
+        L.sarathi_clock_sample.argtypes = [c_void_p, c_void_p]
+        L.sarathi_clock_sample.restype = c_int32
         L.sarathi_status_str.argtypes = [c_int32]
         L.sarathi_status_str.restype = c_char_p
         L.sarathi_last_error.argtypes = []
         L.sarathi_last_error.restype = c_char_p
         _lib = L
     return _lib
+
+
+def sarathi_clock_sample(out: int, stream: int) -> None:
+    """Enqueue a sample of (shader-clock timestamp, 100 MHz real-time counter) into device uint64[2]."""
+    _check(lib().sarathi_clock_sample(out, stream), "sarathi_clock_sample")
 
 
 def sarathi_status_str(status: int) -> str:

@@ -165,6 +165,10 @@ hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const Chunk
 constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
 hipError_t noalloc_scratch(int device, void **out);
 
+// One thread writes the shader-clock timestamp (s_memtime) and the 100 MHz real-time counter
+// (s_memrealtime) to out[0], out[1].
+hipError_t launch_clock_sample(uint64_t *out, hipStream_t s);
+
 // Zero-fill rows [row0, row1) of a [*, cols] storage matrix (row stride ld).
 hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int row1, hipStream_t s);
 

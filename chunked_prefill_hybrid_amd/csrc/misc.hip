@@ -28,7 +28,19 @@ __global__ __launch_bounds__(256) void widen_kmajor_rows(const T *src, int w, in
     d[c] = to_f32(src[((size_t)(c / w) * rows_alloc + r) * w + (c % w)]);
 }
 
+__global__ __launch_bounds__(64) void clock_sample(uint64_t *out) {
+  if (threadIdx.x == 0) {
+    out[0] = __builtin_amdgcn_s_memtime();
+    out[1] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+
 }  // namespace
+
+hipError_t launch_clock_sample(uint64_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(clock_sample, dim3(1), dim3(64), 0, s, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_zero_rows(int type, void *p, int ld, int cols, int row0, int row1, hipStream_t s) {
   if (row1 <= row0) return hipSuccess;

@@ -1118,6 +1118,12 @@ sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_
   return SARATHI_OK;
 }
 
+sarathi_status sarathi_clock_sample(uint64_t *out, void *stream) {
+  if (!out) return fail(SARATHI_ERR_INVALID, "out is null");
+  HIP_TRY(launch_clock_sample(out, static_cast<hipStream_t>(stream)));
+  return SARATHI_OK;
+}
+
 const char *sarathi_status_str(sarathi_status status) {
   switch (status) {
     case SARATHI_OK: return "ok";

@@ -391,6 +391,13 @@ sarathi_status sarathi_paged_forward_timed(sarathi_layer *layer, const sarathi_p
  * timer.  Errors: INVALID, HIP. */
 sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_t *count);
 
+/* Enqueues on `stream` one single-thread kernel that writes two 64-bit counters to the device
+ * buffer `out` (uint64_t[2]): out[0] = the shader-clock timestamp counter (s_memtime), out[1] = the
+ * constant 100 MHz real-time counter (s_memrealtime).  Two samples taken around enqueued work give
+ * the average shader clock over it: 100 MHz x (delta out[0]) / (delta out[1]).  For measurement only.
+ * Errors: INVALID (out is NULL), HIP. */
+sarathi_status sarathi_clock_sample(uint64_t *out, void *stream);
+
 /* ---- Launch plan (inspection) -------------------------------------------------------------------
  * How a forward over a batch would run, computed on the host exactly as the forward computes it, with
  * no device work: for tests and tools.  The four linear ops run as one GEMM each over all C+B rows
