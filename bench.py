@@ -47,7 +47,10 @@ from chunked_prefill_hybrid_amd.profiling import kernel_source_hash, stage_sourc
 
 
 def _split_count(n_keys):
-    return (n_keys + 255) // 256   # key splits of the split-KV attention (256 keys each)
+    """Key splits of a decode row's split-KV attention: 256 keys each, 1024 for rows of more than 2048
+    keys (the library's rule; a CPU test checks the two agree through sarathi_plan_describe)."""
+    per = 1024 if n_keys > 2048 else 256
+    return (n_keys + per - 1) // per
 
 
 def stage_work(shape, chunks, lens, chunk_splits=None):

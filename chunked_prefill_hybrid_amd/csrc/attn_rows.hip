@@ -43,7 +43,7 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
   constexpr int E = Packet<T>::E;      // elements per 16-byte packet
   constexpr int LPK = D / E;           // lanes per key row
   constexpr int KPI = kWave / LPK;     // keys per wave load step
-  constexpr int KPW = kAttnSplit / 4;  // keys per wave per split
+  constexpr int KPW = kAttnSplit / 4;  // keys per wave per pass
   constexpr int NIT = KPW / KPI;
   static_assert(NIT % kUnroll == 0, "whole unrolled steps");
   constexpr int P = (kPre * kUnroll <= NIT && NIT % (kPre * kUnroll) == 0) ? kPre : 1;
@@ -62,6 +62,7 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
   }
   const int per = (n_keys + nsp - 1) / nsp;
   const int k_begin = s * per, k_end = min(n_keys, k_begin + per);
+  const int npass = (per + kAttnSplit - 1) / kAttnSplit;   // 1 .. kAttnLongPasses
   const int sub = lane % LPK, grp = lane / LPK;
 
   float qv[E];
@@ -72,73 +73,84 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
                       : reinterpret_cast<const T *>(rr.k) + (size_t)h * rr.cap * D + sub * E;
   const T *Vh = kPaged ? reinterpret_cast<const T *>(pool.v) + sub * E
                       : reinterpret_cast<const T *>(rr.v) + (size_t)h * rr.cap * D + sub * E;
-  const int wbeg = k_begin + wave * KPW;
-  // Paged caches: lane i holds the pool page of the wave's i-th page (its keys wbeg .. wbeg + KPW - 1
-  // span at most KPW / page_size + 1 pages); a key's page is then one lane shuffle away.
-  int tbl = 0, pg0 = 0;
+  // Pass p of wave w covers keys wbeg(p) .. wbeg(p) + KPW - 1, wbeg(p) = k_begin + (4p + w) KPW.
+  // Paged caches: lane i of tbl[p] holds the pool page of the pass's i-th page (its KPW keys span at
+  // most KPW / page_size + 1 pages); a key's page is then one lane shuffle away.  All passes' tables
+  // are read before the first key.
+  int tbl[kAttnLongPasses] = {}, pg0[kAttnLongPasses] = {};
   if (kPaged) {
-    pg0 = wbeg >> pool.shift;
     const int n_ent = rr.cap >> pool.shift;
-    tbl = pool_page(reinterpret_cast<const int32_t *>(rr.k), min(pg0 + lane, n_ent - 1), pool.n_pages);
+#pragma unroll
+    for (int p = 0; p < kAttnLongPasses; ++p)
+      if (p < npass) {
+        pg0[p] = (k_begin + (4 * p + wave) * KPW) >> pool.shift;
+        tbl[p] = pool_page(reinterpret_cast<const int32_t *>(rr.k), min(pg0[p] + lane, n_ent - 1),
+                           pool.n_pages);
+      }
   }
-  auto key_off = [&](int j) -> size_t {
-    if (!kPaged) return (size_t)j * D;
-    const int page = __shfl(tbl, min((j >> pool.shift) - pg0, kWave - 1), kWave);
-    return paged_off(page, h, j, nh, pool.shift, D);
-  };
 
   float m_run = -INFINITY, l_run = 0.f, o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
 
-  for (int c0 = 0; c0 < NIT; c0 += U) {
-    if (wbeg + c0 * KPI >= k_end) break;
-    uint4 kr[U], vr[U];
-    bool ok[U];
-    size_t ko[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = wbeg + (c0 + u) * KPI + grp;
-      ok[u] = j < k_end;
-      ko[u] = key_off(j);
-      kr[u] = ok[u] ? ld16_stream(Kh + ko[u]) : make_uint4(0, 0, 0, 0);
-    }
+  for (int pass = 0; pass < kAttnLongPasses; ++pass) {
+    if (pass >= npass) break;
+    const int wbeg = k_begin + (4 * pass + wave) * KPW;
+    auto key_off = [&](int j) -> size_t {
+      if (!kPaged) return (size_t)j * D;
+      const int page = __shfl(tbl[pass], min((j >> pool.shift) - pg0[pass], kWave - 1), kWave);
+      return paged_off(page, h, j, nh, pool.shift, D);
+    };
+    for (int c0 = 0; c0 < NIT; c0 += U) {
+      if (wbeg + c0 * KPI >= k_end) break;
+      uint4 kr[U], vr[U];
+      bool ok[U];
+      size_t ko[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      vr[u] = ok[u] ? ld16_stream(Vh + ko[u]) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int h = 0; h < P; ++h) {
-      if (h > 0 && wbeg + (c0 + h * kUnroll) * KPI >= k_end) break;   // the steps one at a time
-      float sc[kUnroll];
-      float cmax = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float kv[E];
-        unpack<T>(kr[h * kUnroll + u], kv);
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
-#pragma unroll
-        for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
-        sc[u] = ok[h * kUnroll + u] ? dot : -INFINITY;
-        cmax = fmaxf(cmax, sc[u]);
+      for (int u = 0; u < U; ++u) {
+        const int j = wbeg + (c0 + u) * KPI + grp;
+        ok[u] = j < k_end;
+        ko[u] = key_off(j);
+        kr[u] = ok[u] ? ld16_stream(Kh + ko[u]) : make_uint4(0, 0, 0, 0);
       }
-      cmax = wave_max(cmax, LPK);
-      const float m_new = fmaxf(m_run, cmax);
-      const float corr = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      l_run *= corr;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] *= corr;
+      for (int u = 0; u < U; ++u)
+        vr[u] = ok[u] ? ld16_stream(Vh + ko[u]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float p = ok[h * kUnroll + u] ? exp2f(sc[u] - m_new) : 0.f;
-        l_run += p;
-        float vv[E];
-        unpack<T>(vr[h * kUnroll + u], vv);
+      for (int h = 0; h < P; ++h) {
+        if (h > 0 && wbeg + (c0 + h * kUnroll) * KPI >= k_end) break;   // the steps one at a time
+        float sc[kUnroll];
+        float cmax = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[e], o[e]);
+        for (int u = 0; u < kUnroll; ++u) {
+          float kv[E];
+          unpack<T>(kr[h * kUnroll + u], kv);
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
+#pragma unroll
+          for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
+          sc[u] = ok[h * kUnroll + u] ? dot : -INFINITY;
+          cmax = fmaxf(cmax, sc[u]);
+        }
+        cmax = wave_max(cmax, LPK);
+        const float m_new = fmaxf(m_run, cmax);
+        const float corr = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+        l_run *= corr;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] *= corr;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const float p = ok[h * kUnroll + u] ? exp2f(sc[u] - m_new) : 0.f;
+          l_run += p;
+          float vv[E];
+          unpack<T>(vr[h * kUnroll + u], vv);
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[e], o[e]);
+        }
+        m_run = m_new;
       }
-      m_run = m_new;
     }
   }
   // Sum over the key groups of the wave (lanes with equal `sub`); scores were replicated per group.

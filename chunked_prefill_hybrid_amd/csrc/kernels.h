@@ -89,14 +89,30 @@ hipError_t launch_rope_append(int type, const float *part, int splits, int rows_
 
 // ---------------------------------------------------------------------------------------------
 // Split-KV single-query attention for rows [row0, row0+n_rows): each (row, head) attends over keys
-// 0..pos of its cache in balanced splits of at most kAttnSplit keys; each split writes its partial
-// (running max m and sum l in the log2 domain, unnormalised output o) to part_ml / part_o, at slot
-// ((r - prow0) * nh + h) * stride + s (stride >= the row's split count; splits past a row's count
-// are written as empty partials).
+// 0..pos of its cache in balanced splits of at most attn_split_keys(pos + 1) keys; each split writes
+// its partial (running max m and sum l in the log2 domain, unnormalised output o) to part_ml /
+// part_o, at slot ((r - prow0) * nh + h) * stride + s (stride >= the row's split count; splits past
+// a row's count are written as empty partials).  A split's four waves walk its keys in passes of
+// kAttnSplit keys (64 per wave).  Rows with more than kAttnLongKeys keys take splits of
+// kAttnLongPasses passes (1024 keys): their workgroups then stream four times the bytes each, and
+// write and merge a quarter of the partials.  The split size depends only on the row's own length,
+// so a row's result does not depend on the batch it is in.
+#ifndef SARATHI_DECODE_LONG_KEYS
+#define SARATHI_DECODE_LONG_KEYS 2048
+#endif
+#ifndef SARATHI_DECODE_LONG_PASSES
+#define SARATHI_DECODE_LONG_PASSES 4
+#endif
 constexpr int kAttnSplit = 256;
+constexpr int kAttnLongKeys = SARATHI_DECODE_LONG_KEYS;
+constexpr int kAttnLongPasses = SARATHI_DECODE_LONG_PASSES;
 constexpr int kMaxKeySplits = 256;   // split partials per (row, head): keys up to 65536
+__host__ __device__ inline int attn_split_keys(int n_keys) {
+  return n_keys > kAttnLongKeys ? kAttnSplit * kAttnLongPasses : kAttnSplit;
+}
 __host__ __device__ inline int attn_splits(int n_keys) {
-  return (n_keys + kAttnSplit - 1) / kAttnSplit;
+  const int sk = attn_split_keys(n_keys);
+  return (n_keys + sk - 1) / sk;
 }
 hipError_t launch_attn_rows(int type, int d, const void *q, int ld_q, int nh, int row0, int n_rows,
                             const ChunkSet &cs, const DecodeGroup &dg, const PagePool &pool,

@@ -340,6 +340,19 @@ def test_plan_of_decode_only_batch(lib):
     assert info.rows == 2
 
 
+def test_plan_decode_key_split_counts(lib):
+    """A decode row's key range is cut into splits of at most 256 keys, or 1024 for rows of more than
+    2048 keys, balanced; the benchmark's merge-byte count uses the same rule."""
+    import bench
+    d = desc(hidden=5120, n_heads=40, head_dim=128, ffn=13824, dtype=_abi.SARATHI_BF16, max_tokens=64,
+             max_pos=40000)
+    for L in (0, 1, 255, 256, 1023, 2046, 2047, 2048, 2049, 4095, 8191, 8192, 39998):
+        b, keep = batch(C=0, lens=(L,))
+        n = L + 1
+        expect = -(-n // 256) if n <= 2048 else -(-n // 1024)
+        assert _abi.plan_describe(d, b).max_key_splits == expect == bench._split_count(n), L
+
+
 def test_plan_of_token_budget_batch(lib):
     """Three chunks (94 tokens at offset 930, a whole 300-token prompt, 100 tokens of a new prompt):
     the chunk with the longest key range gets the most splits."""

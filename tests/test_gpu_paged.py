@@ -77,6 +77,8 @@ def test_paged_bf16_page_sizes(page):
     (MID, [(64, 2100), (100, 0), (30, 50)], [], 8), # per-chunk split counts 3, 1, 1
     (MID, [], [1, 40, 1023], 16),                   # decodes only
     (MID, [(200, 0)], [], 1),                       # one-token pages
+    (MID, [], [2049, 4500], 1),                     # long decodes (1024-key splits), one-token pages
+    (MID, [(30, 10)], [2100, 3333], 16),            # long decodes beside a chunk
 ])
 def test_paged_cases(shape, chunks, lens, page):
     run_paged_case(shape, chunks, lens, page)

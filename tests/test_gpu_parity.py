@@ -182,6 +182,8 @@ def test_mid_bf16_head_dim_64():
     (3, 5, list(range(1, 141, 2))), # 70 decodes: more than one launch group of 64
     (200, 901, [5, 700]),           # chunk offset off the 64-key tile grid
     (64, 2051, [5]),                # one query block, long prefix: its keys split in two
+    (0, 0, [2046, 2047, 2048, 3000]),  # decodes at the 256/1024-key split threshold
+    (5, 2, [6001]),                 # a long decode: 1024-key splits, the last one ragged
 ])
 def test_edge_batches(C, off, lens):
     run_case(MID, C, off, lens, seed=C + len(lens))
