@@ -21,6 +21,8 @@
 // fp32 path: a plain FMA tile kernel (exact float32 products, used by the float32 layer mode).
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace sarathi {
@@ -58,7 +60,10 @@ constexpr int kWaves = kWM * kPlanWaveCols;
 #define SARATHI_GEMM_MBW64 9
 #endif
 constexpr int kMBW64 = SARATHI_GEMM_MBW64;
-constexpr int kMBW = 18;
+#ifndef SARATHI_GEMM_MBW
+#define SARATHI_GEMM_MBW 18
+#endif
+constexpr int kMBW = SARATHI_GEMM_MBW;
 #ifndef SARATHI_GEMM_BN
 #define SARATHI_GEMM_BN 128
 #endif
@@ -97,7 +102,8 @@ template <int MB> struct StageGeom {
   static constexpr int kStages = kFit < kMaxStages ? kFit : kMaxStages;
   static_assert(kStages >= 2, "two stages fit in LDS");
   static constexpr int kLoadsA = kRowsA / K::kRPL;
-  static constexpr int kAI = (kLoadsA + kWaves - 1) / kWaves;   // A loads per wave (some repeated)
+  static constexpr int kAI = (kLoadsA + kWaves - 1) / kWaves;   // A loads of waves 0 .. kARem - 1
+  static constexpr int kARem = kLoadsA % kWaves;                // (the others issue kAI - 1 if > 0)
   static constexpr int kBI = kBN / K::kRPL / kWaves;            // weight loads per wave
   static_assert(kRowsA % K::kRPL == 0, "whole loads of A rows");
   static_assert(kBN % (K::kRPL * kWaves) == 0, "weight rows split evenly over the waves");
@@ -152,10 +158,10 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
 
   // Per-lane sources of this wave's loads.  Load q fills LDS rows kRPL q .. kRPL q + kRPL - 1; lane
   // l lands in row kRPL q + l / kChunks, slot l % kChunks, so it fetches the chunk that the swizzle
-  // stores in that slot.  Every wave issues the same number of loads per stage (the wait counts are
-  // then the same immediate for all waves): a wave whose round-robin share of A loads is one short
-  // repeats the last A load, writing the same bytes to the same rows.  Rows are clamped into the
-  // matrices: rows past the batch fill LDS rows whose products are never stored.
+  // stores in that slot.  The A loads are dealt round-robin, so waves kARem .. 7 issue one fewer per
+  // stage than the first kARem (every request a compute unit keeps in flight counts: the loads are
+  // this kernel's bound); each wave waits on its own count.  Rows are clamped into the matrices:
+  // rows past the batch fill LDS rows whose products are never stored.
   const int lrow = lane / K::kChunks, lslot = lane % K::kChunks;
   const bf16_t *a_src[G::kAI];
   int a_lds[G::kAI];
@@ -194,11 +200,14 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   // Loads of k-tile j (clamped to the last tile, so every wave issues the same loads every step)
   // into LDS stage `st`.  A k-tile of a k-tile-major A lies m_alloc * BK elements after the previous.
   const int a_kstep = g.a_kmajor ? g.m_alloc * BK : BK;
-  auto issue = [&](bf16_t *st, int j) {
+  // kX: this wave issues the extra A load (a template constant, so each form of the k loop below is
+  // straight-line code; a run-time test per load measured 10-35% slower).
+  auto issue = [&](auto kX, bf16_t *st, int j) {
     const int kofs = min(j, ntiles - 1) * BK;
     const int a_kofs = min(j, ntiles - 1) * a_kstep;
 #pragma unroll
-    for (int i = 0; i < G::kAI; ++i) dma16(a_src[i] + a_kofs, st + a_lds[i]);
+    for (int i = 0; i < G::kAI; ++i)
+      if (i < G::kAI - 1 || decltype(kX)::value) dma16(a_src[i] + a_kofs, st + a_lds[i]);
 #pragma unroll
     for (int i = 0; i < G::kBI; ++i) {
       const int q = wave + kWaves * i;
@@ -247,27 +256,30 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   // finished reading, multiply tile j, then wait until this wave's loads of tile j + 1 have landed
   // (at most kNSt - 2 tiles' loads outstanding) and meet the other waves: tile j + 1 is then complete
   // in LDS and nobody reads stage u any more.
-  constexpr int kLoads = G::kAI + G::kBI;
-  auto step = [&](int u, int j) {
-    issue(stage((u + kNSt - 1) % kNSt), j + kNSt - 1);
-    compute(stage(u));
-    wait_vm_lgkm0<(kNSt - 2) * kLoads>();
+  auto k_loop = [&](auto kX) {
+    constexpr int kLoads = G::kAI - 1 + (decltype(kX)::value ? 1 : 0) + G::kBI;   // per stage
+    auto step = [&](int u, int j) {
+      issue(kX, stage((u + kNSt - 1) % kNSt), j + kNSt - 1);
+      compute(stage(u));
+      wait_vm_lgkm0<(kNSt - 2) * kLoads>();
+      stage_barrier();
+    };
+#pragma unroll
+    for (int u = 0; u < kNSt - 1; ++u) issue(kX, stage(u), u);
+    wait_vm_lgkm0<(kNSt - 2) * kLoads>();   // tile 0 landed
     stage_barrier();
+    int j0 = 0;
+    for (; j0 + kNSt <= ntiles; j0 += kNSt) {
+#pragma unroll
+      for (int u = 0; u < kNSt; ++u) step(u, j0 + u);
+    }
+#pragma unroll
+    for (int u = 0; u < kNSt; ++u)
+      if (j0 + u < ntiles) step(u, j0 + u);
+    wait_vm_lgkm0<0>();   // the clamped loads past the last tile land before the workgroup ends
   };
-
-#pragma unroll
-  for (int u = 0; u < kNSt - 1; ++u) issue(stage(u), u);
-  wait_vm_lgkm0<(kNSt - 2) * kLoads>();   // tile 0 landed
-  stage_barrier();
-  int j0 = 0;
-  for (; j0 + kNSt <= ntiles; j0 += kNSt) {
-#pragma unroll
-    for (int u = 0; u < kNSt; ++u) step(u, j0 + u);
-  }
-#pragma unroll
-  for (int u = 0; u < kNSt; ++u)
-    if (j0 + u < ntiles) step(u, j0 + u);
-  wait_vm_lgkm0<0>();   // the clamped loads past the last tile land before the workgroup ends
+  if (G::kARem == 0 || wave < G::kARem) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
 
   // Epilogue.  Lane l of a 16x16 block holds rows 4*(l/16)+i, column l%16.
 #pragma unroll
@@ -372,30 +384,16 @@ hipError_t run_bf16_mb(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI>
+// The kernel instance for the plan's 16-row blocks per wave row (1 .. kMBW).
+template <int EPI, int MB = 1>
 hipError_t run_bf16(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  if (p.wn != kPlanWaveCols) return hipErrorInvalidValue;
-  switch (p.mbw) {
-    case 1: return run_bf16_mb<1, EPI>(g, p, s);
-    case 2: return run_bf16_mb<2, EPI>(g, p, s);
-    case 3: return run_bf16_mb<3, EPI>(g, p, s);
-    case 4: return run_bf16_mb<4, EPI>(g, p, s);
-    case 5: return run_bf16_mb<5, EPI>(g, p, s);
-    case 6: return run_bf16_mb<6, EPI>(g, p, s);
-    case 7: return run_bf16_mb<7, EPI>(g, p, s);
-    case 8: return run_bf16_mb<8, EPI>(g, p, s);
-    case 9: return run_bf16_mb<9, EPI>(g, p, s);
-    case 10: return run_bf16_mb<10, EPI>(g, p, s);
-    case 11: return run_bf16_mb<11, EPI>(g, p, s);
-    case 12: return run_bf16_mb<12, EPI>(g, p, s);
-    case 13: return run_bf16_mb<13, EPI>(g, p, s);
-    case 14: return run_bf16_mb<14, EPI>(g, p, s);
-    case 15: return run_bf16_mb<15, EPI>(g, p, s);
-    case 16: return run_bf16_mb<16, EPI>(g, p, s);
-    case 17: return run_bf16_mb<17, EPI>(g, p, s);
-    case 18: return run_bf16_mb<18, EPI>(g, p, s);
+  if constexpr (MB > kMBW) {
+    return hipErrorInvalidValue;
+  } else {
+    if (p.wn != kPlanWaveCols) return hipErrorInvalidValue;
+    if (p.mbw == MB) return run_bf16_mb<MB, EPI>(g, p, s);
+    return run_bf16<EPI, MB + 1>(g, p, s);
   }
-  return hipErrorInvalidValue;
 }
 
 template <int EPI>
