@@ -50,11 +50,18 @@ template <int NT> __device__ __forceinline__ float block_sum(float v, float *red
 }
 
 constexpr int kMaxSplits = 8;   // split partials a consumer sums (the planner never makes more)
-// A norm row is handled by one workgroup of kNormThreads threads (16 waves, so that the ~300 rows of
-// a batch still keep several waves of memory requests per SIMD in flight).
-constexpr int kNormThreads = 1024;
-constexpr int kRowPieces = 4;   // 4-element pieces per thread: rows up to 16384 wide
-static_assert(4 * kNormThreads * kRowPieces == kMaxHidden, "row width limit");
+// A norm row is handled by one workgroup of NT threads: 1024 (16 waves, so that the ~300 rows of a
+// batch still keep several waves of memory requests per SIMD in flight) while the rows' workgroups
+// all fit on the GPU at once, else 512.  A compute unit holds 32 waves, so 1024-thread workgroups for
+// more than kNormWideRows rows would run in two rounds.
+#ifndef SARATHI_NORM_WIDE_ROWS
+#define SARATHI_NORM_WIDE_ROWS 512
+#endif
+constexpr int kNormWideRows = SARATHI_NORM_WIDE_ROWS;
+template <int NT> struct NormGeom {
+  static constexpr int kPieces = kMaxHidden / (4 * NT);   // 4-element pieces per thread
+  static_assert(4 * NT * kPieces == kMaxHidden, "row width limit");
+};
 
 // v[0..3] += sum_s part[s][off..off+3] in split order; every split's load is issued before its add
 // so a thread keeps several loads in flight.
@@ -74,12 +81,13 @@ __device__ __forceinline__ void add_splits(const float *part, int splits, size_t
 
 // One row per workgroup: the row stays in registers (up to kRowPieces 4-element pieces per thread),
 // so the norm needs one read of its inputs.
-template <typename Tres, typename Tout, bool LN>
-__global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, const float *part,
+template <typename Tres, typename Tout, bool LN, int NT>
+__global__ __launch_bounds__(NT) void norm_rows(const Tres *resid, const float *part,
                                                       int splits, float *sum_out, const float *g,
                                                       const float *b, Tout *out, int H, int rows,
                                                       float eps, int kmajor_rows, int kmajor_shift) {
-  __shared__ float red[kNormThreads / 64];
+  constexpr int kRowPieces = NormGeom<NT>::kPieces;
+  __shared__ float red[NT / 64];
   const int r = blockIdx.x;
   // Element c of this row: row-major, or k-tile-major (tiles of 2^kmajor_shift columns by
   // kmajor_rows rows each).
@@ -90,29 +98,29 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, con
   };
   if (r >= rows) {
     const float z[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c = threadIdx.x * 4; c < H; c += kNormThreads * 4) store4<Tout>(at(c), z);
+    for (int c = threadIdx.x * 4; c < H; c += NT * 4) store4<Tout>(at(c), z);
     return;
   }
   const size_t slice = (size_t)rows * H, row_off = (size_t)r * H;
-  const int nch = (H / 4 - threadIdx.x + kNormThreads - 1) / kNormThreads;   // chunks of this thread
+  const int nch = (H / 4 - threadIdx.x + NT - 1) / NT;   // chunks of this thread
   float v[kRowPieces][4];
 #pragma unroll
   for (int i = 0; i < kRowPieces; ++i)
-    if (i < nch) load4<Tres>(resid + row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
+    if (i < nch) load4<Tres>(resid + row_off + (threadIdx.x + i * NT) * 4, v[i]);
   if (splits > 0) {
 #pragma unroll
     for (int i = 0; i < kRowPieces; ++i)
-      if (i < nch) add_splits(part, splits, slice, row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
+      if (i < nch) add_splits(part, splits, slice, row_off + (threadIdx.x + i * NT) * 4, v[i]);
   }
   float s1 = 0.f;
 #pragma unroll
   for (int i = 0; i < kRowPieces; ++i)
     if (i < nch) {
-      if (sum_out) store4<float>(sum_out + row_off + (threadIdx.x + i * kNormThreads) * 4, v[i]);
+      if (sum_out) store4<float>(sum_out + row_off + (threadIdx.x + i * NT) * 4, v[i]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s1 += LN ? v[i][e] : v[i][e] * v[i][e];
     }
-  s1 = block_sum<kNormThreads>(s1, red);
+  s1 = block_sum<NT>(s1, red);
   float mean = 0.f, ms;
   if (LN) {
     mean = s1 / (float)H;
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, con
 #pragma unroll
         for (int e = 0; e < 4; ++e) q += (v[i][e] - mean) * (v[i][e] - mean);
       }
-    ms = block_sum<kNormThreads>(q, red) / (float)H;
+    ms = block_sum<NT>(q, red) / (float)H;
   } else {
     ms = s1 / (float)H;
   }
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows(const Tres *resid, con
 #pragma unroll
   for (int i = 0; i < kRowPieces; ++i)
     if (i < nch) {
-      const int c = (threadIdx.x + i * kNormThreads) * 4;
+      const int c = (threadIdx.x + i * NT) * 4;
       float w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -177,19 +185,30 @@ __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int split
   store4<Tout>(out + mat_index(r, c, F, kmajor, rows_alloc), v);   // 4 columns within one k-tile
 }
 
+template <typename Tres, typename Tout, bool LN, int NT>
+hipError_t run_norm_nt(const void *resid, const float *part, int splits, float *sum_out,
+                       const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
+                       float eps, int kmajor_rows, int kmajor_shift, hipStream_t s) {
+  hipLaunchKernelGGL((norm_rows<Tres, Tout, LN, NT>), dim3(rows_alloc), dim3(NT), 0, s,
+                     static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
+                     static_cast<Tout *>(out), H, rows, eps, kmajor_rows, kmajor_shift);
+  return hipGetLastError();
+}
+
 template <typename Tres, typename Tout>
 hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, float *sum_out,
                     const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
                     float eps, int kmajor_rows, int kmajor_shift, hipStream_t s) {
-  if (ln)
-    hipLaunchKernelGGL((norm_rows<Tres, Tout, true>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
-                       static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
-                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows, kmajor_shift);
-  else
-    hipLaunchKernelGGL((norm_rows<Tres, Tout, false>), dim3(rows_alloc), dim3(kNormThreads), 0, s,
-                       static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
-                       static_cast<Tout *>(out), H, rows, eps, kmajor_rows, kmajor_shift);
-  return hipGetLastError();
+  const bool wide = rows_alloc <= kNormWideRows;
+#define SARATHI_NORM(LN, NT)                                                                    \
+  return run_norm_nt<Tres, Tout, LN, NT>(resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, \
+                                         eps, kmajor_rows, kmajor_shift, s)
+  if (ln) {
+    if (wide) SARATHI_NORM(true, 1024); else SARATHI_NORM(true, 512);
+  } else {
+    if (wide) SARATHI_NORM(false, 1024); else SARATHI_NORM(false, 512);
+  }
+#undef SARATHI_NORM
 }
 
 }  // namespace
