@@ -249,6 +249,72 @@ hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const 
 // splits issued before their adds.
 constexpr int kCombineWaves = 4;
 constexpr int kCombineSlots = kMaxKeySplits / kWave;   // splits per lane
+constexpr int kFewSplits = 8;
+
+// The merge of a chunk row's ns <= kFewSplits partials, all of which the chunk kernel wrote (o is
+// finite, l = 0 for a split past the query's position).  Every load is issued at once: each lane
+// reads all (m, l) pairs and one 4-column piece of o from each of its splits; the wave's lanes form
+// SPL groups of D / 4, group g taking splits g, g + SPL, ... (summed in that order, then the groups
+// in order g = 0, 1, ...).
+template <typename T, int D>
+__device__ __forceinline__ void combine_few(int ns, size_t base, int r, int h, const float *part_o,
+                                            const float *part_ml, T *out, OutLayout olay) {
+  constexpr int LPS = D / 4;            // lanes per split (4 columns each)
+  constexpr int SPL = kWave / LPS;      // splits per wave load
+  constexpr int NJ = (kFewSplits + SPL - 1) / SPL;
+  const int lane = threadIdx.x & 63, grp = lane / LPS, col = (lane % LPS) * 4;
+  float2 ml[kFewSplits];
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s)
+    ml[s] = s < ns ? *reinterpret_cast<const float2 *>(&part_ml[2 * (base + s)]) : make_float2(-INFINITY, 0.f);
+  float4 ov[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int sp = j * SPL + grp;
+    ov[j] = sp < ns ? *reinterpret_cast<const float4 *>(&part_o[(base + sp) * D + col])
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s)
+    if (ml[s].y > 0.f) M = fmaxf(M, ml[s].x);
+  float L = 0.f, w[kFewSplits];
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s) {
+    w[s] = ml[s].y > 0.f ? exp2f(ml[s].x - M) : 0.f;
+    L = fmaf(ml[s].y, w[s], L);
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float ws = 0.f;
+#pragma unroll
+    for (int s = 0; s < kFewSplits; ++s) ws = (s == j * SPL + grp) ? w[s] : ws;
+    acc[0] = fmaf(ws, ov[j].x, acc[0]);
+    acc[1] = fmaf(ws, ov[j].y, acc[1]);
+    acc[2] = fmaf(ws, ov[j].z, acc[2]);
+    acc[3] = fmaf(ws, ov[j].w, acc[3]);
+  }
+  // Groups in order: after step m, group 0 holds the sum of groups 0 .. 2^(m+1) - 1.
+#pragma unroll
+  for (int o = LPS; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_down(acc[e], o, kWave);
+  }
+  if (grp == 0) {   // 4 consecutive columns, within one k-tile of a k-tile-major output
+    const float inv = 1.0f / L;
+    T *dst = &out[out_index(olay, r, h * D + col)];
+    if constexpr (sizeof(T) == 2) {
+      uint2 u;
+      u.x = (uint32_t)from_f32<T>(acc[0] * inv) | ((uint32_t)from_f32<T>(acc[1] * inv) << 16);
+      u.y = (uint32_t)from_f32<T>(acc[2] * inv) | ((uint32_t)from_f32<T>(acc[3] * inv) << 16);
+      *reinterpret_cast<uint2 *>(dst) = u;
+    } else {
+      *reinterpret_cast<float4 *>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int row0, int n_rows,
                                                                    int chunk_rows, int chunk_splits,
@@ -274,6 +340,10 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
       for (int i = 1; i < kMaxChunks; ++i)
         if (i < table.n && r >= table.row0[i]) ns = table.split[i];
       if (ns <= 1) return;   // written by the chunk kernel
+      if (ns <= kFewSplits) {
+        combine_few<T, D>(ns, base, r, h, part_o, part_ml, out, olay);
+        return;
+      }
       n_used = ns;
     }
   } else {
