@@ -14,15 +14,17 @@ enum StorageType { kF32 = 0, kBF16 = 1 };
 // ---------------------------------------------------------------------------------------------
 // Row norms.  v[r] = resid[r] + sum_{s < splits} part[s][r]  (resid in `res_type` storage, the
 // split partials of a GEMM in float32 with slice stride rows*H; splits may be 0).  If sum_out is
-// non-null it receives v (float32).  out[r] = RMSNorm(v) * g  or  LayerNorm(v) * g + b for r < rows;
-// rows rows..rows_alloc-1 of out are zero-filled.  out is row-major [rows_alloc, H] (kmajor = 0), or
-// k-tile-major [H/w][rows_alloc][w] with w = kmajor, 32 or 64 (the layout the bf16 GEMM reads
-// fastest: w = its stage depth; H % 64 == 0).
+// non-null it receives v (float32); if sum_lo is non-null (and sum_out null) v is rounded to the
+// out type, stored there row-major [rows, H], and normalised as rounded.  out[r] = RMSNorm(v) * g
+// or LayerNorm(v) * g + b for r < rows; rows rows..rows_alloc-1 of out are zero-filled.  out is
+// row-major [rows_alloc, H] (kmajor = 0), or k-tile-major [H/w][rows_alloc][w] with w = kmajor, 32
+// or 64 (the layout the bf16 GEMM reads fastest: w = its stage depth; H % 64 == 0).  Type pairs
+// (resid, out): (f32, f32), (bf16, bf16), (f32, bf16).
 constexpr int kMaxHidden = 16384;   // widest row a norm workgroup holds (1024 threads x 16 elements)
 hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
-                            const float *part, int splits, float *sum_out, const float *g,
-                            const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                            int kmajor, hipStream_t s);
+                            const float *part, int splits, float *sum_out, void *sum_lo,
+                            const float *g, const float *b, void *out, int H, int rows,
+                            int rows_alloc, float eps, int kmajor, hipStream_t s);
 
 // FFN activation from split partials ([splits][rows][n_part] float32): gated (n_part = 2F):
 // out[r, j] = silu(sum_s part[s][r][j]) * sum_s part[s][r][F + j];  else (n_part = F):

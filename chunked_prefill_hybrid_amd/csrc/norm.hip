@@ -81,11 +81,21 @@ __device__ __forceinline__ void add_splits(const float *part, int splits, size_t
 
 // One row per workgroup: the row stays in registers (up to kRowPieces 4-element pieces per thread),
 // so the norm needs one read of its inputs.
+template <typename T> __device__ __forceinline__ float round_to(float v);
+template <> __device__ __forceinline__ float round_to<float>(float v) { return v; }
+template <> __device__ __forceinline__ float round_to<bf16_t>(float v) {
+  return __uint_as_float((uint32_t)f32_to_bf16(v) << 16);
+}
+
+// sum_out: the sum v stored in float32; sum_lo: v rounded to the output type, stored row-major, and
+// the norm then taken of the rounded values (a layer's output y and the next layer's norm 1 in one
+// pass, with the same result as storing y and normalising it in a separate launch).
 template <typename Tres, typename Tout, bool LN, int NT>
 __global__ __launch_bounds__(NT) void norm_rows(const Tres *resid, const float *part,
-                                                      int splits, float *sum_out, const float *g,
-                                                      const float *b, Tout *out, int H, int rows,
-                                                      float eps, int kmajor_rows, int kmajor_shift) {
+                                                      int splits, float *sum_out, Tout *sum_lo,
+                                                      const float *g, const float *b, Tout *out,
+                                                      int H, int rows, float eps, int kmajor_rows,
+                                                      int kmajor_shift) {
   constexpr int kRowPieces = NormGeom<NT>::kPieces;
   __shared__ float red[NT / 64];
   const int r = blockIdx.x;
@@ -117,6 +127,11 @@ __global__ __launch_bounds__(NT) void norm_rows(const Tres *resid, const float *
   for (int i = 0; i < kRowPieces; ++i)
     if (i < nch) {
       if (sum_out) store4<float>(sum_out + row_off + (threadIdx.x + i * NT) * 4, v[i]);
+      if (sum_lo) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[i][e] = round_to<Tout>(v[i][e]);
+        store4<Tout>(sum_lo + row_off + (threadIdx.x + i * NT) * 4, v[i]);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) s1 += LN ? v[i][e] : v[i][e] * v[i][e];
     }
@@ -186,23 +201,24 @@ __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int split
 }
 
 template <typename Tres, typename Tout, bool LN, int NT>
-hipError_t run_norm_nt(const void *resid, const float *part, int splits, float *sum_out,
+hipError_t run_norm_nt(const void *resid, const float *part, int splits, float *sum_out, void *sum_lo,
                        const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
                        float eps, int kmajor_rows, int kmajor_shift, hipStream_t s) {
   hipLaunchKernelGGL((norm_rows<Tres, Tout, LN, NT>), dim3(rows_alloc), dim3(NT), 0, s,
-                     static_cast<const Tres *>(resid), part, splits, sum_out, g, b,
-                     static_cast<Tout *>(out), H, rows, eps, kmajor_rows, kmajor_shift);
+                     static_cast<const Tres *>(resid), part, splits, sum_out,
+                     static_cast<Tout *>(sum_lo), g, b, static_cast<Tout *>(out), H, rows, eps,
+                     kmajor_rows, kmajor_shift);
   return hipGetLastError();
 }
 
 template <typename Tres, typename Tout>
 hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, float *sum_out,
-                    const float *g, const float *b, void *out, int H, int rows, int rows_alloc,
-                    float eps, int kmajor_rows, int kmajor_shift, hipStream_t s) {
+                    void *sum_lo, const float *g, const float *b, void *out, int H, int rows,
+                    int rows_alloc, float eps, int kmajor_rows, int kmajor_shift, hipStream_t s) {
   const bool wide = rows_alloc <= kNormWideRows;
 #define SARATHI_NORM(LN, NT)                                                                    \
-  return run_norm_nt<Tres, Tout, LN, NT>(resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, \
-                                         eps, kmajor_rows, kmajor_shift, s)
+  return run_norm_nt<Tres, Tout, LN, NT>(resid, part, splits, sum_out, sum_lo, g, b, out, H, rows, \
+                                         rows_alloc, eps, kmajor_rows, kmajor_shift, s)
   if (ln) {
     if (wide) SARATHI_NORM(true, 1024); else SARATHI_NORM(true, 512);
   } else {
@@ -214,18 +230,22 @@ hipError_t run_norm(bool ln, const void *resid, const float *part, int splits, f
 }  // namespace
 
 hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const void *resid,
-                            const float *part, int splits, float *sum_out, const float *g,
-                            const float *b, void *out, int H, int rows, int rows_alloc, float eps,
-                            int kmajor, hipStream_t s) {
+                            const float *part, int splits, float *sum_out, void *sum_lo,
+                            const float *g, const float *b, void *out, int H, int rows,
+                            int rows_alloc, float eps, int kmajor, hipStream_t s) {
   if (rows_alloc <= 0) return hipSuccess;
   if (splits > kMaxSplits || H > kMaxHidden || H % 4) return hipErrorInvalidValue;
   if (kmajor != 0 && kmajor != 32 && kmajor != 64) return hipErrorInvalidValue;
   if (kmajor && H % 64) return hipErrorInvalidValue;
+  if (sum_out && sum_lo) return hipErrorInvalidValue;
   const int km = kmajor ? rows_alloc : 0, ks = kmajor == 32 ? 5 : 6;
-  if (res_type == kF32 && out_type == kF32)
-    return run_norm<float, float>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, ks, s);
-  if (res_type == kBF16 && out_type == kBF16)
-    return run_norm<bf16_t, bf16_t>(layernorm, resid, part, splits, sum_out, g, b, out, H, rows, rows_alloc, eps, km, ks, s);
+#define SARATHI_RUN_NORM(TR, TO) \
+  return run_norm<TR, TO>(layernorm, resid, part, splits, sum_out, sum_lo, g, b, out, H, rows, rows_alloc, \
+                          eps, km, ks, s)
+  if (res_type == kF32 && out_type == kF32) SARATHI_RUN_NORM(float, float);
+  if (res_type == kBF16 && out_type == kBF16) SARATHI_RUN_NORM(bf16_t, bf16_t);
+  if (res_type == kF32 && out_type == kBF16) SARATHI_RUN_NORM(float, bf16_t);
+#undef SARATHI_RUN_NORM
   return hipErrorInvalidValue;
 }
 

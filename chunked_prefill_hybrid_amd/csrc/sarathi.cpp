@@ -581,8 +581,11 @@ sarathi_status run_attention(const sarathi_layer_desc *d, const BatchView &b, co
   return SARATHI_OK;
 }
 
+// n1_ready: norm 1 of x is already in the n1 region (written by the previous layer of a stack);
+// next: the following layer of a stack, whose norm 1 this forward then computes with its own output.
 sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspace, size_t ws_bytes,
-                            void *stream, const sarathi_debug_dump *dump, sarathi_timer *timer) {
+                            void *stream, const sarathi_debug_dump *dump, sarathi_timer *timer,
+                            bool n1_ready = false, const sarathi_layer *next = nullptr) {
   if (!L) return fail(SARATHI_ERR_INVALID, "layer is null");
   const sarathi_layer_desc *d = &L->desc;
   sarathi_status st = check_view(d, b, true);
@@ -619,8 +622,9 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
 
   // 1. norm 1 over the C+B rows (pad rows zeroed)
   HIP_TRY(mk.start(SARATHI_STAGE_NORM1));
-  HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, nullptr, 0, nullptr, L->w.norm1_w, L->w.norm1_b, n1,
-                           H, T, R, d->norm_eps, kmajor1, s));
+  if (!n1_ready)
+    HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, nullptr, 0, nullptr, nullptr, L->w.norm1_w,
+                             L->w.norm1_b, n1, H, T, R, d->norm_eps, kmajor1, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM1, true));
   // 2. QKV projection: one GEMM over chunk and decode rows (float32 split partials)
   HIP_TRY(mk.start(SARATHI_STAGE_QKV));
@@ -659,8 +663,8 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   HIP_TRY(mk.end(SARATHI_STAGE_O, true));
   // 6. h1 = x + sum of the O partials (kept in float32), then norm 2
   HIP_TRY(mk.start(SARATHI_STAGE_NORM2));
-  HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, part, p.o.splits, h1, L->w.norm2_w, L->w.norm2_b, n2,
-                           H, T, R, d->norm_eps, kmajor2, s));
+  HIP_TRY(launch_norm_rows(ty, ty, !llama, b.x, part, p.o.splits, h1, nullptr, L->w.norm2_w,
+                           L->w.norm2_b, n2, H, T, R, d->norm_eps, kmajor2, s));
   HIP_TRY(mk.end(SARATHI_STAGE_NORM2, true));
   // 7. FFN up (+gate): activation fused into the GEMM, or split product + activation pass
   HIP_TRY(mk.start(SARATHI_STAGE_FFN_UP));
@@ -683,7 +687,18 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   g.a = act; g.lda = F; g.a_kmajor = kmajor_act; g.w0 = L->w.w_down; g.ldw = F; g.part = part;
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.down, s));
-  HIP_TRY(launch_resid_sum(ty, h1, part, p.down.splits, b.y, T, H, s));
+  if (next) {
+    // y = h1 + sum of the partials, stored, and the next layer's norm 1 of y into the n1 region
+    // (offset 0 of every layer's plan, the same size for layers of one hidden size)
+    const sarathi_layer_desc *dn = &next->desc;
+    const int A_next = dn->n_heads * dn->head_dim;
+    const int kmajor1_next = ty == kBF16 ? gemm_stage_depth(plan_gemm(ty, kEpiPartial, T, 3 * A_next, H, kPlanCUs)) : 0;
+    HIP_TRY(launch_norm_rows(kF32, ty, dn->arch != SARATHI_ARCH_LLAMA, h1, part, p.down.splits, nullptr,
+                             b.y, next->w.norm1_w, next->w.norm1_b, n1, H, T, R, dn->norm_eps,
+                             kmajor1_next, s));
+  } else {
+    HIP_TRY(launch_resid_sum(ty, h1, part, p.down.splits, b.y, T, H, s));
+  }
   HIP_TRY(mk.end(SARATHI_STAGE_FFN_DOWN, true));
   mk.commit();
 
@@ -1017,7 +1032,13 @@ sarathi_status sarathi_stack_forward(sarathi_layer *const *layers, int32_t n_lay
     const void *x = l == 0 ? batch->x : act[(l - 1) & 1];
     void *y = l == n_layers - 1 ? batch->y : act[l & 1];
     const sarathi_batch bl = stack_layer_batch(batch, l, x, y);
-    st = forward_entry(layers[l], &bl, ws, p.layer_ws, stream, nullptr, nullptr);
+    // Each layer but the last ends with the next layer's norm 1 (fused with its output sum), so
+    // each layer but the first starts at its QKV GEMM.
+    BatchView v;
+    st = checked_view(&layers[l]->desc, &bl, true, &v);
+    if (st != SARATHI_OK) return st;
+    st = forward_impl(layers[l], v, ws, p.layer_ws, stream, nullptr, nullptr, l > 0,
+                      l + 1 < n_layers ? layers[l + 1] : nullptr);
     if (st != SARATHI_OK) return st;
   }
   return SARATHI_OK;

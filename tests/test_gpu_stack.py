@@ -133,3 +133,43 @@ def test_stack_chunked_equals_monolithic_on_gpu():
     assert all(v <= 1e-4 for v in errs.values()), errs
     for st in stacks:
         st.close()
+
+
+@pytest.mark.parametrize("shape", [MID, MID_GPT, wl.SHAPES["tiny"]], ids=["llama-bf16", "gpt-bf16", "tiny-f32"])
+def test_stack_equals_layers_run_one_by_one(shape):
+    """A 3-layer stack, whose layers end with the next layer's norm 1 fused into their output sum,
+    gives bit for bit what the three single-layer forwards give when chained by hand (each with its
+    own norm 1), output and caches."""
+    gu.say(f"case stack vs chained layers {shape.name}")
+    rng = np.random.default_rng(31)
+    nh, d, H = shape.n_heads, shape.head_dim, shape.hidden
+    dt = gu.tdtype(shape)
+    n_layers, C, off, lens = 3, 70, 40, [5, 90]
+    W = [wl.make_weights(shape, rng) for _ in range(n_layers)]
+    layers = [hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=C + len(lens), max_pos=256)
+              for w in W]
+
+    def caches():
+        g = torch.Generator(device="cpu").manual_seed(3)
+        mk = lambda n: torch.randn((nh, n, d), generator=g).to(dt).to("cuda")
+        return [(mk(off + C), mk(off + C)) for _ in range(n_layers)], \
+               [[(mk(L + 1), mk(L + 1)) for L in lens] for _ in range(n_layers)]
+    x = gu.dev(rng.standard_normal((C + len(lens), H)).astype(np.float32), dt)
+    ck1, dk1 = caches()
+    ck2, dk2 = caches()
+    y_stack = torch.full_like(x, float("nan"))
+    stack = hl.HybridStack(layers)
+    stack.forward(x, y_stack, C, off, ck1, dk1, lens)
+    cur = x
+    for l in range(n_layers):
+        y = torch.full_like(x, float("nan"))
+        layers[l].forward(cur, y, C, off, ck2[l], dk2[l], lens)
+        cur = y
+    torch.cuda.synchronize()
+    assert torch.equal(y_stack, cur), "stack output differs from the chained layers"
+    for l in range(n_layers):
+        assert torch.equal(ck1[l][0], ck2[l][0]) and torch.equal(ck1[l][1], ck2[l][1]), f"layer {l} chunk cache"
+        for i in range(len(lens)):
+            assert torch.equal(dk1[l][i][0], dk2[l][i][0]) and torch.equal(dk1[l][i][1], dk2[l][i][1]), \
+                f"layer {l} decode {i} cache"
+    stack.close()
