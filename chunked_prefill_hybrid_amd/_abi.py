@@ -112,7 +112,8 @@ class sarathi_plan_info(ctypes.Structure):
                 ("fused_attention", c_int32), ("chunk_splits", c_int32 * SARATHI_MAX_CHUNKS),
                 ("max_key_splits", c_int32), ("chunk_query_blocks", c_int32),
                 ("qkv", sarathi_gemm_plan), ("o", sarathi_gemm_plan), ("up", sarathi_gemm_plan),
-                ("down", sarathi_gemm_plan), ("workspace_bytes", ctypes.c_uint64)]
+                ("down", sarathi_gemm_plan), ("up_tail", sarathi_gemm_plan),
+                ("workspace_bytes", ctypes.c_uint64)]
 
 
 class sarathi_debug_dump(ctypes.Structure):

@@ -492,6 +492,27 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
   return p;
 }
 
+int plan_gemm_tail(int type, int epi, int m, int n_out, int k, int cus, GemmPlan *main, GemmPlan *tail) {
+  if (type != kBF16 || (epi != kEpiSwiGLU && epi != kEpiGelu)) return 0;
+  const GemmPlan whole = plan_gemm(type, epi, m, n_out, k, cus);
+  if (whole.epi == kEpiPartial || whole.n_tiles <= cus) return 0;
+  const int n_main = cus * (epi == kEpiSwiGLU ? kBN / 2 : kBN);
+  if (n_main >= n_out) return 0;
+  const GemmPlan mp = plan_gemm(type, epi, m, n_main, k, cus);
+  if (mp.epi == kEpiPartial) return 0;
+  const int n_tail = n_out - n_main;
+  GemmPlan tp = plan_gemm(type, kEpiPartial, m, epi == kEpiSwiGLU ? 2 * n_tail : n_tail, k, cus);
+  // Both parts read the one input, laid out for the main part's stage depth: the tail takes the
+  // main part's row tiles.
+  tp.m_tiles = mp.m_tiles;
+  tp.mbw = mp.mbw;
+  tp.per_xcd = (tp.m_tiles * tp.n_tiles * tp.splits + 7) / 8;
+  tp.grid = 8 * tp.per_xcd;
+  *main = mp;
+  *tail = tp;
+  return n_main;
+}
+
 int gemm_stage_depth(const GemmPlan &p) { return stage_depth(p.mbw); }
 
 hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s) {

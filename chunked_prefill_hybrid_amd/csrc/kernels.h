@@ -27,11 +27,12 @@ hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const vo
                             int rows_alloc, float eps, int kmajor, hipStream_t s);
 
 // FFN activation from split partials ([splits][rows][n_part] float32): gated (n_part = 2F):
-// out[r, j] = silu(sum_s part[s][r][j]) * sum_s part[s][r][F + j];  else (n_part = F):
-// out[r, j] = gelu(sum_s part[s][r][j]).  out is storage type [rows, F] row-major (kmajor = 0), or
-// k-tile-major [F/w][rows_alloc][w] with w = kmajor (32 or 64, F % w == 0).
+// a[r, j] = silu(sum_s part[s][r][j]) * sum_s part[s][r][F + j];  else (n_part = F):
+// a[r, j] = gelu(sum_s part[s][r][j]); a[r, j] is stored as column col0 + j of out, a storage-type
+// matrix of ld columns (col0 + F <= ld), row-major (kmajor = 0) or k-tile-major [ld/w][rows_alloc][w]
+// with w = kmajor (32 or 64; ld, col0 and F multiples of w).
 hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int splits, void *out,
-                          int rows, int F, int kmajor, int rows_alloc, hipStream_t s);
+                          int rows, int F, int col0, int ld, int kmajor, int rows_alloc, hipStream_t s);
 
 // out[r, c] = resid[r, c] + sum_{s < splits} part[s][r][c]  (resid float32, out storage type).
 hipError_t launch_resid_sum(int out_type, const float *resid, const float *part, int splits,
@@ -74,6 +75,14 @@ struct GemmPlan { int epi, m_tiles, n_tiles, splits, mbw, wn, per_xcd, grid; };
 // product plus a separate activation pass is estimated faster; n is then the product width:
 // 2F for SwiGLU).  n_out is the output width of the epilogue (F for the FFN up products).
 GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus);
+// A fused-activation FFN product (kEpiSwiGLU / kEpiGelu, bf16) whose fused plan needs more than one
+// round of `cus` weight stripes runs as two parts: the first cus stripes as one round of fused tiles
+// (*main, over the first n_main output columns), the remaining output columns as a split product
+// (*tail, kEpiPartial over their gate|up or up weight rows) whose partials an activation pass sums.
+// Returns n_main, or 0 (main and tail untouched) when the product runs whole.  Depends on the
+// weight shape only, never on m beyond the row tiles, which the tail takes from the main part (one
+// input layout serves both).
+int plan_gemm_tail(int type, int epi, int m, int n_out, int k, int cus, GemmPlan *main, GemmPlan *tail);
 // k depth of one LDS stage of a bf16 plan (32 or 64): the k-tile width of a k-tile-major A.
 int gemm_stage_depth(const GemmPlan &p);
 hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s);

@@ -184,7 +184,8 @@ __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erf
 
 template <typename Tout, bool GATED>
 __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int splits, Tout *out,
-                                                    int rows, int F, int kmajor, int rows_alloc) {
+                                                    int rows, int F, int col0, int ld, int kmajor,
+                                                    int rows_alloc) {
   const size_t n4 = (size_t)rows * F / 4;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= n4) return;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void ffn_act(const float *part, int split
   float v[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = GATED ? silu_f(a[e]) * u[e] : gelu_f(a[e]);
-  store4<Tout>(out + mat_index(r, c, F, kmajor, rows_alloc), v);   // 4 columns within one k-tile
+  store4<Tout>(out + mat_index(r, col0 + c, ld, kmajor, rows_alloc), v);   // 4 columns within one k-tile
 }
 
 template <typename Tres, typename Tout, bool LN, int NT>
@@ -250,15 +251,16 @@ hipError_t launch_norm_rows(int res_type, int out_type, bool layernorm, const vo
 }
 
 hipError_t launch_ffn_act(int out_type, bool gated, const float *part, int splits, void *out,
-                          int rows, int F, int kmajor, int rows_alloc, hipStream_t s) {
+                          int rows, int F, int col0, int ld, int kmajor, int rows_alloc, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (splits > kMaxSplits || F % 4) return hipErrorInvalidValue;
-  if (kmajor && ((kmajor != 32 && kmajor != 64) || F % kmajor || rows > rows_alloc))
+  if (splits > kMaxSplits || F % 4 || col0 % 4 || col0 < 0 || col0 + F > ld) return hipErrorInvalidValue;
+  if (kmajor && ((kmajor != 32 && kmajor != 64) || F % kmajor || col0 % kmajor || ld % kmajor ||
+                 rows > rows_alloc))
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(((size_t)rows * F / 4 + kThreads - 1) / kThreads));
 #define SARATHI_ACT(T, GT) \
   hipLaunchKernelGGL((ffn_act<T, GT>), grid, dim3(kThreads), 0, s, part, splits, static_cast<T *>(out), \
-                     rows, F, kmajor, rows_alloc)
+                     rows, F, col0, ld, kmajor, rows_alloc)
   if (out_type == kF32) {
     if (gated) SARATHI_ACT(float, true); else SARATHI_ACT(float, false);
   } else {

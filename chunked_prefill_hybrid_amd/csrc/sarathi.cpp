@@ -323,6 +323,8 @@ struct Plan {
   int stride_c;       // attention partials per (chunk row, head): 0 when no chunk row leaves partials
   int stride_d;       // attention partials per (decode row, head)
   GemmPlan qkv, o, up, down;
+  GemmPlan up_tail;   // with up_main > 0: the split product of the FFN up columns past up_main
+  int up_main;        // 0, or the FFN up columns of the fused part `up` (plan_gemm_tail)
   size_t n1, q, attn, h1, n2, act, part, part_o_c, part_ml_c, part_o_d, part_ml_d, total;
 };
 
@@ -420,11 +422,14 @@ Plan make_plan(const sarathi_layer_desc *d, const BatchView &b) {
   p.qkv = plan_gemm(ty, kEpiPartial, p.T, 3 * A, H, kPlanCUs);
   p.o = plan_gemm(ty, kEpiPartial, p.T, H, A, kPlanCUs);
   p.up = plan_gemm(ty, llama ? kEpiSwiGLU : kEpiGelu, p.T, F, H, kPlanCUs);
+  p.up_main = plan_gemm_tail(ty, llama ? kEpiSwiGLU : kEpiGelu, p.T, F, H, kPlanCUs, &p.up, &p.up_tail);
   p.down = plan_gemm(ty, kEpiPartial, p.T, H, F, kPlanCUs);
   const size_t up_cols = p.up.epi == kEpiPartial ? (llama ? 2 * (size_t)F : F) : 0;
+  const size_t tail_cols = p.up_main > 0 ? (llama ? 2 : 1) * (size_t)(F - p.up_main) : 0;
   const size_t part_elems = std::max({(size_t)p.qkv.splits * p.T * 3 * A, (size_t)p.o.splits * p.T * H,
                                       (size_t)p.down.splits * p.T * H,
-                                      (size_t)p.up.splits * p.T * up_cols});
+                                      (size_t)p.up.splits * p.T * up_cols,
+                                      p.up_main > 0 ? (size_t)p.up_tail.splits * p.T * tail_cols : 0});
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   p.n1 = take(R * H * el);
@@ -675,10 +680,23 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   if (p.up.epi == kEpiPartial) {
     g.part = part; g.n = llama ? 2 * F : F; g.n_w0 = F;
     HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.up, s));
-    HIP_TRY(launch_ffn_act(ty, llama, part, p.up.splits, act, T, F, kmajor_act, R, s));
+    HIP_TRY(launch_ffn_act(ty, llama, part, p.up.splits, act, T, F, 0, F, kmajor_act, R, s));
   } else {
-    g.out = act; g.ldo = F; g.n = F; g.out_kmajor = kmajor_act;
+    g.out = act; g.ldo = F; g.n = p.up_main > 0 ? p.up_main : F; g.out_kmajor = kmajor_act;
     HIP_TRY(launch_gemm(ty, p.up.epi, g, p.up, s));
+    if (p.up_main > 0) {
+      // the columns past up_main: split product of their weight rows, then the activation pass
+      const int n_tail = F - p.up_main;
+      const size_t wofs = (size_t)p.up_main * H * elem_size(ty);
+      GemmArgs t = g;
+      t.out = nullptr; t.ldo = 0; t.out_kmajor = 0;
+      t.w0 = static_cast<const char *>(g.w0) + wofs;
+      t.w1 = g.w1 ? static_cast<const char *>(g.w1) + wofs : nullptr;
+      t.part = part; t.n = llama ? 2 * n_tail : n_tail; t.n_w0 = n_tail;
+      HIP_TRY(launch_gemm(ty, kEpiPartial, t, p.up_tail, s));
+      HIP_TRY(launch_ffn_act(ty, llama, part, p.up_tail.splits, act, T, n_tail, p.up_main, F, kmajor_act,
+                             R, s));
+    }
   }
   HIP_TRY(mk.end(SARATHI_STAGE_FFN_UP, true));
   // 8. down projection (split partials), y = h1 + sum of the partials
@@ -772,6 +790,7 @@ sarathi_status describe_entry(const sarathi_layer_desc *d, const Batch *b, sarat
   out.o = gemm_info(p.o);
   out.up = gemm_info(p.up);
   out.down = gemm_info(p.down);
+  if (p.up_main > 0) out.up_tail = gemm_info(p.up_tail);
   out.workspace_bytes = p.total;
   *info = out;
   return SARATHI_OK;

@@ -420,8 +420,11 @@ typedef struct {
     int32_t max_key_splits;                      /* split partials per row and head */
     int32_t chunk_query_blocks;                  /* 16-query blocks per wave of the chunk attention (1 or 2; 1 when fused) */
     sarathi_gemm_plan qkv, o, up, down;          /* up: gate|up for LLAMA, up for GPT */
+    sarathi_gemm_plan up_tail;                   /* all zero, or: up covers the first 256 weight stripes
+                                                    (one round of fused tiles) and this split product
+                                                    the remaining FFN columns */
     uint64_t workspace_bytes;                    /* as the matching *_workspace_size */
-} sarathi_plan_info;     /* 160 bytes */
+} sarathi_plan_info;     /* 176 bytes */
 
 /* Fill *info for a forward over `batch`.  Errors: as the matching *_batch_check (without the x/y
  * requirement), or INVALID for a null info; *info is left unchanged then. */

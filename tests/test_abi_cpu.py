@@ -265,9 +265,10 @@ def gemms(info):
 
 def test_plan_info_layout():
     assert ctypes.sizeof(_abi.sarathi_gemm_plan) == 16
-    assert ctypes.sizeof(_abi.sarathi_plan_info) == 160
+    assert ctypes.sizeof(_abi.sarathi_plan_info) == 176
     assert _abi.sarathi_plan_info.chunk_splits.offset == 16
-    assert _abi.sarathi_plan_info.qkv.offset == 88 and _abi.sarathi_plan_info.workspace_bytes.offset == 152
+    assert _abi.sarathi_plan_info.qkv.offset == 88 and _abi.sarathi_plan_info.up_tail.offset == 152
+    assert _abi.sarathi_plan_info.workspace_bytes.offset == 168
 
 
 def test_plan_of_hybrid_batch(lib):
@@ -351,6 +352,26 @@ def test_plan_decode_key_split_counts(lib):
         n = L + 1
         expect = -(-n // 256) if n <= 2048 else -(-n // 1024)
         assert _abi.plan_describe(d, b).max_key_splits == expect == bench._split_count(n), L
+
+
+def test_plan_wide_ffn_main_and_tail(lib):
+    """A gate|up product of more than 256 weight stripes (llama-33b: F = 17920, 280 stripes of 64
+    columns) runs its first 256 stripes as one round of fused tiles and the other 1536 columns as a
+    split product, whatever the batch rows; narrower products run whole."""
+    d33 = desc(hidden=6656, n_heads=52, head_dim=128, ffn=17920, dtype=_abi.SARATHI_BF16, max_tokens=1024,
+               max_pos=2048)
+    tails = set()
+    for C, lens in ((512, (1024,) * 32), (0, (100,)), (257, (1024,) * 32), (1, ())):
+        b, keep = batch(C=C, off=0, cap=max(C, 1), lens=lens)
+        info = _abi.plan_describe(d33, b)
+        assert info.up.epilogue == 2 and info.up.col_tiles == 256 and info.up.k_splits == 1
+        t = info.up_tail
+        assert t.epilogue == 1 and t.col_tiles == 2 * 1536 // 128 and t.k_splits > 1
+        tails.add(t.k_splits)
+    assert len(tails) == 1                    # the tail's k-sum cut does not depend on the rows
+    b, keep = batch(C=256, off=768, cap=1024, lens=(1024,) * 18)
+    info = _abi.plan_describe(desc13b(), b)
+    assert info.up.col_tiles == 216 and info.up_tail.col_tiles == 0
 
 
 def test_plan_of_token_budget_batch(lib):

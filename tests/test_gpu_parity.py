@@ -18,6 +18,9 @@ pytestmark = pytest.mark.gpu
 MID = wl.LayerShape("mid-llama", "llama", 512, 4, 128, 1408, "bf16", 1e-6, 10000.0, None)
 MID_GPT = wl.LayerShape("mid-gpt", "gpt", 512, 4, 128, 1024, "bf16", 1e-5, 10000.0, None)
 MID_F32 = wl.LayerShape("mid-llama-f32", "llama", 512, 4, 128, 1408, "f32", 1e-6, 10000.0, None)
+# FFN products of more than 256 weight stripes: a fused main part and a split tail
+MID_WIDE_FFN = wl.LayerShape("mid-llama-wide-ffn", "llama", 512, 4, 128, 17920, "bf16", 1e-6, 10000.0, None)
+MID_GPT_WIDE_FFN = wl.LayerShape("mid-gpt-wide-ffn", "gpt", 512, 4, 128, 34816, "bf16", 1e-5, 10000.0, None)
 MID_D64 = wl.LayerShape("mid-llama-d64", "llama", 256, 4, 64, 704, "bf16", 1e-6, 10000.0, None)
 # A llama-7b-sized layer: at 400+ rows every one of its GEMMs takes one 576-row tile per column
 # stripe (32-deep stages)
@@ -169,6 +172,11 @@ def test_mid_fp32_llama():
     run_case(MID_F32, 100, 37, [0, 1, 63, 64, 300])
 
 
+@pytest.mark.parametrize("shape", [MID_WIDE_FFN, MID_GPT_WIDE_FFN], ids=["swiglu", "gelu"])
+def test_mid_bf16_wide_ffn(shape):
+    run_case(shape, 100, 37, [0, 1, 300])
+
+
 def test_mid_bf16_head_dim_64():
     run_case(MID_D64, 65, 200, [5, 511, 512, 1000])
 
@@ -193,8 +201,8 @@ def test_edge_batches(C, off, lens):
 # Invariants on the GPU
 # ------------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape,C", [(MID, 60), (MID_F32, 60), (BIG, 400)],
-                         ids=["bf16", "f32", "bf16-tall-tiles"])
+@pytest.mark.parametrize("shape,C", [(MID, 60), (MID_F32, 60), (BIG, 400), (MID_WIDE_FFN, 300)],
+                         ids=["bf16", "f32", "bf16-tall-tiles", "bf16-ffn-tail"])
 def test_decode_row_alone_equals_in_batch(shape, C):
     """A decode row run alone (one GEMM row, 288-row tiles with 64-deep stages) equals the same
     decode inside a batch, bit for bit; with C = 400 the batch's GEMMs take 576-row tiles with
