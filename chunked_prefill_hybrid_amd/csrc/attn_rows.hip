@@ -25,6 +25,13 @@ namespace sarathi {
 namespace {
 
 constexpr int kUnroll = 8;       // keys per lane and online-softmax step
+
+// c + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
 // Steps whose K/V loads the fused kernel issues together.  Its occupancy is set by the chunk work's
 // registers and LDS, so its decode waves are fewer; each keeps two steps of loads in flight.  The
 // arithmetic is the same step by step, so a decode row's result does not depend on which kernel
@@ -65,10 +72,16 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
   const int npass = (per + kAttnSplit - 1) / kAttnSplit;   // 1 .. kAttnLongPasses
   const int sub = lane % LPK, grp = lane / LPK;
 
+  // bf16: q stays packed and a lane's part of a score is four bf16-pair dot products (exact
+  // products, float32 sums), scaled once; float32: q scaled, one multiply-add per element.
+  constexpr bool kBf16 = sizeof(T) == 2;
+  const uint4 q_raw = ld16(q + (size_t)r * ld_q + h * D + sub * E);
   float qv[E];
-  unpack<T>(ld16(q + (size_t)r * ld_q + h * D + sub * E), qv);
+  if constexpr (!kBf16) {
+    unpack<T>(q_raw, qv);
 #pragma unroll
-  for (int e = 0; e < E; ++e) qv[e] *= qscale;
+    for (int e = 0; e < E; ++e) qv[e] *= qscale;
+  }
   const T *Kh = kPaged ? reinterpret_cast<const T *>(pool.k) + sub * E
                       : reinterpret_cast<const T *>(rr.k) + (size_t)h * rr.cap * D + sub * E;
   const T *Vh = kPaged ? reinterpret_cast<const T *>(pool.v) + sub * E
@@ -124,13 +137,22 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
         float cmax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-          float kv[E];
-          unpack<T>(kr[h * kUnroll + u], kv);
           float dot = 0.f;
+          if constexpr (kBf16) {
+            const uint4 kw = kr[h * kUnroll + u];
+            dot = dot2_bf16(kw.x, q_raw.x, dot);
+            dot = dot2_bf16(kw.y, q_raw.y, dot);
+            dot = dot2_bf16(kw.z, q_raw.z, dot);
+            dot = dot2_bf16(kw.w, q_raw.w, dot);
+          } else {
+            float kv[E];
+            unpack<T>(kr[h * kUnroll + u], kv);
 #pragma unroll
-          for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
+            for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
+          }
 #pragma unroll
           for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
+          if constexpr (kBf16) dot *= qscale;
           sc[u] = ok[h * kUnroll + u] ? dot : -INFINITY;
           cmax = fmaxf(cmax, sc[u]);
         }
