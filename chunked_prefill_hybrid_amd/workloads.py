@@ -197,11 +197,12 @@ def workload(key: str, **batch_changes) -> Workload:
 
 def sweep_changes(key: str) -> List[dict]:
     """The C or B sweep a workload is measured on, as BatchSpec field changes: chunk length C for
-    llama33b (tile quantization, with C = 257 one row past a tile), the number of piggybacked decodes B
-    for gpt3tp8 (the P:D sweep) and llama13b."""
+    llama33b (tile quantization: with its 32 decodes C = 257 is one row into a new 32-row step, C = 544
+    fills a 576-row GEMM tile and C = 545 is one row past it), the number of piggybacked decodes B for
+    gpt3tp8 (the P:D sweep) and llama13b."""
     b = WORKLOADS[key].batch
     if key == "llama33b":
-        return [dict(chunk_len=c, prompt_len=max(c, b.chunk_offset + c)) for c in (128, 256, 257, 512)]
+        return [dict(chunk_len=c, prompt_len=max(c, b.chunk_offset + c)) for c in (128, 256, 257, 512, 544, 545)]
     if key == "gpt3tp8":
         return [dict(n_decodes=n, decode_lens=(2048,) * n) for n in (1, 2, 4, 8, 16, 32, 64)]
     if key == "llama13b":

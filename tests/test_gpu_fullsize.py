@@ -42,7 +42,8 @@ def test_full_size_workload(key):
 @pytest.mark.parametrize("key,changes", [
     ("llama13b", dict(chunk_len=0)),                         # decode-only part
     ("llama13b", dict(n_decodes=0, decode_lens=())),         # chunk-only part
-    ("llama33b", dict(chunk_len=257, prompt_len=257)),       # tile-quantization point
+    ("llama33b", dict(chunk_len=257, prompt_len=257)),       # a new 32-row step (289 rows)
+    ("llama33b", dict(chunk_len=545, prompt_len=545)),       # one row past a 576-row GEMM tile
     ("gpt3tp8", dict(n_decodes=1, decode_lens=(2048,))),     # P:D sweep end point
 ])
 def test_full_size_sweep_points(key, changes):

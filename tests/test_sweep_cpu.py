@@ -7,7 +7,7 @@ from chunked_prefill_hybrid_amd import workloads as wl
 def test_sweep_points_are_valid_batches():
     for key, field, values in (("gpt3tp8", "n_decodes", [1, 2, 4, 8, 16, 32, 64]),
                                ("llama13b", "n_decodes", [1, 4, 8, 18, 32, 64]),
-                               ("llama33b", "chunk_len", [128, 256, 257, 512])):
+                               ("llama33b", "chunk_len", [128, 256, 257, 512, 544, 545])):
         pts = wl.sweep_changes(key)
         assert [p[field] for p in pts] == values
         for ch in pts:
