@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
 // The chunk items are few and latency-bound (one 64-query block each, walking its key range tile by
 // tile) and leave most compute units idle; the memory-bound decode splits fill them, so the two kinds
 // of attention of a hybrid batch overlap instead of running one after the other.
-template <int D, bool kPaged>
+template <int D, bool kPaged, int RB>
 __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int nh, ChunkSet cs,
                                                   PagePool pool, bf16_t *out, OutLayout olay,
                                                   float chunk_qscale, int n_split, AttnParts parts,
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int
   __shared__ float sm[4], sl[4], so[4 * D];
   const int b = blockIdx.x;
   if (b < chunk_grid) {
-    chunk_attn_item<D, kPaged, 1>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, olay,
+    chunk_attn_item<D, kPaged, RB>(chunk_item_of(b, per_xcd), q, ld_q, nh, cs, pool, out, olay,
                                chunk_qscale, n_split, parts.stride_c, parts.o_c, parts.ml_c, k0s, v0s,
                                k1s, v1s, k2s, v2s);
   } else {
@@ -248,17 +248,17 @@ __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int
   }
 }
 
-template <int D, bool kPaged>
+template <int D, bool kPaged, int RB>
 hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const PagePool &pool, void *out,
                      OutLayout olay, int n_split, const AttnParts &parts, const DecodeGroup &dg, int dec_row0,
                      int dec_rows, hipStream_t s) {
   int items = 0;
-  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh, kBQ);
+  for (int j = 0; j < cs.n; ++j) items += chunk_items(cs.len[j], cs.split[j], nh, kBQ * RB);
   const int per_xcd = (items + 7) / 8;
   const int chunk_grid = 8 * per_xcd;
   const int grid = chunk_grid + dec_rows * parts.stride_d * nh;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fused<D, kPaged>), dim3(grid), dim3(256), 0, s,
+  hipLaunchKernelGGL((attn_fused<D, kPaged, RB>), dim3(grid), dim3(256), 0, s,
                      static_cast<const bf16_t *>(q), ld_q, nh, cs, pool, static_cast<bf16_t *>(out),
                      olay, qscale, n_split, parts, per_xcd, chunk_grid, dg, dec_row0, dec_rows,
                      qscale);
@@ -526,15 +526,19 @@ hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const Chunk
   for (int j = 0; j < cs.n; ++j)
     if (cs.split[j] < 1 || cs.split[j] > n_split) return hipErrorInvalidValue;
   const bool paged = pool.k != 0;
-#define SARATHI_FUSED(D, P) \
-  return run_fused<D, P>(q, ld_q, nh, cs, pool, out, olay, n_split, parts, dg, dec_row0, dec_rows, s)
+  // two 16-query blocks per wave: contiguous caches only
+  if (cs.qblocks != 1 && !(cs.qblocks == 2 && !paged)) return hipErrorInvalidValue;
+#define SARATHI_FUSED(D, P, RB) \
+  return run_fused<D, P, RB>(q, ld_q, nh, cs, pool, out, olay, n_split, parts, dg, dec_row0, dec_rows, s)
   if (d == 128) {
-    if (paged) SARATHI_FUSED(128, true);
-    SARATHI_FUSED(128, false);
+    if (paged) SARATHI_FUSED(128, true, 1);
+    if (cs.qblocks == 2) SARATHI_FUSED(128, false, 2);
+    SARATHI_FUSED(128, false, 1);
   }
   if (d == 64) {
-    if (paged) SARATHI_FUSED(64, true);
-    SARATHI_FUSED(64, false);
+    if (paged) SARATHI_FUSED(64, true, 1);
+    if (cs.qblocks == 2) SARATHI_FUSED(64, false, 2);
+    SARATHI_FUSED(64, false, 1);
   }
 #undef SARATHI_FUSED
   return hipErrorInvalidValue;

@@ -179,8 +179,9 @@ hipError_t launch_attn_chunk(int d, const void *q, int ld_q, int nh, const Chunk
 // The chunk attention of every chunk of the set and the split-KV attention of decode rows
 // [dec_row0, dec_row0 + dec_rows) (one decode group, dg) in one launch (bf16).  Chunk rows are
 // handled as by launch_attn_chunk with n_split key splits (partials in region c of `parts` when
-// n_split > 1, stride_c = n_split); decode rows write split partials to region d as
-// launch_attn_rows does (stride_d, first row of the region = cs.rows).
+// n_split > 1, stride_c = n_split) and cs.qblocks 16-query blocks per wave (2: contiguous caches
+// only); decode rows write split partials to region d as launch_attn_rows does (stride_d, first row
+// of the region = cs.rows).
 hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const ChunkSet &cs,
                              const PagePool &pool, void *out, OutLayout olay, int n_split,
                              const AttnParts &parts, const DecodeGroup &dg, int dec_row0,

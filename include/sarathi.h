@@ -418,7 +418,7 @@ typedef struct {
     int32_t fused_attention;                     /* 1: chunk and decode attention in one launch */
     int32_t chunk_splits[SARATHI_MAX_CHUNKS];    /* key-range splits of each chunk's query blocks */
     int32_t max_key_splits;                      /* split partials per row and head */
-    int32_t chunk_query_blocks;                  /* 16-query blocks per wave of the chunk attention (1 or 2; 1 when fused) */
+    int32_t chunk_query_blocks;                  /* 16-query blocks per wave of the chunk attention (1 or 2) */
     sarathi_gemm_plan qkv, o, up, down;          /* up: gate|up for LLAMA, up for GPT */
     sarathi_gemm_plan up_tail;                   /* all zero, or: up covers the first 256 weight stripes
                                                     (one round of fused tiles) and this split product

@@ -313,7 +313,8 @@ def test_plan_splits_long_chunk(lib):
 def test_plan_two_query_blocks_per_wave(lib):
     """A separate chunk launch takes two 16-query blocks per wave when its items would otherwise need
     more than one round of the resident workgroups: the 13B long-context chunk and the 20-head GPU
-    test batches do; fused launches, short chunks and paged caches keep one."""
+    test batches do; short chunks and paged caches keep one.  A fused launch takes two when it has
+    at least 128 64-query items."""
     b, keep = batch(C=512, off=7680, cap=8192, lens=(4000,) * 48)
     assert _abi.plan_describe(desc13b(), b).chunk_query_blocks == 2
     for hd in (128, 64):
@@ -326,7 +327,11 @@ def test_plan_two_query_blocks_per_wave(lib):
             assert info.fused_attention == 0 and info.chunk_query_blocks == 2, (hd, chunks, lens)
             assert info.chunk_splits[0] == 3
     b, keep = batch(C=256, off=768, cap=1024, lens=(1024,) * 18, caps=[1025] * 18)
-    assert _abi.plan_describe(desc13b(), b).chunk_query_blocks == 1                 # fused
+    info = _abi.plan_describe(desc13b(), b)
+    assert info.fused_attention == 1 and info.chunk_query_blocks == 2              # fused, 160 items
+    b, keep = batch(C=64, off=768, cap=1024, lens=(1024,) * 18, caps=[1025] * 18)
+    info = _abi.plan_describe(desc13b(), b)
+    assert info.fused_attention == 1 and info.chunk_query_blocks == 1              # fused, 40 items
     b, keep = multi(chunks=((94, 930, 1024), (300, 0, 300), (100, 0, 1024)), lens=(1024,) * 12)
     assert _abi.plan_describe(desc13b(), b).chunk_query_blocks == 1                 # short chunks
     b, keep = paged(chunks=((512, 7680, 512),), lens=(), dec_entries=(), pool=(addr(60), addr(61), 1000, 16))
