@@ -332,6 +332,12 @@ def test_plan_two_query_blocks_per_wave(lib):
     b, keep = batch(C=64, off=768, cap=1024, lens=(1024,) * 18, caps=[1025] * 18)
     info = _abi.plan_describe(desc13b(), b)
     assert info.fused_attention == 1 and info.chunk_query_blocks == 1              # fused, 40 items
+    for hd in (128, 64):   # the two-block fused cases of test_gpu_multi.py
+        d = desc(hidden=20 * hd, n_heads=20, head_dim=hd, ffn=1024, dtype=_abi.SARATHI_BF16, max_tokens=1024,
+                 max_pos=1024)
+        b, keep = multi(chunks=((300, 50, 350), (200, 0, 200)), lens=(40, 500))
+        info = _abi.plan_describe(d, b)
+        assert info.fused_attention == 1 and info.chunk_query_blocks == 2, hd
     b, keep = multi(chunks=((94, 930, 1024), (300, 0, 300), (100, 0, 1024)), lens=(1024,) * 12)
     assert _abi.plan_describe(desc13b(), b).chunk_query_blocks == 1                 # short chunks
     b, keep = paged(chunks=((512, 7680, 512),), lens=(), dec_entries=(), pool=(addr(60), addr(61), 1000, 16))

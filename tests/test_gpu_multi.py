@@ -74,6 +74,8 @@ def run_case(shape, chunk_specs, dec_lens, seed=0, label=None):
     (WIDE, [(1024, 2000)], [30]),                                  # 128-query blocks, 3 key splits
     (WIDE, [(1000, 2000), (37, 100)], []),                         # the same, ragged, splits 3 and 1
     (WIDE_D64, [(1000, 2000), (37, 100)], [30]),                   # d = 64
+    (WIDE, [(300, 50), (200, 0)], [40, 500]),                      # fused launch, two blocks per wave
+    (WIDE_D64, [(300, 50), (200, 0)], [40, 500]),                  # the same, d = 64
 ])
 def test_multi_bf16(shape, chunks, lens):
     run_case(shape, chunks, lens)
