@@ -12,12 +12,14 @@
 // the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 288 rows x 32 columns.  A and W
 // k-tiles (64 deep for tiles of up to 288 rows, 32 deep above) travel from global memory straight
 // into LDS (global_load_lds_dwordx4: no staging registers, no LDS store instructions) through a ring
-// of up to 3 stages, so the loads of tile j + 2 are in flight while tile j is multiplied.  The loads are what bounds this kernel at
-// small batches: a compute unit keeps only ~10 KB of reads in flight, so its fetch rate is set by
-// memory latency, and the A tile is fetched by every workgroup.  When the weight stripes alone do
-// not fill the 256 compute units, the k range is split: each split writes a float32 partial and the
-// kernel that consumes the product sums the partials in a fixed order (deterministic, no atomics).
-// Workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight stripe.
+// of as many stages as fit (up to 5), so the loads of the next tiles are in flight while tile j is
+// multiplied.  The loads are what bounds this kernel: a compute unit keeps only ~10 KB of reads in
+// flight, so its fetch rate is set by memory latency, and the A tile is fetched by every workgroup.
+// When the weight stripes alone do not fill the 256 compute units, the k range is split: each split
+// writes a float32 partial and the kernel that consumes the product sums the partials in a fixed
+// order (deterministic, no atomics); a fused-activation product with more stripes than one round
+// runs its first 256 stripes fused and the rest split (plan_gemm_tail).  Workgroup b runs on XCD
+// b % 8; consecutive workgroups of one XCD share a weight stripe.
 // fp32 path: a plain FMA tile kernel (exact float32 products, used by the float32 layer mode).
 #include <math.h>
 
