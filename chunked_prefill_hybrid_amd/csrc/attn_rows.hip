@@ -216,9 +216,12 @@ __global__ __launch_bounds__(256) void attn_rows_split(const T *q, int ld_q, int
                                                        int stride, int prow0,
                                                        float *part_o, float *part_ml, float qscale) {
   __shared__ float sm[4], sl[4], so[4 * D];
-  split_attn_item<T, D, kChunkRows, kPaged>(row0 + blockIdx.x, blockIdx.y, blockIdx.z, q, ld_q, nh, cs,
-                                            dg, pool, stride, prow0, part_o, part_ml, qscale, sm, sl,
-                                            so);
+  // Decode rows (at most kMaxDecodesPerLaunch): grid (heads, rows, splits), so a row's heads run
+  // together and the splits come last; chunk rows (any number): grid (rows, splits, heads).
+  const int r = kChunkRows ? blockIdx.x : blockIdx.y, s = kChunkRows ? blockIdx.y : blockIdx.z,
+            h = kChunkRows ? blockIdx.z : blockIdx.x;
+  split_attn_item<T, D, kChunkRows, kPaged>(row0 + r, s, h, q, ld_q, nh, cs, dg, pool, stride, prow0,
+                                            part_o, part_ml, qscale, sm, sl, so);
 }
 
 // Chunk and decode attention in one launch.  Workgroups [0, chunk_grid) run the chunk work items
@@ -240,10 +243,10 @@ __global__ __launch_bounds__(256) void attn_fused(const bf16_t *q, int ld_q, int
                                chunk_qscale, n_split, parts.stride_c, parts.o_c, parts.ml_c, k0s, v0s,
                                k1s, v1s, k2s, v2s);
   } else {
-    const int d = b - chunk_grid;
-    const int r = d % dec_rows, rest = d / dec_rows;
+    const int d = b - chunk_grid;   // heads fastest, then rows, then splits
+    const int hd = d % nh, rest = d / nh;
     split_attn_item<bf16_t, D, false, kPaged, kPrefetchFused>(
-        dec_row0 + r, rest % parts.stride_d, rest / parts.stride_d, q, ld_q, nh, cs, dg, pool,
+        dec_row0 + rest % dec_rows, rest / dec_rows, hd, q, ld_q, nh, cs, dg, pool,
         parts.stride_d, cs.rows, parts.o_d, parts.ml_d, dec_qscale, sm, sl, so);
   }
 }
@@ -444,9 +447,9 @@ hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, cons
                      const DecodeGroup &dg, const PagePool &pool, int stride, int prow0, float *po,
                      float *pml, hipStream_t s) {
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  const dim3 grid(n_rows, stride, nh);
 #define SARATHI_SPLIT(CR, PG)                                                                   \
-  hipLaunchKernelGGL((attn_rows_split<T, D, CR, PG>), grid, dim3(256), 0, s,                   \
+  hipLaunchKernelGGL((attn_rows_split<T, D, CR, PG>), CR ? dim3(n_rows, stride, nh) : dim3(nh, n_rows, stride), \
+                     dim3(256), 0, s,                                                            \
                      static_cast<const T *>(q), ld_q, nh, row0, cs, dg, pool, stride, prow0, po, pml, qscale)
   const bool chunk_rows = row0 < cs.rows, paged = pool.k != 0;
   if (chunk_rows) {
