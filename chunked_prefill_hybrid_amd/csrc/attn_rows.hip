@@ -11,12 +11,16 @@
 // Memory-bound design: the head-major cache makes each (request, head) key stream contiguous; a key
 // row of d elements is read by d*size/16 lanes with 16-byte loads, so one wave load instruction covers
 // 4 bf16 keys of d=128 (1 KiB).  Each wave streams its keys in steps of 8 loads of K and 8 of V per
-// lane (an online softmax across steps), the four waves of a workgroup merge through LDS, and each
-// workgroup writes one split partial (max m and sum l in the log2 domain, unnormalised output).
+// lane (an online softmax across steps; the next step's K loads go out once a step's scores are
+// taken and its V loads once the step's accumulation is done, so loads are always in flight), the
+// four waves of a workgroup merge through LDS, and each workgroup writes one split partial (max m
+// and sum l in the log2 domain, unnormalised output).
 // With a paged cache a key row is located through the request's block table (one table entry per
 // page, held in a lane of the wave and shuffled to the lanes reading that page); a page's
 // [page_size, d] slab per head is contiguous, so each 16-byte load stays a full-row read.
 #include <math.h>
+
+#include <type_traits>
 
 #include "attn_chunk_body.h"
 #include "kernels.h"
@@ -31,6 +35,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
                                          false);
+}
+// f(integral_constant<int, I>) for I = B .. E - 1, in order.
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 // Steps whose K/V loads the fused kernel issues together.  Its occupancy is set by the chunk work's
 // registers and LDS, so its decode waves are fewer; each keeps two steps of loads in flight.  The
@@ -59,7 +70,7 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
   const int n_keys = rr.pos + 1;
   const int nsp = attn_splits(n_keys);
   const size_t pidx = ((size_t)(r - prow0) * nh + h) * stride + s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (s >= nsp) {  // no keys for this split: an empty partial
     if (tid == 0) {
       part_ml[2 * pidx] = -INFINITY;
@@ -106,74 +117,145 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
 
+  // Element offset of key j in this wave's K or V stream; `pass` (a compile-time index) names the
+  // page-table register of the pass that key j belongs to.
+  auto key_off = [&](auto pass_, int j) -> size_t {
+    constexpr int pass = decltype(pass_)::value;
+    if (!kPaged) return (size_t)j * D;
+    const int page = __shfl(tbl[pass], min((j >> pool.shift) - pg0[pass], kWave - 1), kWave);
+    return paged_off(page, h, j, nh, pool.shift, D);
+  };
+  // One online-softmax step over kUnroll loads of keys (ok[u]: load u holds a key of the split): the
+  // scores from the step's K registers, then the rescale and the V accumulation.
+  float sc[kUnroll], m_new = 0.f;
+  auto scores = [&](const uint4 *kw, const bool *ok) {
+    float cmax = -INFINITY;
 #pragma unroll
-  for (int pass = 0; pass < kAttnLongPasses; ++pass) {
-    if (pass >= npass) break;
-    const int wbeg = k_begin + (4 * pass + wave) * KPW;
-    auto key_off = [&](int j) -> size_t {
-      if (!kPaged) return (size_t)j * D;
-      const int page = __shfl(tbl[pass], min((j >> pool.shift) - pg0[pass], kWave - 1), kWave);
-      return paged_off(page, h, j, nh, pool.shift, D);
-    };
-    for (int c0 = 0; c0 < NIT; c0 += U) {
-      if (wbeg + c0 * KPI >= k_end) break;
-      uint4 kr[U], vr[U];
-      bool ok[U];
-      size_t ko[U];
+    for (int u = 0; u < kUnroll; ++u) {
+      float dot = 0.f;
+      if constexpr (kBf16) {
+        dot = dot2_bf16(kw[u].x, q_raw.x, dot);
+        dot = dot2_bf16(kw[u].y, q_raw.y, dot);
+        dot = dot2_bf16(kw[u].z, q_raw.z, dot);
+        dot = dot2_bf16(kw[u].w, q_raw.w, dot);
+      } else {
+        float kv[E];
+        unpack<T>(kw[u], kv);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = wbeg + (c0 + u) * KPI + grp;
-        ok[u] = j < k_end;
-        ko[u] = key_off(j);
-        kr[u] = ok[u] ? ld16_stream(Kh + ko[u]) : make_uint4(0, 0, 0, 0);
+        for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        vr[u] = ok[u] ? ld16_stream(Vh + ko[u]) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int h = 0; h < P; ++h) {
-        if (h > 0 && wbeg + (c0 + h * kUnroll) * KPI >= k_end) break;   // the steps one at a time
-        float sc[kUnroll];
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          float dot = 0.f;
-          if constexpr (kBf16) {
-            const uint4 kw = kr[h * kUnroll + u];
-            dot = dot2_bf16(kw.x, q_raw.x, dot);
-            dot = dot2_bf16(kw.y, q_raw.y, dot);
-            dot = dot2_bf16(kw.z, q_raw.z, dot);
-            dot = dot2_bf16(kw.w, q_raw.w, dot);
-          } else {
-            float kv[E];
-            unpack<T>(kr[h * kUnroll + u], kv);
-#pragma unroll
-            for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kv[e], dot);
-          }
-#pragma unroll
-          for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
-          if constexpr (kBf16) dot *= qscale;
-          sc[u] = ok[h * kUnroll + u] ? dot : -INFINITY;
-          cmax = fmaxf(cmax, sc[u]);
-        }
-        cmax = wave_max(cmax, LPK);
-        const float m_new = fmaxf(m_run, cmax);
-        const float corr = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-        l_run *= corr;
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] *= corr;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const float p = ok[h * kUnroll + u] ? exp2f(sc[u] - m_new) : 0.f;
-          l_run += p;
-          float vv[E];
-          unpack<T>(vr[h * kUnroll + u], vv);
-#pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[e], o[e]);
-        }
-        m_run = m_new;
-      }
+      for (int m = LPK / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
+      if constexpr (kBf16) dot *= qscale;
+      sc[u] = ok[u] ? dot : -INFINITY;
+      cmax = fmaxf(cmax, sc[u]);
     }
+    cmax = wave_max(cmax, LPK);
+    m_new = fmaxf(m_run, cmax);
+  };
+  auto accumulate = [&](const uint4 *vw, const bool *ok) {
+    const float corr = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    l_run *= corr;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float p = ok[u] ? exp2f(sc[u] - m_new) : 0.f;
+      l_run += p;
+      float vv[E];
+      unpack<T>(vw[u], vv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[e], o[e]);
+      if constexpr (P == 1 && !kPaged) __builtin_amdgcn_sched_barrier(0);   // one key's values at a time
+    }
+    m_run = m_new;
+  };
+
+  if constexpr (P == 1 && !kPaged) {
+    // Software-pipelined walk: the wave's steps in key order (pass by pass), the K loads of step
+    // t + 1 issued as soon as step t's scores are taken and its V loads as soon as step t's
+    // accumulation is done, so some of the wave's loads are always in flight.  (Paged caches take
+    // the walk below: their page lookups would need more registers than four workgroups per compute
+    // unit leave.)
+    constexpr int SPP = NIT / kUnroll;               // steps per pass
+    constexpr int kSteps = kAttnLongPasses * SPP;
+    auto step_key = [&](int t) {
+      const int pass = t / SPP;
+      return k_begin + (4 * pass + wave) * KPW + (t - pass * SPP) * kUnroll * KPI;
+    };
+    int n_steps = 0;   // first keys rise with t, so the non-empty steps are a prefix
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) n_steps += (t < npass * SPP && step_key(t) < k_end) ? 1 : 0;
+    uint4 kr[kUnroll], vr[kUnroll];
+    // Loads of step t into dst from the K or V stream.  Every load is issued, so the wait before a
+    // step's use can count the loads issued after it: a key past the split's end reads the split's
+    // last key instead (its score is masked), and a step past the wave's last (t >= n_steps) reads
+    // this lane's q piece, a cache hit (the values are not used).
+    const T *q_lane = q + (size_t)r * ld_q + h * D + sub * E;
+    auto load = [&](auto t_, uint4 *dst, const T *base) {
+      constexpr int t = decltype(t_)::value;
+      const bool real = t < n_steps;
+      int j0 = step_key(t) + grp;
+      // An opaque copy: the V loads recompute their offsets instead of holding the K loads' offsets
+      // in registers across the accumulation.
+      asm volatile("" : "+v"(j0));
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = min(j0 + u * KPI, k_end - 1);
+        dst[u] = ld16_stream(real ? base + (size_t)j * D : q_lane);
+      }
+    };
+    // The walk is unrolled (steps past n_steps are skipped); the scheduling barriers keep each step's
+    // four phases in order, since the compiler would otherwise hoist the next step's loads above the
+    // arithmetic and hold two steps in registers.
+    load(std::integral_constant<int, 0>{}, kr, Kh);
+    load(std::integral_constant<int, 0>{}, vr, Vh);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, kSteps>([&](auto t_) {
+      constexpr int t = decltype(t_)::value;
+      if (t < n_steps) {
+        bool ok[kUnroll];
+        const int j0 = step_key(t) + grp;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) ok[u] = j0 + u * KPI < k_end;
+        scores(kr, ok);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (t + 1 < kSteps) load(std::integral_constant<int, t + 1>{}, kr, Kh);
+        __builtin_amdgcn_sched_barrier(0);
+        accumulate(vr, ok);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (t + 1 < kSteps) load(std::integral_constant<int, t + 1>{}, vr, Vh);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  } else {
+    // P steps of loads issued together, then the steps one at a time.
+    static_for<0, kAttnLongPasses>([&](auto pass_) {
+      constexpr int pass = decltype(pass_)::value;
+      if (pass >= npass) return;
+      const int wbeg = k_begin + (4 * pass + wave) * KPW;
+      for (int c0 = 0; c0 < NIT; c0 += U) {
+        if (wbeg + c0 * KPI >= k_end) break;
+        uint4 kr[U], vr[U];
+        bool ok[U];
+        size_t ko[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {   // a key past the split's end reads its last key (masked)
+          const int j = wbeg + (c0 + u) * KPI + grp;
+          ok[u] = j < k_end;
+          ko[u] = key_off(pass_, min(j, k_end - 1));
+          kr[u] = ld16_stream(Kh + ko[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) vr[u] = ld16_stream(Vh + ko[u]);
+#pragma unroll
+        for (int st = 0; st < P; ++st) {
+          if (st > 0 && wbeg + (c0 + st * kUnroll) * KPI >= k_end) break;   // the steps one at a time
+          scores(kr + st * kUnroll, ok + st * kUnroll);
+          accumulate(vr + st * kUnroll, ok + st * kUnroll);
+        }
+      }
+    });
   }
   // Sum over the key groups of the wave (lanes with equal `sub`); scores were replicated per group.
   l_run = wave_sum(l_run, LPK);
@@ -197,15 +279,39 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
       w[i] = (sm[i] == -INFINITY) ? 0.f : exp2f(sm[i] - M);
       L = fmaf(sl[i], w[i], L);
     }
-    for (int c = lane; c < D; c += kWave) {
-      float acc = 0.f;
+    // Lane l writes columns CPL l .. CPL l + CPL - 1 with one store.  A long split's partial is
+    // stored non-temporally: written back from the L2 at random times, partials slow the cache
+    // stream around them (a load-only replay of the long-context grid: 688 us without the partial
+    // writes, 710 us with plain stores, 697 us with non-temporal ones), while short splits' partials
+    // are better kept in the L2 for the merge that follows.
+    constexpr int CPL = D / kWave;
+    typedef float cvec_t __attribute__((ext_vector_type(CPL)));
+    cvec_t acc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = (w[i] != 0.f) ? fmaf(so[i * D + c], w[i], acc) : acc;
-      part_o[pidx * D + c] = acc;
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane * CPL + j;
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a = (w[i] != 0.f) ? fmaf(so[i * D + c], w[i], a) : a;
+      acc[j] = a;
     }
-    if (lane == 0) {
-      part_ml[2 * pidx] = M;
-      part_ml[2 * pidx + 1] = L;
+    cvec_t *dst = reinterpret_cast<cvec_t *>(&part_o[pidx * D + lane * CPL]);
+    if (npass > 1) {
+      __builtin_nontemporal_store(acc, dst);
+      if (lane == 0) {
+        __builtin_nontemporal_store(M, &part_ml[2 * pidx]);
+        __builtin_nontemporal_store(L, &part_ml[2 * pidx + 1]);
+      }
+    } else {
+      // (The empty asm statements keep the compiler from merging these stores with the
+      // non-temporal ones above, which would drop the non-temporal hint.)
+      asm volatile("" ::: "memory");
+      *dst = acc;
+      if (lane == 0) {
+        part_ml[2 * pidx] = M;
+        part_ml[2 * pidx + 1] = L;
+      }
+      asm volatile("" ::: "memory");
     }
   }
 }
