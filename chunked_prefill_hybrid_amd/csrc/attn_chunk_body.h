@@ -232,8 +232,7 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      tmax = max_xor(max_xor(tmax, 16), 32);
       // The exponent base m_run moves only when a tile's maximum exceeds it by more than kRebase (in
       // log2 units): probabilities then stay below 2^kRebase, well inside float32 and bfloat16
       // range, and the running sums are rescaled on a few tiles instead of on every tile with a new
@@ -322,8 +321,7 @@ __device__ __forceinline__ void chunk_attn_item(int item, const bf16_t *q, int l
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float l = l_run[rb];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    l = sum_xor(sum_xor(l, 16), 32);
     const int qr = my_q[rb];
     if (ns > 1) {   // a split chunk: partials for attn_combine (an unsplit one writes its rows)
       if (qr < C) {

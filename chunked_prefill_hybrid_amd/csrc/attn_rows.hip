@@ -499,8 +499,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
     }
     M = fmaxf(M, m[k]);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  M = wave_max(M);
   // A row's non-empty splits come first (l >= 1 for each: its largest score contributes 2^0); the
   // empty ones after them hold no output, so only the leading non-empty splits are read.
   int n_keyed = 0;
@@ -516,8 +515,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
     w[k] = l[k] > 0.f ? exp2f(m[k] - M) : 0.f;
     L = fmaf(l[k], w[k], L);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, kWave);
+  L = wave_sum(L);
   constexpr int PER = D / kWave;
   float acc[PER] = {};
   constexpr int kGroup = 4;

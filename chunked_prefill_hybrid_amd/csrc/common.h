@@ -123,17 +123,45 @@ __host__ __device__ __forceinline__ size_t out_index(const OutLayout &o, int r, 
   return mat_index(r, c, o.ld, o.kw, o.rows_alloc);
 }
 
-// Butterfly reductions over the lanes whose index differs only in the bits of [lo_mask, 32].
+// This lane's value and that of lane l ^ 32 (swap32) or l ^ 16 (swap16), through gfx950's permlane
+// swaps: VALU instructions, where a shuffle through ds_bpermute takes an LDS round trip.  The pair
+// comes back in a lane-dependent order (measured with an in-bounds probe: with both operands v,
+// permlane32_swap gives lanes 0..31 (v[l], v[l + 32]) and lanes 32..63 (v[l - 32], v[l]);
+// permlane16_swap gives the even 16-lane rows (v[l], v[l + 16]) and the odd ones (v[l - 16], v[l])),
+// so only commutative merges use them: the sum or maximum is then the same as own op partner.
+struct LanePair {
+  float a, b;
+};
+__device__ __forceinline__ LanePair swap32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+__device__ __forceinline__ LanePair swap16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+__device__ __forceinline__ float sum_xor(float v, int m) {
+  if (m == 32) { const LanePair p = swap32(v); return p.a + p.b; }
+  if (m == 16) { const LanePair p = swap16(v); return p.a + p.b; }
+  return v + __shfl_xor(v, m, kWave);
+}
+__device__ __forceinline__ float max_xor(float v, int m) {
+  if (m == 32) { const LanePair p = swap32(v); return fmaxf(p.a, p.b); }
+  if (m == 16) { const LanePair p = swap16(v); return fmaxf(p.a, p.b); }
+  return fmaxf(v, __shfl_xor(v, m, kWave));
+}
+
+// Butterfly reductions over the lanes whose index differs only in the bits of [from, 32].
 __device__ __forceinline__ float wave_sum(float v, int from = 1) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1)
-    if (m >= from) v += __shfl_xor(v, m, kWave);
+    if (m >= from) v = sum_xor(v, m);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v, int from = 1) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1)
-    if (m >= from) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    if (m >= from) v = max_xor(v, m);
   return v;
 }
 
