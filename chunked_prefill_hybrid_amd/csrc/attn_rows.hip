@@ -382,8 +382,9 @@ constexpr int kCombineWaves = 4;
 constexpr int kCombineSlots = kMaxKeySplits / kWave;   // splits per lane
 constexpr int kFewSplits = 8;
 
-// The merge of a chunk row's ns <= kFewSplits partials, all of which the chunk kernel wrote (o is
-// finite, l = 0 for a split past the query's position).  Every load is issued at once: each lane
+// The merge of ns <= kFewSplits partials of one (row, head).  Every (m, l) pair is written (l = 0
+// for a split with no keys of the row), but a split with l = 0 may have left its o slot unwritten,
+// so such a split is skipped rather than multiplied by 0.  Every load is issued at once: each lane
 // reads all (m, l) pairs and one 4-column piece of o from each of its splits; the wave's lanes form
 // SPL groups of D / 4, group g taking splits g, g + SPL, ... (summed in that order, then the groups
 // in order g = 0, 1, ...).
@@ -421,16 +422,19 @@ __device__ __forceinline__ void combine_few(int ns, size_t base, int r, int h, c
     float ws = 0.f;
 #pragma unroll
     for (int s = 0; s < kFewSplits; ++s) ws = (s == j * SPL + grp) ? w[s] : ws;
-    acc[0] = fmaf(ws, ov[j].x, acc[0]);
-    acc[1] = fmaf(ws, ov[j].y, acc[1]);
-    acc[2] = fmaf(ws, ov[j].z, acc[2]);
-    acc[3] = fmaf(ws, ov[j].w, acc[3]);
+    if (ws != 0.f) {
+      acc[0] = fmaf(ws, ov[j].x, acc[0]);
+      acc[1] = fmaf(ws, ov[j].y, acc[1]);
+      acc[2] = fmaf(ws, ov[j].z, acc[2]);
+      acc[3] = fmaf(ws, ov[j].w, acc[3]);
+    }
   }
-  // Groups in order: after step m, group 0 holds the sum of groups 0 .. 2^(m+1) - 1.
+  // Groups in order: after step m, group 0 holds the sum of groups 0 .. 2^(m+1) - 1 (each step adds
+  // the group LPS 2^m lanes up, through sum_xor: the same sum as a shuffle down).
 #pragma unroll
   for (int o = LPS; o < kWave; o <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += __shfl_down(acc[e], o, kWave);
+    for (int e = 0; e < 4; ++e) acc[e] = sum_xor(acc[e], o);
   }
   if (grp == 0) {   // 4 consecutive columns, within one k-tile of a k-tile-major output
     const float inv = 1.0f / L;
@@ -482,6 +486,10 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
     part_o = parts.o_d;
     part_ml = parts.ml_d;
     n_used = parts.stride_d;
+    if (n_used <= kFewSplits) {   // every decode of the group has at most this many splits
+      combine_few<T, D>(n_used, base, r, h, part_o, part_ml, out, olay);
+      return;
+    }
   }
   float m[kCombineSlots], l[kCombineSlots], w[kCombineSlots];
   float M = -INFINITY;
