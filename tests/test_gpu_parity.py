@@ -201,15 +201,20 @@ def test_edge_batches(C, off, lens):
 # Invariants on the GPU
 # ------------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape,C", [(MID, 60), (MID_F32, 60), (BIG, 400), (MID_WIDE_FFN, 300)],
-                         ids=["bf16", "f32", "bf16-tall-tiles", "bf16-ffn-tail"])
-def test_decode_row_alone_equals_in_batch(shape, C):
+@pytest.mark.parametrize("shape,C,lens", [(MID, 60, [4, 250, 31]), (MID_F32, 60, [4, 250, 31]),
+                                           (BIG, 400, [4, 250, 31]), (MID_WIDE_FFN, 300, [4, 250, 31]),
+                                           (MID, 60, [2500, 4, 6001])],
+                         ids=["bf16", "f32", "bf16-tall-tiles", "bf16-ffn-tail", "bf16-long-splits"])
+def test_decode_row_alone_equals_in_batch(shape, C, lens):
     """A decode row run alone (one GEMM row, 288-row tiles with 64-deep stages) equals the same
     decode inside a batch, bit for bit; with C = 400 the batch's GEMMs take 576-row tiles with
-    32-deep stages, whose k-sums must be cut at the same points."""
-    gu.say(f"case decode alone vs in batch {shape.name} C={C}")
-    w, b = case(shape, C, 9, [4, 250, 31], seed=3)
-    layer = hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=C + 3, max_pos=512)
+    32-deep stages, whose k-sums must be cut at the same points.  Alone, a decode's attention runs
+    in the split-KV kernel's pipelined key walk; in a batch with a short chunk, in the fused kernel's
+    walk (two steps of loads at a time); the long rows take 1024-key splits of four passes."""
+    gu.say(f"case decode alone vs in batch {shape.name} C={C} lens={lens}")
+    w, b = case(shape, C, 9, lens, seed=3)
+    layer = hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=C + 3,
+                           max_pos=max(512, max(lens) + 1))
     db = gu.upload_batch(shape, b)
     gu.run(layer, db, dump=False)
     y_full = db["y"].clone()
