@@ -58,6 +58,10 @@ __device__ __forceinline__ void split_attn_item(int r, int s, int h, const T *q,
                                                 const PagePool &pool, int stride, int prow0,
                                                 float *part_o, float *part_ml, float qscale, float *sm,
                                                 float *sl, float *so) {
+  // No contraction of separate operations into fused multiply-adds (only the explicit fmaf calls
+  // fuse): the two walks below order the same operations differently, and a row's result must not
+  // depend on which walk, kernel or batch served it.
+#pragma clang fp contract(off)
   constexpr int E = Packet<T>::E;      // elements per 16-byte packet
   constexpr int LPK = D / E;           // lanes per key row
   constexpr int KPI = kWave / LPK;     // keys per wave load step
