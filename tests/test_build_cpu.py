@@ -28,12 +28,14 @@ def test_no_kernel_uses_scratch():
 
 
 def test_hot_kernels_fit_their_occupancy_targets():
-    """The GEMM runs 8 waves (2 per SIMD) per workgroup and the chunk attention two 4-wave workgroups
-    per CU: their register budgets must allow that."""
+    """The GEMM runs 8 waves (2 per SIMD) per workgroup, the chunk attention two 4-wave workgroups
+    per CU and the split-KV decode attention four: their register budgets must allow that."""
     res = _resources()
     gemm = {k: v for k, v in res.items() if "gemm_bf16_rows" in k}
     chunk = {k: v for k, v in res.items() if "attn_chunk_mfma" in k}
-    assert gemm and chunk
+    split = {k: v for k, v in res.items() if "attn_rows_split" in k}
+    assert gemm and chunk and split
+    assert all(v["Occupancy"] >= 4 for v in split.values()), split
     assert all(v["Occupancy"] >= 2 for v in gemm.values()), gemm
     assert len(chunk) == 6, chunk   # d in {64, 128} x (contiguous: one or two query blocks; paged: one)
     assert all(v["Occupancy"] >= 2 for v in chunk.values()), chunk
