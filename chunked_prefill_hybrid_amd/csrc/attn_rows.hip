@@ -378,10 +378,12 @@ hipError_t run_fused(const void *q, int ld_q, int nh, const ChunkSet &cs, const 
   return hipGetLastError();
 }
 
-// One wave per (row, head), four per workgroup.  Lane l holds the (m, l) of splits l, l + 64, ...;
-// the wave max M and the weights w_s = 2^(m_s - M) (0 for empty splits) come from lane shuffles,
-// then each lane accumulates its D / 64 output elements over the splits, all loads of a group of
-// splits issued before their adds.
+// Merge of the split partials, four waves per workgroup.  Pairs with at most kFewSplits splits are
+// merged by D / 4 lanes each (several per wave) or a whole wave (combine_few); the general merge
+// takes a whole wave per pair: lane l holds the (m, l) of splits l, l + 64, ...; the wave max M and
+// the weights w_s = 2^(m_s - M) (0 for empty splits) come from lane shuffles, then each lane
+// accumulates its D / 64 output elements over the splits, all loads of a group of splits issued
+// before their adds.
 constexpr int kCombineWaves = 4;
 constexpr int kCombineSlots = kMaxKeySplits / kWave;   // splits per lane
 constexpr int kFewSplits = 8;
@@ -454,47 +456,103 @@ __device__ __forceinline__ void combine_few(int ns, size_t base, int r, int h, c
   }
 }
 
+// The same merge with D / 4 lanes per (row, head) pair, so a wave merges kWave / (D / 4) pairs: each
+// lane reads the (m, l) of all its pair's splits and its 4 columns of o from every split, all loads
+// issued at once.  The sum runs in combine_few's order (per group g the splits g, g + SPL, ..., then
+// the groups' sums as combine_few's lane tree adds them), so a pair gets the same bits from either.
 template <typename T, int D>
-__global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int row0, int n_rows,
-                                                                   int chunk_rows, int chunk_splits,
-                                                                   ChunkSplits table,
-                                                                   AttnParts parts, T *out,
-                                                                   OutLayout olay) {
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);   // (row, head) index
-  if (pair >= n_rows * nh) return;
-  const int r = row0 + pair / nh, h = pair % nh;
+__device__ __forceinline__ void combine_lanes(int ns, size_t base, int r, int h, const float *part_o,
+                                              const float *part_ml, T *out, OutLayout olay) {
+#pragma clang fp contract(off)
+  constexpr int LPS = D / 4;
+  constexpr int SPL = kWave / LPS;
+  const int col = (threadIdx.x % LPS) * 4;
+  float2 ml[kFewSplits];
+  float4 ov[kFewSplits];
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s) {
+    ml[s] = s < ns ? *reinterpret_cast<const float2 *>(&part_ml[2 * (base + s)]) : make_float2(-INFINITY, 0.f);
+    ov[s] = s < ns ? *reinterpret_cast<const float4 *>(&part_o[(base + s) * D + col])
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s)
+    if (ml[s].y > 0.f) M = fmaxf(M, ml[s].x);
+  float L = 0.f, acc[SPL][4] = {};
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s) {
+    const float w = ml[s].y > 0.f ? exp2f(ml[s].x - M) : 0.f;
+    L = fmaf(ml[s].y, w, L);
+    if (w != 0.f) {
+      float *a = acc[s % SPL];
+      a[0] = fmaf(w, ov[s].x, a[0]);
+      a[1] = fmaf(w, ov[s].y, a[1]);
+      a[2] = fmaf(w, ov[s].z, a[2]);
+      a[3] = fmaf(w, ov[s].w, a[3]);
+    }
+  }
+#pragma unroll
+  for (int st = 1; st < SPL; st <<= 1)
+#pragma unroll
+    for (int g = 0; g < SPL; g += 2 * st)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[g][e] = acc[g][e] + acc[g + st][e];
+  const float inv = 1.0f / L;
+  T *dst = &out[out_index(olay, r, h * D + col)];
+  if constexpr (sizeof(T) == 2) {
+    uint2 u;
+    u.x = (uint32_t)from_f32<T>(acc[0][0] * inv) | ((uint32_t)from_f32<T>(acc[0][1] * inv) << 16);
+    u.y = (uint32_t)from_f32<T>(acc[0][2] * inv) | ((uint32_t)from_f32<T>(acc[0][3] * inv) << 16);
+    *reinterpret_cast<uint2 *>(dst) = u;
+  } else {
+    *reinterpret_cast<float4 *>(dst) =
+        make_float4(acc[0][0] * inv, acc[0][1] * inv, acc[0][2] * inv, acc[0][3] * inv);
+  }
+}
+
+// Where a (row, head) pair's partials are, and how it is merged: kind 0 leaves it alone (a row of
+// an unsplit chunk, written by the chunk kernel), 1 takes the few-split merge over ns splits, 2 the
+// general one over n_used slots.
+struct PairMerge {
   size_t base;
-  int n_used;
-  const float *part_o, *part_ml;
+  const float *o, *ml;
+  int n, kind;
+};
+__device__ __forceinline__ PairMerge pair_merge(int r, int h, int nh, int chunk_rows, int chunk_splits,
+                                                const ChunkSplits &table, const AttnParts &parts) {
+  PairMerge p;
   if (r < chunk_rows) {
-    base = ((size_t)r * nh + h) * parts.stride_c;
-    part_o = parts.o_c;
-    part_ml = parts.ml_c;
-    n_used = chunk_splits;
+    p.base = ((size_t)r * nh + h) * parts.stride_c;
+    p.o = parts.o_c;
+    p.ml = parts.ml_c;
+    p.n = chunk_splits;
+    p.kind = 2;
     if (chunk_splits == 0) {
       // The row's chunk, found with constant-index selects (the table is a by-value argument).
       int ns = table.split[0];
 #pragma unroll
       for (int i = 1; i < kMaxChunks; ++i)
         if (i < table.n && r >= table.row0[i]) ns = table.split[i];
-      if (ns <= 1) return;   // written by the chunk kernel
-      if (ns <= kFewSplits) {
-        combine_few<T, D>(ns, base, r, h, part_o, part_ml, out, olay);
-        return;
-      }
-      n_used = ns;
+      p.n = ns;
+      p.kind = ns <= 1 ? 0 : ns <= kFewSplits ? 1 : 2;
     }
   } else {
-    base = ((size_t)(r - chunk_rows) * nh + h) * parts.stride_d;
-    part_o = parts.o_d;
-    part_ml = parts.ml_d;
-    n_used = parts.stride_d;
-    if (n_used <= kFewSplits) {   // every decode of the group has at most this many splits
-      combine_few<T, D>(n_used, base, r, h, part_o, part_ml, out, olay);
-      return;
-    }
+    p.base = ((size_t)(r - chunk_rows) * nh + h) * parts.stride_d;
+    p.o = parts.o_d;
+    p.ml = parts.ml_d;
+    p.n = parts.stride_d;   // every decode of the group has at most this many splits
+    p.kind = parts.stride_d <= kFewSplits ? 1 : 2;
   }
+  return p;
+}
+
+// The general merge of one (row, head) pair's n_used split slots by a whole wave.
+template <typename T, int D>
+__device__ __forceinline__ void combine_general(int n_used, size_t base, int r, int h,
+                                                const float *part_o, const float *part_ml, T *out,
+                                                OutLayout olay) {
+  const int lane = threadIdx.x & 63;
   float m[kCombineSlots], l[kCombineSlots], w[kCombineSlots];
   float M = -INFINITY;
 #pragma unroll
@@ -558,6 +616,45 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int r
     out[out_index(olay, r, h * D + lane + i * kWave)] = from_f32<T>(acc[i] * inv);
 }
 
+// One launch merges every split row of the batch.  A wave takes kWave / (D / 4) consecutive (row, head)
+// pairs; when none of them needs the general merge, each pair gets D / 4 lanes (combine_lanes),
+// otherwise the wave merges them one after the other with all its lanes.
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kCombineWaves) void attn_combine(int nh, int row0, int n_rows,
+                                                                   int chunk_rows, int chunk_splits,
+                                                                   ChunkSplits table,
+                                                                   AttnParts parts, T *out,
+                                                                   OutLayout olay) {
+  constexpr int LPS = D / 4, PPW = kWave / LPS;   // lanes per pair, pairs per wave
+  const int wave = blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_pairs = n_rows * nh;
+  {
+    const int pair = wave * PPW + (threadIdx.x & 63) / LPS;
+    PairMerge p{0, nullptr, nullptr, 0, 0};
+    int r = 0, h = 0;
+    if (pair < n_pairs) {
+      r = row0 + pair / nh;
+      h = pair % nh;
+      p = pair_merge(r, h, nh, chunk_rows, chunk_splits, table, parts);
+    }
+    if (!__any(p.kind == 2)) {
+      if (p.kind == 1) combine_lanes<T, D>(p.n, p.base, r, h, p.o, p.ml, out, olay);
+      return;
+    }
+  }
+#pragma unroll 1
+  for (int i = 0; i < PPW; ++i) {
+    const int pair = wave * PPW + i;   // wave-uniform
+    if (pair >= n_pairs) return;
+    const int r = row0 + pair / nh, h = pair % nh;
+    const PairMerge p = pair_merge(r, h, nh, chunk_rows, chunk_splits, table, parts);
+    if (p.kind == 1)
+      combine_few<T, D>(p.n, p.base, r, h, p.o, p.ml, out, olay);
+    else if (p.kind == 2)
+      combine_general<T, D>(p.n, p.base, r, h, p.o, p.ml, out, olay);
+  }
+}
+
 template <typename T, int D>
 hipError_t run_split(const void *q, int ld_q, int nh, int row0, int n_rows, const ChunkSet &cs,
                      const DecodeGroup &dg, const PagePool &pool, int stride, int prow0, float *po,
@@ -581,8 +678,8 @@ template <typename T, int D>
 hipError_t run_combine(int nh, int row0, int n_rows, int chunk_rows, int chunk_splits,
                        const ChunkSplits &table, const AttnParts &parts, void *out, OutLayout olay,
                        hipStream_t s) {
-  const int pairs = n_rows * nh;
-  hipLaunchKernelGGL((attn_combine<T, D>), dim3((pairs + kCombineWaves - 1) / kCombineWaves),
+  const int waves = (n_rows * nh + kWave / (D / 4) - 1) / (kWave / (D / 4));
+  hipLaunchKernelGGL((attn_combine<T, D>), dim3((waves + kCombineWaves - 1) / kCombineWaves),
                      dim3(64 * kCombineWaves), 0, s, nh, row0, n_rows, chunk_rows, chunk_splits,
                      table, parts, static_cast<T *>(out), olay);
   return hipGetLastError();

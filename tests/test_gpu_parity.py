@@ -21,6 +21,8 @@ MID_F32 = wl.LayerShape("mid-llama-f32", "llama", 512, 4, 128, 1408, "f32", 1e-6
 # FFN products of more than 256 weight stripes: a fused main part and a split tail
 MID_WIDE_FFN = wl.LayerShape("mid-llama-wide-ffn", "llama", 512, 4, 128, 17920, "bf16", 1e-6, 10000.0, None)
 MID_GPT_WIDE_FFN = wl.LayerShape("mid-gpt-wide-ffn", "gpt", 512, 4, 128, 34816, "bf16", 1e-5, 10000.0, None)
+# Five heads: with an odd number of (row, head) pairs per row, one merge wave holds pairs of two rows.
+MID_F32_5H = wl.LayerShape("mid-llama-f32-5h", "llama", 640, 5, 128, 1408, "f32", 1e-6, 10000.0, None)
 MID_D64 = wl.LayerShape("mid-llama-d64", "llama", 256, 4, 64, 704, "bf16", 1e-6, 10000.0, None)
 # A llama-7b-sized layer: at 400+ rows every one of its GEMMs takes one 576-row tile per column
 # stripe (32-deep stages)
@@ -203,14 +205,18 @@ def test_edge_batches(C, off, lens):
 
 @pytest.mark.parametrize("shape,C,lens", [(MID, 60, [4, 250, 31]), (MID_F32, 60, [4, 250, 31]),
                                            (BIG, 400, [4, 250, 31]), (MID_WIDE_FFN, 300, [4, 250, 31]),
-                                           (MID, 60, [2500, 4, 6001])],
-                         ids=["bf16", "f32", "bf16-tall-tiles", "bf16-ffn-tail", "bf16-long-splits"])
+                                           (MID, 60, [2500, 4, 6001]), (MID_F32_5H, 7, [600, 4, 1100])],
+                         ids=["bf16", "f32", "bf16-tall-tiles", "bf16-ffn-tail", "bf16-long-splits",
+                              "f32-odd-heads"])
 def test_decode_row_alone_equals_in_batch(shape, C, lens):
     """A decode row run alone (one GEMM row, 288-row tiles with 64-deep stages) equals the same
     decode inside a batch, bit for bit; with C = 400 the batch's GEMMs take 576-row tiles with
     32-deep stages, whose k-sums must be cut at the same points.  Alone, a decode's attention runs
     in the split-KV kernel's pipelined key walk; in a batch with a short chunk, in the fused kernel's
-    walk (two steps of loads at a time); the long rows take 1024-key splits of four passes."""
+    walk (two steps of loads at a time); the long rows take 1024-key splits of four passes.  With
+    five heads and a 7-row float32 chunk (whose rows take the general merge), the merge wave of the
+    last chunk row's last head also holds decode 0's first head, which it then merges with a whole
+    wave; alone, that pair is merged by a lane group of a wave: both must give the same bits."""
     gu.say(f"case decode alone vs in batch {shape.name} C={C} lens={lens}")
     w, b = case(shape, C, 9, lens, seed=3)
     layer = hl.HybridLayer(shape, gu.upload_weights(shape, w), max_tokens=C + 3,
