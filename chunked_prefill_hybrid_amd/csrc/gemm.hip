@@ -10,11 +10,14 @@
 // bf16 path.  One workgroup (8 waves as 2 x 4) owns ALL rows of the batch (up to 576; larger batches
 // take a few row tiles) and a 128-column stripe of the weights, so a weight tile is read once for
 // the whole batch.  v_mfma_f32_16x16x32_bf16; a wave computes up to 288 rows x 32 columns.  A and W
-// k-tiles (64 deep for tiles of up to 288 rows, 32 deep above) travel from global memory straight
-// into LDS (global_load_lds_dwordx4: no staging registers, no LDS store instructions) through a ring
-// of as many stages as fit (up to 5), so the loads of the next tiles are in flight while tile j is
-// multiplied.  The loads are what bounds this kernel: a compute unit keeps only ~10 KB of reads in
-// flight, so its fetch rate is set by memory latency, and the A tile is fetched by every workgroup.
+// k-tiles, 32 deep, travel from global memory straight into LDS (global_load_lds_dwordx4: no staging
+// registers, no LDS store instructions) through a ring of as many stages as fit (up to 6), so the
+// loads of the next tiles are in flight while tile j is multiplied.  Both operands are k-tile-major,
+// [k/32][rows][32] (the norms write A that way, the layer packs its weights that way once), so the
+// 32-deep rows of one 1 KiB load are 1 KiB of consecutive bytes in whole 128-byte lines.  The loads
+// are what bounds this kernel: a compute unit keeps only ~10 KB of reads in flight, so its fetch rate
+// is set by memory latency and by how many requests the tiles cost, and the A tile is fetched by
+// every workgroup.
 // When the weight stripes alone do not fill the 256 compute units, the k range is split: each split
 // writes a float32 partial and the kernel that consumes the product sums the partials in a fixed
 // order (deterministic, no atomics); a fused-activation product with more stripes than one round
@@ -30,10 +33,12 @@
 namespace sarathi {
 namespace {
 
-// Stage depth.  A workgroup tile of up to 288 rows takes 64-deep k-tiles (an LDS row of 128 bytes =
-// 8 chunks of 16 bytes, two MFMA k-steps per stage).  Taller tiles (up to 576 rows, so batches of up
-// to 576 rows stream each weight stripe once) take 32-deep k-tiles (64-byte LDS rows, one k-step per
-// stage): three stages of 576 + 128 rows then still fit in LDS.
+// Stage depth.  Every tile takes 32-deep k-tiles (64-byte LDS rows, one MFMA k-step per stage): six
+// stages of a 288-row tile, three of a 576-row one (so batches of up to 576 rows stream each weight
+// stripe once) fit in LDS.  Against 64-deep stages (128-byte LDS rows, two k-steps) for tiles of up
+// to 288 rows, with the weights k-tile-major in both: gate/up at 274 rows 95.6 -> 84.3 us, QKV 52.4
+// -> 50.3 us, O and down within 1 us (same box, five interleaved runs each).  64-deep stages stay
+// selectable at build time (SARATHI_GEMM_MBW64 = 9) for tiles of up to 288 rows.
 template <int BK> struct KGeom {
   static_assert(BK == 32 || BK == 64, "stage depth");
   static constexpr int kChunks = BK / 8;          // 16-byte chunks per LDS row
@@ -49,17 +54,16 @@ template <int BK> __device__ __forceinline__ int swz_slot(int row, int chunk) {
   return BK == 64 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 1) & 3);
 }
 #ifndef SARATHI_GEMM_MAX_STAGES
-#define SARATHI_GEMM_MAX_STAGES 5
+#define SARATHI_GEMM_MAX_STAGES 6
 #endif
 constexpr int kMaxStages = SARATHI_GEMM_MAX_STAGES;
 constexpr int kPlanWaveCols = 4;   // wave columns of a workgroup (8 waves: 2 rows x 4 columns)
 constexpr int kWM = 2;             // wave rows of a workgroup
 constexpr int kWaves = kWM * kPlanWaveCols;
-// 16-row blocks per wave row: up to 9 (288-row tiles) with 64-deep stages, up to 18 (576-row tiles)
-// with 32-deep stages.  A 320-row tile with 64-deep stages would leave room for only two stages (it
-// measured as slow as two 160-row tiles).
+// 16-row blocks per wave row: up to 18 (576-row tiles); tiles of up to kMBW64 blocks per wave row
+// would take 64-deep stages (0: none do).
 #ifndef SARATHI_GEMM_MBW64
-#define SARATHI_GEMM_MBW64 9
+#define SARATHI_GEMM_MBW64 0
 #endif
 constexpr int kMBW64 = SARATHI_GEMM_MBW64;
 #ifndef SARATHI_GEMM_MBW
@@ -92,9 +96,7 @@ __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erf
 // 16 bytes = 1 KiB, i.e. kRPL LDS rows; the A rows of a stage take kRowsA / kRPL such loads, the
 // weight rows kBN / kRPL, dealt round-robin to the 8 waves.  As many stages as fit in LDS (up to
 // kMaxStages) are kept in flight: the loads of a tile are issued that many steps before its use,
-// which is what hides the memory latency.  Five stages (where they fit: tall tiles of up to 416
-// rows) measured 2% faster than three on the 320-row GPT shard batch and the same elsewhere; all
-// tiles at 32-deep stages with up to six measured 7% slower on the 274-row gate/up product.
+// which is what hides the memory latency.
 template <int MB> struct StageGeom {
   static constexpr int kBK = stage_depth(MB);
   using K = KGeom<kBK>;
@@ -177,26 +179,36 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
     a_lds[i] = K::kRPL * q * BK;
   }
   const bf16_t *b_src[G::kBI];
+  int b_step[G::kBI];   // elements from one k-tile of a lane's weight row to the next
 #pragma unroll
   for (int i = 0; i < G::kBI; ++i) {
     const int row = K::kRPL * (wave + kWaves * i) + lrow;   // weight row within the stripe's LDS block
     int src_row;
-    const bf16_t *Wp = W0;
+    bool second = false;
     if (kGlu) {
       // LDS rows of wave column wv: its gate block(s), then the up block(s) of the same columns.
       const int wv = row / (16 * kNB), bb = (row >> 4) % kNB, rl = row & 15;
       const int cb = wv * (kNB / 2) + bb % (kNB / 2);
       src_row = min(n0 + cb * 16 + rl, g.n - 1);
-      Wp = (bb >= kNB / 2) ? W1 : W0;
+      second = bb >= kNB / 2;
     } else {
       src_row = min(n0 + row, g.n - 1);
       if (g.w1 && src_row >= g.n_w0) {   // the second weight continues the product's rows
-        Wp = W1;
+        second = true;
         src_row -= g.n_w0;
       }
     }
+    const bf16_t *Wp = second ? W1 : W0;
     // kRowsA is a multiple of 16, so the weight block's rows swizzle like rows 0..kBN-1
-    b_src[i] = Wp + (size_t)src_row * g.ldw + (size_t)kb * BK + swz_slot<BK>(row, lslot) * 8;
+    const int chunk = swz_slot<BK>(row, lslot) * 8;
+    if (g.w_kmajor) {
+      const int slab = second ? g.w_slab1 : g.w_slab0;
+      b_src[i] = Wp + (size_t)kb * slab + (size_t)src_row * BK + chunk;
+      b_step[i] = slab;
+    } else {
+      b_src[i] = Wp + (size_t)src_row * g.ldw + (size_t)kb * BK + chunk;
+      b_step[i] = BK;
+    }
   }
 
   // Loads of k-tile j (clamped to the last tile, so every wave issues the same loads every step)
@@ -205,15 +217,15 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   // kX: this wave issues the extra A load (a template constant, so each form of the k loop below is
   // straight-line code; a run-time test per load measured 10-35% slower).
   auto issue = [&](auto kX, bf16_t *st, int j) {
-    const int kofs = min(j, ntiles - 1) * BK;
-    const int a_kofs = min(j, ntiles - 1) * a_kstep;
+    const int jj = min(j, ntiles - 1);
+    const int a_kofs = jj * a_kstep;
 #pragma unroll
     for (int i = 0; i < G::kAI; ++i)
       if (i < G::kAI - 1 || decltype(kX)::value) dma16(a_src[i] + a_kofs, st + a_lds[i]);
 #pragma unroll
     for (int i = 0; i < G::kBI; ++i) {
       const int q = wave + kWaves * i;
-      dma16(b_src[i] + kofs, st + (G::kRowsA + K::kRPL * q) * BK);
+      dma16(b_src[i] + jj * b_step[i], st + (G::kRowsA + K::kRPL * q) * BK);
     }
   };
 
@@ -380,6 +392,19 @@ __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs g) {
   }
 }
 
+// k-tile-major repack of a weight: thread i moves the 16-byte piece i of the source (8 elements of
+// one row, k fastest), so the reads are coalesced; the writes land as 16-byte pieces of the
+// destination's w-element rows.
+__global__ __launch_bounds__(256) void pack_kmajor(const bf16_t *__restrict__ src, int rows, int k, int ld,
+                                                   int w, bf16_t *__restrict__ dst) {
+  const int per_row = k / 8;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)rows * per_row) return;
+  const int r = (int)(i / per_row), c = (int)(i % per_row) * 8;
+  const uint4 v = *reinterpret_cast<const uint4 *>(src + (size_t)r * ld + c);
+  *reinterpret_cast<uint4 *>(dst + ((size_t)(c / w) * rows + r) * w + c % w) = v;
+}
+
 template <int MB, int EPI>
 hipError_t run_bf16_mb(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_rows<MB, EPI>), dim3(p.grid), dim3(64 * kWaves), 0, s, g, p);
@@ -462,12 +487,12 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
       p.splits = 1;
     }
   }
-  // Row tiles: as few 576-row tiles (32-deep stages) as hold the batch, or 288-row ones (64-deep
-  // stages), whichever gives the shorter estimate of whole rounds of `cus` workgroups times one
-  // workgroup's time.  A workgroup's time grows with its rows from its weight stream (about 0.55 of
-  // a 288-row workgroup, measured at 1 row) up to 1.0 at 288 rows (64-deep) and 1.6 at 576 rows
-  // (32-deep), measured on the llama-13b gate/up product.  The rows of a batch never change its
-  // split count, so either choice gives a row the same k-sum.
+  // Row tiles: as few 576-row tiles as hold the batch.  (In a build with 64-deep stages for tiles of
+  // up to 288 rows, those are the alternative, and the shorter estimate of whole rounds of `cus`
+  // workgroups times one workgroup's time wins: a workgroup's time grows with its rows from its
+  // weight stream, about 0.55 of a 288-row workgroup at 1 row, up to 1.0 at 288 rows with 64-deep
+  // stages and 1.6 at 576 rows, measured on the llama-13b gate/up product with row-major weights.)
+  // The rows of a batch never change its split count, so every choice gives a row the same k-sum.
   auto wg_time = [](int rows) {
     return stage_depth((rows + 31) / 32) == 64 ? 0.55 + 0.45 * rows / 288.0 : 0.55 + 0.525 * rows / 288.0;
   };
@@ -517,12 +542,32 @@ int plan_gemm_tail(int type, int epi, int m, int n_out, int k, int cus, GemmPlan
 
 int gemm_stage_depth(const GemmPlan &p) { return stage_depth(p.mbw); }
 
+hipError_t launch_pack_kmajor(const void *src, int rows, int k, int ld, int w, void *dst, hipStream_t s) {
+  if (!src || !dst || rows <= 0 || k <= 0 || (w != 32 && w != 64) || k % w || ld < k || ld % 8 ||
+      (long long)rows * k >= (1ll << 31))
+    return hipErrorInvalidValue;
+  const long long n = (long long)rows * (k / 8);
+  hipLaunchKernelGGL(pack_kmajor, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16_t *>(src), rows, k, ld, w, static_cast<bf16_t *>(dst));
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   // k-tile-major A: bf16 only, tiles as wide as the plan's stage depth, and its whole extent
   // addressable with 32-bit offsets
   if (g.a_kmajor && (type == kF32 || g.a_kmajor != stage_depth(p.mbw) ||
                      (long long)g.m_alloc * g.k >= (1ll << 31)))
     return hipErrorInvalidValue;
+  // k-tile-major weights: the same, with each k-tile step of either weight a 32-bit offset that
+  // covers at least the product's rows taken from it
+  if (g.w_kmajor) {
+    const long long rows0 = g.w1 && epi != kEpiSwiGLU ? g.n_w0 : g.n;
+    const long long rows1 = g.w1 ? (epi == kEpiSwiGLU ? g.n : g.n - g.n_w0) : 0;
+    if (type == kF32 || g.w_kmajor != stage_depth(p.mbw) || g.w_slab0 < rows0 * g.w_kmajor ||
+        (g.w1 && g.w_slab1 < rows1 * g.w_kmajor) || (long long)g.w_slab0 * (g.k / g.w_kmajor) >= (1ll << 31) ||
+        (long long)g.w_slab1 * (g.k / g.w_kmajor) >= (1ll << 31))
+      return hipErrorInvalidValue;
+  }
   if (type == kBF16 && (g.k % kSplitK || p.mbw < 1 || p.mbw > kMBW)) return hipErrorInvalidValue;
   if (g.out_kmajor && (type == kF32 || (epi != kEpiSwiGLU && epi != kEpiGelu) ||
                        (g.out_kmajor != 32 && g.out_kmajor != 64) || g.n % g.out_kmajor))

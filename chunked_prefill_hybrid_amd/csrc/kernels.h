@@ -65,6 +65,11 @@ struct GemmArgs {
   int a_kmajor;       // 0: a is row-major.  bf16 only, w = 32 or 64 (the plan's stage depth): a is
                       // k-tile-major, [k/w][m_alloc][w] (lda unused).  A k-tile of 1024 / (2 w) rows
                       // is then 1 KiB of consecutive bytes, which the LDS DMA fetches faster
+  int w_kmajor;       // 0: w0 / w1 are row-major (row stride ldw).  bf16 only, w = the plan's stage
+                      // depth: each is k-tile-major, [k/w][rows][w] (ldw unused), and k-tile j of
+                      // row r of w0 is at w0 + j * w_slab0 + r * w (w1: w_slab1); with w = 32 two
+                      // weight rows of one k-tile then fill one 128-byte line instead of half of two
+  int w_slab0, w_slab1;   // with w_kmajor: elements between consecutive k-tiles of w0 / w1
 };
 
 // Launch shape of one GEMM: m_tiles x n_tiles output tiles, each k range cut into `splits`;
@@ -86,6 +91,10 @@ int plan_gemm_tail(int type, int epi, int m, int n_out, int k, int cus, GemmPlan
 // k depth of one LDS stage of a bf16 plan (32 or 64): the k-tile width of a k-tile-major A.
 int gemm_stage_depth(const GemmPlan &p);
 hipError_t launch_gemm(int type, int epi, const GemmArgs &g, const GemmPlan &p, hipStream_t s);
+// Repacks a bf16 weight [rows, k] (row stride ld elements) into k-tile-major [k/w][rows][w]
+// (w = 32 or 64, k a multiple of w, rows * k < 2^31): element (r, c) moves to ((c / w) * rows + r) * w
+// + c % w.  dst must not overlap src.
+hipError_t launch_pack_kmajor(const void *src, int rows, int k, int ld, int w, void *dst, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // RoPE + KV append: for rows [row0, row0+n_rows) of the batch, sums the QKV GEMM's split partials

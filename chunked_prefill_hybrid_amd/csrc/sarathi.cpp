@@ -25,8 +25,10 @@ using namespace sarathi;
 
 struct sarathi_layer {
   sarathi_layer_desc desc;
-  sarathi_weights w;
+  sarathi_weights w;   // bf16: the projection weights point into wpack
   float2 *rope_tab;  // device [max_pos, head_dim/2] (LLAMA), else null
+  void *wpack;       // bf16: device copy of the projection weights, each k-tile-major [k/wk][rows][wk]
+  int wk;            // k-tile width of the packed weights (bf16), 0: row-major caller weights (f32)
   int device;
 };
 
@@ -88,6 +90,11 @@ sarathi_status check_desc(const sarathi_layer_desc *d) {
                 d->hidden, kMaxHidden);
   if ((long long)d->max_tokens * 3 * d->n_heads * d->head_dim > (1ll << 31))
     return fail(SARATHI_ERR_UNSUPPORTED, "max_tokens too large");
+  // the packed bf16 weights and the GEMM's k-tile steps through them use 32-bit element offsets
+  const long long A = (long long)d->n_heads * d->head_dim;
+  if (d->dtype == SARATHI_BF16 &&
+      (3 * A * d->hidden >= (1ll << 31) || (long long)d->ffn * d->hidden >= (1ll << 31)))
+    return fail(SARATHI_ERR_UNSUPPORTED, "a weight matrix of 2^31 or more elements");
   return SARATHI_OK;
 }
 
@@ -492,6 +499,55 @@ DecodeGroup decode_group(const BatchView &b, int base) {
   return g;
 }
 
+// A bf16 layer's projection weights, copied once into one device buffer, each k-tile-major
+// [k/32][rows][32]: the GEMM's 32-deep k-tiles of a weight stripe are then whole 128-byte lines
+// (two rows per line) instead of half lines of row-major rows, and a stripe's k-tile is 8 KiB of
+// consecutive bytes.  The caller's weight buffers are not read after this.
+constexpr int kWeightTile = 32;
+sarathi_status pack_weights(sarathi_layer *L) {
+  const sarathi_layer_desc *d = &L->desc;
+  const int H = d->hidden, A = d->n_heads * d->head_dim, F = d->ffn;
+  struct Mat {
+    const void **w;
+    int rows, k;
+  } mats[5] = {{&L->w.w_qkv, 3 * A, H}, {&L->w.w_o, H, A}, {&L->w.w_gate, F, H}, {&L->w.w_up, F, H},
+               {&L->w.w_down, H, F}};
+  size_t ofs[5], total = 0;
+  for (int i = 0; i < 5; ++i) {
+    ofs[i] = total;
+    if (*mats[i].w) total += ((size_t)mats[i].rows * mats[i].k * 2 + 255) / 256 * 256;
+  }
+  hipError_t e = hipMalloc(&L->wpack, total);
+  if (e != hipSuccess) {
+    L->wpack = nullptr;
+    return fail(SARATHI_ERR_NOMEM, "hipMalloc of %zu bytes of packed weights failed: %s", total,
+                hipGetErrorString(e));
+  }
+  for (int i = 0; i < 5; ++i) {
+    if (!*mats[i].w) continue;
+    void *dst = static_cast<char *>(L->wpack) + ofs[i];
+    e = launch_pack_kmajor(*mats[i].w, mats[i].rows, mats[i].k, mats[i].k, kWeightTile, dst, nullptr);
+    if (e != hipSuccess) return fail(SARATHI_ERR_HIP, "packing weight %d failed: %s", i, hipGetErrorString(e));
+    *mats[i].w = dst;
+  }
+  e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return fail(SARATHI_ERR_HIP, "packing the weights failed: %s", hipGetErrorString(e));
+  L->wk = kWeightTile;
+  return SARATHI_OK;
+}
+
+// Weight operands of a GEMM of layer L: w0 with rows0 rows, w1 (or null) with rows1; each [rows, k]
+// row-major (f32 layers) or packed (bf16 layers).
+void set_weights(GemmArgs &g, const sarathi_layer *L, const void *w0, int rows0, const void *w1, int rows1,
+                 int k) {
+  g.w0 = w0;
+  g.w1 = w1;
+  g.ldw = k;
+  g.w_kmajor = L->wk;
+  g.w_slab0 = rows0 * L->wk;
+  g.w_slab1 = w1 ? rows1 * L->wk : 0;
+}
+
 #define HIP_TRY(expr)                                                                     \
   do {                                                                                    \
     hipError_t e_ = (expr);                                                               \
@@ -643,7 +699,8 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   // 2. QKV projection: one GEMM over chunk and decode rows (float32 split partials)
   HIP_TRY(mk.start(SARATHI_STAGE_QKV));
   GemmArgs g{};
-  g.a = n1; g.lda = H; g.a_kmajor = kmajor1; g.w0 = L->w.w_qkv; g.ldw = H; g.part = part;
+  g.a = n1; g.lda = H; g.a_kmajor = kmajor1; g.part = part;
+  set_weights(g, L, L->w.w_qkv, 3 * A, nullptr, 0, H);
   g.m_alloc = R; g.m_store = T; g.n = 3 * A; g.k = H;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.qkv, s));
   HIP_TRY(mk.end(SARATHI_STAGE_QKV, true));
@@ -671,7 +728,8 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   // 5. O projection (float32 split partials)
   HIP_TRY(mk.start(SARATHI_STAGE_O));
   g = GemmArgs{};
-  g.a = attn; g.lda = A; g.a_kmajor = kmajor_attn; g.w0 = L->w.w_o; g.ldw = A; g.part = part;
+  g.a = attn; g.lda = A; g.a_kmajor = kmajor_attn; g.part = part;
+  set_weights(g, L, L->w.w_o, H, nullptr, 0, A);
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = A;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.o, s));
   HIP_TRY(mk.end(SARATHI_STAGE_O, true));
@@ -683,9 +741,8 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   // 7. FFN up (+gate): activation fused into the GEMM, or split product + activation pass
   HIP_TRY(mk.start(SARATHI_STAGE_FFN_UP));
   g = GemmArgs{};
-  g.a = n2; g.lda = H; g.a_kmajor = kmajor2; g.ldw = H; g.m_alloc = R; g.m_store = T; g.k = H;
-  g.w0 = llama ? L->w.w_gate : L->w.w_up;
-  g.w1 = llama ? L->w.w_up : nullptr;
+  g.a = n2; g.lda = H; g.a_kmajor = kmajor2; g.m_alloc = R; g.m_store = T; g.k = H;
+  set_weights(g, L, llama ? L->w.w_gate : L->w.w_up, F, llama ? L->w.w_up : nullptr, F, H);
   if (p.up.epi == kEpiPartial) {
     g.part = part; g.n = llama ? 2 * F : F; g.n_w0 = F;
     HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.up, s));
@@ -696,7 +753,8 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
     if (p.up_main > 0) {
       // the columns past up_main: split product of their weight rows, then the activation pass
       const int n_tail = F - p.up_main;
-      const size_t wofs = (size_t)p.up_main * H * elem_size(ty);
+      // row up_main of a weight: a row offset within each k-tile when packed
+      const size_t wofs = (size_t)p.up_main * (L->wk ? L->wk : H) * elem_size(ty);
       GemmArgs t = g;
       t.out = nullptr; t.ldo = 0; t.out_kmajor = 0;
       t.w0 = static_cast<const char *>(g.w0) + wofs;
@@ -711,7 +769,8 @@ sarathi_status forward_impl(sarathi_layer *L, const BatchView &b, void *workspac
   // 8. down projection (split partials), y = h1 + sum of the partials
   HIP_TRY(mk.start(SARATHI_STAGE_FFN_DOWN));
   g = GemmArgs{};
-  g.a = act; g.lda = F; g.a_kmajor = kmajor_act; g.w0 = L->w.w_down; g.ldw = F; g.part = part;
+  g.a = act; g.lda = F; g.a_kmajor = kmajor_act; g.part = part;
+  set_weights(g, L, L->w.w_down, H, nullptr, 0, F);
   g.m_alloc = R; g.m_store = T; g.n = H; g.k = F;
   HIP_TRY(launch_gemm(ty, kEpiPartial, g, p.down, s));
   if (next) {
@@ -817,6 +876,7 @@ sarathi_status forward_entry(sarathi_layer *L, const Batch *b, void *workspace, 
 
 static_assert(SARATHI_MAX_CHUNKS == kMaxChunks, "chunk table size");
 
+
 }  // namespace
 
 extern "C" {
@@ -841,9 +901,19 @@ sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarath
   L->w = *weights;
   if (!llama) L->w.w_gate = nullptr;
   L->rope_tab = nullptr;
+  L->wpack = nullptr;
+  L->wk = 0;
   if (hipGetDevice(&L->device) != hipSuccess) {
     delete L;
     return fail(SARATHI_ERR_HIP, "hipGetDevice failed");
+  }
+  if (desc->dtype == SARATHI_BF16) {
+    st = pack_weights(L);
+    if (st != SARATHI_OK) {
+      if (L->wpack) (void)hipFree(L->wpack);
+      delete L;
+      return st;
+    }
   }
   if (llama) {
     const int half = desc->head_dim / 2;
@@ -878,6 +948,7 @@ sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarath
 void sarathi_layer_destroy(sarathi_layer *layer) {
   if (!layer) return;
   if (layer->rope_tab) (void)hipFree(layer->rope_tab);
+  if (layer->wpack) (void)hipFree(layer->wpack);
   delete layer;
 }
 
