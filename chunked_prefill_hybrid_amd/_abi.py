@@ -104,7 +104,8 @@ class sarathi_paged_batch(ctypes.Structure):
 
 
 class sarathi_gemm_plan(ctypes.Structure):
-    _fields_ = [("epilogue", c_int32), ("row_tiles", c_int32), ("col_tiles", c_int32), ("k_splits", c_int32)]
+    _fields_ = [("epilogue", c_int32), ("row_tiles", c_int32), ("col_tiles", c_int32), ("k_splits", c_int32),
+                ("tile_cols", c_int32)]
 
 
 class sarathi_plan_info(ctypes.Structure):

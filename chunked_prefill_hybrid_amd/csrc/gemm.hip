@@ -74,6 +74,17 @@ constexpr int kMBW = SARATHI_GEMM_MBW;
 #define SARATHI_GEMM_BN 128
 #endif
 constexpr int kBN = SARATHI_GEMM_BN;   // columns per tile (weight rows per stripe)
+// Wide tiles for batches of 289..576 rows: two 288-row tiles of 256 columns instead of one 576-row
+// tile of 128, the same number of workgroups and k-splits.  A workgroup then fetches half the
+// activation rows per k-tile and twice the weight rows (the two row tiles of a stripe run side by
+// side on one XCD, so the second fetch of a weight line mostly hits its L2), reads 13 instead of 20
+// LDS fragments per 36 MFMAs a wave, and keeps four LDS stages in flight instead of three.
+#ifndef SARATHI_GEMM_WIDE
+#define SARATHI_GEMM_WIDE 1
+#endif
+constexpr bool kWideTiles = SARATHI_GEMM_WIDE != 0;
+constexpr int kBNWide = 256;
+constexpr int kMBWide = 9;   // 16-row blocks per wave row of a wide tile: 288 rows
 constexpr int kBMX = 16 * kMBW * kWM;
 constexpr int kLdsBudget = 160 * 1024;
 // Split-K boundaries lie on multiples of 64 k whatever a tile's stage depth, so a row's k-sum is cut
@@ -97,32 +108,33 @@ __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erf
 // weight rows kBN / kRPL, dealt round-robin to the 8 waves.  As many stages as fit in LDS (up to
 // kMaxStages) are kept in flight: the loads of a tile are issued that many steps before its use,
 // which is what hides the memory latency.
-template <int MB> struct StageGeom {
+template <int MB, int BN> struct StageGeom {
   static constexpr int kBK = stage_depth(MB);
   using K = KGeom<kBK>;
   static constexpr int kRowsA = 32 * MB;
-  static constexpr int kElems = (kRowsA + kBN) * kBK;
+  static constexpr int kElems = (kRowsA + BN) * kBK;
   static constexpr int kFit = kLdsBudget / (kElems * 2);
   static constexpr int kStages = kFit < kMaxStages ? kFit : kMaxStages;
   static_assert(kStages >= 2, "two stages fit in LDS");
   static constexpr int kLoadsA = kRowsA / K::kRPL;
   static constexpr int kAI = (kLoadsA + kWaves - 1) / kWaves;   // A loads of waves 0 .. kARem - 1
   static constexpr int kARem = kLoadsA % kWaves;                // (the others issue kAI - 1 if > 0)
-  static constexpr int kBI = kBN / K::kRPL / kWaves;            // weight loads per wave
+  static constexpr int kBI = BN / K::kRPL / kWaves;             // weight loads per wave
   static_assert(kRowsA % K::kRPL == 0, "whole loads of A rows");
-  static_assert(kBN % (K::kRPL * kWaves) == 0, "weight rows split evenly over the waves");
+  static_assert(BN % (K::kRPL * kWaves) == 0, "weight rows split evenly over the waves");
   static_assert((kStages - 2) * (kAI + kBI) < 64, "loads in flight fit the wait counter");
 };
 
-template <int MB, int EPI>
+template <int MB, int EPI, int BN>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   static_assert(MB >= 1 && MB <= kMBW, "16-row blocks per wave row");
-  using G = StageGeom<MB>;
+  static_assert(BN == kBN || (BN == kBNWide && MB <= kMBWide), "tile shape");
+  using G = StageGeom<MB, BN>;
   constexpr int BK = G::kBK;
   using K = KGeom<BK>;
   constexpr int WN = kPlanWaveCols;
-  constexpr int kNB = kBN / (16 * WN);  // 16-column blocks per wave
+  constexpr int kNB = BN / (16 * WN);   // 16-column blocks per wave
   constexpr bool kGlu = EPI == kEpiSwiGLU;
   constexpr int kNSt = G::kStages;
   // One array per stage: the compiler then knows that reading one stage does not depend on the
@@ -147,7 +159,7 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
   const int split = rest % p.splits;
   const int n_tile = rest / p.splits;
   const int m0 = m_tile * G::kRowsA;
-  const int n0 = n_tile * (kGlu ? kBN / 2 : kBN);
+  const int n0 = n_tile * (kGlu ? BN / 2 : BN);
   const int nk = g.k / kSplitK;
   const int kb = (int)((long long)split * nk / p.splits) * (kSplitK / BK);   // in BK-deep k-tiles
   const int ke = (int)((long long)(split + 1) * nk / p.splits) * (kSplitK / BK);
@@ -199,7 +211,7 @@ void gemm_bf16_rows(GemmArgs g, GemmPlan p) {
       }
     }
     const bf16_t *Wp = second ? W1 : W0;
-    // kRowsA is a multiple of 16, so the weight block's rows swizzle like rows 0..kBN-1
+    // kRowsA is a multiple of 16, so the weight block's rows swizzle like rows 0..BN-1
     const int chunk = swz_slot<BK>(row, lslot) * 8;
     if (g.w_kmajor) {
       const int slab = second ? g.w_slab1 : g.w_slab0;
@@ -405,9 +417,9 @@ __global__ __launch_bounds__(256) void pack_kmajor(const bf16_t *__restrict__ sr
   *reinterpret_cast<uint4 *>(dst + ((size_t)(c / w) * rows + r) * w + c % w) = v;
 }
 
-template <int MB, int EPI>
+template <int MB, int EPI, int BN>
 hipError_t run_bf16_mb(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_bf16_rows<MB, EPI>), dim3(p.grid), dim3(64 * kWaves), 0, s, g, p);
+  hipLaunchKernelGGL((gemm_bf16_rows<MB, EPI, BN>), dim3(p.grid), dim3(64 * kWaves), 0, s, g, p);
   return hipGetLastError();
 }
 
@@ -418,7 +430,13 @@ hipError_t run_bf16(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
     return hipErrorInvalidValue;
   } else {
     if (p.wn != kPlanWaveCols) return hipErrorInvalidValue;
-    if (p.mbw == MB) return run_bf16_mb<MB, EPI>(g, p, s);
+    if (p.mbw == MB) {
+      if (p.bn == kBN) return run_bf16_mb<MB, EPI, kBN>(g, p, s);
+      if constexpr (kWideTiles && MB >= (kMBWide + 1) / 2 && MB <= kMBWide) {
+        if (p.bn == kBNWide) return run_bf16_mb<MB, EPI, kBNWide>(g, p, s);
+      }
+      return hipErrorInvalidValue;
+    }
     return run_bf16<EPI, MB + 1>(g, p, s);
   }
 }
@@ -443,6 +461,7 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
     return p;
   }
   p.wn = kPlanWaveCols;
+  p.bn = kBN;
   const int nk = k / kSplitK;
   // The split count and the epilogue form depend on the weight shape only, never on the number of
   // batch rows: a row's k-sum is then cut at the same points whatever else is in the batch, so a
@@ -513,6 +532,17 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
     p.m_tiles = mt_short;
     p.mbw = mb_short;
   }
+  // Wide tiles: one 576-row tile of 289..576 rows whose product width is a whole number of
+  // 256-column stripes (128 output columns of a fused gate|up tile) becomes two 288-row tiles of
+  // twice the columns: the same workgroups, k-splits and k-sum order.
+  const int tile_cols = p.epi == kEpiSwiGLU ? kBN / 2 : kBN;
+  const int width = p.epi == kEpiPartial && epi == kEpiSwiGLU ? 2 * n_out : n_out;
+  if (kWideTiles && p.m_tiles == 1 && m > 16 * kMBWide * kWM && width % (2 * tile_cols) == 0) {
+    p.bn = kBNWide;
+    p.n_tiles /= 2;
+    p.m_tiles = 2;
+    p.mbw = ((m + 1) / 2 + 31) / 32;
+  }
   const int total = p.m_tiles * p.n_tiles * p.splits;
   p.per_xcd = (total + 7) / 8;
   p.grid = 8 * p.per_xcd;
@@ -522,19 +552,16 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
 int plan_gemm_tail(int type, int epi, int m, int n_out, int k, int cus, GemmPlan *main, GemmPlan *tail) {
   if (type != kBF16 || (epi != kEpiSwiGLU && epi != kEpiGelu)) return 0;
   const GemmPlan whole = plan_gemm(type, epi, m, n_out, k, cus);
-  if (whole.epi == kEpiPartial || whole.n_tiles <= cus) return 0;
+  // (counted in 128-column stripes: a wide tile covers two)
+  if (whole.epi == kEpiPartial || whole.n_tiles * (whole.bn / kBN) <= cus) return 0;
   const int n_main = cus * (epi == kEpiSwiGLU ? kBN / 2 : kBN);
   if (n_main >= n_out) return 0;
   const GemmPlan mp = plan_gemm(type, epi, m, n_main, k, cus);
   if (mp.epi == kEpiPartial) return 0;
   const int n_tail = n_out - n_main;
-  GemmPlan tp = plan_gemm(type, kEpiPartial, m, epi == kEpiSwiGLU ? 2 * n_tail : n_tail, k, cus);
-  // Both parts read the one input, laid out for the main part's stage depth: the tail takes the
-  // main part's row tiles.
-  tp.m_tiles = mp.m_tiles;
-  tp.mbw = mp.mbw;
-  tp.per_xcd = (tp.m_tiles * tp.n_tiles * tp.splits + 7) / 8;
-  tp.grid = 8 * tp.per_xcd;
+  const GemmPlan tp = plan_gemm(type, kEpiPartial, m, epi == kEpiSwiGLU ? 2 * n_tail : n_tail, k, cus);
+  // Both parts read the one input, k-tile-major at their (common) stage depth.
+  if (stage_depth(tp.mbw) != stage_depth(mp.mbw)) return 0;
   *main = mp;
   *tail = tp;
   return n_main;

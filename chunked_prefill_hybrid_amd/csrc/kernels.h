@@ -73,9 +73,10 @@ struct GemmArgs {
 };
 
 // Launch shape of one GEMM: m_tiles x n_tiles output tiles, each k range cut into `splits`;
-// mbw = 16-row blocks per wave row; wn = wave columns (4: 8 waves, 2: 4 waves); the grid is
+// mbw = 16-row blocks per wave row; wn = wave columns (4: 8 waves, 2: 4 waves); bn = product
+// columns per tile (128, or 256 for the wide tiles of 289..576-row batches); the grid is
 // 8 * per_xcd workgroups.
-struct GemmPlan { int epi, m_tiles, n_tiles, splits, mbw, wn, per_xcd, grid; };
+struct GemmPlan { int epi, m_tiles, n_tiles, splits, mbw, wn, per_xcd, grid, bn; };
 // Plans a GEMM with epilogue `epi` (kEpiSwiGLU / kEpiGelu may come back as kEpiPartial when a split
 // product plus a separate activation pass is estimated faster; n is then the product width:
 // 2F for SwiGLU).  n_out is the output width of the epilogue (F for the FFN up products).

@@ -834,6 +834,7 @@ sarathi_gemm_plan gemm_info(const GemmPlan &g) {
   out.row_tiles = g.m_tiles;
   out.col_tiles = g.n_tiles;
   out.k_splits = g.splits;
+  out.tile_cols = g.epi == kEpiSwiGLU ? g.bn / 2 : g.bn;
   return out;
 }
 

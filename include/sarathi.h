@@ -414,7 +414,9 @@ typedef struct {
     int32_t row_tiles;   /* workgroup tiles along the batch rows */
     int32_t col_tiles;   /* workgroup tiles along the output columns */
     int32_t k_splits;    /* split-K factor (partials summed in split order by the next kernel) */
-} sarathi_gemm_plan;     /* 16 bytes */
+    int32_t tile_cols;   /* output columns of one tile: 128, or 256 for the two-row-tile form of
+                            289..576-row batches (a fused gate|up tile: 64 or 128 of each) */
+} sarathi_gemm_plan;     /* 20 bytes */
 
 typedef struct {
     int32_t rows;                                /* C + B */
@@ -429,7 +431,7 @@ typedef struct {
                                                     (one round of fused tiles) and this split product
                                                     the remaining FFN columns */
     uint64_t workspace_bytes;                    /* as the matching *_workspace_size */
-} sarathi_plan_info;     /* 176 bytes */
+} sarathi_plan_info;     /* 200 bytes */
 
 /* Fill *info for a forward over `batch`.  Errors: as the matching *_batch_check (without the x/y
  * requirement), or INVALID for a null info; *info is left unchanged then. */

@@ -264,11 +264,11 @@ def gemms(info):
 
 
 def test_plan_info_layout():
-    assert ctypes.sizeof(_abi.sarathi_gemm_plan) == 16
-    assert ctypes.sizeof(_abi.sarathi_plan_info) == 176
+    assert ctypes.sizeof(_abi.sarathi_gemm_plan) == 20
+    assert ctypes.sizeof(_abi.sarathi_plan_info) == 200
     assert _abi.sarathi_plan_info.chunk_splits.offset == 16
-    assert _abi.sarathi_plan_info.qkv.offset == 88 and _abi.sarathi_plan_info.up_tail.offset == 152
-    assert _abi.sarathi_plan_info.workspace_bytes.offset == 168
+    assert _abi.sarathi_plan_info.qkv.offset == 88 and _abi.sarathi_plan_info.up_tail.offset == 168
+    assert _abi.sarathi_plan_info.workspace_bytes.offset == 192
 
 
 def test_plan_of_hybrid_batch(lib):
@@ -288,15 +288,23 @@ def test_plan_of_hybrid_batch(lib):
 
 def test_gemm_plan_independent_of_batch_rows(lib):
     """Split-K counts and epilogues depend on the weight shape alone, so a row's k-sum is cut at the
-    same points in a one-decode batch and in a hybrid batch of several hundred rows."""
+    same points in a one-decode batch and in a hybrid batch of several hundred rows.  Batches of
+    289..576 rows take two 288-row tiles of twice the columns instead of one 576-row tile: the same
+    workgroups, splits and output columns."""
     d = desc13b()
     plans = []
     for kw in (dict(C=0, lens=(10,)), dict(C=0, cap=8192, lens=(4000,) * 48),
                dict(C=256, off=768, cap=1024, lens=(1024,) * 18), dict(C=512, off=7680, cap=8192, lens=(4000,) * 48)):
         b, keep = batch(**kw)
         info = _abi.plan_describe(d, b)
-        assert info.rows == kw["C"] + len(kw["lens"])
-        plans.append([(g.epilogue, g.k_splits, g.col_tiles) for g in gemms(info)])
+        T = kw["C"] + len(kw["lens"])
+        assert info.rows == T
+        plans.append([(g.epilogue, g.k_splits, g.col_tiles * g.tile_cols) for g in gemms(info)])
+        wide = T > 288
+        for g, narrow_tiles in zip(gemms(info), (3 * 5120 // 128, 5120 // 128, 13824 // 64, 5120 // 128)):
+            assert g.row_tiles == (2 if wide else 1)
+            assert g.tile_cols == (2 if wide else 1) * (64 if g.epilogue == 2 else 128)
+            assert g.row_tiles * g.col_tiles == narrow_tiles
     assert all(p == plans[0] for p in plans)
 
 
@@ -375,9 +383,10 @@ def test_plan_wide_ffn_main_and_tail(lib):
     for C, lens in ((512, (1024,) * 32), (0, (100,)), (257, (1024,) * 32), (1, ())):
         b, keep = batch(C=C, off=0, cap=max(C, 1), lens=lens)
         info = _abi.plan_describe(d33, b)
-        assert info.up.epilogue == 2 and info.up.col_tiles == 256 and info.up.k_splits == 1
+        assert info.up.epilogue == 2 and info.up.k_splits == 1
+        assert info.up.col_tiles * info.up.tile_cols == 256 * 64 and info.up.row_tiles * info.up.col_tiles == 256
         t = info.up_tail
-        assert t.epilogue == 1 and t.col_tiles == 2 * 1536 // 128 and t.k_splits > 1
+        assert t.epilogue == 1 and t.col_tiles * t.tile_cols == 2 * 1536 and t.k_splits > 1
         tails.add(t.k_splits)
     assert len(tails) == 1                    # the tail's k-sum cut does not depend on the rows
     b, keep = batch(C=256, off=768, cap=1024, lens=(1024,) * 18)
