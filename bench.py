@@ -130,9 +130,13 @@ def load_traffic(stage, workload_key):
 
 
 class DeviceClock:
-    """Average shader clock over enqueued work: one single-thread kernel before and one after it each
-    sample the shader-clock timestamp counter (s_memtime) and the 100 MHz real-time counter
-    (s_memrealtime); the clock is 100 MHz x (timestamp delta) / (real-time delta)."""
+    """Average shader clock over enqueued work: a kernel before and one after it each sample, on every
+    compute unit it reaches, that unit's shader-clock timestamp counter (s_memtime) and the 100 MHz
+    real-time counter (s_memrealtime).  Per unit the clock is 100 MHz x (timestamp delta) / (real-time
+    delta); the figure is the median over the units sampled both times (each unit counts on its
+    own, so samples of two different units are never paired)."""
+
+    SLOTS = 2048
 
     def __init__(self, stream):
         import torch
@@ -140,21 +144,33 @@ class DeviceClock:
         from chunked_prefill_hybrid_amd import _abi
         self._abi = _abi
         self.stream = stream
-        self.buf = torch.zeros(4, dtype=torch.int64, device="cuda")
+        self.buf = torch.zeros(4 * self.SLOTS, dtype=torch.int64, device="cuda")
 
     def start(self):
         self._abi.sarathi_clock_sample(self.buf.data_ptr(), self.stream)
 
     def stop(self):
-        self._abi.sarathi_clock_sample(self.buf.data_ptr() + 16, self.stream)
+        self._abi.sarathi_clock_sample(self.buf.data_ptr() + 16 * self.SLOTS, self.stream)
+
+    def per_unit(self):
+        v = [int(x) for x in self.buf.cpu().tolist()]
+        before, after = v[:2 * self.SLOTS], v[2 * self.SLOTS:]
+        out = []
+        for u in range(self.SLOTS):
+            t0, r0, t1, r1 = before[2 * u], before[2 * u + 1], after[2 * u], after[2 * u + 1]
+            if r0 and r1 > r0:
+                out.append((100.0 * (t1 - t0) / (r1 - r0), (r1 - r0) / 1e5))
+        return out
 
     def summary(self):
-        t0, r0, t1, r1 = [int(v) for v in self.buf.cpu().tolist()]
-        if r1 <= r0:
-            return {"source": "s_memtime / s_memrealtime", "error": "no real-time interval"}
-        return {"source": "s_memtime / s_memrealtime around the timed steps",
-                "gfx_mhz_avg": round(100.0 * (t1 - t0) / (r1 - r0), 1),
-                "interval_ms": round((r1 - r0) / 1e5, 3)}
+        units = self.per_unit()
+        if not units:
+            return {"source": "s_memtime / s_memrealtime per compute unit", "error": "no real-time interval"}
+        mhz = sorted(m for m, _ in units)
+        return {"source": "s_memtime / s_memrealtime per compute unit around the timed steps",
+                "gfx_mhz_avg": round(statistics.median(mhz), 1),
+                "gfx_mhz_p10_p90": [round(mhz[len(mhz) // 10], 1), round(mhz[(9 * len(mhz)) // 10], 1)],
+                "units": len(mhz), "interval_ms": round(max(s for _, s in units), 3)}
 
 
 def host_cpu():

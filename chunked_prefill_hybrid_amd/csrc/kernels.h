@@ -203,8 +203,11 @@ hipError_t launch_attn_fused(int d, const void *q, int ld_q, int nh, const Chunk
 constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
 hipError_t noalloc_scratch(int device, void **out);
 
-// One thread writes the shader-clock timestamp (s_memtime) and the 100 MHz real-time counter
-// (s_memrealtime) to out[0], out[1].
+// kClockWorkgroups single-wave workgroups; one running on compute unit u (slot u = XCD * 256 + bits
+// 15:8 of its HW_ID) writes the unit's shader-clock timestamp (s_memtime) and the 100 MHz real-time
+// counter (s_memrealtime) to out[2u], out[2u + 1] (out: kClockSlots pairs).
+constexpr int kClockSlots = 2048;
+constexpr int kClockWorkgroups = 4096;
 hipError_t launch_clock_sample(uint64_t *out, hipStream_t s);
 
 // Zero-fill rows [row0, row1) of a [*, cols] storage matrix (row stride ld).

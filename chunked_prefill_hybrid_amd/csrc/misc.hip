@@ -28,17 +28,26 @@ __global__ __launch_bounds__(256) void widen_kmajor_rows(const T *src, int w, in
     d[c] = to_f32(src[((size_t)(c / w) * rows_alloc + r) * w + (c % w)]);
 }
 
+// The shader-clock counter is not common to a chip, nor to an XCD (pairs taken on different compute
+// units of one XCD measured 2.0 to 3.4 GHz over the same few milliseconds), so a sample holds one
+// (s_memtime, s_memrealtime) pair per compute unit: kClockWorkgroups single-wave workgroups spread
+// over the units, each writing its pair to the slot of the unit it runs on, from the XCC_ID hardware
+// register (hwreg 20, bits 3:0) and bits 15:8 of HW_ID (hwreg 4: compute unit, shader array and
+// shader engine).  Workgroups that share a unit write the same slot; either pair serves.
 __global__ __launch_bounds__(64) void clock_sample(uint64_t *out) {
   if (threadIdx.x == 0) {
-    out[0] = __builtin_amdgcn_s_memtime();
-    out[1] = __builtin_amdgcn_s_memrealtime();
+    const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;
+    const int unit = (__builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4) >> 8) & 255;
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    const uint64_t r = __builtin_amdgcn_s_memrealtime();
+    *reinterpret_cast<ulonglong2 *>(&out[2 * (xcc * 256 + unit)]) = make_ulonglong2(t, r);
   }
 }
 
 }  // namespace
 
 hipError_t launch_clock_sample(uint64_t *out, hipStream_t s) {
-  hipLaunchKernelGGL(clock_sample, dim3(1), dim3(64), 0, s, out);
+  hipLaunchKernelGGL(clock_sample, dim3(kClockWorkgroups), dim3(64), 0, s, out);
   return hipGetLastError();
 }
 

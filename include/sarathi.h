@@ -396,11 +396,15 @@ sarathi_status sarathi_paged_forward_timed(sarathi_layer *layer, const sarathi_p
  * timer.  Errors: INVALID, HIP. */
 sarathi_status sarathi_timer_read(sarathi_timer *timer, double *total_ms, int32_t *count);
 
-/* Enqueues on `stream` one single-thread kernel that writes two 64-bit counters to the device
- * buffer `out` (uint64_t[2]): out[0] = the shader-clock timestamp counter (s_memtime), out[1] = the
- * constant 100 MHz real-time counter (s_memrealtime).  Two samples taken around enqueued work give
- * the average shader clock over it: 100 MHz x (delta out[0]) / (delta out[1]).  For measurement only.
- * Errors: INVALID (out is NULL), HIP. */
+/* Enqueues on `stream` one kernel of 4096 single-wave workgroups spread over the compute units.  A
+ * workgroup on compute unit u writes two 64-bit counters of that unit to the device buffer `out`
+ * (uint64_t[4096], 2048 slots of two): out[2u] = the shader-clock timestamp counter (s_memtime),
+ * out[2u+1] = the constant 100 MHz real-time counter (s_memrealtime), where u = 256 * XCD id + bits
+ * 15:8 of the wave's HW_ID register (compute unit, shader array, shader engine).  Slots of units no
+ * workgroup ran on are left unchanged (the caller zeroes the buffer first).  Each compute unit
+ * counts on its own, so two samples taken around enqueued work give the average shader clock over
+ * it for each unit present in both: 100 MHz x (delta out[2u]) / (delta out[2u+1]).  For
+ * measurement only.  Errors: INVALID (out is NULL), HIP. */
 sarathi_status sarathi_clock_sample(uint64_t *out, void *stream);
 
 /* ---- Launch plan (inspection) -------------------------------------------------------------------
