@@ -56,8 +56,10 @@ class HybridLayer:
     """One decoder layer bound to caller-owned device weights.
 
     weights: dict with w_qkv [3A,H], w_o [H,A], w_gate [F,H] (llama), w_up [F,H], w_down [H,F] in the
-    storage dtype, and float32 norm1_w, norm2_w (+ norm1_b, norm2_b for gpt).  The tensors must stay
-    alive and unchanged while the layer exists (the wrapper keeps references)."""
+    storage dtype, and float32 norm1_w, norm2_w (+ norm1_b, norm2_b for gpt).  A bf16 layer copies
+    the five projection weights into its own packed layout at create; the norm weights (and every
+    weight of a float32 layer) must stay alive and unchanged while the layer exists (the wrapper
+    keeps references to all of them)."""
 
     def __init__(self, shape, weights: dict, max_tokens: int, max_pos: int):
         self.shape = shape

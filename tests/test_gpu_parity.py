@@ -245,6 +245,30 @@ def test_run_twice_bitwise():
     layer.close()
 
 
+@pytest.mark.parametrize("shape", [MID, MID_GPT], ids=lambda s: s.name)
+def test_projection_weights_copied_at_create(shape):
+    """A bf16 layer packs its projection weights at create and never reads the caller's projection
+    buffers again: overwriting them with NaN after create leaves the forward's output unchanged
+    (bit for bit) and still equal to the oracle's."""
+    gu.say(f"case weights copied at create {shape.name}")
+    w, b = case(shape, 40, 24, [7, 90], seed=9)
+    ref = oracle.layer_forward(shape, w, b)
+    wd = gu.upload_weights(shape, w)
+    layer = hl.HybridLayer(shape, wd, max_tokens=42, max_pos=512)
+    db = gu.upload_batch(shape, b)
+    gu.run(layer, db, dump=False)
+    y1 = db["y"].clone()
+    for name in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"):
+        if wd.get(name) is not None:
+            wd[name].fill_(float("nan"))
+    torch.cuda.synchronize()
+    db = gu.upload_batch(shape, b)   # fresh caches: the first forward appended its rows
+    dd = gu.run(layer, db)
+    assert torch.equal(y1, db["y"])
+    gu.compare(shape, b, ref, db, dd, label=f"{shape.name} weights copied")
+    layer.close()
+
+
 def test_capacity_error_writes_nothing():
     gu.say("case capacity error")
     w, b = case(MID, 8, 0, [5], seed=5, extra=0)
