@@ -124,8 +124,9 @@ typedef struct sarathi_layer sarathi_layer;   /* opaque, immutable after create 
 /* Creates a layer handle for the current HIP device.  Copies *desc.  Allocates the device RoPE
  * cos/sin table [max_pos, head_dim/2] (LLAMA), built on the host in float64, and in bf16 mode one
  * device buffer holding the packed copies of the projection weights (as large as the five weights),
- * filled by kernels on the null stream before this call returns; float32 layers keep the weight
- * pointers.  Errors: INVALID (null pointers, non-positive sizes), UNSUPPORTED (head_dim not 64/128,
+ * filled by kernels on the null stream before this call returns (the caller's weights must be
+ * fully written when the call is made: the copy is ordered after earlier work on the null stream
+ * only); float32 layers keep the weight pointers.  Errors: INVALID (null pointers, non-positive sizes), UNSUPPORTED (head_dim not 64/128,
  * widths not multiples of 64, ffn not a multiple of 16 in f32 mode, hidden above 16384, a bf16
  * weight of 2^31 or more elements), NOMEM, HIP.  On error *out is set to NULL. */
 sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarathi_weights *weights,
