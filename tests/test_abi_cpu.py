@@ -109,6 +109,11 @@ def test_invalid_batches(lib, kw, status):
     (dict(dtype=1, ffn=688), _abi.SARATHI_ERR_UNSUPPORTED),   # bf16 needs ffn % 64 == 0
     (dict(ffn=680), _abi.SARATHI_ERR_UNSUPPORTED),            # f32 needs ffn % 16 == 0
     (dict(hidden=20480), _abi.SARATHI_ERR_UNSUPPORTED),       # a norm row holds at most 16384
+    # a bf16 layer's packed weights and the GEMM's steps through them take 32-bit element offsets:
+    # ffn x hidden = 131072 x 16384 = 2^31 elements is one too many, 3A x H likewise
+    (dict(dtype=1, hidden=16384, n_heads=128, head_dim=128, ffn=131072), _abi.SARATHI_ERR_UNSUPPORTED),
+    (dict(dtype=1, hidden=16384, n_heads=128, head_dim=128, ffn=131008), _abi.SARATHI_OK),
+    (dict(dtype=1, hidden=16384, n_heads=352, head_dim=128, ffn=1024), _abi.SARATHI_ERR_UNSUPPORTED),
     (dict(arch=7), _abi.SARATHI_ERR_INVALID),
     (dict(max_pos=0), _abi.SARATHI_ERR_INVALID),
 ])
