@@ -74,11 +74,12 @@ constexpr int kMBW = SARATHI_GEMM_MBW;
 #define SARATHI_GEMM_BN 128
 #endif
 constexpr int kBN = SARATHI_GEMM_BN;   // columns per tile (weight rows per stripe)
-// Wide tiles for batches of 289..576 rows: two 288-row tiles of 256 columns instead of one 576-row
-// tile of 128, the same number of workgroups and k-splits.  A workgroup then fetches half the
-// activation rows per k-tile and twice the weight rows (the two row tiles of a stripe run side by
-// side on one XCD, so the second fetch of a weight line mostly hits its L2), reads 13 instead of 20
-// LDS fragments per 36 MFMAs a wave, and keeps four LDS stages in flight instead of three.
+// Wide tiles for batches of more than 288 rows: two row tiles of at most 288 rows and 256 columns
+// instead of one of 289..576 rows and 128 columns, the same number of workgroups and k-splits.  A
+// workgroup then fetches half the activation rows per k-tile and twice the weight rows (the two row
+// tiles of a stripe run side by side on one XCD, so the second fetch of a weight line mostly hits its
+// L2), reads 13 instead of 20 LDS fragments per 36 MFMAs a wave, and keeps four LDS stages in flight
+// instead of three.
 #ifndef SARATHI_GEMM_WIDE
 #define SARATHI_GEMM_WIDE 1
 #endif
@@ -532,16 +533,17 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
     p.m_tiles = mt_short;
     p.mbw = mb_short;
   }
-  // Wide tiles: one 576-row tile of 289..576 rows whose product width is a whole number of
-  // 256-column stripes (128 output columns of a fused gate|up tile) becomes two 288-row tiles of
-  // twice the columns: the same workgroups, k-splits and k-sum order.
+  // Wide tiles: row tiles of 289..576 rows, for a product width that is a whole number of
+  // 256-column stripes (128 output columns of a fused gate|up tile), become twice as many row tiles
+  // of at most 288 rows and twice the columns: the same workgroups, k-splits and k-sum order.
   const int tile_cols = p.epi == kEpiSwiGLU ? kBN / 2 : kBN;
   const int width = p.epi == kEpiPartial && epi == kEpiSwiGLU ? 2 * n_out : n_out;
-  if (kWideTiles && p.m_tiles == 1 && m > 16 * kMBWide * kWM && width % (2 * tile_cols) == 0) {
+  const int tile_rows = (m + p.m_tiles - 1) / p.m_tiles;
+  if (kWideTiles && tile_rows > 16 * kMBWide * kWM && width % (2 * tile_cols) == 0) {
     p.bn = kBNWide;
     p.n_tiles /= 2;
-    p.m_tiles = 2;
-    p.mbw = ((m + 1) / 2 + 31) / 32;
+    p.m_tiles *= 2;
+    p.mbw = ((m + p.m_tiles - 1) / p.m_tiles + 31) / 32;
   }
   const int total = p.m_tiles * p.n_tiles * p.splits;
   p.per_xcd = (total + 7) / 8;

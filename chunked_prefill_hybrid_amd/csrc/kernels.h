@@ -74,7 +74,7 @@ struct GemmArgs {
 
 // Launch shape of one GEMM: m_tiles x n_tiles output tiles, each k range cut into `splits`;
 // mbw = 16-row blocks per wave row; wn = wave columns (4: 8 waves, 2: 4 waves); bn = product
-// columns per tile (128, or 256 for the wide tiles of 289..576-row batches); the grid is
+// columns per tile (128, or 256 for the wide tiles of batches of more than 288 rows); the grid is
 // 8 * per_xcd workgroups.
 struct GemmPlan { int epi, m_tiles, n_tiles, splits, mbw, wn, per_xcd, grid, bn; };
 // Plans a GEMM with epilogue `epi` (kEpiSwiGLU / kEpiGelu may come back as kEpiPartial when a split

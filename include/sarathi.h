@@ -419,8 +419,9 @@ typedef struct {
     int32_t row_tiles;   /* workgroup tiles along the batch rows */
     int32_t col_tiles;   /* workgroup tiles along the output columns */
     int32_t k_splits;    /* split-K factor (partials summed in split order by the next kernel) */
-    int32_t tile_cols;   /* output columns of one tile: 128, or 256 for the two-row-tile form of
-                            289..576-row batches (a fused gate|up tile: 64 or 128 of each) */
+    int32_t tile_cols;   /* output columns of one tile: 128, or 256 where row tiles of more than
+                            288 rows are split into twice as many of at most 288 rows (batches of
+                            more than 288 rows; a fused gate|up tile: 64 or 128 of each) */
 } sarathi_gemm_plan;     /* 20 bytes */
 
 typedef struct {

@@ -77,7 +77,9 @@ def run_case(shape, C, off, lens, seed=0, label=None, max_pos=None):
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (17, 384, 320), (36, 768, 256), (105, 1536, 512),
                                    (274, 640, 5120), (289, 192, 1408), (560, 256, 640),
                                    # enough columns for one round of 576-row tiles (32-deep stages)
-                                   (300, 30720, 256), (560, 30720, 512)])
+                                   (300, 30720, 256), (560, 30720, 512),
+                                   # more than 576 rows: four 192-row tiles of 256 columns per stripe
+                                   (700, 768, 512)])
 def test_gemm_bf16(m, n, k):
     gu.say(f"gemm bf16 m={m} n={n} k={k}")
     rng = np.random.default_rng(m * 7 + n)
