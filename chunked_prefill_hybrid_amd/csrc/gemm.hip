@@ -34,8 +34,8 @@ namespace sarathi {
 namespace {
 
 // Stage depth.  Every tile takes 32-deep k-tiles (64-byte LDS rows, one MFMA k-step per stage): six
-// stages of a 288-row tile, three of a 576-row one (so batches of up to 576 rows stream each weight
-// stripe once) fit in LDS.  Against 64-deep stages (128-byte LDS rows, two k-steps) for tiles of up
+// stages of a 288 x 128 tile, four of a 288 x 256 one, three of a 576 x 128 one (the row tiles of
+// products whose width is not a whole number of 256-column stripes) fit in LDS.  Against 64-deep stages (128-byte LDS rows, two k-steps) for tiles of up
 // to 288 rows, with the weights k-tile-major in both: gate/up at 274 rows 95.6 -> 84.3 us, QKV 52.4
 // -> 50.3 us, O and down within 1 us (same box, five interleaved runs each).  64-deep stages stay
 // selectable at build time (SARATHI_GEMM_MBW64 = 9) for tiles of up to 288 rows.
@@ -507,7 +507,7 @@ GemmPlan plan_gemm(int type, int epi, int m, int n_out, int k, int cus) {
       p.splits = 1;
     }
   }
-  // Row tiles: as few 576-row tiles as hold the batch.  (In a build with 64-deep stages for tiles of
+  // Row tiles: as few 576-row tiles as hold the batch (then made wide, below).  (In a build with 64-deep stages for tiles of
   // up to 288 rows, those are the alternative, and the shorter estimate of whole rounds of `cus`
   // workgroups times one workgroup's time wins: a workgroup's time grows with its rows from its
   // weight stream, about 0.55 of a 288-row workgroup at 1 row, up to 1.0 at 288 rows with 64-deep

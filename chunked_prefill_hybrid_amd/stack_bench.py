@@ -209,7 +209,7 @@ def table2(model, reps: int):
 
 
 ROW_STEP = 32      # the layer GEMMs' time rises every 32 batch rows (measured by tile_sweep)
-ROW_TILE = 576     # ... and steps up further past a 576-row tile
+ROW_TILE = 576     # ... and steps up further past 576 rows (a second round of GEMM workgroups)
 
 
 def aligned_chunks(chunk: int, nd: int):

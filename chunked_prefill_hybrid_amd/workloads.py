@@ -198,7 +198,7 @@ def workload(key: str, **batch_changes) -> Workload:
 def sweep_changes(key: str) -> List[dict]:
     """The C or B sweep a workload is measured on, as BatchSpec field changes: chunk length C for
     llama33b (tile quantization: with its 32 decodes C = 257 is one row into a new 32-row step, C = 544
-    fills a 576-row GEMM tile and C = 545 is one row past it), the number of piggybacked decodes B for
+    fills the 576 rows of one round of GEMM workgroups and C = 545 is one row past it), the number of piggybacked decodes B for
     gpt3tp8 (the P:D sweep) and llama13b."""
     b = WORKLOADS[key].batch
     if key == "llama33b":

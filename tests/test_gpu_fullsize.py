@@ -43,7 +43,7 @@ def test_full_size_workload(key):
     ("llama13b", dict(chunk_len=0)),                         # decode-only part
     ("llama13b", dict(n_decodes=0, decode_lens=())),         # chunk-only part
     ("llama33b", dict(chunk_len=257, prompt_len=257)),       # a new 32-row step (289 rows)
-    ("llama33b", dict(chunk_len=545, prompt_len=545)),       # one row past a 576-row GEMM tile
+    ("llama33b", dict(chunk_len=545, prompt_len=545)),       # one row past 576 rows: a second round of GEMM workgroups
     ("gpt3tp8", dict(n_decodes=1, decode_lens=(2048,))),     # P:D sweep end point
 ])
 def test_full_size_sweep_points(key, changes):

@@ -24,8 +24,8 @@ MID_GPT_WIDE_FFN = wl.LayerShape("mid-gpt-wide-ffn", "gpt", 512, 4, 128, 34816, 
 # Five heads: with an odd number of (row, head) pairs per row, one merge wave holds pairs of two rows.
 MID_F32_5H = wl.LayerShape("mid-llama-f32-5h", "llama", 640, 5, 128, 1408, "f32", 1e-6, 10000.0, None)
 MID_D64 = wl.LayerShape("mid-llama-d64", "llama", 256, 4, 64, 704, "bf16", 1e-6, 10000.0, None)
-# A llama-7b-sized layer: at 400+ rows every one of its GEMMs takes one 576-row tile per column
-# stripe (32-deep stages)
+# A llama-7b-sized layer: at 400+ rows every one of its GEMMs takes two row tiles of 256 columns per
+# weight stripe
 BIG = wl.LayerShape("big-llama", "llama", 4096, 32, 128, 11008, "bf16", 1e-6, 10000.0, None)
 
 
@@ -76,7 +76,7 @@ def run_case(shape, C, off, lens, seed=0, label=None, max_pos=None):
 
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (17, 384, 320), (36, 768, 256), (105, 1536, 512),
                                    (274, 640, 5120), (289, 192, 1408), (560, 256, 640),
-                                   # enough columns for one round of 576-row tiles (32-deep stages)
+                                   # enough columns for one round of two-row-tile stripes of 256 columns
                                    (300, 30720, 256), (560, 30720, 512),
                                    # more than 576 rows: four 192-row tiles of 256 columns per stripe
                                    (700, 768, 512)])
@@ -211,9 +211,9 @@ def test_edge_batches(C, off, lens):
                          ids=["bf16", "f32", "bf16-tall-tiles", "bf16-ffn-tail", "bf16-long-splits",
                               "f32-odd-heads"])
 def test_decode_row_alone_equals_in_batch(shape, C, lens):
-    """A decode row run alone (one GEMM row, 288-row tiles with 64-deep stages) equals the same
-    decode inside a batch, bit for bit; with C = 400 the batch's GEMMs take 576-row tiles with
-    32-deep stages, whose k-sums must be cut at the same points.  Alone, a decode's attention runs
+    """A decode row run alone (one GEMM row: a 32-row tile of 128 columns) equals the same decode
+    inside a batch, bit for bit; with C = 400 the batch's GEMMs take two row tiles of 256 columns,
+    whose k-sums must be cut at the same points and accumulated in the same order.  Alone, a decode's attention runs
     in the split-KV kernel's pipelined key walk; in a batch with a short chunk, in the fused kernel's
     walk (two steps of loads at a time); the long rows take 1024-key splits of four passes.  With
     five heads and a 7-row float32 chunk (whose rows take the general merge), the merge wave of the
