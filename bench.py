@@ -153,24 +153,34 @@ class DeviceClock:
         self._abi.sarathi_clock_sample(self.buf.data_ptr() + 16 * self.SLOTS, self.stream)
 
     def per_unit(self):
-        v = [int(x) for x in self.buf.cpu().tolist()]
-        before, after = v[:2 * self.SLOTS], v[2 * self.SLOTS:]
-        out = []
-        for u in range(self.SLOTS):
-            t0, r0, t1, r1 = before[2 * u], before[2 * u + 1], after[2 * u], after[2 * u + 1]
-            if r0 and r1 > r0:
-                out.append((100.0 * (t1 - t0) / (r1 - r0), (r1 - r0) / 1e5))
-        return out
+        return unit_clocks([int(x) for x in self.buf.cpu().tolist()], self.SLOTS)
 
     def summary(self):
-        units = self.per_unit()
-        if not units:
-            return {"source": "s_memtime / s_memrealtime per compute unit", "error": "no real-time interval"}
-        mhz = sorted(m for m, _ in units)
-        return {"source": "s_memtime / s_memrealtime per compute unit around the timed steps",
-                "gfx_mhz_avg": round(statistics.median(mhz), 1),
-                "gfx_mhz_p10_p90": [round(mhz[len(mhz) // 10], 1), round(mhz[(9 * len(mhz)) // 10], 1)],
-                "units": len(mhz), "interval_ms": round(max(s for _, s in units), 3)}
+        return clock_summary(self.per_unit())
+
+
+def unit_clocks(values, slots):
+    """(MHz, interval ms) per compute unit from two clock samples: values holds the first sample's
+    `slots` (s_memtime, s_memrealtime) pairs, then the second's.  A unit counts only if the first
+    sample wrote its slot (nonzero real time) and its real-time counter advanced."""
+    before, after = values[:2 * slots], values[2 * slots:4 * slots]
+    out = []
+    for u in range(slots):
+        t0, r0, t1, r1 = before[2 * u], before[2 * u + 1], after[2 * u], after[2 * u + 1]
+        if r0 and r1 > r0:
+            out.append((100.0 * (t1 - t0) / (r1 - r0), (r1 - r0) / 1e5))
+    return out
+
+
+def clock_summary(units):
+    """The bench line's gpu_clock: the median over the units, their 10th and 90th percentiles."""
+    if not units:
+        return {"source": "s_memtime / s_memrealtime per compute unit", "error": "no real-time interval"}
+    mhz = sorted(m for m, _ in units)
+    return {"source": "s_memtime / s_memrealtime per compute unit around the timed steps",
+            "gfx_mhz_avg": round(statistics.median(mhz), 1),
+            "gfx_mhz_p10_p90": [round(mhz[len(mhz) // 10], 1), round(mhz[(9 * len(mhz)) // 10], 1)],
+            "units": len(mhz), "interval_ms": round(max(s for _, s in units), 3)}
 
 
 def host_cpu():
