@@ -896,6 +896,12 @@ sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarath
   if (llama && !weights->w_gate) return fail(SARATHI_ERR_INVALID, "w_gate is required for LLAMA");
   if (!llama && (!weights->norm1_b || !weights->norm2_b))
     return fail(SARATHI_ERR_INVALID, "LayerNorm biases are required for GPT");
+  // every weight is read in 16-byte pieces (the packing copy, the GEMM, the norms)
+  const void *all[9] = {weights->w_qkv, weights->w_o, llama ? weights->w_gate : nullptr, weights->w_up,
+                        weights->w_down, weights->norm1_w, weights->norm2_w,
+                        llama ? nullptr : weights->norm1_b, llama ? nullptr : weights->norm2_b};
+  for (const void *w : all)
+    if ((uintptr_t)w % 16) return fail(SARATHI_ERR_INVALID, "weight pointer %p is not 16-byte aligned", w);
   sarathi_layer *L = new (std::nothrow) sarathi_layer();
   if (!L) return fail(SARATHI_ERR_NOMEM, "host allocation failed");
   L->desc = *desc;

@@ -71,10 +71,11 @@ typedef struct {
     int32_t max_pos;     /* every position must be < max_pos (size of the RoPE table); at most 65536 */
 } sarathi_layer_desc;
 
-/* Device pointers to caller-owned weights.  A bf16 layer copies the five projection weights at
- * create (into its own k-tile-major layout, [in/32][out][32], which its GEMM reads as whole 128-byte
- * lines) and does not read the caller's projection buffers afterwards; the norm weights, and every
- * weight of a float32 layer, are referenced and must stay valid and unchanged while the layer exists.
+/* Device pointers to caller-owned weights, each 16-byte aligned.  A bf16 layer copies the five
+ * projection weights at create (into its own k-tile-major layout, [in/32][out][32], which its GEMM
+ * reads as whole 128-byte lines) and does not read the caller's projection buffers afterwards; the
+ * norm weights, and every weight of a float32 layer, are referenced and must stay valid and
+ * unchanged while the layer exists.
  *   w_qkv [3A, H]: rows [Q | K | V], each block head-major (head h = rows h*d .. h*d+d-1 of it)
  *   w_o [H, A];  w_gate [F, H] (LLAMA only; NULL for GPT);  w_up [F, H];  w_down [H, F]
  *   norm1_w, norm2_w: float32 [H];  norm1_b, norm2_b: float32 [H] (GPT only; NULL for LLAMA) */
@@ -126,14 +127,15 @@ typedef struct sarathi_layer sarathi_layer;   /* opaque, immutable after create 
  * device buffer holding the packed copies of the projection weights (as large as the five weights),
  * filled by kernels on the null stream before this call returns (the caller's weights must be
  * fully written when the call is made: the copy is ordered after earlier work on the null stream
- * only); float32 layers keep the weight pointers.  Errors: INVALID (null pointers, non-positive sizes), UNSUPPORTED (head_dim not 64/128,
- * widths not multiples of 64, ffn not a multiple of 16 in f32 mode, hidden above 16384, a bf16
- * weight of 2^31 or more elements), NOMEM, HIP.  On error *out is set to NULL. */
+ * only); float32 layers keep the weight pointers.  Errors: INVALID (null or misaligned weight
+ * pointers, non-positive sizes), UNSUPPORTED (head_dim not 64/128, widths not multiples of 64, ffn
+ * not a multiple of 16 in f32 mode, hidden above 16384, a bf16 weight of 2^31 or more elements),
+ * NOMEM, HIP.  On error *out is set to NULL. */
 sarathi_status sarathi_layer_create(const sarathi_layer_desc *desc, const sarathi_weights *weights,
                                     sarathi_layer **out);
 
-/* Frees the handle, its RoPE table and its packed weights.  NULL is a no-op.  No call using the handle may be in flight
- * (the caller synchronises its streams first). */
+/* Frees the handle, its RoPE table and its packed weights.  NULL is a no-op.  No call using the
+ * handle may be in flight (the caller synchronises its streams first). */
 void sarathi_layer_destroy(sarathi_layer *layer);
 
 /* Host-only validation of a batch against a layer description (no HIP call).  Checks: C, B >= 0 and

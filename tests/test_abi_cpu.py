@@ -140,6 +140,21 @@ def test_create_rejects_bad_description_before_any_hip_call(lib):
     assert e.value.status == _abi.SARATHI_ERR_UNSUPPORTED
 
 
+def test_create_rejects_misaligned_weights_before_any_hip_call(lib):
+    """Every weight is read in 16-byte pieces: a pointer off a 16-byte boundary is refused (for GPT
+    the LayerNorm biases too; its gate slot is unused)."""
+    # field order: w_qkv, w_o, w_gate, w_up, w_down, norm1_w, norm1_b, norm2_w, norm2_b
+    for arch, used in ((_abi.SARATHI_ARCH_LLAMA, (0, 1, 2, 3, 4, 5, 7)),
+                       (_abi.SARATHI_ARCH_GPT, (0, 1, 3, 4, 5, 6, 7, 8))):
+        for i in used:
+            ptrs = [addr(20 + j) for j in range(9)]
+            ptrs[i] += 8
+            with pytest.raises(_abi.SarathiError) as e:
+                _abi.sarathi_layer_create(desc(arch=arch), _abi.sarathi_weights(*ptrs))
+            assert e.value.status == _abi.SARATHI_ERR_INVALID, (arch, i)
+            assert "aligned" in _abi.sarathi_last_error()
+
+
 def test_stack_rejects_empty_or_null_before_any_hip_call(lib):
     b, keep = _abi.make_stack_batch(4, 0, [(addr(2), addr(3), 64)], [[]], [], addr(0), addr(1))
     assert _abi.sarathi_stack_workspace_size([], b) == 0
