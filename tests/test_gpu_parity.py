@@ -196,6 +196,7 @@ def test_mid_bf16_head_dim_64():
     (64, 2051, [5]),                # one query block, long prefix: its keys split in two
     (0, 0, [2046, 2047, 2048, 3000]),  # decodes at the 256/1024-key split threshold
     (5, 2, [6001]),                 # a long decode: 1024-key splits, the last one ragged
+    (650, 40, [3, 0, 90, 257, 1]),  # 655 rows, past 576: four row tiles of 256 columns per stripe
 ])
 def test_edge_batches(C, off, lens):
     run_case(MID, C, off, lens, seed=C + len(lens))
