@@ -393,6 +393,23 @@ def test_plan_decode_key_split_counts(lib):
         assert _abi.plan_describe(d, b).max_key_splits == expect == bench._split_count(n), L
 
 
+def test_plan_row_tiles_past_576_rows(lib):
+    """Past 576 rows (a second round of workgroups) the row tiles stay at most 288 rows of 256
+    columns: 700 rows take four per weight stripe, 1024 rows four, with the split counts of every
+    other batch size."""
+    d = desc13b()
+    b, keep = batch(C=0, lens=(10,))
+    one = [(g.epilogue, g.k_splits) for g in gemms(_abi.plan_describe(d, b))]
+    for C in (700, 1024):
+        b, keep = batch(C=C, off=0, cap=C, lens=())
+        info = _abi.plan_describe(d, b)
+        assert info.rows == C
+        assert [(g.epilogue, g.k_splits) for g in gemms(info)] == one
+        for g, narrow_tiles in zip(gemms(info), (3 * 5120 // 128, 5120 // 128, 13824 // 64, 5120 // 128)):
+            assert g.row_tiles == 4 and g.col_tiles * 2 == narrow_tiles
+            assert g.tile_cols == (128 if g.epilogue == 2 else 256)
+
+
 def test_plan_wide_ffn_main_and_tail(lib):
     """A gate|up product of more than 256 weight stripes (llama-33b: F = 17920, 280 stripes of 64
     columns) runs its first 256 stripes as one round of fused tiles and the other 1536 columns as a
